@@ -1,0 +1,362 @@
+/*
+ * moe_oracle.c -- plain, slow, obviously-correct CPU definition of one routed
+ * mixture-of-experts FFN layer with block-scaled expert weights.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code, header, table or constant generator with the
+ * HIP library.
+ *
+ * Arithmetic: every value is decoded exactly and every sum is taken in IEEE
+ * double precision, in plain loops, in the order the definition states.
+ * Compile without -ffast-math and with -ffp-contract=off so that each float
+ * operation the definition names is exactly one rounded operation.
+ *
+ * What is computed (sources are the three pages the method is described on):
+ *   - the expert chain gate -> clamped SwiGLU -> down, per routed slot
+ *     ("memra-engine src/dsv4_ep.rs", fn chain; "memra-engine
+ *     src/bin/ep_step_fp8_gate.rs", fn reference_expert and
+ *     fn reference_grouped_projections);
+ *   - the clamped activation silu(min(g, L)) * clamp(u, -L, L)
+ *     ("spark_model glm5next_mlp/forward.rs", doc of swiglu_rows);
+ *   - the per-token combine in canonical slot order with a separate multiply
+ *     and add ("memra-engine src/bin/ep_step_fp8_gate.rs",
+ *     fn combine_down_rows_host and the combine_numeric label of
+ *     run_dynamic_owner_grouped_fp8_combine_gate);
+ *   - the expert-sorted route tables: per-expert prefix offsets, sorted row ->
+ *     token, slot -> sorted row ("spark_model glm5next_mlp/forward.rs",
+ *     struct Glm5NextMlpWorkspace);
+ *   - block-scaled E4M3 banks (one FP32 scale per 128x128 block, expert-major,
+ *     "memra-engine src/bin/ep_step_fp8_gate.rs", fn expert_matrix) and NVFP4
+ *     banks (E2M1 nibbles, one E4M3 scale per 16, one FP32 scale_2 per expert
+ *     projection; "memra-engine src/dsv4_ep.rs", fn chain strides, and
+ *     "spark_model glm5next_mlp/forward.rs", fn w4a16_gemv);
+ *   - per 1x128 group FP8 quantization of activations for the wide-M tier
+ *     ("memra-engine src/dsv4_ep.rs", EpScratch xq/xs and the act_quant_fp8
+ *     step of fn chain).
+ * Readings of points the pages leave open are listed beside the function
+ * that takes them.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Code tables                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* OCP E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits; no infinity;
+ * the only NaN encodings are S.1111.111.  Subnormals: m * 2^-9. */
+double oracle_e4m3_value(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) mag = ldexp((double)m, -9);
+    else mag = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* OCP E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; subnormal m/2. */
+double oracle_e2m1_value(uint8_t nib)
+{
+    int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* bfloat16 bits -> value (the upper half of an IEEE binary32). */
+double oracle_bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round a binary32 value to E4M3FN, nearest with ties to the even code,
+ * saturating to +-448 (finite inputs only; NaN maps to 0x7F).  The search is a
+ * plain walk over the 127 non-negative finite codes, which are increasing in
+ * value, so the result is the nearest code by construction. */
+uint8_t oracle_e4m3_encode(float v)
+{
+    double a = fabs((double)v);
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    uint8_t best = 0;
+    if (isnan(v)) return 0x7F;
+    if (a >= 448.0) return sign | 0x7E;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double lo = oracle_e4m3_value((uint8_t)c);
+        double hi;
+        if (c == 0x7E) { best = 0x7E; break; }
+        hi = oracle_e4m3_value((uint8_t)(c + 1));
+        if (a >= lo && a <= hi) {
+            double dlo = a - lo, dhi = hi - a;
+            if (dlo < dhi) best = (uint8_t)c;
+            else if (dhi < dlo) best = (uint8_t)(c + 1);
+            else best = (c & 1) ? (uint8_t)(c + 1) : (uint8_t)c; /* tie: even */
+            break;
+        }
+    }
+    return sign | best;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activation quantization for the FP8 tier                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Per row and per group of 128 consecutive columns: amax = max |x| over the
+ * group (binary32, exact); scale = amax / 448 in binary32 (1.0 when amax is 0);
+ * code = E4M3(binary32(x / scale)).  The pages give the layout (one FP32 scale
+ * per 128 activations) but not the rule; this is the plain reading where the
+ * group maximum lands on the largest finite E4M3 magnitude. */
+void oracle_quant_1x128(const float *x, int64_t rows, int64_t cols,
+                        uint8_t *q, float *s)
+{
+    int64_t groups = cols / 128;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t g = 0; g < groups; ++g) {
+            const float *xg = x + r * cols + g * 128;
+            float amax = 0.0f, scale;
+            for (int i = 0; i < 128; ++i) {
+                float a = fabsf(xg[i]);
+                if (a > amax) amax = a;
+            }
+            scale = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+            s[r * groups + g] = scale;
+            for (int i = 0; i < 128; ++i) {
+                float t = xg[i] / scale;
+                q[r * cols + g * 128 + i] = oracle_e4m3_encode(t);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Route pack                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Stable counting sort of the S = M*k route slots by expert id.
+ * Slot s = t*k + j is token t's j-th choice.  Ids in [0, E) are valid; -1
+ * means "slot unfilled"; anything else is invalid.  Neither of the latter is
+ * placed, and token_to_perm holds -1 for them.  Within an expert, slots keep
+ * ascending flat slot order (the pages name the tables but not their order
+ * inside one expert; ascending slot order makes the result unique).
+ * Returns the number of invalid ids (not counting -1). */
+int oracle_route_pack(const int32_t *ids, int32_t M, int32_t k, int32_t E,
+                      int32_t *offsets, int32_t *sorted_slot,
+                      int32_t *sorted_token, int32_t *token_to_perm,
+                      int32_t *active, int32_t *num_active)
+{
+    int64_t S = (int64_t)M * k;
+    int32_t *count = calloc((size_t)E, sizeof(int32_t));
+    int32_t *fill = calloc((size_t)E, sizeof(int32_t));
+    int invalid = 0, na = 0;
+    for (int64_t s = 0; s < S; ++s) {
+        int32_t e = ids[s];
+        if (e >= 0 && e < E) count[e]++;
+        else if (e != -1) invalid++;
+    }
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + count[e];
+    for (int64_t s = 0; s < S; ++s) {
+        int32_t e = ids[s];
+        if (e >= 0 && e < E) {
+            int32_t pos = offsets[e] + fill[e]++;
+            sorted_slot[pos] = (int32_t)s;
+            sorted_token[pos] = (int32_t)(s / k);
+            token_to_perm[s] = pos;
+        } else {
+            token_to_perm[s] = -1;
+        }
+    }
+    for (int32_t e = 0; e < E; ++e)
+        if (count[e] > 0) active[na++] = e;
+    *num_active = na;
+    free(count);
+    free(fill);
+    return invalid;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert banks                                                              */
+/* ------------------------------------------------------------------------ */
+
+enum { ORACLE_E4M3_B128 = 1, ORACLE_NVFP4_B16 = 2 };
+
+/* One projection bank for every expert, expert-major.
+ * E4M3:  codes [E][n][k] bytes; scales float [E][n/128][k/128].
+ * NVFP4: codes [E][n][k/2] bytes, element 2i in the low nibble of byte i and
+ *        element 2i+1 in the high nibble (the pages do not fix the nibble
+ *        order; low-first is the OCP packing convention); scales are E4M3
+ *        bytes [E][n][k/16]; scale2 float [E]. */
+typedef struct {
+    int32_t fmt, num_experts, n_out, k_in;
+    const uint8_t *codes;
+    const void *scales;
+    const float *scale2;
+} oracle_bank_t;
+
+/* The decode functions above, evaluated once per code so that the matrix
+ * loops do not call ldexp per element.  Filled before any parallel region. */
+static double e4m3_tab[256], e2m1_tab[16];
+static int tabs_ready = 0;
+static void fill_tables(void)
+{
+    if (tabs_ready) return;
+    for (int c = 0; c < 256; ++c) e4m3_tab[c] = oracle_e4m3_value((uint8_t)c);
+    for (int c = 0; c < 16; ++c) e2m1_tab[c] = oracle_e2m1_value((uint8_t)c);
+    tabs_ready = 1;
+}
+
+/* Exact value of W[e][n][kk]. */
+static double bank_weight(const oracle_bank_t *b, int64_t e, int64_t n,
+                          int64_t kk)
+{
+    int64_t N = b->n_out, K = b->k_in;
+    if (b->fmt == ORACLE_E4M3_B128) {
+        const float *sc = (const float *)b->scales;
+        uint8_t c = b->codes[(e * N + n) * K + kk];
+        double sblk = sc[(e * (N / 128) + n / 128) * (K / 128) + kk / 128];
+        return e4m3_tab[c] * sblk;
+    } else {
+        const uint8_t *sc = (const uint8_t *)b->scales;
+        uint8_t byte = b->codes[(e * N + n) * (K / 2) + kk / 2];
+        uint8_t nib = (kk & 1) ? (byte >> 4) : (byte & 15);
+        double s16 = e4m3_tab[sc[(e * N + n) * (K / 16) + kk / 16]];
+        return e2m1_tab[nib] * s16 * (double)b->scale2[e];
+    }
+}
+
+/* Dense dequantized copy of one expert's matrix, [n][k] doubles. */
+void oracle_dequant_expert(const oracle_bank_t *b, int32_t e, double *out)
+{
+    fill_tables();
+    for (int64_t n = 0; n < b->n_out; ++n)
+        for (int64_t kk = 0; kk < b->k_in; ++kk)
+            out[n * b->k_in + kk] = bank_weight(b, e, n, kk);
+}
+
+/* y[n] = sum_kk W[e][n][kk] * v[kk], FP64, kk ascending. */
+static void expert_matvec(const oracle_bank_t *b, int32_t e, const double *v,
+                          double *y)
+{
+    int64_t N = b->n_out, K = b->k_in;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t kk = 0; kk < K; ++kk) acc += bank_weight(b, e, n, kk) * v[kk];
+        y[n] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* The clamped SwiGLU                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* silu(min(g, L)) * clamp(u, -L, L), silu(z) = z / (1 + exp(-z)). */
+double oracle_swiglu_clamp(double g, double u, double limit)
+{
+    double gc = g < limit ? g : limit;
+    double uc = u < -limit ? -limit : (u > limit ? limit : u);
+    double silu = gc / (1.0 + exp(-gc));
+    return silu * uc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The expert FFN per routed slot                                            */
+/* ------------------------------------------------------------------------ */
+
+/* For every slot in slot_list (flat slot index s = t*k + j with a valid id):
+ *   xhat = x[t] decoded from bf16             (act_fp8 == 0), or
+ *   xhat = dec(q) * scale, (q, scale) = 1x128 quantization of x[t] (act_fp8)
+ *   g = Wg[e] xhat,  u = Wu[e] xhat            (FP64 sums)
+ *   h = swiglu_clamp(g, u, L)                  (FP64)
+ *   act_fp8: h <- dec(q) * scale of the 1x128 quantization of binary32(h)
+ *   y = Wd[e] h
+ * Outputs are row-major per listed slot: g,u,h [n_list][inter], y [n_list][hidden].
+ * Any output pointer may be NULL.  Slots whose id is not in [0, E) get zero
+ * rows. */
+void oracle_expert_slots(const oracle_bank_t *gate, const oracle_bank_t *up,
+                         const oracle_bank_t *down, const uint16_t *x_bf16,
+                         const int32_t *ids, int32_t M, int32_t k,
+                         int32_t hidden, int32_t inter, float limit,
+                         int32_t act_fp8, const int32_t *slot_list,
+                         int32_t n_list, double *g_out, double *u_out,
+                         double *h_out, double *y_out)
+{
+    double *xv = malloc(sizeof(double) * (size_t)hidden);
+    double *g = malloc(sizeof(double) * (size_t)inter);
+    double *u = malloc(sizeof(double) * (size_t)inter);
+    double *h = malloc(sizeof(double) * (size_t)inter);
+    double *y = malloc(sizeof(double) * (size_t)hidden);
+    float *tmp = malloc(sizeof(float) * (size_t)(hidden > inter ? hidden : inter));
+    uint8_t *q = malloc((size_t)(hidden > inter ? hidden : inter));
+    float *qs = malloc(sizeof(float) * (size_t)(hidden > inter ? hidden : inter) / 128);
+    (void)M;
+    fill_tables();
+    for (int32_t li = 0; li < n_list; ++li) {
+        int32_t s = slot_list[li];
+        int32_t t = s / k, e = ids[s];
+        int valid = (e >= 0 && e < gate->num_experts);
+        if (!valid) {
+            if (g_out) memset(g_out + (int64_t)li * inter, 0, sizeof(double) * inter);
+            if (u_out) memset(u_out + (int64_t)li * inter, 0, sizeof(double) * inter);
+            if (h_out) memset(h_out + (int64_t)li * inter, 0, sizeof(double) * inter);
+            if (y_out) memset(y_out + (int64_t)li * hidden, 0, sizeof(double) * hidden);
+            continue;
+        }
+        if (!act_fp8) {
+            for (int32_t i = 0; i < hidden; ++i)
+                xv[i] = oracle_bf16_value(x_bf16[(int64_t)t * hidden + i]);
+        } else {
+            for (int32_t i = 0; i < hidden; ++i)
+                tmp[i] = (float)oracle_bf16_value(x_bf16[(int64_t)t * hidden + i]);
+            oracle_quant_1x128(tmp, 1, hidden, q, qs);
+            for (int32_t i = 0; i < hidden; ++i)
+                xv[i] = oracle_e4m3_value(q[i]) * (double)qs[i / 128];
+        }
+        expert_matvec(gate, e, xv, g);
+        expert_matvec(up, e, xv, u);
+        for (int32_t i = 0; i < inter; ++i)
+            h[i] = oracle_swiglu_clamp(g[i], u[i], (double)limit);
+        if (act_fp8) {
+            for (int32_t i = 0; i < inter; ++i) tmp[i] = (float)h[i];
+            oracle_quant_1x128(tmp, 1, inter, q, qs);
+            for (int32_t i = 0; i < inter; ++i)
+                h[i] = oracle_e4m3_value(q[i]) * (double)qs[i / 128];
+        }
+        expert_matvec(down, e, h, y);
+        if (g_out) memcpy(g_out + (int64_t)li * inter, g, sizeof(double) * inter);
+        if (u_out) memcpy(u_out + (int64_t)li * inter, u, sizeof(double) * inter);
+        if (h_out) memcpy(h_out + (int64_t)li * inter, h, sizeof(double) * inter);
+        if (y_out) memcpy(y_out + (int64_t)li * hidden, y, sizeof(double) * hidden);
+    }
+    free(xv); free(g); free(u); free(h); free(y); free(tmp); free(q); free(qs);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* out[t][m] = sum over j = 0..k-1 of w[t][j] * y[t*k + j][m], slot order,
+ * multiply then add.  y is indexed by flat slot; rows of slots whose valid[]
+ * flag is 0 contribute nothing. */
+void oracle_combine(const double *y_by_slot, const float *w,
+                    const int32_t *valid, int32_t M, int32_t k, int32_t hidden,
+                    double *out)
+{
+    for (int64_t t = 0; t < M; ++t) {
+        for (int64_t m = 0; m < hidden; ++m) out[t * hidden + m] = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t s = t * k + j;
+            double wt = (double)w[s];
+            if (!valid[s]) continue;
+            for (int64_t m = 0; m < hidden; ++m) {
+                double prod = wt * y_by_slot[s * hidden + m];
+                out[t * hidden + m] += prod;
+            }
+        }
+    }
+}
