@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE FFN layer on one MI355X.
+
+A step is one full layer: moe_route_pack -> moe_expert_ffn -> moe_combine on
+one stream, inputs resident in HBM.  The headline workload is single-token
+decode (H7168, I2048, 256 block-scaled E4M3 experts, top-8, M=1); the value is
+microseconds per layer.  16 route sets are rotated across steps so that
+consecutive steps read different experts and the 256 MB last-level cache
+cannot serve a repeated working set.
+
+Printed: ONE JSON line with the contract fields, the dominant kernel's
+roofline (algorithmic bytes / its average duration from HIP events recorded
+on its own stream during a stage-timing pass), and the CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA (no sparsity)
+METRIC = "µs/MoE layer + weight-read GB/s (% HBM peak) at M=1; tokens/s at M=4096"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_e4m3_m1")
+    ap.add_argument("--route-sets", type=int, default=16)
+    ap.add_argument("--also", default="verify_e4m3_m8,nvfp4_m1,nvfp4_m16",
+                    help="comma-separated extra workloads reported under 'also' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# HIP events on the stream the kernels run on (ctypes, no torch wrapper)
+# --------------------------------------------------------------------------
+class Hip:
+    def __init__(self):
+        self.h = C.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.h.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def events(self, n):
+        arr = (C.c_void_p * n)()
+        for i in range(n):
+            p = C.c_void_p()
+            assert self.h.hipEventCreate(C.byref(p)) == 0
+            arr[i] = p.value
+        return arr
+
+    def record(self, ev, stream):
+        assert self.h.hipEventRecord(ev, stream) == 0
+
+    def ms(self, a, b):
+        f = C.c_float()
+        assert self.h.hipEventSynchronize(b) == 0
+        assert self.h.hipEventElapsedTime(C.byref(f), a, b) == 0
+        return f.value
+
+
+def algorithmic_bytes(wl, banks, ids):
+    """Bytes a layer must move at least: codes + scales of every expert the
+    routes select (each once), x read, out written, ids and weights read."""
+    import numpy as np
+    E = wl.experts
+    used = np.unique(ids[(ids >= 0) & (ids < E)])
+    per_expert = sum(b.nbytes_per_expert() for b in banks)
+    gu_per_expert = banks[0].nbytes_per_expert() + banks[1].nbytes_per_expert()
+    M = ids.shape[0]
+    io = M * wl.hidden * 2 + M * wl.hidden * 4 + ids.size * 8
+    return len(used) * per_expert + io, len(used) * gu_per_expert + M * wl.hidden * 2, len(used)
+
+
+def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True):
+    import numpy as np
+    import torch
+
+    import workloads
+    from fp4_block_scaled_amd import binding as B
+    from fp4_block_scaled_amd.layer import MoeLayer
+
+    x = workloads.make_x(wl, "cuda")
+    sets = [workloads.make_routes(wl, r) for r in range(route_sets)]
+    ids_d = [torch.from_numpy(s[0]).cuda() for s in sets]
+    w_d = [torch.from_numpy(s[1]).cuda() for s in sets]
+    cb = [B.Bank.from_device_bank(b) for b in banks]
+    layer = MoeLayer(*cb, wl.hidden, wl.inter, wl.top_k, wl.M, wl.limit)
+    mode = B.moe_resolve_mode(wl.M, wl.fmt)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    for i in range(warmup):
+        layer(x, ids_d[i % route_sets], w_d[i % route_sets])
+    torch.cuda.synchronize()
+    ref = layer(x, ids_d[0], w_d[0]).clone()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` layers, events on the layer's stream
+    e0, e1 = hip.events(2)
+    torch.cuda.synchronize()
+    hip.record(e0, sh)
+    for i in range(steps):
+        layer(x, ids_d[i % route_sets], w_d[i % route_sets])
+    hip.record(e1, sh)
+    torch.cuda.synchronize()
+    total_ms = hip.ms(e0, e1)
+    us_layer = total_ms * 1000.0 / steps
+
+    # output must not drift across runs (deterministic kernels)
+    again = layer(x, ids_d[0], w_d[0])
+    torch.cuda.synchronize()
+    stable = bool(torch.equal(again.view(torch.int32), ref.view(torch.int32)))
+
+    stages = None
+    if want_stages:
+        nst = B.moe_set_stage_events(None, wl.fmt, wl.hidden, wl.inter, mode)
+        per = nst + 3       # route start, ffn stage marks (nst+1), combine end
+        evs = [hip.events(per) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            ev = evs[i]
+            sub = (C.c_void_p * (nst + 1))(*[ev[1 + j] for j in range(nst + 1)])
+            evs[i] = (ev, sub)
+            hip.record(ev[0], sh)
+            B.moe_set_stage_events(sub, wl.fmt, wl.hidden, wl.inter, mode)
+            layer(x, ids_d[i % route_sets], w_d[i % route_sets])
+            hip.record(ev[per - 1], sh)
+        B.moe_set_stage_events(None, wl.fmt, wl.hidden, wl.inter, mode)
+        torch.cuda.synchronize()
+        names = ["route_pack", "gateup_gemv", "swiglu", "down_gemv", "combine"]
+        acc = np.zeros(per - 1)
+        for ev, _ in evs:
+            for j in range(per - 1):
+                acc[j] += hip.ms(ev[j], ev[j + 1])
+        stages = {names[j]: float(acc[j] * 1000.0 / steps) for j in range(per - 1)}
+
+    alg = [algorithmic_bytes(wl, banks, s[0]) for s in sets]
+    alg_layer = float(np.mean([a[0] for a in alg]))
+    alg_gateup = float(np.mean([a[1] for a in alg]))
+    uniq = float(np.mean([a[2] for a in alg]))
+    return dict(us_layer=us_layer, ms_total=total_ms, stable=stable, stages=stages,
+                alg_layer_bytes=alg_layer, alg_gateup_bytes=alg_gateup, unique_experts=uniq,
+                layer=layer, x=x, sets=sets)
+
+
+def cpu_baseline(wl, banks, x, sets, budget_s):
+    """The oracle, as it stands, on whole layers of the same workload."""
+    import numpy as np
+
+    import oracle  # CPU baseline leg only
+    import torch
+    E = wl.experts
+    times = []
+    n = 0
+    for ids, w, _ in sets:
+        used = np.unique(ids[(ids >= 0) & (ids < E)])
+        hb = []
+        for b in banks:
+            sub = b.select(used)
+            hb.append(oracle.Bank(sub.fmt, sub.codes.cpu().numpy(), sub.scales.cpu().numpy(),
+                                  None if sub.scale2 is None else sub.scale2.cpu().numpy()))
+        remap = np.searchsorted(used, ids).astype(np.int32)
+        xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.moe_layer(*hb, xb, remap, w, wl.limit, False)
+        times.append(time.perf_counter() - t0)
+        n += 1
+        if sum(times) >= budget_s:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=float(np.mean(times) * 1e6), unit="us/layer", cores=threads, kind="oracle",
+                sample=f"{n} whole layers of {wl.name} (route sets 0..{n - 1}), FP64, "
+                       f"selected experts copied to host before timing")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer keeps every "
+              f"expert resident on a single MI355X and has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import numpy as np
+    import torch
+
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hip = Hip()
+
+    wl = workloads.WORKLOADS[args.workload]
+    t0 = time.time()
+    banks = workloads.make_banks(wl, "cuda")
+    torch.cuda.synchronize()
+    print(f"# banks for {wl.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    r = measure(wl, banks, args.steps, args.warmup, args.route_sets, hip)
+    print(f"# {wl.name}: {r['us_layer']:.2f} us/layer, stages {r['stages']}", file=sys.stderr,
+          flush=True)
+
+    gbps = r["alg_layer_bytes"] / (r["us_layer"] * 1e-6) / 1e9
+    gu_us = r["stages"]["gateup_gemv"]
+    gu_gbps = r["alg_gateup_bytes"] / (gu_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(r["us_layer"], 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_total"] / args.steps, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3*bf16->f32" if wl.fmt == 1 else "e2m1*bf16->f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "hidden": wl.hidden, "inter": wl.inter,
+                   "experts": wl.experts, "top_k": wl.top_k, "M": wl.M,
+                   "route_sets": args.route_sets, "unique_experts": r["unique_experts"]},
+        "weight_read_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(wl.M / (r["us_layer"] * 1e-6), 1),
+        "stages_us": {k: round(v, 3) for k, v in r["stages"].items()},
+        "output_stable": r["stable"],
+        "roofline": {"kernel": "gemv_gateup", "bound": "hbm", "achieved": round(gu_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
+                     "alg_bytes_per_launch": round(r["alg_gateup_bytes"]),
+                     "avg_launch_us": round(gu_us, 3)},
+    }
+    also = {}
+    for name in [a for a in args.also.split(",") if a]:
+        w2 = workloads.WORKLOADS[name]
+        same = (w2.hidden, w2.inter, w2.experts, w2.fmt) == (wl.hidden, wl.inter, wl.experts, wl.fmt)
+        b2 = banks if same else workloads.make_banks(w2, "cuda")
+        r2 = measure(w2, b2, max(20, args.steps // 2), args.warmup, args.route_sets, hip)
+        g2 = r2["alg_layer_bytes"] / (r2["us_layer"] * 1e-6) / 1e9
+        also[name] = {"us_layer": round(r2["us_layer"], 3), "weight_read_GBps": round(g2, 1),
+                      "hbm_frac": round(g2 / HBM_PEAK_GBPS, 4),
+                      "tokens_per_s": round(w2.M / (r2["us_layer"] * 1e-6), 1),
+                      "unique_experts": r2["unique_experts"],
+                      "stages_us": {k: round(v, 3) for k, v in r2["stages"].items()},
+                      "output_stable": r2["stable"]}
+        print(f"# {name}: {r2['us_layer']:.2f} us/layer", file=sys.stderr, flush=True)
+        if not same:
+            del b2
+        del r2
+        torch.cuda.empty_cache()
+    if also:
+        line["also"] = also
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, banks, r["x"], r["sets"], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

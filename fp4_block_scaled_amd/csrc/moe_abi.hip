@@ -1,0 +1,291 @@
+// moe_abi.hip -- the C ABI of libmoe: argument checks, workspace carving and
+// tier dispatch for the routed MoE FFN layer (declared in include/moe.h).
+//
+// Everything here runs on the host before any launch; a failed check returns
+// a status without touching the GPU.  The calls never allocate, synchronise
+// or read device memory back, so a caller may capture them in a HIP graph.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local void *const *g_stage_events = nullptr;
+thread_local int32_t g_stage_n = 0;
+
+// Records stage event i (if stage timing is on and i is in range).
+void stage_mark(int i, hipStream_t s)
+{
+    if (g_stage_events && i < g_stage_n && g_stage_events[i])
+        (void)hipEventRecord((hipEvent_t)g_stage_events[i], s);
+}
+
+moe_status_t fail(moe_status_t code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+moe_status_t hip_fail(hipError_t e, const char *what)
+{
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+int64_t gemv_gateup_slices(int32_t fmt, int32_t hidden)
+{
+    const int slice = fmt == MOE_W_NVFP4_B16 ? kGemvSliceNVFP4 : kGemvSliceE4M3;
+    return (hidden + slice - 1) / slice;
+}
+
+// FFN scratch of the GEMV tier for S slots.
+size_t gemv_scratch_bytes(int64_t S, int32_t hidden, int32_t inter, int32_t fmt)
+{
+    const int64_t nks = gemv_gateup_slices(fmt, hidden);
+    const int64_t nkd = gemv_down_slices(inter);
+    size_t b = moe::align256(sizeof(float) * (size_t)(nks * S * 2 * inter));   // gate/up partials
+    b += moe::align256(sizeof(float) * (size_t)(S * inter));                   // h
+    if (nkd > 1) b += moe::align256(sizeof(float) * (size_t)(nkd * S * hidden)); // down slices
+    return b;
+}
+
+struct GemvScratch {
+    float *partials, *h, *down_slices;
+};
+
+GemvScratch carve_gemv(char *base, int64_t S, int32_t hidden, int32_t inter, int32_t fmt)
+{
+    GemvScratch s;
+    const int64_t nks = gemv_gateup_slices(fmt, hidden);
+    s.partials = (float *)base;
+    base += moe::align256(sizeof(float) * (size_t)(nks * S * 2 * inter));
+    s.h = (float *)base;
+    base += moe::align256(sizeof(float) * (size_t)(S * inter));
+    s.down_slices = gemv_down_slices(inter) > 1 ? (float *)base : nullptr;
+    return s;
+}
+
+bool sizes_ok(int32_t M, int32_t top_k, int32_t E)
+{
+    return M >= 1 && top_k >= 1 && E >= 1 && top_k <= E && E <= MOE_MAX_EXPERTS &&
+           (int64_t)M * top_k < (1ll << 31);
+}
+
+int32_t resolve(int32_t M, int32_t fmt, int32_t requested)
+{
+    if (requested == MOE_MODE_GEMV_A16 || requested == MOE_MODE_GEMM_A8) return requested;
+    (void)fmt;
+    return M <= MOE_GEMV_MAX_M ? MOE_MODE_GEMV_A16 : MOE_MODE_GEMM_A8;
+}
+
+bool ffn_dims_ok(int32_t fmt, int32_t hidden, int32_t inter)
+{
+    if (hidden <= 0 || inter <= 0 || hidden % 128 || inter % 128) return false;
+    if (fmt == MOE_W_NVFP4_B16 && (hidden % 256 || inter % 256)) return false;
+    return true;
+}
+
+size_t ffn_bytes(int64_t S, int32_t hidden, int32_t inter, int32_t fmt, int32_t mode)
+{
+    if (mode == MOE_MODE_GEMV_A16) return gemv_scratch_bytes(S, hidden, inter, fmt);
+    return 0;  // GEMM tier: not served by this build
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt, int32_t hidden,
+                             int32_t inter, int32_t mode)
+{
+    g_stage_events = events;
+    g_stage_n = events ? n_events : 0;
+    (void)fmt; (void)hidden; (void)inter;
+    if (mode == MOE_MODE_GEMM_A8) return 0;
+    return 3;  // gate/up GEMV, SwiGLU, down GEMV (with its slice sum, if any)
+}
+
+int32_t moe_resolve_mode(int32_t M, int32_t fmt, int32_t requested)
+{
+    return resolve(M, fmt, requested);
+}
+
+size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts, int32_t hidden,
+                           int32_t inter, int32_t fmt, int32_t mode)
+{
+    if (!sizes_ok(max_M, top_k, num_experts)) return 0;
+    if (fmt != MOE_W_E4M3_B128 && fmt != MOE_W_NVFP4_B16) return 0;
+    if (mode < MOE_MODE_AUTO || mode > MOE_MODE_GEMM_A8) return 0;
+    if (!ffn_dims_ok(fmt, hidden, inter)) return 0;
+    const int64_t S = (int64_t)max_M * top_k;
+    size_t ffn;
+    if (mode == MOE_MODE_AUTO) {
+        const int64_t mg = max_M < MOE_GEMV_MAX_M ? max_M : MOE_GEMV_MAX_M;
+        ffn = ffn_bytes(mg * top_k, hidden, inter, fmt, MOE_MODE_GEMV_A16);
+        if (max_M > MOE_GEMV_MAX_M) {
+            const size_t g = ffn_bytes(S, hidden, inter, fmt, MOE_MODE_GEMM_A8);
+            ffn = g > ffn ? g : ffn;
+        }
+    } else {
+        ffn = ffn_bytes(S, hidden, inter, fmt, mode);
+    }
+    return moe::route_region_bytes(S, num_experts) + ffn;
+}
+
+moe_status_t moe_route_pack(const int32_t *topk_ids, int32_t M, int32_t top_k, int32_t num_experts,
+                            void *ws, size_t ws_bytes, moe_route_t *route, void *stream)
+{
+    if (!topk_ids || !ws || !route) return fail(MOE_ERR_ARG, "moe_route_pack: null pointer");
+    if (!sizes_ok(M, top_k, num_experts))
+        return fail(MOE_ERR_SHAPE,
+                    "moe_route_pack: need M >= 1, 1 <= top_k <= num_experts <= %d, M*top_k < 2^31 "
+                    "(M=%d top_k=%d E=%d)",
+                    MOE_MAX_EXPERTS, M, top_k, num_experts);
+    const int64_t S = (int64_t)M * top_k;
+    const size_t need = moe::route_region_bytes(S, num_experts);
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_route_pack: workspace %zu bytes < %zu", ws_bytes, need);
+    if (((uintptr_t)ws & 255) != 0) return fail(MOE_ERR_ARG, "moe_route_pack: ws not 256-byte aligned");
+
+    char *p = (char *)ws;
+    const int64_t A = S < num_experts ? S : num_experts;
+    route->M = M;
+    route->top_k = top_k;
+    route->num_experts = num_experts;
+    route->num_slots = (int32_t)S;
+    route->expert_offsets = (int32_t *)p; p += moe::align256(sizeof(int32_t) * (num_experts + 1));
+    route->sorted_slot = (int32_t *)p;    p += moe::align256(sizeof(int32_t) * S);
+    route->sorted_token = (int32_t *)p;   p += moe::align256(sizeof(int32_t) * S);
+    route->token_to_perm = (int32_t *)p;  p += moe::align256(sizeof(int32_t) * S);
+    route->active_experts = (int32_t *)p; p += moe::align256(sizeof(int32_t) * (A > 0 ? A : 1));
+    route->num_active = (int32_t *)p;
+    route->status = (int32_t *)p + 1;
+
+    MoeRouteDev r{route->expert_offsets, route->sorted_slot, route->sorted_token,
+                  route->token_to_perm, route->active_experts, route->num_active, route->status};
+    hipError_t e = launch_route_pack(topk_ids, M, top_k, num_experts, r, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_route_pack: route_pack launch");
+    return MOE_OK;
+}
+
+static moe_status_t check_bank(const moe_bank_t *b, const char *name, int32_t fmt, int32_t E,
+                               int32_t n_out, int32_t k_in)
+{
+    if (!b || !b->codes || !b->scales)
+        return fail(MOE_ERR_ARG, "moe_expert_ffn: %s bank or its codes/scales is null", name);
+    if (b->fmt != fmt)
+        return fail(MOE_ERR_FORMAT, "moe_expert_ffn: %s bank format %d differs from gate's %d",
+                    name, b->fmt, fmt);
+    if (fmt == MOE_W_E4M3_B128 && b->scale2)
+        return fail(MOE_ERR_FORMAT, "moe_expert_ffn: %s bank: scale2 must be NULL for E4M3", name);
+    if (fmt == MOE_W_NVFP4_B16 && !b->scale2)
+        return fail(MOE_ERR_FORMAT, "moe_expert_ffn: %s bank: NVFP4 needs scale2", name);
+    if (b->num_experts != E || b->n_out != n_out || b->k_in != k_in)
+        return fail(MOE_ERR_SHAPE,
+                    "moe_expert_ffn: %s bank is E=%d %dx%d, expected E=%d %dx%d", name,
+                    b->num_experts, b->n_out, b->k_in, E, n_out, k_in);
+    if (!aligned16(b->codes))
+        return fail(MOE_ERR_ARG, "moe_expert_ffn: %s codes not 16-byte aligned", name);
+    return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
+                            const uint16_t *x_bf16, const moe_route_t *route, int32_t hidden,
+                            int32_t inter, float limit, int32_t mode, float *y_packed, void *ws,
+                            size_t ws_bytes, void *stream)
+{
+    if (!gate || !up || !down || !x_bf16 || !route || !y_packed || !ws)
+        return fail(MOE_ERR_ARG, "moe_expert_ffn: null pointer");
+    const int32_t fmt = gate->fmt;
+    if (fmt != MOE_W_E4M3_B128 && fmt != MOE_W_NVFP4_B16)
+        return fail(MOE_ERR_FORMAT, "moe_expert_ffn: unknown weight format %d", fmt);
+    if (mode < MOE_MODE_AUTO || mode > MOE_MODE_GEMM_A8)
+        return fail(MOE_ERR_ARG, "moe_expert_ffn: unknown mode %d", mode);
+    if (!ffn_dims_ok(fmt, hidden, inter))
+        return fail(MOE_ERR_SHAPE,
+                    "moe_expert_ffn: hidden %d and inter %d must be positive multiples of %d",
+                    hidden, inter, fmt == MOE_W_NVFP4_B16 ? 256 : 128);
+    if (route->expert_offsets != (int32_t *)ws || !sizes_ok(route->M, route->top_k, route->num_experts) ||
+        route->num_slots != route->M * route->top_k)
+        return fail(MOE_ERR_ARG, "moe_expert_ffn: route does not come from moe_route_pack on this ws");
+    const int32_t E = route->num_experts;
+    moe_status_t st;
+    if ((st = check_bank(gate, "gate", fmt, E, inter, hidden))) return st;
+    if ((st = check_bank(up, "up", fmt, E, inter, hidden))) return st;
+    if ((st = check_bank(down, "down", fmt, E, hidden, inter))) return st;
+    if (!aligned16(x_bf16) || !aligned16(y_packed))
+        return fail(MOE_ERR_ARG, "moe_expert_ffn: x and y must be 16-byte aligned");
+    if (!(limit > 0.0f)) return fail(MOE_ERR_ARG, "moe_expert_ffn: limit must be > 0");
+    const int32_t M = route->M, k = route->top_k;
+    const int32_t tier = resolve(M, fmt, mode);
+    if (tier == MOE_MODE_GEMM_A8)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: GEMM_A8 tier is not available in this build");
+    const size_t need = moe_workspace_bytes(M, k, E, hidden, inter, fmt, tier);
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu bytes < %zu", ws_bytes, need);
+
+    const int64_t S = (int64_t)M * k;
+    hipStream_t s = (hipStream_t)stream;
+    MoeRouteDev r{route->expert_offsets, route->sorted_slot, route->sorted_token,
+                  route->token_to_perm, route->active_experts, route->num_active, route->status};
+    char *scratch = (char *)ws + moe::route_region_bytes(S, E);
+    GemvScratch g = carve_gemv(scratch, S, hidden, inter, fmt);
+    GemvBankDev bg{gate->codes, gate->scales, gate->scale2};
+    GemvBankDev bu{up->codes, up->scales, up->scale2};
+    GemvBankDev bd{down->codes, down->scales, down->scale2};
+    const int32_t nks = (int32_t)gemv_gateup_slices(fmt, hidden);
+    hipError_t e;
+    stage_mark(0, s);
+    if (fmt == MOE_W_E4M3_B128)
+        e = launch_gemv_gateup_e4m3(bg, bu, x_bf16, r, (int32_t)S, E, hidden, inter, g.partials,
+                                    nks, s);
+    else
+        e = launch_gemv_gateup_nvfp4(bg, bu, x_bf16, r, (int32_t)S, E, hidden, inter, g.partials,
+                                     nks, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: gate/up GEMV launch");
+    stage_mark(1, s);
+    e = launch_swiglu_partials(g.partials, nks, (int32_t)S, inter, r.offsets, E, limit, g.h, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: SwiGLU launch");
+    stage_mark(2, s);
+    if (fmt == MOE_W_E4M3_B128)
+        e = launch_gemv_down_e4m3(bd, g.h, r, (int32_t)S, E, hidden, inter, y_packed,
+                                  g.down_slices, s);
+    else
+        e = launch_gemv_down_nvfp4(bd, g.h, r, (int32_t)S, E, hidden, inter, y_packed,
+                                   g.down_slices, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: down GEMV launch");
+    stage_mark(3, s);
+    return MOE_OK;
+}
+
+moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
+                         const float *topk_weights, int32_t hidden, float *out, void *stream)
+{
+    if (!y_packed || !route || !topk_weights || !out || !route->token_to_perm)
+        return fail(MOE_ERR_ARG, "moe_combine: null pointer");
+    if (!sizes_ok(route->M, route->top_k, route->num_experts))
+        return fail(MOE_ERR_ARG, "moe_combine: route is not filled");
+    if (hidden <= 0 || hidden % 4)
+        return fail(MOE_ERR_SHAPE, "moe_combine: hidden %d must be a positive multiple of 4", hidden);
+    if (!aligned16(y_packed) || !aligned16(out))
+        return fail(MOE_ERR_ARG, "moe_combine: y and out must be 16-byte aligned");
+    hipError_t e = launch_combine(y_packed, route->token_to_perm, topk_weights, route->M,
+                                  route->top_k, hidden, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_combine: launch");
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// moe_internal.h -- launchers and device helpers shared by libmoe's kernels.
+// gfx950 (CDNA4) only: 64-lane wavefronts, OCP FP8 conversions, MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// workspace layout (shared by the host entry points)
+// ---------------------------------------------------------------------------
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Bytes of the route region for S = M*k slots and E experts.
+inline size_t route_region_bytes(int64_t S, int64_t E)
+{
+    int64_t A = S < E ? S : E;
+    return align256(sizeof(int32_t) * (size_t)(E + 1)) +      // expert_offsets
+           3 * align256(sizeof(int32_t) * (size_t)S) +         // sorted_slot, sorted_token, token_to_perm
+           align256(sizeof(int32_t) * (size_t)(A > 0 ? A : 1)) + // active_experts
+           align256(sizeof(int32_t) * 2);                      // num_active, status
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum over each aligned group of 8 lanes; every lane of the group ends with
+// the group sum.  quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror.
+__device__ __forceinline__ float sum8_lanes(float v)
+{
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    return v;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// launchers (return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+struct MoeRouteDev {
+    int32_t *offsets, *sorted_slot, *sorted_token, *token_to_perm, *active, *num_active, *status;
+};
+
+hipError_t launch_route_pack(const int32_t *ids, int32_t M, int32_t k, int32_t E,
+                             const MoeRouteDev &r, hipStream_t st);
+
+// E4M3 dequant-GEMV tier.
+struct GemvBankDev {
+    const uint8_t *codes;
+    const void *scales;
+    const float *scale2;
+};
+
+hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
+                                   const uint16_t *x, const MoeRouteDev &r,
+                                   int32_t S, int32_t E, int32_t hidden, int32_t inter,
+                                   float *partials, int32_t nks, hipStream_t st);
+// Down projection; when inter > 2048 the K slices go to slice_scratch
+// ([gemv_down_slices(inter)][S][hidden] floats) and are summed in order into y.
+int gemv_down_slices(int32_t inter);
+hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
+                                 int32_t S, int32_t E, int32_t hidden, int32_t inter,
+                                 float *y, float *slice_scratch, hipStream_t st);
+
+hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
+                                    const uint16_t *x, const MoeRouteDev &r,
+                                    int32_t S, int32_t E, int32_t hidden, int32_t inter,
+                                    float *partials, int32_t nks, hipStream_t st);
+hipError_t launch_gemv_down_nvfp4(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
+                                  int32_t S, int32_t E, int32_t hidden, int32_t inter,
+                                  float *y, float *slice_scratch, hipStream_t st);
+
+// h[p][n] = swiglu_clamp(sum_ks P[ks][p][n], sum_ks P[ks][p][I + n]) for p < offsets[E].
+hipError_t launch_swiglu_partials(const float *partials, int32_t nks, int32_t S, int32_t inter,
+                                  const int32_t *offsets, int32_t E, float limit, float *h,
+                                  hipStream_t st);
+
+hipError_t launch_combine(const float *y, const int32_t *token_to_perm, const float *w,
+                          int32_t M, int32_t k, int32_t hidden, float *out, hipStream_t st);
+
+// Slices of the GEMV tier's gate/up K loop (k values per slice).
+constexpr int kGemvSliceE4M3 = 1024;
+constexpr int kGemvSliceNVFP4 = 2048;

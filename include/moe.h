@@ -1,0 +1,196 @@
+/*
+ * moe.h -- C ABI of libmoe, the routed mixture-of-experts FFN layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one token t, its k routed slots s = t*k + j, expert e = ids[s]):
+ *   g = Wg[e] x[t],  u = Wu[e] x[t]                        gate and up
+ *   h = silu(min(g, L)) * clamp(u, -L, L)                  clamped SwiGLU
+ *   y[s] = Wd[e] h                                         down
+ *   out[t] = sum_{j=0..k-1} w[t, j] * y[t*k + j]           combine
+ * Sources: "memra-engine src/dsv4_ep.rs" (fn chain: gate/up, clamped SwiGLU,
+ * FP8 h, down, per routed slot); "spark_model glm5next_mlp/forward.rs" (doc
+ * of swiglu_rows for the activation, struct Glm5NextMlpWorkspace for the
+ * expert-sorted route tables, the combine kernels of fn forward_moe);
+ * "memra-engine src/bin/ep_step_fp8_gate.rs" (fn combine_down_rows_host for
+ * the slot-order combine, fn expert_matrix for the bank layout).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns
+ *     every buffer and keeps it alive until the work queued on `stream`
+ *     completes.  `stream` is a hipStream_t (NULL = the null stream).
+ *   - The library never allocates, frees, synchronises the stream or copies
+ *     device -> host inside these calls, so the three layer calls can be
+ *     captured in a HIP graph.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed check returns a non-zero status and launches nothing.
+ *     moe_last_error() then describes it (thread-local).
+ *   - A launch failure returns MOE_ERR_HIP with HIP's message.
+ *   - Ids outside [0, E) never fault: -1 marks an unfilled slot and any other
+ *     out-of-range id is counted in route.status; both contribute zero.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+enum {
+    MOE_OK = 0,
+    MOE_ERR_ARG = 1,         /* null pointer or inconsistent argument        */
+    MOE_ERR_SHAPE = 2,       /* a size rule below is broken                  */
+    MOE_ERR_FORMAT = 3,      /* weight formats disagree / scale2 misuse      */
+    MOE_ERR_WORKSPACE = 4,   /* ws_bytes below moe_workspace_bytes()         */
+    MOE_ERR_HIP = 5,         /* a HIP launch failed                          */
+    MOE_ERR_UNSUPPORTED = 6  /* valid request this build does not serve      */
+};
+
+/* Weight formats. */
+enum {
+    /* E4M3FN codes, one FP32 scale per 128x128 block ("memra-engine
+     * src/bin/ep_step_fp8_gate.rs", fn expert_matrix: expert-major codes and
+     * a scale_rows x scale_cols grid per expert). */
+    MOE_W_E4M3_B128 = 1,
+    /* NVFP4: E2M1 codes two per byte (element 2i in the low nibble), one E4M3
+     * scale byte per 16 consecutive inputs, one FP32 scale_2 per expert
+     * ("memra-engine src/dsv4_ep.rs", fn chain strides inter*hidden/2 and
+     * inter*hidden/16; "spark_model glm5next_mlp/forward.rs", fn w4a16_gemv,
+     * scale_2 as a scalar). */
+    MOE_W_NVFP4_B16 = 2
+};
+
+/* Execution tiers. */
+enum {
+    MOE_MODE_AUTO = 0,      /* GEMV_A16 for M <= MOE_GEMV_MAX_M, else GEMM_A8   */
+    /* Dequant-GEMV, bf16 activations, each active expert's weights streamed
+     * once for all slots routed to it ("spark_model glm5next_mlp/forward.rs",
+     * fn w4a16_gemv_moe_batchm: the union of the rows' experts, each swept
+     * once). */
+    MOE_MODE_GEMV_A16 = 1,
+    /* Grouped FP8 MFMA GEMM over expert-sorted rows, activations and h
+     * quantized to E4M3 per 1x128 group ("spark_model glm5next_mlp/forward.rs",
+     * grouped prefill arm of fn forward_moe; "memra-engine src/dsv4_ep.rs",
+     * EpScratch xq/xs/hq/hs).  E4M3 banks only. */
+    MOE_MODE_GEMM_A8 = 2
+};
+
+#define MOE_GEMV_MAX_M 16
+#define MOE_MAX_EXPERTS 512
+
+/* One projection bank holding every expert, expert-major (host struct of
+ * device pointers).  n_out x k_in is the matrix shape per expert:
+ *   gate, up: n_out = inter,  k_in = hidden
+ *   down:     n_out = hidden, k_in = inter
+ * E4M3:  codes  uint8 [E][n_out][k_in]
+ *        scales float [E][n_out/128][k_in/128]
+ *        scale2 must be NULL
+ * NVFP4: codes  uint8 [E][n_out][k_in/2]
+ *        scales uint8 (E4M3) [E][n_out][k_in/16]
+ *        scale2 float [E]                                                    */
+typedef struct {
+    int32_t fmt;
+    int32_t num_experts;
+    int32_t n_out;
+    int32_t k_in;
+    const uint8_t *codes;
+    const void *scales;
+    const float *scale2;
+} moe_bank_t;
+
+/* Expert-sorted route tables (host struct of device pointers into the
+ * caller's workspace; "spark_model glm5next_mlp/forward.rs", struct
+ * Glm5NextMlpWorkspace: expert_offsets, sorted_token_ids, token_to_perm).
+ * S = M * top_k slots; slot s = t*top_k + j.  A slot's packed row is its
+ * position in the expert-sorted order; within one expert, rows keep
+ * ascending slot order.
+ *   expert_offsets [E+1]  exclusive prefix sum of per-expert slot counts;
+ *                         expert_offsets[E] = number of valid slots
+ *   sorted_slot    [S]    packed row -> slot          (first expert_offsets[E])
+ *   sorted_token   [S]    packed row -> token
+ *   token_to_perm  [S]    slot -> packed row, -1 for an invalid/unfilled id
+ *   active_experts [min(E,S)]  ascending ids of experts with >= 1 slot
+ *   num_active     [1]    length of active_experts
+ *   status         [1]    number of ids outside [0, E) other than -1       */
+typedef struct {
+    int32_t M;
+    int32_t top_k;
+    int32_t num_experts;
+    int32_t num_slots;
+    int32_t *expert_offsets;
+    int32_t *sorted_slot;
+    int32_t *sorted_token;
+    int32_t *token_to_perm;
+    int32_t *active_experts;
+    int32_t *num_active;
+    int32_t *status;
+} moe_route_t;
+
+/* Bytes of device workspace one layer call sequence needs for any M <= max_M
+ * (route tables first, then the FFN's scratch).  0 if the sizes break a rule
+ * of moe_route_pack / moe_expert_ffn.  Needs no GPU. */
+size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts,
+                           int32_t hidden, int32_t inter, int32_t fmt,
+                           int32_t mode);
+
+/* The tier moe_expert_ffn runs for `requested` at M tokens (AUTO resolves by
+ * M).  Needs no GPU. */
+int32_t moe_resolve_mode(int32_t M, int32_t fmt, int32_t requested);
+
+/* Route pack: stable counting sort of the M*top_k slots of topk_ids
+ * (int32 [M][top_k], device) by expert, into the route region at the start
+ * of `ws`.  Fills *route (host) with pointers into ws.
+ * Rules: M >= 1, 1 <= top_k <= num_experts <= MOE_MAX_EXPERTS, M*top_k
+ * < 2^31; ws_bytes >= moe_workspace_bytes(M, top_k, num_experts, 128, 128,
+ * MOE_W_E4M3_B128, MOE_MODE_GEMV_A16) at least (the route region). */
+moe_status_t moe_route_pack(const int32_t *topk_ids, int32_t M, int32_t top_k,
+                            int32_t num_experts, void *ws, size_t ws_bytes,
+                            moe_route_t *route, void *stream);
+
+/* Expert FFN: for every valid slot, in packed order,
+ *   y_packed[row] = Wd[e] (silu(min(Wg[e] x[t], L)) * clamp(Wu[e] x[t], -L, L))
+ * x_bf16: bf16 [M][hidden]; y_packed: float [M*top_k][hidden], rows past
+ * expert_offsets[E] are left untouched.  `route` (host) must come from
+ * moe_route_pack on this same `ws`.
+ * Rules: hidden % 128 == 0, inter % 128 == 0; gate/up are inter x hidden,
+ * down is hidden x inter; all banks share one format and num_experts;
+ * GEMM_A8 needs E4M3 banks; ws_bytes >= moe_workspace_bytes(route->M, ...,
+ * mode). */
+moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up,
+                            const moe_bank_t *down, const uint16_t *x_bf16,
+                            const moe_route_t *route, int32_t hidden,
+                            int32_t inter, float limit, int32_t mode,
+                            float *y_packed, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Combine: out[t][m] = sum_{j=0..top_k-1} w[t][j] * y_packed[token_to_perm[t*top_k+j]][m],
+ * in slot order j, each product rounded before it is added (FP32); slots
+ * with token_to_perm = -1 contribute nothing ("memra-engine
+ * src/bin/ep_step_fp8_gate.rs", fn combine_down_rows_host).
+ * topk_weights: float [M][top_k]; out: float [M][hidden]; hidden % 4 == 0. */
+moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
+                         const float *topk_weights, int32_t hidden, float *out,
+                         void *stream);
+
+/* Stage timing (optional, thread-local).  With events != NULL, later
+ * moe_expert_ffn calls on this thread record events[0] on their stream before
+ * the first kernel and events[i] after the i-th kernel, for at most
+ * n_events events; NULL turns it off.  The handles are the caller's
+ * hipEvent_t.  Returns the number of stages the given tier records (GEMV
+ * tier: gate/up, SwiGLU, down), so n_events = that + 1 covers them all.  Mirrors the
+ * per-stage timers of "spark_model glm5next_mlp/forward.rs" (profile::start /
+ * profile::end around the MoE stages). */
+int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt,
+                             int32_t hidden, int32_t inter, int32_t mode);
+
+/* Message for the last non-OK status returned on this thread. */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

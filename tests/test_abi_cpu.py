@@ -1,0 +1,151 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moe.h declares, sizes its workspace as documented, resolves tiers,
+and rejects bad arguments on the host before launching anything."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    from fp4_block_scaled_amd import binding as B
+    names = header_functions()
+    assert set(names) == set(B.EXPORTS)
+    lib = C.CDLL(os.path.join(ROOT, "fp4_block_scaled_amd", "libmoe.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def a256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_workspace_bytes_hand_computed():
+    from fp4_block_scaled_amd import binding as B
+    # decode: H7168 I2048 E256 k8 M=1, E4M3, GEMV tier
+    S, E, H, I = 8, 256, 7168, 2048
+    route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
+    nks = 7  # 1024-wide K slices of H
+    gemv = a256(4 * nks * S * 2 * I) + a256(4 * S * I)
+    assert B.moe_workspace_bytes(1, 8, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16) == route + gemv
+    # NVFP4 M=16: H6144 I1536 E160; 2048-wide K slices of H -> 3
+    S, E, H, I = 128, 160, 6144, 1536
+    route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
+    gemv = a256(4 * 3 * S * 2 * I) + a256(4 * S * I)
+    assert B.moe_workspace_bytes(16, 8, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_AUTO) == route + gemv
+    # inter beyond one 2048-wide down slice adds the slice buffer
+    S, E, H, I = 2, 4, 256, 2304
+    route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
+    gemv = a256(4 * 1 * S * 2 * I) + a256(4 * S * I) + a256(4 * 2 * S * H)
+    assert B.moe_workspace_bytes(1, 2, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16) == route + gemv
+    # monotone in max_M
+    sizes = [B.moe_workspace_bytes(m, 8, 256, 7168, 2048, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16)
+             for m in (1, 2, 4, 8, 16)]
+    assert sizes == sorted(sizes)
+
+
+@pytest.mark.parametrize("args", [
+    (0, 8, 256, 7168, 2048, 1, 0),      # M = 0
+    (1, 0, 256, 7168, 2048, 1, 0),      # top_k = 0
+    (1, 9, 8, 7168, 2048, 1, 0),        # top_k > E
+    (1, 8, 513, 7168, 2048, 1, 0),      # E > max
+    (1, 8, 256, 7100, 2048, 1, 0),      # hidden % 128
+    (1, 8, 256, 7168, 2000, 1, 0),      # inter % 128
+    (1, 8, 256, 6144, 1664, 2, 0),      # NVFP4 needs % 256
+    (1, 8, 256, 7168, 2048, 3, 0),      # unknown format
+    (1, 8, 256, 7168, 2048, 1, 7),      # unknown mode
+])
+def test_workspace_bytes_rejects_bad_sizes(args):
+    from fp4_block_scaled_amd import binding as B
+    assert B.lib.moe_workspace_bytes(*args) == 0
+
+
+def test_resolve_mode():
+    from fp4_block_scaled_amd import binding as B
+    assert B.moe_resolve_mode(1, B.MOE_W_E4M3_B128) == B.MOE_MODE_GEMV_A16
+    assert B.moe_resolve_mode(16, B.MOE_W_NVFP4_B16) == B.MOE_MODE_GEMV_A16
+    assert B.moe_resolve_mode(17, B.MOE_W_E4M3_B128) == B.MOE_MODE_GEMM_A8
+    assert B.moe_resolve_mode(4096, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16) == B.MOE_MODE_GEMV_A16
+
+
+# Fake device addresses: the checks below fail before anything is launched or
+# dereferenced, so no GPU is needed.
+FAKE = 0x7F0000000000
+
+
+def _bank(B, fmt=1, E=16, n=128, k=256, scale2=None, codes=FAKE):
+    return B.moe_bank_t(fmt, E, n, k, codes, FAKE + 0x1000, scale2)
+
+
+def _route(B, ws, M=1, k=4, E=16):
+    r = B.moe_route_t()
+    r.M, r.top_k, r.num_experts, r.num_slots = M, k, E, M * k
+    r.expert_offsets = ws
+    r.token_to_perm = ws + 0x400
+    return r
+
+
+def _ffn(B, gate, up, down, route, ws, hidden=256, inter=128, mode=0, limit=7.0,
+         ws_bytes=1 << 30, x=FAKE + 0x2000, y=FAKE + 0x3000):
+    return B.lib.moe_expert_ffn(C.byref(gate), C.byref(up), C.byref(down), x, C.byref(route),
+                                hidden, inter, limit, mode, y, ws, ws_bytes, None)
+
+
+def test_ffn_error_contract_on_host():
+    from fp4_block_scaled_amd import binding as B
+    ws = FAKE + 0x100000
+    g, u, d = _bank(B), _bank(B), _bank(B, n=256, k=128)
+    r = _route(B, ws)
+    # null pointers
+    assert B.lib.moe_expert_ffn(None, C.byref(u), C.byref(d), FAKE, C.byref(r), 256, 128, 7.0, 0,
+                                FAKE, ws, 1 << 30, None) == B.MOE_ERR_ARG
+    assert _ffn(B, g, u, d, r, ws, x=None) == B.MOE_ERR_ARG
+    assert "null" in B.moe_last_error()
+    # shapes
+    assert _ffn(B, g, u, d, r, ws, hidden=200) == B.MOE_ERR_SHAPE
+    assert _ffn(B, g, u, _bank(B, n=128, k=128), r, ws) == B.MOE_ERR_SHAPE
+    assert _ffn(B, _bank(B, E=8), u, d, r, ws) == B.MOE_ERR_SHAPE
+    # formats
+    assert _ffn(B, g, _bank(B, fmt=2, scale2=FAKE), d, r, ws) == B.MOE_ERR_FORMAT
+    assert _ffn(B, _bank(B, scale2=FAKE), u, d, r, ws) == B.MOE_ERR_FORMAT
+    assert _ffn(B, _bank(B, fmt=9), u, d, r, ws) == B.MOE_ERR_FORMAT
+    assert _ffn(B, _bank(B, fmt=2, k=256, n=256), _bank(B, fmt=2, k=256, n=256),
+                _bank(B, fmt=2, n=256, k=256), r, ws, hidden=256, inter=256) == B.MOE_ERR_FORMAT
+    # workspace too small
+    assert _ffn(B, g, u, d, r, ws, ws_bytes=4096) == B.MOE_ERR_WORKSPACE
+    # route not from this workspace
+    assert _ffn(B, g, u, d, _route(B, ws + 256), ws) == B.MOE_ERR_ARG
+    # misaligned codes
+    assert _ffn(B, _bank(B, codes=FAKE + 3), u, d, r, ws) == B.MOE_ERR_ARG
+    # bad limit, unknown mode
+    assert _ffn(B, g, u, d, r, ws, limit=0.0) == B.MOE_ERR_ARG
+    assert _ffn(B, g, u, d, r, ws, mode=5) == B.MOE_ERR_ARG
+
+
+def test_route_pack_and_combine_error_contract_on_host():
+    from fp4_block_scaled_amd import binding as B
+    ws = FAKE + 0x100000
+    r = B.moe_route_t()
+    L = B.lib
+    assert L.moe_route_pack(None, 1, 4, 16, ws, 1 << 20, C.byref(r), None) == B.MOE_ERR_ARG
+    assert L.moe_route_pack(FAKE, 0, 4, 16, ws, 1 << 20, C.byref(r), None) == B.MOE_ERR_SHAPE
+    assert L.moe_route_pack(FAKE, 1, 17, 16, ws, 1 << 20, C.byref(r), None) == B.MOE_ERR_SHAPE
+    assert L.moe_route_pack(FAKE, 1, 4, 600, ws, 1 << 20, C.byref(r), None) == B.MOE_ERR_SHAPE
+    assert L.moe_route_pack(FAKE, 1, 4, 16, ws, 64, C.byref(r), None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_route_pack(FAKE, 1, 4, 16, ws + 8, 1 << 20, C.byref(r), None) == B.MOE_ERR_ARG
+    rr = _route(B, ws)
+    assert L.moe_combine(None, C.byref(rr), FAKE, 256, FAKE, None) == B.MOE_ERR_ARG
+    assert L.moe_combine(FAKE, C.byref(rr), FAKE, 258, FAKE, None) == B.MOE_ERR_SHAPE
+    assert L.moe_combine(FAKE + 4, C.byref(rr), FAKE, 256, FAKE, None) == B.MOE_ERR_ARG
+    empty = B.moe_route_t()
+    empty.token_to_perm = FAKE
+    assert L.moe_combine(FAKE, C.byref(empty), FAKE, 256, FAKE, None) == B.MOE_ERR_ARG

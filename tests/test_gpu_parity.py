@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Route tables are compared bit for bit; layer outputs to
+max|err| <= 2e-3 * max|ref| and relative L2 <= 1e-3 (whole [M, hidden]
+output, and per packed y row as a diagnostic)."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from fp4_block_scaled_amd import binding as B
+from moe_cases import GpuCase, check_fp, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# route pack: bit-exact
+# --------------------------------------------------------------------------
+
+def gpu_pack(ids: np.ndarray, E: int):
+    M, k = ids.shape
+    nbytes = B.moe_workspace_bytes(M, k, E, 128, 128, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16)
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    ids_d = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+    route = B.moe_route_pack(ids_d, M, k, E, ws)
+    torch.cuda.synchronize()
+    return {k_: v.cpu().numpy() for k_, v in B.route_tensors(route, ws).items()}
+
+
+def assert_pack_equal(got, ref, S):
+    nv = int(ref["expert_offsets"][-1])
+    assert np.array_equal(got["expert_offsets"], ref["expert_offsets"])
+    assert np.array_equal(got["sorted_slot"][:nv], ref["sorted_slot"])
+    assert np.array_equal(got["sorted_token"][:nv], ref["sorted_token"])
+    assert np.array_equal(got["token_to_perm"], ref["token_to_perm"])
+    assert int(got["num_active"][0]) == ref["num_active"]
+    assert np.array_equal(got["active_experts"][:ref["num_active"]], ref["active_experts"])
+    assert int(got["status"][0]) == ref["invalid"]
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+@pytest.mark.parametrize("route_set", [0, 1, 2])
+def test_route_pack_bit_exact_on_workloads(name, route_set):
+    wl = workloads.WORKLOADS[name]
+    ids, _, _ = workloads.make_routes(wl, route_set)
+    print(f"route_pack {name} set {route_set} M={wl.M}", flush=True)
+    assert_pack_equal(gpu_pack(ids, wl.experts), oracle.route_pack(ids, wl.experts), ids.size)
+
+
+@pytest.mark.parametrize("case", ["one_expert", "E1", "E2", "k_eq_E", "invalid", "all_invalid",
+                                  "dups", "max_experts", "ragged_chunks", "big"])
+def test_route_pack_bit_exact_adversarial(case):
+    rng = np.random.default_rng(17)
+    if case == "one_expert":
+        ids, E = np.full((600, 4), 5, np.int32), 9
+    elif case == "E1":
+        ids, E = np.zeros((1500, 1), np.int32), 1
+    elif case == "E2":
+        ids, E = rng.integers(0, 2, (777, 2)).astype(np.int32), 2
+    elif case == "k_eq_E":
+        E = 6
+        ids = np.stack([rng.permutation(E) for _ in range(300)]).astype(np.int32)
+    elif case == "invalid":
+        E = 64
+        ids = rng.integers(0, E, (300, 6)).astype(np.int32)
+        flat = ids.ravel()
+        pos = rng.choice(flat.size, 100, replace=False)
+        flat[pos[:40]] = -1
+        flat[pos[40:70]] = E + rng.integers(0, 1000, 30)
+        flat[pos[70:]] = -rng.integers(2, 1 << 30, 30)
+    elif case == "all_invalid":
+        ids, E = np.full((5, 3), -1, np.int32), 4
+        ids[2, 2] = 4
+    elif case == "dups":
+        ids, E = rng.integers(0, 5, (2000, 4)).astype(np.int32), 5
+    elif case == "max_experts":
+        E = B.MOE_MAX_EXPERTS
+        ids = np.stack([rng.choice(E, 8, replace=False) for _ in range(700)]).astype(np.int32)
+    elif case == "ragged_chunks":
+        E = 37
+        ids = rng.integers(0, E, (1025, 3)).astype(np.int32)
+    else:
+        E = 256
+        bias = rng.normal(0, 0.5, E)
+        ids, _ = workloads.topk_softmax(rng.standard_normal((8192, E)) + bias, 8)
+    print(f"route_pack adversarial {case} S={ids.size} E={E}", flush=True)
+    assert_pack_equal(gpu_pack(ids, E), oracle.route_pack(ids, E), ids.size)
+
+
+# --------------------------------------------------------------------------
+# layer parity
+# --------------------------------------------------------------------------
+
+def run_and_check(case: GpuCase, ids, w, mode=B.MOE_MODE_AUTO, tokens=None, label=""):
+    wl = case.wl
+    resolved = B.moe_resolve_mode(ids.shape[0], wl.fmt, mode)
+    act_fp8 = resolved == B.MOE_MODE_GEMM_A8
+    out, y, tabs, _ = case.run(ids, w, mode)
+    ref_out, ref_y = oracle_layer(case.banks, case.x, ids, w, wl.limit, act_fp8, tokens)
+    sel = np.arange(ids.shape[0]) if tokens is None else np.asarray(tokens)
+    r = check_fp(out[sel], ref_out, f"{label} out")
+    # per packed row diagnostics (valid slots of the checked tokens)
+    t2p = tabs["token_to_perm"].reshape(ids.shape)
+    rows = []
+    for i, t in enumerate(sel):
+        for j in range(ids.shape[1]):
+            if t2p[t, j] >= 0:
+                rows.append((t2p[t, j], i * ids.shape[1] + j))
+    if rows:
+        p, s = np.array(rows).T
+        check_fp(y[p], ref_y[s], f"{label} y rows")
+    return r
+
+
+_cache = {}
+
+
+def get_case(name_or_wl):
+    wl = workloads.WORKLOADS[name_or_wl] if isinstance(name_or_wl, str) else name_or_wl
+    key = (wl.name, wl.hidden, wl.inter, wl.experts, wl.top_k, wl.fmt, wl.seed)
+    if key not in _cache:
+        _cache.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+        _cache[key] = GpuCase(wl)
+    return _cache[key]
+
+
+@pytest.mark.parametrize("name", ["tiny_e4m3_m1", "decode_e4m3_m1", "verify_e4m3_m8",
+                                  "nvfp4_m1", "nvfp4_m16"])
+def test_layer_parity_gemv_tier_full_workloads(name):
+    wl = workloads.WORKLOADS[name]
+    print(f"layer parity {name}", flush=True)
+    case = get_case(wl)
+    ids, w, info = workloads.make_routes(wl, 0)
+    r = run_and_check(case, ids, w, label=name)
+    print(f"  {name}: max err frac {r[0]:.2e}, rel L2 {r[1]:.2e}, routes {info}", flush=True)
+
+
+REDUCED = [
+    # (name, base, overrides, M list)
+    ("e4m3_h384_i256", "tiny_e4m3_m1", dict(hidden=384, inter=256, experts=8, top_k=3), [1, 3, 16]),
+    ("e4m3_h1152_i384", "tiny_e4m3_m1", dict(hidden=1152, inter=384, experts=6, top_k=2), [1, 7]),
+    ("e4m3_h256_i2304", "tiny_e4m3_m1", dict(hidden=256, inter=2304, experts=4, top_k=2), [1, 5]),
+    ("nvfp4_h2304_i512", "nvfp4_m1", dict(hidden=2304, inter=512, experts=8, top_k=3), [1, 16]),
+    ("nvfp4_h256_i2560", "nvfp4_m1", dict(hidden=256, inter=2560, experts=4, top_k=2), [2]),
+]
+
+
+@pytest.mark.parametrize("name,base,over,Ms", REDUCED, ids=[r[0] for r in REDUCED])
+def test_layer_parity_reduced_shapes_ragged(name, base, over, Ms):
+    wl = workloads.with_shape(workloads.WORKLOADS[base], name=name, M=max(Ms), **over)
+    case = get_case(wl)
+    for M in Ms:
+        ids, w, _ = workloads.make_routes(wl, 0, M=M)
+        print(f"layer parity {name} M={M}", flush=True)
+        run_and_check(case, ids, w, label=f"{name} M={M}")
+
+
+def test_layer_parity_many_slots_per_expert_gemv():
+    # 40 tokens on 3 experts: slot tiles of the GEMV kernels loop several times
+    wl = workloads.with_shape(workloads.WORKLOADS["tiny_e4m3_m1"], name="e4m3_crowded",
+                              hidden=512, inter=256, experts=3, top_k=2, M=40)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 0)
+    run_and_check(case, ids, w, mode=B.MOE_MODE_GEMV_A16, label="crowded e4m3")
+
+
+def test_layer_parity_many_slots_per_expert_gemv_nvfp4():
+    wl = workloads.with_shape(workloads.WORKLOADS["nvfp4_m1"], name="nvfp4_crowded",
+                              hidden=512, inter=512, experts=3, top_k=2, M=40)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 0)
+    run_and_check(case, ids, w, mode=B.MOE_MODE_GEMV_A16, label="crowded nvfp4")
+
+
+def test_invalid_and_unfilled_ids_contribute_zero():
+    wl = workloads.with_shape(workloads.WORKLOADS["tiny_e4m3_m1"], name="e4m3_invalid", M=6)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 0)
+    ids[1, 2] = -1
+    ids[3, 0] = wl.experts + 3
+    ids[4, 1] = -9
+    out, y, tabs, _ = case.run(ids, w)
+    assert int(tabs["status"][0]) == 2
+    ref_out, _ = oracle_layer(case.banks, case.x, ids, w, wl.limit, False)
+    check_fp(out, ref_out, "invalid ids out")
+
+
+def test_repeat_runs_bit_identical_and_canaries_survive():
+    wl = workloads.WORKLOADS["nvfp4_m16"]
+    wl = workloads.with_shape(wl, name="nvfp4_canary", hidden=1024, inter=512, experts=20)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 0)
+    L = case.layer(max_M=wl.M + 4)
+    # NaN canaries in every row the layer must not write
+    L.y.fill_(float("nan"))
+    L.out.fill_(float("nan"))
+    out1, y1, tabs, _ = case.run(ids, w, layer=L)
+    nv = int(tabs["expert_offsets"][-1])
+    assert np.all(np.isnan(y1[nv:])), "rows past the valid slots were written"
+    assert np.all(np.isnan(L.out[wl.M:].cpu().numpy())), "output rows past M were written"
+    out2, y2, _, _ = case.run(ids, w, layer=L)
+    assert np.array_equal(out1.view(np.uint32), out2.view(np.uint32))
+    assert np.array_equal(y1[:nv].view(np.uint32), y2[:nv].view(np.uint32))
+
+
+def test_grouping_rows_never_changes_a_row():
+    # a token's output does not depend on which other tokens share the sweep
+    wl = workloads.with_shape(workloads.WORKLOADS["tiny_e4m3_m1"], name="e4m3_group", M=12,
+                              hidden=512, inter=256, experts=16, top_k=4)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 0)
+    full, _, _, _ = case.run(ids, w)
+    for t in (0, 5, 11):
+        x1 = case.x[t:t + 1].contiguous()
+        one, _, _, _ = case.run(ids[t:t + 1], w[t:t + 1], x=x1)
+        assert np.array_equal(one[0].view(np.uint32), full[t].view(np.uint32)), t
