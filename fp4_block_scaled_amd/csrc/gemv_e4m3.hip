@@ -30,9 +30,24 @@ using moe::bf16x2;
 using moe::f32x2;
 
 constexpr int kThreads = 256;                    // 4 waves
-constexpr int kGUSegs = kGemvSliceE4M3 / 128;    // 8 segments of 128 K per slice
-constexpr int kDownSlice = 2048;
-constexpr int kDownSegs = kDownSlice / 128;      // 16
+
+// Launch-shape constants (rows per wave = 8 * RG; slots per weight pass = ST).
+#ifndef MOE_E4M3_GU_RG
+#define MOE_E4M3_GU_RG 1
+#endif
+#ifndef MOE_E4M3_GU_ST
+#define MOE_E4M3_GU_ST 8
+#endif
+#ifndef MOE_E4M3_DN_RG
+#define MOE_E4M3_DN_RG 1
+#endif
+#ifndef MOE_E4M3_DN_ST
+#define MOE_E4M3_DN_ST 4
+#endif
+// minimum waves per SIMD the register allocation must allow
+#ifndef MOE_GEMV_MIN_WAVES
+#define MOE_GEMV_MIN_WAVES 1
+#endif
 
 struct GateUpArgs {
     const uint8_t *gcodes, *ucodes;
@@ -40,7 +55,7 @@ struct GateUpArgs {
     const uint16_t *x;
     const int32_t *offsets, *sorted_token, *active, *num_active;
     float *partials;
-    int32_t S, H, I, nks, ntiles;
+    int32_t S, H, I, nks, ntiles, st;   // st: slots per weight pass (<= ST)
 };
 
 struct DownArgs {
@@ -49,12 +64,20 @@ struct DownArgs {
     const float *h;
     const int32_t *offsets, *active, *num_active;
     float *out;          // y [S][H] when nks == 1, else partials [nks][S][H]
-    int32_t S, H, I, nks, ntiles;
+    int32_t S, H, I, nks, ntiles, st;   // st: slots per weight pass (<= ST)
 };
 
+// Weights are streamed once per call: non-temporal loads keep them from
+// displacing the activations and partial sums in the caches.
 __device__ __forceinline__ uint4 load16(const uint8_t *p)
 {
+#ifndef MOE_GEMV_CACHED_LOADS
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
     return *reinterpret_cast<const uint4 *>(p);
+#endif
 }
 
 // 4 code bytes -> two bf16 pairs (bytes 0,1 and 2,3).  E4M3 values are exact
@@ -73,13 +96,19 @@ __device__ __forceinline__ float dot2(bf16x2 a, uint32_t b, float c)
 // ---------------------------------------------------------------------------
 // gate + up
 // ---------------------------------------------------------------------------
-// RG: 8-row groups per wave; ST: slots per pass over the weights.
-template <int RG, int ST>
-__global__ __launch_bounds__(kThreads) void gemv_gateup_e4m3_kernel(GateUpArgs a)
+// SEGS: 128-wide K segments per slice (the slice width divides hidden);
+// RG: 8-row groups per wave; ST: slots per pass over the weights.  A wave
+// issues all RG*SEGS 16-byte loads of its rows before the first multiply, so
+// up to RG*SEGS KB per wave are in flight.  The block's 128 rows share one
+// 128-row scale block, so the SEGS scales are loaded once per block.
+template <int SEGS, int RG, int ST>
+__global__ __launch_bounds__(kThreads, MOE_GEMV_MIN_WAVES) void gemv_gateup_e4m3_kernel(GateUpArgs a)
 {
     constexpr int RPW = RG * 8;
     constexpr int RPB = RPW * (kThreads / 64);
-    __shared__ uint4 xs[ST][kGUSegs * 16];           // bf16 x slice per slot (1024 values)
+    static_assert(128 % RPB == 0, "block rows inside one 128-row scale block");
+    extern __shared__ uint4 lds_x[];                 // bf16 x slice per slot: [a.st][SEGS*16]
+    uint4 (*xs)[SEGS * 16] = reinterpret_cast<uint4 (*)[SEGS * 16]>(lds_x);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
@@ -89,79 +118,80 @@ __global__ __launch_bounds__(kThreads) void gemv_gateup_e4m3_kernel(GateUpArgs a
     bid /= a.nks;
     const int tile = bid % a.ntiles;
     const int ai = bid / a.ntiles;
-    if (ai >= *a.num_active) return;
-    const int e = a.active[ai];
-    const int p0 = a.offsets[e];
-    const int ne = a.offsets[e + 1] - p0;
+    const int e = a.active[ai];              // -1 past the active experts
+    if (e < 0) return;
     const int H = a.H, I = a.I;
     const int half = a.ntiles >> 1;
     const bool is_up = tile >= half;
     const uint8_t *codes = (is_up ? a.ucodes : a.gcodes) + (size_t)e * I * H;
     const int sc_cols = H >> 7;
-    const float *sc_e = (is_up ? a.uscales : a.gscales) + (size_t)e * (I >> 7) * sc_cols;
     const int row_b0 = (is_up ? tile - half : tile) * RPB;
     const int col_b0 = (is_up ? I : 0) + row_b0;
-    const int k0 = ks * kGemvSliceE4M3;
-    const int segs = min(kGUSegs, (H - k0) >> 7);
+    const int k0 = ks * SEGS * 128;
     const size_t pstride = (size_t)2 * I;
 
-    for (int st = 0; st < ne; st += ST) {
-        const int nt = min(ST, ne - st);
-        const int cpr = segs * 16;                   // uint4 chunks per staged row
-        for (int c = tid; c < nt * cpr; c += kThreads) {
-            const int j = c / cpr, r = c - j * cpr;
+    // block scales of this slice: lane l holds scale (l % SEGS)
+    const float *sc_blk = (is_up ? a.uscales : a.gscales) + (size_t)e * (I >> 7) * sc_cols +
+                          (size_t)(row_b0 >> 7) * sc_cols + (k0 >> 7);
+    const float sc_lane = sc_blk[lane % SEGS];
+
+    const uint8_t *rp = codes + (size_t)(row_b0 + wave * RPW + grp) * H + k0 + sub * 16;
+    // weight loads go out first; the slot range is read while they fly
+    int p0 = 0, ne = 1;
+    for (int st = 0; st < ne; st += a.st) {
+        uint4 w[RG][SEGS];
+#ifdef MOE_GEMV_X_FIRST
+        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
+        const int nt = min(a.st, ne - st);
+        for (int c = tid; c < nt * SEGS * 16; c += kThreads) {
+            const int j = c / (SEGS * 16), r = c - j * (SEGS * 16);
             const int tok = a.sorted_token[p0 + st + j];
             xs[j][r] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok * H + k0 + r * 8);
         }
+#endif
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) w[rg][sg] = load16(rp + (size_t)rg * 8 * H + sg * 128);
+#ifndef MOE_GEMV_X_FIRST
+        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
+        const int nt = min(a.st, ne - st);
+        for (int c = tid; c < nt * SEGS * 16; c += kThreads) {
+            const int j = c / (SEGS * 16), r = c - j * (SEGS * 16);
+            const int tok = a.sorted_token[p0 + st + j];
+            xs[j][r] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok * H + k0 + r * 8);
+        }
+#endif
         __syncthreads();
 
-        uint4 wn[kGUSegs];
-        {
-            const uint8_t *rp = codes + (size_t)(row_b0 + wave * RPW + grp) * H + k0 + sub * 16;
-#pragma unroll
-            for (int sg = 0; sg < kGUSegs; ++sg)
-                if (sg < segs) wn[sg] = load16(rp + sg * 128);
-        }
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-            uint4 w[kGUSegs];
-#pragma unroll
-            for (int sg = 0; sg < kGUSegs; ++sg) w[sg] = wn[sg];
-            const int wrow0 = row_b0 + wave * RPW + rg * 8;
-            if (rg + 1 < RG) {
-                const uint8_t *rp = codes + (size_t)(wrow0 + 8 + grp) * H + k0 + sub * 16;
-#pragma unroll
-                for (int sg = 0; sg < kGUSegs; ++sg)
-                    if (sg < segs) wn[sg] = load16(rp + sg * 128);
-            }
-            const float *sp = sc_e + (size_t)(wrow0 >> 7) * sc_cols + (k0 >> 7);
             float acc[ST];
 #pragma unroll
             for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
 #pragma unroll
-            for (int sg = 0; sg < kGUSegs; ++sg) {
-                if (sg < segs) {
-                    const float s = sp[sg];
-                    bf16x2 wb[8];
-                    e4m3x4_to_bf16(w[sg].x, wb[0], wb[1]);
-                    e4m3x4_to_bf16(w[sg].y, wb[2], wb[3]);
-                    e4m3x4_to_bf16(w[sg].z, wb[4], wb[5]);
-                    e4m3x4_to_bf16(w[sg].w, wb[6], wb[7]);
+            for (int sg = 0; sg < SEGS; ++sg) {
+                const float s = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_lane), sg));
+                bf16x2 wb[8];
+                e4m3x4_to_bf16(w[rg][sg].x, wb[0], wb[1]);
+                e4m3x4_to_bf16(w[rg][sg].y, wb[2], wb[3]);
+                e4m3x4_to_bf16(w[rg][sg].z, wb[4], wb[5]);
+                e4m3x4_to_bf16(w[rg][sg].w, wb[6], wb[7]);
 #pragma unroll
-                    for (int j = 0; j < ST; ++j) {
-                        if (j < nt) {
-                            const uint4 xa = xs[j][sg * 16 + sub * 2];
-                            const uint4 xb = xs[j][sg * 16 + sub * 2 + 1];
-                            float d = dot2(wb[0], xa.x, 0.0f);
-                            d = dot2(wb[1], xa.y, d);
-                            d = dot2(wb[2], xa.z, d);
-                            d = dot2(wb[3], xa.w, d);
-                            d = dot2(wb[4], xb.x, d);
-                            d = dot2(wb[5], xb.y, d);
-                            d = dot2(wb[6], xb.z, d);
-                            d = dot2(wb[7], xb.w, d);
-                            acc[j] = fmaf(d, s, acc[j]);
-                        }
+                for (int j = 0; j < ST; ++j) {
+                    if (j < nt) {
+                        const uint4 xa = xs[j][sg * 16 + sub * 2];
+                        const uint4 xb = xs[j][sg * 16 + sub * 2 + 1];
+                        float d = dot2(wb[0], xa.x, 0.0f);
+                        d = dot2(wb[1], xa.y, d);
+                        d = dot2(wb[2], xa.z, d);
+                        d = dot2(wb[3], xa.w, d);
+                        d = dot2(wb[4], xb.x, d);
+                        d = dot2(wb[5], xb.y, d);
+                        d = dot2(wb[6], xb.z, d);
+                        d = dot2(wb[7], xb.w, d);
+                        acc[j] = fmaf(d, s, acc[j]);
                     }
                 }
             }
@@ -184,13 +214,16 @@ __global__ __launch_bounds__(kThreads) void gemv_gateup_e4m3_kernel(GateUpArgs a
 // ---------------------------------------------------------------------------
 // h slice staged in LDS with the float4 of lane `sub`, part q of segment sg at
 // index sg*32 + q*8 + sub, so the 8 lanes of a group read 128 contiguous
-// bytes per LDS instruction (no bank conflicts).
-template <int RG, int ST>
-__global__ __launch_bounds__(kThreads) void gemv_down_e4m3_kernel(DownArgs a)
+// bytes per LDS instruction (no bank conflicts).  The block's 64 rows lie in
+// one 128-row scale block.
+template <int SEGS, int RG, int ST>
+__global__ __launch_bounds__(kThreads, MOE_GEMV_MIN_WAVES) void gemv_down_e4m3_kernel(DownArgs a)
 {
     constexpr int RPW = RG * 8;
     constexpr int RPB = RPW * (kThreads / 64);
-    __shared__ float4 hs[ST][kDownSegs * 32];        // 2048 floats per slot
+    static_assert(128 % RPB == 0, "block rows inside one 128-row scale block");
+    extern __shared__ float4 lds_h[];                // FP32 h slice per slot: [a.st][SEGS*32]
+    float4 (*hs)[SEGS * 32] = reinterpret_cast<float4 (*)[SEGS * 32]>(lds_h);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
@@ -200,78 +233,78 @@ __global__ __launch_bounds__(kThreads) void gemv_down_e4m3_kernel(DownArgs a)
     bid /= a.nks;
     const int tile = bid % a.ntiles;
     const int ai = bid / a.ntiles;
-    if (ai >= *a.num_active) return;
-    const int e = a.active[ai];
-    const int p0 = a.offsets[e];
-    const int ne = a.offsets[e + 1] - p0;
+    const int e = a.active[ai];              // -1 past the active experts
+    if (e < 0) return;
     const int H = a.H, I = a.I;
     const uint8_t *codes = a.codes + (size_t)e * H * I;
     const int sc_cols = I >> 7;
-    const float *sc_e = a.scales + (size_t)e * (H >> 7) * sc_cols;
     const int row_b0 = tile * RPB;
-    const int k0 = ks * kDownSlice;
-    const int segs = min(kDownSegs, (I - k0) >> 7);
+    const int k0 = ks * SEGS * 128;
     float *out = a.out + (size_t)ks * a.S * H;
 
-    for (int st = 0; st < ne; st += ST) {
-        const int nt = min(ST, ne - st);
-        const int cpr = segs * 32;                   // float4 per staged row
-        for (int c = tid; c < nt * cpr; c += kThreads) {
-            const int j = c / cpr, f = c - j * cpr;  // f = source float4 index
+    const float *sc_blk = a.scales + (size_t)e * (H >> 7) * sc_cols +
+                          (size_t)(row_b0 >> 7) * sc_cols + (k0 >> 7);
+    const float sc_lane = sc_blk[lane % SEGS];
+
+    const uint8_t *rp = codes + (size_t)(row_b0 + wave * RPW + grp) * I + k0 + sub * 16;
+    int p0 = 0, ne = 1;
+    for (int st = 0; st < ne; st += a.st) {
+        uint4 w[RG][SEGS];
+#ifdef MOE_GEMV_X_FIRST
+        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
+        const int nt = min(a.st, ne - st);
+        for (int c = tid; c < nt * SEGS * 32; c += kThreads) {
+            const int j = c / (SEGS * 32), f = c - j * (SEGS * 32);  // f = source float4 index
             const int sg = f >> 5, r = f & 31, sb = r >> 2, q = r & 3;
             hs[j][sg * 32 + q * 8 + sb] =
                 *reinterpret_cast<const float4 *>(a.h + (size_t)(p0 + st + j) * I + k0 + f * 4);
         }
+#endif
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) w[rg][sg] = load16(rp + (size_t)rg * 8 * I + sg * 128);
+#ifndef MOE_GEMV_X_FIRST
+        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
+        const int nt = min(a.st, ne - st);
+        for (int c = tid; c < nt * SEGS * 32; c += kThreads) {
+            const int j = c / (SEGS * 32), f = c - j * (SEGS * 32);  // f = source float4 index
+            const int sg = f >> 5, r = f & 31, sb = r >> 2, q = r & 3;
+            hs[j][sg * 32 + q * 8 + sb] =
+                *reinterpret_cast<const float4 *>(a.h + (size_t)(p0 + st + j) * I + k0 + f * 4);
+        }
+#endif
         __syncthreads();
 
-        uint4 wn[kDownSegs];
-        {
-            const uint8_t *rp = codes + (size_t)(row_b0 + wave * RPW + grp) * I + k0 + sub * 16;
-#pragma unroll
-            for (int sg = 0; sg < kDownSegs; ++sg)
-                if (sg < segs) wn[sg] = load16(rp + sg * 128);
-        }
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-            uint4 w[kDownSegs];
-#pragma unroll
-            for (int sg = 0; sg < kDownSegs; ++sg) w[sg] = wn[sg];
-            const int wrow0 = row_b0 + wave * RPW + rg * 8;
-            if (rg + 1 < RG) {
-                const uint8_t *rp = codes + (size_t)(wrow0 + 8 + grp) * I + k0 + sub * 16;
-#pragma unroll
-                for (int sg = 0; sg < kDownSegs; ++sg)
-                    if (sg < segs) wn[sg] = load16(rp + sg * 128);
-            }
-            const float *sp = sc_e + (size_t)(wrow0 >> 7) * sc_cols + (k0 >> 7);
             float acc[ST];
 #pragma unroll
             for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
 #pragma unroll
-            for (int sg = 0; sg < kDownSegs; ++sg) {
-                if (sg < segs) {
-                    const float s = sp[sg];
-                    f32x2 wf[8];
-                    const uint32_t dw[4] = {w[sg].x, w[sg].y, w[sg].z, w[sg].w};
+            for (int sg = 0; sg < SEGS; ++sg) {
+                const float s = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_lane), sg));
+                f32x2 wf[8];
+                const uint32_t dw[4] = {w[rg][sg].x, w[rg][sg].y, w[rg][sg].z, w[rg][sg].w};
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        wf[2 * q] = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[q], false);
-                        wf[2 * q + 1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[q], true);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    wf[2 * q] = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[q], false);
+                    wf[2 * q + 1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[q], true);
+                }
 #pragma unroll
-                    for (int j = 0; j < ST; ++j) {
-                        if (j < nt) {
-                            float d = 0.0f;
+                for (int j = 0; j < ST; ++j) {
+                    if (j < nt) {
+                        float d = 0.0f;
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const float4 hv = hs[j][sg * 32 + q * 8 + sub];
-                                d = fmaf(wf[2 * q].x, hv.x, d);
-                                d = fmaf(wf[2 * q].y, hv.y, d);
-                                d = fmaf(wf[2 * q + 1].x, hv.z, d);
-                                d = fmaf(wf[2 * q + 1].y, hv.w, d);
-                            }
-                            acc[j] = fmaf(d, s, acc[j]);
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 hv = hs[j][sg * 32 + q * 8 + sub];
+                            d = fmaf(wf[2 * q].x, hv.x, d);
+                            d = fmaf(wf[2 * q].y, hv.y, d);
+                            d = fmaf(wf[2 * q + 1].x, hv.z, d);
+                            d = fmaf(wf[2 * q + 1].y, hv.w, d);
                         }
+                        acc[j] = fmaf(d, s, acc[j]);
                     }
                 }
             }
@@ -279,7 +312,8 @@ __global__ __launch_bounds__(kThreads) void gemv_down_e4m3_kernel(DownArgs a)
             for (int j = 0; j < ST; ++j) {
                 if (j < nt) {
                     const float v = moe::sum8_lanes(acc[j]);
-                    if (sub == 0) out[(size_t)(p0 + st + j) * H + wrow0 + grp] = v;
+                    if (sub == 0)
+                        out[(size_t)(p0 + st + j) * H + row_b0 + wave * RPW + rg * 8 + grp] = v;
                 }
             }
         }
@@ -308,47 +342,82 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float *__restrict
 
 // Launch shapes.  Grid = (upper bound on active experts) x (row tiles) x
 // (K slices); blocks whose active index is past num_active exit at once, so
-// the host never needs the routing.  Row tiles (128 rows for gate/up, 64 for
-// down) divide every legal size because n_out % 128 == 0.
+// the host never needs the routing.
+namespace {
+
+template <int SEGS>
+void gateup_launch(const GateUpArgs &a, int grid, hipStream_t st)
+{
+    const size_t lds = (size_t)a.st * SEGS * 16 * sizeof(uint4);
+    hipLaunchKernelGGL((gemv_gateup_e4m3_kernel<SEGS, MOE_E4M3_GU_RG, MOE_E4M3_GU_ST>), dim3(grid),
+                       dim3(kThreads), lds, st, a);
+}
+
+template <int SEGS>
+void down_launch(const DownArgs &a, int grid, hipStream_t st)
+{
+    const size_t lds = (size_t)a.st * SEGS * 32 * sizeof(float4);
+    hipLaunchKernelGGL((gemv_down_e4m3_kernel<SEGS, MOE_E4M3_DN_RG, MOE_E4M3_DN_ST>), dim3(grid),
+                       dim3(kThreads), lds, st, a);
+}
+
+}  // namespace
+
 hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
-                                   const uint16_t *x, const MoeRouteDev &r, int32_t S,
+                                   const uint16_t *x, const MoeRouteDev &r, int32_t M, int32_t S,
                                    int32_t E, int32_t hidden, int32_t inter, float *partials,
                                    int32_t nks, hipStream_t st)
 {
-    constexpr int RG = 4, ST = 8;
-    constexpr int RPB = RG * 8 * (kThreads / 64);
-    static_assert(128 % RPB == 0 || RPB % 128 == 0, "row tile vs 128-row blocks");
     GateUpArgs a;
+    a.st = M < MOE_E4M3_GU_ST ? M : MOE_E4M3_GU_ST;
     a.gcodes = gate.codes; a.ucodes = up.codes;
     a.gscales = (const float *)gate.scales; a.uscales = (const float *)up.scales;
     a.x = x; a.offsets = r.offsets; a.sorted_token = r.sorted_token; a.active = r.active;
     a.num_active = r.num_active; a.partials = partials;
-    a.S = S; a.H = hidden; a.I = inter; a.nks = nks;
-    a.ntiles = 2 * (inter / RPB);
-    const int amax = S < E ? S : E;
-    hipLaunchKernelGGL((gemv_gateup_e4m3_kernel<RG, ST>), dim3(amax * a.ntiles * nks),
-                       dim3(kThreads), 0, st, a);
+    a.S = S; a.H = hidden; a.I = inter;
+    const int segs = gemv_segs_gateup(kFmtE4M3, hidden);
+    a.nks = gemv_gateup_slices(kFmtE4M3, hidden);
+    if (a.nks != nks) return hipErrorInvalidValue;
+    a.ntiles = 2 * (inter / (MOE_E4M3_GU_RG * 32));
+    const int grid = (S < E ? S : E) * a.ntiles * a.nks;
+    switch (segs) {
+    case 8: gateup_launch<8>(a, grid, st); break;
+    case 7: gateup_launch<7>(a, grid, st); break;
+    case 6: gateup_launch<6>(a, grid, st); break;
+    case 5: gateup_launch<5>(a, grid, st); break;
+    case 4: gateup_launch<4>(a, grid, st); break;
+    case 3: gateup_launch<3>(a, grid, st); break;
+    case 2: gateup_launch<2>(a, grid, st); break;
+    default: gateup_launch<1>(a, grid, st); break;
+    }
     return hipGetLastError();
 }
 
-int gemv_down_slices(int32_t inter) { return (inter + kDownSlice - 1) / kDownSlice; }
-
 hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
-                                 int32_t S, int32_t E, int32_t hidden, int32_t inter, float *y,
-                                 float *slice_scratch, hipStream_t st)
+                                 int32_t M, int32_t S, int32_t E, int32_t hidden, int32_t inter,
+                                 float *y, float *slice_scratch, hipStream_t st)
 {
-    constexpr int RG = 2, ST = 4;
-    constexpr int RPB = RG * 8 * (kThreads / 64);
     DownArgs a;
+    a.st = M < MOE_E4M3_DN_ST ? M : MOE_E4M3_DN_ST;
     a.codes = down.codes; a.scales = (const float *)down.scales; a.h = h;
     a.offsets = r.offsets; a.active = r.active; a.num_active = r.num_active;
     a.S = S; a.H = hidden; a.I = inter;
-    a.nks = gemv_down_slices(inter);
+    const int segs = gemv_segs_down(kFmtE4M3, inter);
+    a.nks = gemv_down_slices(kFmtE4M3, inter);
     a.out = a.nks == 1 ? y : slice_scratch;
-    a.ntiles = hidden / RPB;
-    const int amax = S < E ? S : E;
-    hipLaunchKernelGGL((gemv_down_e4m3_kernel<RG, ST>), dim3(amax * a.ntiles * a.nks),
-                       dim3(kThreads), 0, st, a);
+    a.ntiles = hidden / (MOE_E4M3_DN_RG * 32);
+    const int grid = (S < E ? S : E) * a.ntiles * a.nks;
+    switch (segs) {
+    case 16: down_launch<16>(a, grid, st); break;
+    case 8: down_launch<8>(a, grid, st); break;
+    case 7: down_launch<7>(a, grid, st); break;
+    case 6: down_launch<6>(a, grid, st); break;
+    case 5: down_launch<5>(a, grid, st); break;
+    case 4: down_launch<4>(a, grid, st); break;
+    case 3: down_launch<3>(a, grid, st); break;
+    case 2: down_launch<2>(a, grid, st); break;
+    default: down_launch<1>(a, grid, st); break;
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.nks == 1) return err;
     const size_t n4 = (size_t)S * hidden / 4;

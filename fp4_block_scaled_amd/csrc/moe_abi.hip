@@ -43,17 +43,11 @@ moe_status_t hip_fail(hipError_t e, const char *what)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
-int64_t gemv_gateup_slices(int32_t fmt, int32_t hidden)
-{
-    const int slice = fmt == MOE_W_NVFP4_B16 ? kGemvSliceNVFP4 : kGemvSliceE4M3;
-    return (hidden + slice - 1) / slice;
-}
-
 // FFN scratch of the GEMV tier for S slots.
 size_t gemv_scratch_bytes(int64_t S, int32_t hidden, int32_t inter, int32_t fmt)
 {
     const int64_t nks = gemv_gateup_slices(fmt, hidden);
-    const int64_t nkd = gemv_down_slices(inter);
+    const int64_t nkd = gemv_down_slices(fmt, inter);
     size_t b = moe::align256(sizeof(float) * (size_t)(nks * S * 2 * inter));   // gate/up partials
     b += moe::align256(sizeof(float) * (size_t)(S * inter));                   // h
     if (nkd > 1) b += moe::align256(sizeof(float) * (size_t)(nkd * S * hidden)); // down slices
@@ -72,7 +66,7 @@ GemvScratch carve_gemv(char *base, int64_t S, int32_t hidden, int32_t inter, int
     base += moe::align256(sizeof(float) * (size_t)(nks * S * 2 * inter));
     s.h = (float *)base;
     base += moe::align256(sizeof(float) * (size_t)(S * inter));
-    s.down_slices = gemv_down_slices(inter) > 1 ? (float *)base : nullptr;
+    s.down_slices = gemv_down_slices(fmt, inter) > 1 ? (float *)base : nullptr;
     return s;
 }
 
@@ -246,14 +240,14 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
     GemvBankDev bg{gate->codes, gate->scales, gate->scale2};
     GemvBankDev bu{up->codes, up->scales, up->scale2};
     GemvBankDev bd{down->codes, down->scales, down->scale2};
-    const int32_t nks = (int32_t)gemv_gateup_slices(fmt, hidden);
+    const int32_t nks = gemv_gateup_slices(fmt, hidden);
     hipError_t e;
     stage_mark(0, s);
     if (fmt == MOE_W_E4M3_B128)
-        e = launch_gemv_gateup_e4m3(bg, bu, x_bf16, r, (int32_t)S, E, hidden, inter, g.partials,
+        e = launch_gemv_gateup_e4m3(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, g.partials,
                                     nks, s);
     else
-        e = launch_gemv_gateup_nvfp4(bg, bu, x_bf16, r, (int32_t)S, E, hidden, inter, g.partials,
+        e = launch_gemv_gateup_nvfp4(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, g.partials,
                                      nks, s);
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: gate/up GEMV launch");
     stage_mark(1, s);
@@ -261,10 +255,10 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: SwiGLU launch");
     stage_mark(2, s);
     if (fmt == MOE_W_E4M3_B128)
-        e = launch_gemv_down_e4m3(bd, g.h, r, (int32_t)S, E, hidden, inter, y_packed,
+        e = launch_gemv_down_e4m3(bd, g.h, r, M, (int32_t)S, E, hidden, inter, y_packed,
                                   g.down_slices, s);
     else
-        e = launch_gemv_down_nvfp4(bd, g.h, r, (int32_t)S, E, hidden, inter, y_packed,
+        e = launch_gemv_down_nvfp4(bd, g.h, r, M, (int32_t)S, E, hidden, inter, y_packed,
                                    g.down_slices, s);
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: down GEMV launch");
     stage_mark(3, s);

@@ -66,23 +66,25 @@ struct GemvBankDev {
     const float *scale2;
 };
 
+// M bounds the slots one expert usually holds (one per token); it sizes the
+// LDS slot tile.  Experts holding more slots are swept in several passes.
 hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
-                                   const uint16_t *x, const MoeRouteDev &r,
+                                   const uint16_t *x, const MoeRouteDev &r, int32_t M,
                                    int32_t S, int32_t E, int32_t hidden, int32_t inter,
                                    float *partials, int32_t nks, hipStream_t st);
-// Down projection; when inter > 2048 the K slices go to slice_scratch
-// ([gemv_down_slices(inter)][S][hidden] floats) and are summed in order into y.
-int gemv_down_slices(int32_t inter);
+// Down projection; with more than one K slice the slices go to slice_scratch
+// ([gemv_down_slices(fmt, inter)][S][hidden] floats) and are summed in order
+// into y.
 hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
-                                 int32_t S, int32_t E, int32_t hidden, int32_t inter,
+                                 int32_t M, int32_t S, int32_t E, int32_t hidden, int32_t inter,
                                  float *y, float *slice_scratch, hipStream_t st);
 
 hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
-                                    const uint16_t *x, const MoeRouteDev &r,
+                                    const uint16_t *x, const MoeRouteDev &r, int32_t M,
                                     int32_t S, int32_t E, int32_t hidden, int32_t inter,
                                     float *partials, int32_t nks, hipStream_t st);
 hipError_t launch_gemv_down_nvfp4(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
-                                  int32_t S, int32_t E, int32_t hidden, int32_t inter,
+                                  int32_t M, int32_t S, int32_t E, int32_t hidden, int32_t inter,
                                   float *y, float *slice_scratch, hipStream_t st);
 
 // h[p][n] = swiglu_clamp(sum_ks P[ks][p][n], sum_ks P[ks][p][I + n]) for p < offsets[E].
@@ -93,6 +95,31 @@ hipError_t launch_swiglu_partials(const float *partials, int32_t nks, int32_t S,
 hipError_t launch_combine(const float *y, const int32_t *token_to_perm, const float *w,
                           int32_t M, int32_t k, int32_t hidden, float *out, hipStream_t st);
 
-// Slices of the GEMV tier's gate/up K loop (k values per slice).
-constexpr int kGemvSliceE4M3 = 1024;
-constexpr int kGemvSliceNVFP4 = 2048;
+// K slicing of the GEMV tier.  A segment is the K span of one 128-byte row
+// chunk (128 values for E4M3, 256 for NVFP4); a slice is SEGS segments with
+// SEGS the largest divisor of the segment count not above the cap (8, or 16
+// for the E4M3 down projection when it divides).  Host sizing and launches
+// both use these.
+constexpr int kFmtE4M3 = 1, kFmtNVFP4 = 2;
+inline int gemv_seg_k(int fmt) { return fmt == kFmtNVFP4 ? 256 : 128; }
+inline int gemv_pick_segs(int nsegs, int cap)
+{
+    for (int d = cap; d > 1; --d)
+        if (nsegs % d == 0) return d;
+    return 1;
+}
+inline int gemv_segs_gateup(int fmt, int hidden) { return gemv_pick_segs(hidden / gemv_seg_k(fmt), 8); }
+inline int gemv_segs_down(int fmt, int inter)
+{
+    const int n = inter / gemv_seg_k(fmt);
+    if (fmt == kFmtE4M3 && n % 16 == 0) return 16;
+    return gemv_pick_segs(n, 8);
+}
+inline int gemv_gateup_slices(int fmt, int hidden)
+{
+    return hidden / gemv_seg_k(fmt) / gemv_segs_gateup(fmt, hidden);
+}
+inline int gemv_down_slices(int fmt, int inter)
+{
+    return inter / gemv_seg_k(fmt) / gemv_segs_down(fmt, inter);
+}

@@ -81,6 +81,14 @@ __global__ __launch_bounds__(kThreads) void route_pack_kernel(
         if (tid == E - 1) { offsets[E] = ex_c + c; *num_active = ex_f + f; }
     }
     __syncthreads();
+    // entries past num_active hold -1, so a consumer that reads active[i]
+    // for i < min(E, S) can tell an unused entry without reading num_active
+    {
+        int na = 0;
+        for (int w = 0; w < kWaves; ++w) na += wsum_f[w];
+        const int A = S < E ? S : E;
+        for (int i = na + tid; i < A; i += kThreads) active[i] = -1;
+    }
 
     // 3. stable placement, 1024 slots per chunk
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));

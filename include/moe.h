@@ -112,8 +112,9 @@ typedef struct {
  *   sorted_slot    [S]    packed row -> slot          (first expert_offsets[E])
  *   sorted_token   [S]    packed row -> token
  *   token_to_perm  [S]    slot -> packed row, -1 for an invalid/unfilled id
- *   active_experts [min(E,S)]  ascending ids of experts with >= 1 slot
- *   num_active     [1]    length of active_experts
+ *   active_experts [min(E,S)]  ascending ids of experts with >= 1 slot,
+ *                         then -1 up to min(E,S)
+ *   num_active     [1]    number of experts with >= 1 slot
  *   status         [1]    number of ids outside [0, E) other than -1       */
 typedef struct {
     int32_t M;

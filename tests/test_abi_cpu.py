@@ -42,10 +42,12 @@ def test_workspace_bytes_hand_computed():
     route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
     gemv = a256(4 * 3 * S * 2 * I) + a256(4 * S * I)
     assert B.moe_workspace_bytes(16, 8, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_AUTO) == route + gemv
-    # inter beyond one 2048-wide down slice adds the slice buffer
+    # inter = 2304 = 18 segments of 128: the down slice is 6 segments (the
+    # largest divisor <= 8, since 16 does not divide 18), so 3 slices and a
+    # slice buffer; hidden 256 = 2 segments -> one gate/up slice
     S, E, H, I = 2, 4, 256, 2304
     route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
-    gemv = a256(4 * 1 * S * 2 * I) + a256(4 * S * I) + a256(4 * 2 * S * H)
+    gemv = a256(4 * 1 * S * 2 * I) + a256(4 * S * I) + a256(4 * 3 * S * H)
     assert B.moe_workspace_bytes(1, 2, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16) == route + gemv
     # monotone in max_M
     sizes = [B.moe_workspace_bytes(m, 8, 256, 7168, 2048, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16)

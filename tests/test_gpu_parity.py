@@ -46,6 +46,7 @@ def assert_pack_equal(got, ref, S):
     assert np.array_equal(got["token_to_perm"], ref["token_to_perm"])
     assert int(got["num_active"][0]) == ref["num_active"]
     assert np.array_equal(got["active_experts"][:ref["num_active"]], ref["active_experts"])
+    assert np.all(got["active_experts"][ref["num_active"]:] == -1)
     assert int(got["status"][0]) == ref["invalid"]
 
 
