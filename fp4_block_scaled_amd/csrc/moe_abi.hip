@@ -90,10 +90,43 @@ bool ffn_dims_ok(int32_t fmt, int32_t hidden, int32_t inter)
     return true;
 }
 
-size_t ffn_bytes(int64_t S, int32_t hidden, int32_t inter, int32_t fmt, int32_t mode)
+// FFN scratch of the FP8 GEMM tier for M tokens and S slots.
+struct GemmScratch {
+    uint8_t *xq, *hq;
+    float *xs, *hs;
+    int2 *tiles;
+    int32_t *ntiles;
+};
+
+size_t gemm_scratch_bytes(int64_t M, int64_t S, int32_t E, int32_t hidden, int32_t inter)
+{
+    const int64_t tmax = gemm_max_tiles((int32_t)S, E);
+    return moe::align256((size_t)(M * hidden)) +                          // xq
+           moe::align256(sizeof(float) * (size_t)(M * (hidden / 128))) +  // xs
+           moe::align256((size_t)(S * inter)) +                           // hq
+           moe::align256(sizeof(float) * (size_t)(S * (inter / 128))) +   // hs
+           moe::align256(sizeof(int2) * (size_t)tmax) + 256;              // tiles, count
+}
+
+GemmScratch carve_gemm(char *p, int64_t M, int64_t S, int32_t E, int32_t hidden, int32_t inter)
+{
+    GemmScratch g;
+    const int64_t tmax = gemm_max_tiles((int32_t)S, E);
+    g.xq = (uint8_t *)p;  p += moe::align256((size_t)(M * hidden));
+    g.xs = (float *)p;    p += moe::align256(sizeof(float) * (size_t)(M * (hidden / 128)));
+    g.hq = (uint8_t *)p;  p += moe::align256((size_t)(S * inter));
+    g.hs = (float *)p;    p += moe::align256(sizeof(float) * (size_t)(S * (inter / 128)));
+    g.tiles = (int2 *)p;  p += moe::align256(sizeof(int2) * (size_t)tmax);
+    g.ntiles = (int32_t *)p;
+    return g;
+}
+
+size_t ffn_bytes(int64_t M, int64_t S, int32_t E, int32_t hidden, int32_t inter, int32_t fmt,
+                 int32_t mode)
 {
     if (mode == MOE_MODE_GEMV_A16) return gemv_scratch_bytes(S, hidden, inter, fmt);
-    return 0;  // GEMM tier: not served by this build
+    if (fmt != MOE_W_E4M3_B128) return 0;
+    return gemm_scratch_bytes(M, S, E, hidden, inter);
 }
 
 }  // namespace
@@ -107,9 +140,10 @@ int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt,
 {
     g_stage_events = events;
     g_stage_n = events ? n_events : 0;
-    (void)fmt; (void)hidden; (void)inter;
-    if (mode == MOE_MODE_GEMM_A8) return 0;
-    return 3;  // gate/up GEMV, SwiGLU, down GEMV (with its slice sum, if any)
+    (void)fmt; (void)hidden; (void)inter; (void)mode;
+    // GEMV tier: gate/up GEMV, SwiGLU, down GEMV (with its slice sum, if any)
+    // GEMM tier: activation quantization + tile schedule, gate/up GEMM, down GEMM
+    return 3;
 }
 
 int32_t moe_resolve_mode(int32_t M, int32_t fmt, int32_t requested)
@@ -128,13 +162,13 @@ size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts, in
     size_t ffn;
     if (mode == MOE_MODE_AUTO) {
         const int64_t mg = max_M < MOE_GEMV_MAX_M ? max_M : MOE_GEMV_MAX_M;
-        ffn = ffn_bytes(mg * top_k, hidden, inter, fmt, MOE_MODE_GEMV_A16);
+        ffn = ffn_bytes(mg, mg * top_k, num_experts, hidden, inter, fmt, MOE_MODE_GEMV_A16);
         if (max_M > MOE_GEMV_MAX_M) {
-            const size_t g = ffn_bytes(S, hidden, inter, fmt, MOE_MODE_GEMM_A8);
+            const size_t g = ffn_bytes(max_M, S, num_experts, hidden, inter, fmt, MOE_MODE_GEMM_A8);
             ffn = g > ffn ? g : ffn;
         }
     } else {
-        ffn = ffn_bytes(S, hidden, inter, fmt, mode);
+        ffn = ffn_bytes(max_M, S, num_experts, hidden, inter, fmt, mode);
     }
     return moe::route_region_bytes(S, num_experts) + ffn;
 }
@@ -225,8 +259,8 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
     if (!(limit > 0.0f)) return fail(MOE_ERR_ARG, "moe_expert_ffn: limit must be > 0");
     const int32_t M = route->M, k = route->top_k;
     const int32_t tier = resolve(M, fmt, mode);
-    if (tier == MOE_MODE_GEMM_A8)
-        return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: GEMM_A8 tier is not available in this build");
+    if (tier == MOE_MODE_GEMM_A8 && fmt != MOE_W_E4M3_B128)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: the FP8 GEMM tier serves E4M3 banks only");
     const size_t need = moe_workspace_bytes(M, k, E, hidden, inter, fmt, tier);
     if (ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu bytes < %zu", ws_bytes, need);
@@ -236,6 +270,27 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
     MoeRouteDev r{route->expert_offsets, route->sorted_slot, route->sorted_token,
                   route->token_to_perm, route->active_experts, route->num_active, route->status};
     char *scratch = (char *)ws + moe::route_region_bytes(S, E);
+    if (tier == MOE_MODE_GEMM_A8) {
+        GemmScratch gs = carve_gemm(scratch, M, S, E, hidden, inter);
+        const int32_t tmax = gemm_max_tiles((int32_t)S, E);
+        hipError_t e;
+        stage_mark(0, s);
+        e = launch_quant_act(x_bf16, M, hidden, gs.xq, gs.xs, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: activation quantization launch");
+        e = launch_gemm_tiles(r.offsets, E, tmax, gs.tiles, gs.ntiles, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: tile schedule launch");
+        stage_mark(1, s);
+        e = launch_gemm_gateup(gs.xq, gs.xs, r.sorted_token, gate->codes, (const float *)gate->scales,
+                               up->codes, (const float *)up->scales, r.offsets, gs.tiles,
+                               gs.ntiles, tmax, hidden, inter, limit, gs.hq, gs.hs, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: gate/up GEMM launch");
+        stage_mark(2, s);
+        e = launch_gemm_down(gs.hq, gs.hs, down->codes, (const float *)down->scales, r.offsets,
+                             gs.tiles, gs.ntiles, tmax, hidden, inter, y_packed, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: down GEMM launch");
+        stage_mark(3, s);
+        return MOE_OK;
+    }
     GemvScratch g = carve_gemv(scratch, S, hidden, inter, fmt);
     GemvBankDev bg{gate->codes, gate->scales, gate->scale2};
     GemvBankDev bu{up->codes, up->scales, up->scale2};

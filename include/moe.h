@@ -180,8 +180,9 @@ moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
  * moe_expert_ffn calls on this thread record events[0] on their stream before
  * the first kernel and events[i] after the i-th kernel, for at most
  * n_events events; NULL turns it off.  The handles are the caller's
- * hipEvent_t.  Returns the number of stages the given tier records (GEMV
- * tier: gate/up, SwiGLU, down), so n_events = that + 1 covers them all.  Mirrors the
+ * hipEvent_t.  Returns the number of stages a tier records (3: GEMV tier
+ * gate/up, SwiGLU, down; GEMM tier activation quantization + tile
+ * schedule, gate/up with SwiGLU, down), so n_events = 4 covers them all.  Mirrors the
  * per-stage timers of "spark_model glm5next_mlp/forward.rs" (profile::start /
  * profile::end around the MoE stages). */
 int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt,

@@ -81,3 +81,88 @@ class GpuCase:
         torch.cuda.synchronize()
         tabs = {k: v.cpu().numpy() for k, v in L.route_tables().items()}
         return out.cpu().numpy(), L.y.cpu().numpy(), tabs, L
+
+
+def _a256(n):
+    return (n + 255) // 256 * 256
+
+
+def route_region_bytes(S, E):
+    A = min(S, E)
+    return _a256(4 * (E + 1)) + 3 * _a256(4 * S) + _a256(4 * max(A, 1)) + _a256(8)
+
+
+def gemm_scratch_views(ws: torch.Tensor, M, S, E, hidden, inter):
+    """xq, xs, hq, hs of the FP8 GEMM tier inside the workspace (the carving
+    order of the library's GEMM scratch: xq, xs, hq, hs, tiles, count)."""
+    o = route_region_bytes(S, E)
+    xq = ws[o:o + M * hidden].view(M, hidden)
+    o += _a256(M * hidden)
+    xs = ws[o:o + 4 * M * (hidden // 128)].view(torch.float32).view(M, hidden // 128)
+    o += _a256(4 * M * (hidden // 128))
+    hq = ws[o:o + S * inter].view(S, inter)
+    o += _a256(S * inter)
+    hs = ws[o:o + 4 * S * (inter // 128)].view(torch.float32).view(S, inter // 128)
+    return xq, xs, hq, hs
+
+
+# Accuracy of one FP8 MFMA dot product on gfx950.  Measured on MI355X with
+# random E4M3 operands against FP64: the error of a 128-term dot product is at
+# most 5.3e-4 of its largest term (v_mfma_f32_16x16x128_f8f6f4 and four
+# v_mfma_f32_16x16x32_fp8_fp8 agree).  Twice that, per 128-wide K block, is
+# the bound used here.
+MFMA_DOT_EPS = 1e-3
+
+
+def blockmax_sum(w_abs: np.ndarray, x_abs: np.ndarray) -> np.ndarray:
+    """For rows x (n, K) and a matrix |W| (N, K): sum over 128-wide K blocks
+    of the largest |w_k x_k| in the block -> (n, N)."""
+    N, K = w_abs.shape
+    Wr = w_abs.reshape(N, K // 128, 128)
+    out = np.empty((x_abs.shape[0], N))
+    for i in range(x_abs.shape[0]):
+        out[i] = (Wr * x_abs[i].reshape(K // 128, 128)[None]).max(axis=2).sum(axis=1)
+    return out
+
+
+def h_error_bound(g, u, g_blk, u_blk, limit, eps=MFMA_DOT_EPS):
+    """Bound on |h_gpu - h_exact| when g and u carry absolute errors up to
+    dg = eps * g_blk, du = eps * u_blk (g_blk, u_blk from blockmax_sum).
+    |silu'| <= 1.1 everywhere; the gate term vanishes once g is surely above
+    the cap, the up term once |u| is surely above it."""
+    dg, du = eps * g_blk, eps * u_blk
+    gc = np.minimum(g, limit)
+    silu = gc / (1.0 + np.exp(-gc))
+    gate = np.where(g - dg < limit, 1.1 * dg, 0.0) * np.minimum(np.abs(u) + du, limit)
+    up = np.where(np.abs(u) - du < limit, (np.abs(silu) + 1.1 * dg) * du, 0.0)
+    return gate + up + 1e-6 * np.abs(silu * np.clip(u, -limit, limit))
+
+
+def check_h_codes(hq_gpu, hs_gpu, h_exact, dh_bound, label):
+    """h is re-quantized per 1x128 group from g and u that the GPU accumulates
+    on FP8 MFMA, so its rounding decisions are taken on values the oracle
+    knows only to within dh_bound (a decision the oracle cannot take in the
+    kernel's precision).  Valid: a code between the roundings of v - d and
+    v + d, with v = h_exact / scale and d = dh_bound / scale + |v| * (scale
+    tolerance) in code units (rounding is monotone).  The group scale must
+    agree to the bound of the group's largest element."""
+    tab = oracle.e4m3_table()
+    hf = h_exact.astype(np.float32)
+    q_ref, s_ref = oracle.quant_1x128(hf)
+    amax = np.abs(hf.reshape(hf.shape[0], -1, 128)).max(axis=2).astype(np.float64)
+    gb = dh_bound.reshape(hf.shape[0], -1, 128).max(axis=2)
+    rel = np.abs(hs_gpu.astype(np.float64) / s_ref - 1.0)
+    tol = gb / np.maximum(amax, 1e-30) + 1e-6
+    assert np.all(rel <= tol), f"{label}: h scales differ by {rel.max():.2e}"
+    sc = np.repeat(s_ref.astype(np.float64), 128, axis=1)
+    v = hf.astype(np.float64) / sc
+    d = dh_bound / sc + np.abs(v) * np.repeat(tol, 128, axis=1) + 1e-9
+    diff = hq_gpu != q_ref
+    idx = np.nonzero(diff)
+    if idx[0].size:
+        lo = oracle.e4m3_encode((v[idx] - d[idx]).astype(np.float32))
+        hi = oracle.e4m3_encode((v[idx] + d[idx]).astype(np.float32))
+        gv = tab[hq_gpu[idx]]
+        ok = (gv >= tab[lo]) & (gv <= tab[hi])
+        assert ok.all(), f"{label}: {int((~ok).sum())} h codes outside the kernel's error bound"
+    return float(diff.mean())
