@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_e4m3_m1")
     ap.add_argument("--route-sets", type=int, default=16)
-    ap.add_argument("--also", default="verify_e4m3_m8,nvfp4_m1,nvfp4_m16",
+    ap.add_argument("--also", default="verify_e4m3_m8,nvfp4_m1,nvfp4_m16,prefill_e4m3_m4096",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -140,7 +140,10 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True):
             hip.record(ev[per - 1], sh)
         B.moe_set_stage_events(None, wl.fmt, wl.hidden, wl.inter, mode)
         torch.cuda.synchronize()
-        names = ["route_pack", "gateup_gemv", "swiglu", "down_gemv", "combine"]
+        if mode == B.MOE_MODE_GEMM_A8:
+            names = ["route_pack", "act_quant_tiles", "gateup_gemm", "down_gemm", "combine"]
+        else:
+            names = ["route_pack", "gateup_gemv", "swiglu", "down_gemv", "combine"]
         acc = np.zeros(per - 1)
         for ev, _ in evs:
             for j in range(per - 1):
@@ -151,9 +154,12 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True):
     alg_layer = float(np.mean([a[0] for a in alg]))
     alg_gateup = float(np.mean([a[1] for a in alg]))
     uniq = float(np.mean([a[2] for a in alg]))
+    # dense-equivalent FLOPs of the valid slots: 2 (gate, up) + 1 (down) products of I*H
+    flops = float(np.mean([6.0 * int(((s[0] >= 0) & (s[0] < wl.experts)).sum()) * wl.hidden * wl.inter
+                           for s in sets]))
     return dict(us_layer=us_layer, ms_total=total_ms, stable=stable, stages=stages,
                 alg_layer_bytes=alg_layer, alg_gateup_bytes=alg_gateup, unique_experts=uniq,
-                layer=layer, x=x, sets=sets)
+                flops=flops, mode=mode, layer=layer, x=x, sets=sets)
 
 
 def cpu_baseline(wl, banks, x, sets, budget_s):
@@ -186,6 +192,24 @@ def cpu_baseline(wl, banks, x, sets, budget_s):
                        f"selected experts copied to host before timing")
 
 
+def roofline(r):
+    """Roofline of the dominant kernel of the tier that ran: the gate/up GEMV
+    against HBM bandwidth, or the gate/up FP8 GEMM against the FP8 MFMA peak."""
+    if r["mode"] == 2:
+        us = r["stages"]["gateup_gemm"]
+        flop = r["flops"] * 2.0 / 3.0
+        tf = flop / (us * 1e-6) / 1e12
+        return {"kernel": "gemm_gateup", "bound": "mfma", "achieved": round(tf, 1),
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                "traffic": None, "alg_flop_per_launch": round(flop), "avg_launch_us": round(us, 3)}
+    us = r["stages"]["gateup_gemv"]
+    gbps = r["alg_gateup_bytes"] / (us * 1e-6) / 1e9
+    return {"kernel": "gemv_gateup", "bound": "hbm", "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None, "alg_bytes_per_launch": round(r["alg_gateup_bytes"]),
+            "avg_launch_us": round(us, 3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -210,8 +234,6 @@ def main():
           flush=True)
 
     gbps = r["alg_layer_bytes"] / (r["us_layer"] * 1e-6) / 1e9
-    gu_us = r["stages"]["gateup_gemv"]
-    gu_gbps = r["alg_gateup_bytes"] / (gu_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(r["us_layer"], 3),
@@ -233,12 +255,10 @@ def main():
         "tokens_per_s": round(wl.M / (r["us_layer"] * 1e-6), 1),
         "stages_us": {k: round(v, 3) for k, v in r["stages"].items()},
         "output_stable": r["stable"],
-        "roofline": {"kernel": "gemv_gateup", "bound": "hbm", "achieved": round(gu_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
-                     "alg_bytes_per_launch": round(r["alg_gateup_bytes"]),
-                     "avg_launch_us": round(gu_us, 3)},
+        "roofline": roofline(r),
     }
+    if r["mode"] == 2:
+        line["alg_TFLOPs"] = round(r["flops"] / (r["us_layer"] * 1e-6) / 1e12, 1)
     also = {}
     for name in [a for a in args.also.split(",") if a]:
         w2 = workloads.WORKLOADS[name]
@@ -246,12 +266,18 @@ def main():
         b2 = banks if same else workloads.make_banks(w2, "cuda")
         r2 = measure(w2, b2, max(20, args.steps // 2), args.warmup, args.route_sets, hip)
         g2 = r2["alg_layer_bytes"] / (r2["us_layer"] * 1e-6) / 1e9
+        tf = r2["flops"] / (r2["us_layer"] * 1e-6) / 1e12
         also[name] = {"us_layer": round(r2["us_layer"], 3), "weight_read_GBps": round(g2, 1),
                       "hbm_frac": round(g2 / HBM_PEAK_GBPS, 4),
                       "tokens_per_s": round(w2.M / (r2["us_layer"] * 1e-6), 1),
                       "unique_experts": r2["unique_experts"],
                       "stages_us": {k: round(v, 3) for k, v in r2["stages"].items()},
                       "output_stable": r2["stable"]}
+        also[name]["roofline"] = roofline(r2)
+        if r2["mode"] == 2:
+            also[name].update({"tier": "fp8_mfma_grouped_gemm", "alg_TFLOPs": round(tf, 1),
+                               "mfma_frac_fp8": round(tf / FP8_PEAK_TFLOPS, 4)})
+            line["prefill_tokens_per_s"] = also[name]["tokens_per_s"]
         print(f"# {name}: {r2['us_layer']:.2f} us/layer", file=sys.stderr, flush=True)
         if not same:
             del b2

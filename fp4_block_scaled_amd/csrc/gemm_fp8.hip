@@ -22,9 +22,8 @@
 //                       the 128-wide h row segment (exactly one 1x128 group)
 //                       to E4M3 + scale in the epilogue.
 //   gemm_down_kernel    one block = 128 packed rows x 128 outputs of y.
-// Tiles: 4 waves as 2x2, 64x64 (x2 for gate/up) per wave; A and B staged
-// through LDS with a 16-byte row pad (conflict-free operand reads), two LDS
-// stages and a two-deep register prefetch of the global tiles.
+// Tiles: 4 waves as 2x2, 64x64 (x2 for gate/up) per wave; A and B move from
+// global memory straight into three swizzled LDS stages (see below).
 #include "moe_internal.h"
 
 namespace {
@@ -35,7 +34,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int BM = 128;       // packed rows per tile
 constexpr int BK = 128;       // K per step = one scale block = one MFMA
-constexpr int PITCH = 144;    // LDS row pitch in bytes (128 + 16 pad)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
 
@@ -127,6 +125,18 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t *__restr
 // ---------------------------------------------------------------------------
 // shared pieces of the two GEMMs
 // ---------------------------------------------------------------------------
+// Block: 256 threads = 4 waves as 2 (rows) x 2 (columns).  Tiles move from
+// global memory straight into LDS (global_load_lds_dwordx4: lane i of one
+// instruction fills bytes 16i..16i+15 of a 1 KB run = 8 rows x 128 bytes),
+// three LDS stages deep, so two K steps of loads are always in flight without
+// holding any VGPRs.  Inside a stage a row's eight 16-byte chunks are stored
+// XOR-swizzled by (row >> 1) & 7: the 16 lanes that feed one MFMA operand
+// half (16 rows, same K chunk) then hit 16 distinct bank groups.  Each wave
+// loads the activation scales of its own 64 rows into its own 256-byte slot.
+// Every wave issues the same number of DMA instructions per stage, so an
+// immediate vmcnt wait tells a wave its share of a stage has landed; one
+// barrier per K step publishes the stage to all waves and retires the stage
+// that the next DMA overwrites.
 struct GemmArgs {
     const uint8_t *a;          // gate/up: xq [M][K]; down: hq [S][K]
     const float *as;           // activation scales [rows][K/128]
@@ -143,29 +153,61 @@ struct GemmArgs {
     float limit;
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8 &a, const i32x8 &b)
 {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ i32x8 lds_op(const uint8_t *lds_tile, int row, int lane)
+__device__ __forceinline__ float lane_f(float v, int l)
 {
-    const uint8_t *p = lds_tile + row * PITCH + (lane >> 4) * 32;
-    const uint4 lo = *reinterpret_cast<const uint4 *>(p);
-    const uint4 hi = *reinterpret_cast<const uint4 *>(p + 16);
-    i32x8 r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-__device__ __forceinline__ uint4 ldg_nt(const uint8_t *p)
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// 32-byte MFMA operand of lane `lane` for tile row `row` (K chunks 2q, 2q+1, q = lane/16)
+// (one byte offset per 16-byte read, so every LDS access stays a direct
+// offset of its stage array and the compiler can tell the stages apart when
+// it places waits for the DMA)
+__device__ __forceinline__ i32x8 lds_op(const uint8_t *tile, int row, int lane)
 {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
+    const int c = (lane >> 4) * 2;
+    const i32x4 lo = *reinterpret_cast<const i32x4 *>(tile + (row * 128 + swz(row, c) * 16));
+    const i32x4 hi = *reinterpret_cast<const i32x4 *>(tile + (row * 128 + swz(row, c + 1) * 16));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+
+// LDS DMA: lane i of the wave reads `size` bytes at base + off_i (base
+// wave-uniform, off_i a 32-bit byte offset) and the hardware writes them to
+// LDS at M0 + i * size (M0 = the wave-uniform LDS byte address of the run).  Written as inline asm so the compiler does
+// not track these loads: it would otherwise place a full vmcnt(0) before the
+// first LDS read of each loop trip.  The waits for them are the explicit
+// vmcnt waits below; the compiler's own waits for its own loads only get more
+// conservative, since vector memory loads retire in order.  One wait state
+// separates the M0 write from the DMA.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(size_t)(const lds_void *)p;
+}
+
+__device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ void dma4(const void *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" :: "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt with only vmcnt = N (expcnt and lgkmcnt left alone), and lgkmcnt(0)
+#define MOE_WAIT_VM(N) __builtin_amdgcn_s_waitcnt((((N) & 15) | (7 << 4) | (15 << 8) | ((((N) >> 4) & 3) << 14)))
+#define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+#define MOE_BARRIER() asm volatile("s_barrier" ::: "memory")
 
 __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 {
@@ -177,237 +219,214 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 // ---------------------------------------------------------------------------
 // gate + up (+ SwiGLU + h quantization)
 // ---------------------------------------------------------------------------
-// 512 threads = 8 waves as 2 (rows) x 4 (columns); a wave owns 64 rows x 32
-// h-columns of both the gate and the up product (64 FP32 accumulators per
-// lane), so SwiGLU is elementwise in registers.
-// LDS stage: A [128][PITCH] | B [256][PITCH] (rows 0-127 gate, 128-255 up) | as[128] floats
-constexpr int GU_THREADS = 512;
-constexpr int GU_A = 0, GU_B = BM * PITCH, GU_S = GU_B + 256 * PITCH, GU_STAGE = GU_S + BM * 4;
+// 512 threads = 8 waves as 4 (32 rows each) x 2 (64 h columns each, gate and
+// up both), two waves per SIMD.
+// Stage: A [128 rows][128 B] | B [256 rows][128 B] (0-127 gate, 128-255 up) | S [8 waves][64] f32
+constexpr int kGuThreads = 512;
+constexpr int GU_A = 0, GU_B = 128 * 128, GU_S = GU_B + 256 * 128, GU_STAGE = GU_S + 8 * 256;
+constexpr int GU_DMA = 2 + 4 + 1;   // DMA instructions per wave per stage
 
-__global__ __launch_bounds__(GU_THREADS, 1) void gemm_gateup_kernel(GemmArgs a)
+__global__ __launch_bounds__(kGuThreads, 1) void gemm_gateup_kernel(GemmArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ __attribute__((aligned(16))) uint8_t st0[GU_STAGE], st1[GU_STAGE], st2[GU_STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 3, wn = wave >> 2;
     const int t = blockIdx.x / a.ntn, nb = blockIdx.x - t * a.ntn;
     if (t >= *a.ntiles) return;
     const int2 tile = a.tiles[t];
-    const int e = tile.x, p0 = tile.y;
-    const int rows = min(BM, a.offsets[e + 1] - p0);
+    const int e = moe::uniform(tile.x), p0 = moe::uniform(tile.y);
+    const int rows = moe::uniform(min(BM, a.offsets[e + 1] - p0));
     const int K = a.K, N = a.N, KB = K / BK;
     const int n0 = nb * 128;
 
-    // loaders: A 2 chunks, B 4 chunks (2 gate rows, 2 up rows) of 16 bytes per
-    // thread and K step; 32-bit offsets from per-expert bases
+    // per-lane byte offsets of this wave's DMA runs (rows past the tile read
+    // the tile's first row and are never stored)
     uint32_t aoff[2];
-    bool aok[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int c = tid + GU_THREADS * j, r = c >> 3;
-        aok[j] = r < rows;
-        const int tok = aok[j] ? a.sorted_token[p0 + r] : 0;
-        aoff[j] = (uint32_t)tok * K + (c & 7) * 16;
+        const int r = (wave * 2 + j) * 8 + (lane >> 3);
+        const int tok = a.sorted_token[p0 + (r < rows ? r : 0)];
+        aoff[j] = (uint32_t)tok * K + swz(r, lane & 7) * 16;
     }
-    const uint8_t *gbase = a.w0 + (size_t)e * N * K;
-    const uint8_t *ubase = a.w1 + (size_t)e * N * K;
-    // B chunk j: rows (tid >> 3) + 64 * (j & 1) of gate (j < 2) or up (j >= 2)
-    const uint32_t boff = (uint32_t)(n0 + (tid >> 3)) * K + (tid & 7) * 16;
-    const uint32_t brow64 = (uint32_t)64 * K;
-    uint32_t soff = 0;
-    bool sok = false;
-    if (tid < BM) {
-        sok = tid < rows;
-        soff = (uint32_t)(sok ? a.sorted_token[p0 + tid] : 0) * KB;
+    const uint8_t *wbase = (wave < 4 ? a.w0 : a.w1) + ((size_t)e * N + n0) * K;
+    uint32_t boff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rb = (wave * 4 + j) * 8 + (lane >> 3);   // 0..255
+        boff[j] = (uint32_t)(rb & 127) * K + swz(rb, lane & 7) * 16;
     }
+    const int srow = wm * 32 + (lane & 31);             // both half-waves load the same 32 rows
+    const uint32_t soff = (uint32_t)a.sorted_token[p0 + (srow < rows ? srow : 0)] * KB * 4;
+    // weight block scales of this column block, K block j in lane j % 64 of
+    // register j / 64 (K <= 16384); a uniform readlane picks one per K step
     const float *sw0 = a.ws0 + ((size_t)e * (N / 128) + nb) * KB;
     const float *sw1 = a.ws1 + ((size_t)e * (N / 128) + nb) * KB;
+    const float g_lo = lane < KB ? sw0[lane] : 0.0f, g_hi = lane + 64 < KB ? sw0[lane + 64] : 0.0f;
+    const float u_lo = lane < KB ? sw1[lane] : 0.0f, u_hi = lane + 64 < KB ? sw1[lane + 64] : 0.0f;
 
-    uint4 ra[2][2], rb[2][4];
-    float rs[2];
-    auto gload = [&](int buf, int kb) {
-        const uint32_t ko = (uint32_t)kb * BK;
+    auto issue = [&](int kb, uint8_t *st) {
+        const uint8_t *ab = a.a + (size_t)kb * BK, *bb = wbase + (size_t)kb * BK;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            ra[buf][j] = aok[j] ? *reinterpret_cast<const uint4 *>(a.a + aoff[j] + ko) : make_uint4(0, 0, 0, 0);
-        rb[buf][0] = ldg_nt(gbase + boff + ko);
-        rb[buf][1] = ldg_nt(gbase + boff + brow64 + ko);
-        rb[buf][2] = ldg_nt(ubase + boff + ko);
-        rb[buf][3] = ldg_nt(ubase + boff + brow64 + ko);
-        rs[buf] = sok ? a.as[soff + kb] : 0.0f;
-    };
-    auto sstore = [&](int buf, int stage) {
-        uint8_t *st = lds + stage * GU_STAGE;
+        for (int j = 0; j < 2; ++j) dma16(ab, aoff[j], lds_addr(st + GU_A + (wave * 2 + j) * 1024));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = tid + GU_THREADS * j;
-            *reinterpret_cast<uint4 *>(st + GU_A + (c >> 3) * PITCH + (c & 7) * 16) = ra[buf][j];
-        }
-        const int r = tid >> 3, part = (tid & 7) * 16;
-        *reinterpret_cast<uint4 *>(st + GU_B + r * PITCH + part) = rb[buf][0];
-        *reinterpret_cast<uint4 *>(st + GU_B + (r + 64) * PITCH + part) = rb[buf][1];
-        *reinterpret_cast<uint4 *>(st + GU_B + (r + 128) * PITCH + part) = rb[buf][2];
-        *reinterpret_cast<uint4 *>(st + GU_B + (r + 192) * PITCH + part) = rb[buf][3];
-        if (tid < BM) reinterpret_cast<float *>(st + GU_S)[tid] = rs[buf];
+        for (int j = 0; j < 4; ++j) dma16(bb, boff[j], lds_addr(st + GU_B + (wave * 4 + j) * 1024));
+        dma4(a.as + kb, soff, lds_addr(st + GU_S + wave * 256));
     };
 
-    f32x4 accg[4][2], accu[4][2];
+    f32x4 accg[2][4], accu[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) { accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f}; accu[i][j] = accg[i][j]; }
+        for (int j = 0; j < 4; ++j) { accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f}; accu[i][j] = accg[i][j]; }
 
-    auto compute = [&](int stage, int kb) {
-        const uint8_t *st = lds + stage * GU_STAGE;
-        const float swg = sw0[kb], swu = sw1[kb];
-        i32x8 av[4];
-        f32x4 fa[4];
+    auto compute = [&](const uint8_t *st, int kb) {
+        const float swg = kb < 64 ? lane_f(g_lo, kb) : lane_f(g_hi, kb - 64);
+        const float swu = kb < 64 ? lane_f(u_lo, kb) : lane_f(u_hi, kb - 64);
+        const float *sa = reinterpret_cast<const float *>(st + GU_S) + wave * 64;
+        i32x8 av[2];
+        f32x4 fg[2], fu[2];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            av[mt] = lds_op(st + GU_A, wm * 64 + mt * 16 + (lane & 15), lane);
-            fa[mt] = *reinterpret_cast<const f32x4 *>(st + GU_S + (wm * 64 + mt * 16 + (lane >> 4) * 4) * 4);
+        for (int mt = 0; mt < 2; ++mt) {
+            av[mt] = lds_op(st + GU_A, wm * 32 + mt * 16 + (lane & 15), lane);
+            const f32x4 fa = *reinterpret_cast<const f32x4 *>(sa + mt * 16 + (lane >> 4) * 4);
+            fg[mt] = fa * swg;
+            fu[mt] = fa * swu;
         }
+        // per column group: four independent products, then their scaled
+        // accumulation (the block scales change every K step)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const i32x8 bg = lds_op(st + GU_B, wn * 32 + nt * 16 + (lane & 15), lane);
-            const i32x8 bu = lds_op(st + GU_B, 128 + wn * 32 + nt * 16 + (lane & 15), lane);
+        for (int nt = 0; nt < 4; ++nt) {
+            const i32x8 bg = lds_op(st + GU_B, wn * 64 + nt * 16 + (lane & 15), lane);
+            const i32x8 bu = lds_op(st + GU_B, 128 + wn * 64 + nt * 16 + (lane & 15), lane);
+            f32x4 pg[2], pu[2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const f32x4 pg = mfma_fp8(av[mt], bg);
-                const f32x4 pu = mfma_fp8(av[mt], bu);
+            for (int mt = 0; mt < 2; ++mt) {
+                pg[mt] = mfma_fp8(av[mt], bg);
+                pu[mt] = mfma_fp8(av[mt], bu);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    accg[mt][nt][i] = fmaf(pg[i], fa[mt][i] * swg, accg[mt][nt][i]);
-                    accu[mt][nt][i] = fmaf(pu[i], fa[mt][i] * swu, accu[mt][nt][i]);
+                    accg[mt][nt][i] = fmaf(pg[mt][i], fg[mt][i], accg[mt][nt][i]);
+                    accu[mt][nt][i] = fmaf(pu[mt][i], fu[mt][i], accu[mt][nt][i]);
                 }
-            }
         }
     };
 
-    // prologue: tiles 0 and 1 in flight, tile 0 staged
-    gload(0, 0);
-    if (KB > 1) gload(1, 1);
-    sstore(0, 0);
-    __syncthreads();
-    for (int kb = 0; kb < KB; kb += 2) {
-        // even step: compute stage 0, prefetch kb+2 into regs 0, stage kb+1 from regs 1
-        if (kb + 2 < KB) gload(0, kb + 2);
-        compute(0, kb);
-        if (kb + 1 < KB) sstore(1, 1);
-        __syncthreads();
+    auto step = [&](int kb, const uint8_t *cur, uint8_t *later) {
+        if (kb + 1 < KB) MOE_WAIT_VM(GU_DMA); else MOE_WAIT_VM(0);
+        MOE_WAIT_LGKM0();
+        MOE_BARRIER();
+        if (kb + 2 < KB) issue(kb + 2, later);
+        compute(cur, kb);
+    };
+
+    MOE_WAIT_VM(0);    // retire the offset and scale loads above before the DMA starts
+    issue(0, st0);
+    if (KB > 1) issue(1, st1);
+    for (int kb = 0; kb < KB; kb += 3) {
+        step(kb, st0, st2);
         if (kb + 1 >= KB) break;
-        if (kb + 3 < KB) gload(1, kb + 3);
-        compute(1, kb + 1);
-        if (kb + 2 < KB) sstore(0, 0);
-        __syncthreads();
+        step(kb + 1, st1, st0);
+        if (kb + 2 >= KB) break;
+        step(kb + 2, st2, st1);
     }
+    MOE_WAIT_VM(0);
+    __syncthreads();
 
     // epilogue: h = SwiGLU(g, u); per-row amax over the block's 128 columns
-    float h[4][2][4];
-    float rmax[4][4];
+    float h[2][4][4];
+    float rmax[2][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float m = 0.0f;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < 4; ++nt) {
                 h[mt][nt][i] = swiglu_clamp(accg[mt][nt][i], accu[mt][nt][i], a.limit);
                 m = fmaxf(m, fabsf(h[mt][nt][i]));
             }
-            // max over the 16 lanes holding this row's columns
 #pragma unroll
             for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
             rmax[mt][i] = m;
         }
-    // combine the four column quarters (wn = 0..3) through LDS
-    float *xm = reinterpret_cast<float *>(lds);   // [4][128]
+    float *xm = reinterpret_cast<float *>(st0);    // [2 column halves][128 rows]
     if ((lane & 15) == 0) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xm[wn * 128 + wm * 64 + mt * 16 + (lane >> 4) * 4 + i] = rmax[mt][i];
+            for (int i = 0; i < 4; ++i) xm[wn * 128 + wm * 32 + mt * 16 + (lane >> 4) * 4 + i] = rmax[mt][i];
     }
     __syncthreads();
-    uint8_t *ct = lds + 2048;                      // codes tile [128][PITCH]
+    uint8_t *ct = st1;                             // codes tile [128][144]
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = wm * 64 + mt * 16 + (lane >> 4) * 4 + i;
-            const float amax = fmaxf(fmaxf(xm[r], xm[128 + r]), fmaxf(xm[256 + r], xm[384 + r]));
+            const int r = wm * 32 + mt * 16 + (lane >> 4) * 4 + i;
+            const float amax = fmaxf(xm[r], xm[128 + r]);
             const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < 4; ++nt) {
                 const uint32_t code = e4m3_pair(h[mt][nt][i] / scale, 0.0f) & 0xFFu;
-                ct[r * PITCH + wn * 32 + nt * 16 + (lane & 15)] = (uint8_t)code;
+                ct[r * 144 + wn * 64 + nt * 16 + (lane & 15)] = (uint8_t)code;
             }
             if (wn == 0 && (lane & 15) == 0 && r < rows) a.hs[(size_t)(p0 + r) * a.ntn + nb] = scale;
         }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int c = tid + GU_THREADS * j, r = c >> 3, part = c & 7;
+        const int c = tid + kGuThreads * j, r = c >> 3, part = c & 7;
         if (r < rows)
             *reinterpret_cast<uint4 *>(a.hq + (size_t)(p0 + r) * N + n0 + part * 16) =
-                *reinterpret_cast<const uint4 *>(ct + r * PITCH + part * 16);
+                *reinterpret_cast<const uint4 *>(ct + r * 144 + part * 16);
     }
 }
 
 // ---------------------------------------------------------------------------
 // down
 // ---------------------------------------------------------------------------
-constexpr int DN_A = 0, DN_B = BM * PITCH, DN_S = DN_B + 128 * PITCH, DN_STAGE = DN_S + BM * 4;
+// Stage: A [128][128 B] | B [128][128 B] | S [4 waves][64] f32
+constexpr int DN_A = 0, DN_B = 128 * 128, DN_S = DN_B + 128 * 128, DN_STAGE = DN_S + 4 * 256;
+constexpr int DN_DMA = 4 + 4 + 1;
 
 __global__ __launch_bounds__(kThreads, 1) void gemm_down_kernel(GemmArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ __attribute__((aligned(16))) uint8_t st0[DN_STAGE], st1[DN_STAGE], st2[DN_STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int t = blockIdx.x / a.ntn, nb = blockIdx.x - t * a.ntn;
     if (t >= *a.ntiles) return;
     const int2 tile = a.tiles[t];
-    const int e = tile.x, p0 = tile.y;
-    const int rows = min(BM, a.offsets[e + 1] - p0);
+    const int e = moe::uniform(tile.x), p0 = moe::uniform(tile.y);
+    const int rows = moe::uniform(min(BM, a.offsets[e + 1] - p0));
     const int K = a.K, N = a.N, KB = K / BK;
     const int n0 = nb * 128;
 
-    const uint8_t *asrc[4];
-    bool aok[4];
+    uint32_t aoff[4], boff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int c = tid + 256 * j, r = c >> 3;
-        aok[j] = r < rows;
-        asrc[j] = a.a + (size_t)(p0 + (aok[j] ? r : 0)) * K + (c & 7) * 16;
+        const int r = (wave * 4 + j) * 8 + (lane >> 3);
+        aoff[j] = (uint32_t)(p0 + (r < rows ? r : 0)) * K + swz(r, lane & 7) * 16;
+        boff[j] = (uint32_t)r * K + swz(r, lane & 7) * 16;
     }
-    const uint8_t *bsrc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = tid + 256 * j, r = c >> 3;
-        bsrc[j] = a.w0 + ((size_t)e * N + n0 + r) * K + (c & 7) * 16;
-    }
-    const float *ssrc = a.as + (size_t)(p0 + (tid < rows ? tid : 0)) * KB;
+    const uint8_t *wbase = a.w0 + ((size_t)e * N + n0) * K;
+    const int srow = wm * 64 + lane;
+    const uint32_t soff = (uint32_t)(p0 + (srow < rows ? srow : 0)) * KB * 4;
     const float *sw0 = a.ws0 + ((size_t)e * (N / 128) + nb) * KB;
+    const float w_lo = lane < KB ? sw0[lane] : 0.0f, w_hi = lane + 64 < KB ? sw0[lane + 64] : 0.0f;
 
-    uint4 ra[2][4], rb[2][4];
-    float rs[2];
-    auto gload = [&](int buf, int kb) {
+    auto issue = [&](int kb, uint8_t *st) {
+        const uint8_t *ab = a.a + (size_t)kb * BK, *bb = wbase + (size_t)kb * BK;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ra[buf][j] = aok[j] ? *reinterpret_cast<const uint4 *>(asrc[j] + kb * BK) : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) dma16(ab, aoff[j], lds_addr(st + DN_A + (wave * 4 + j) * 1024));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rb[buf][j] = ldg_nt(bsrc[j] + kb * BK);
-        rs[buf] = (tid < BM && tid < rows) ? ssrc[kb] : 0.0f;
-    };
-    auto sstore = [&](int buf, int stage) {
-        uint8_t *st = lds + stage * DN_STAGE;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = tid + 256 * j;
-            *reinterpret_cast<uint4 *>(st + DN_A + (c >> 3) * PITCH + (c & 7) * 16) = ra[buf][j];
-            *reinterpret_cast<uint4 *>(st + DN_B + (c >> 3) * PITCH + (c & 7) * 16) = rb[buf][j];
-        }
-        if (tid < BM) reinterpret_cast<float *>(st + DN_S)[tid] = rs[buf];
+        for (int j = 0; j < 4; ++j) dma16(bb, boff[j], lds_addr(st + DN_B + (wave * 4 + j) * 1024));
+        dma4(a.as + kb, soff, lds_addr(st + DN_S + wave * 256));
     };
 
     f32x4 acc[4][4];
@@ -416,42 +435,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_down_kernel(GemmArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int stage, int kb) {
-        const uint8_t *st = lds + stage * DN_STAGE;
-        const float sw = sw0[kb];
+    auto compute = [&](const uint8_t *st, int kb) {
+        const float sw = kb < 64 ? lane_f(w_lo, kb) : lane_f(w_hi, kb - 64);
+        const float *sa = reinterpret_cast<const float *>(st + DN_S) + wave * 64;
         i32x8 av[4];
         f32x4 fa[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             av[mt] = lds_op(st + DN_A, wm * 64 + mt * 16 + (lane & 15), lane);
-            fa[mt] = *reinterpret_cast<const f32x4 *>(st + DN_S + (wm * 64 + mt * 16 + (lane >> 4) * 4) * 4);
+            fa[mt] = *reinterpret_cast<const f32x4 *>(sa + mt * 16 + (lane >> 4) * 4) * sw;
         }
+        f32x4 p[4][4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const i32x8 bv = lds_op(st + DN_B, wn * 64 + nt * 16 + (lane & 15), lane);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const f32x4 p = mfma_fp8(av[mt], bv);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(p[i], fa[mt][i] * sw, acc[mt][nt][i]);
-            }
+            for (int mt = 0; mt < 4; ++mt) p[mt][nt] = mfma_fp8(av[mt], bv);
         }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(p[mt][nt][i], fa[mt][i], acc[mt][nt][i]);
     };
 
-    gload(0, 0);
-    if (KB > 1) gload(1, 1);
-    sstore(0, 0);
-    __syncthreads();
-    for (int kb = 0; kb < KB; kb += 2) {
-        if (kb + 2 < KB) gload(0, kb + 2);
-        compute(0, kb);
-        if (kb + 1 < KB) sstore(1, 1);
-        __syncthreads();
+    auto step = [&](int kb, const uint8_t *cur, uint8_t *later) {
+        if (kb + 1 < KB) MOE_WAIT_VM(DN_DMA); else MOE_WAIT_VM(0);
+        MOE_WAIT_LGKM0();
+        MOE_BARRIER();
+        if (kb + 2 < KB) issue(kb + 2, later);
+        compute(cur, kb);
+    };
+
+    MOE_WAIT_VM(0);    // retire the offset and scale loads above before the DMA starts
+    issue(0, st0);
+    if (KB > 1) issue(1, st1);
+    for (int kb = 0; kb < KB; kb += 3) {
+        step(kb, st0, st2);
         if (kb + 1 >= KB) break;
-        if (kb + 3 < KB) gload(1, kb + 3);
-        compute(1, kb + 1);
-        if (kb + 2 < KB) sstore(0, 0);
-        __syncthreads();
+        step(kb + 1, st1, st0);
+        if (kb + 2 >= KB) break;
+        step(kb + 2, st2, st1);
     }
 
 #pragma unroll
@@ -499,16 +524,7 @@ hipError_t launch_gemm_gateup(const uint8_t *xq, const float *xs, const int32_t 
     a.w0 = gcodes; a.w1 = ucodes; a.ws0 = gscales; a.ws1 = uscales;
     a.offsets = offsets; a.tiles = tiles; a.ntiles = ntiles;
     a.hq = hq; a.hs = hs; a.K = hidden; a.N = inter; a.ntn = inter / 128; a.limit = limit;
-    const size_t lds = 2 * GU_STAGE;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_gateup_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
-    hipLaunchKernelGGL(gemm_gateup_kernel, dim3((unsigned)(tmax * a.ntn)), dim3(GU_THREADS), lds, st,
-                       a);
+    hipLaunchKernelGGL(gemm_gateup_kernel, dim3((unsigned)(tmax * a.ntn)), dim3(kGuThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -521,14 +537,6 @@ hipError_t launch_gemm_down(const uint8_t *hq, const float *hs, const uint8_t *d
     a.a = hq; a.as = hs; a.w0 = dcodes; a.ws0 = dscales;
     a.offsets = offsets; a.tiles = tiles; a.ntiles = ntiles;
     a.y = y; a.K = inter; a.N = hidden; a.ntn = hidden / 128;
-    const size_t lds = 2 * DN_STAGE;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_down_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
-    hipLaunchKernelGGL(gemm_down_kernel, dim3((unsigned)(tmax * a.ntn)), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL(gemm_down_kernel, dim3((unsigned)(tmax * a.ntn)), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }

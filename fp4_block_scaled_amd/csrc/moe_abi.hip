@@ -121,11 +121,20 @@ GemmScratch carve_gemm(char *p, int64_t M, int64_t S, int32_t E, int32_t hidden,
     return g;
 }
 
+// The GEMM tier keeps the K-block weight scales of a column block in two
+// registers per lane (K <= 128 blocks of 128) and addresses activation rows
+// with 32-bit byte offsets (M * hidden and S * inter below 2^31).
+bool gemm_dims_ok(int64_t M, int64_t S, int32_t hidden, int32_t inter)
+{
+    return hidden <= MOE_GEMM_MAX_K && inter <= MOE_GEMM_MAX_K && M * hidden < (int64_t(1) << 31) &&
+           S * inter < (int64_t(1) << 31);
+}
+
 size_t ffn_bytes(int64_t M, int64_t S, int32_t E, int32_t hidden, int32_t inter, int32_t fmt,
                  int32_t mode)
 {
     if (mode == MOE_MODE_GEMV_A16) return gemv_scratch_bytes(S, hidden, inter, fmt);
-    if (fmt != MOE_W_E4M3_B128) return 0;
+    if (fmt != MOE_W_E4M3_B128 || !gemm_dims_ok(M, S, hidden, inter)) return 0;
     return gemm_scratch_bytes(M, S, E, hidden, inter);
 }
 
@@ -163,12 +172,16 @@ size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts, in
     if (mode == MOE_MODE_AUTO) {
         const int64_t mg = max_M < MOE_GEMV_MAX_M ? max_M : MOE_GEMV_MAX_M;
         ffn = ffn_bytes(mg, mg * top_k, num_experts, hidden, inter, fmt, MOE_MODE_GEMV_A16);
+        // GEMM scratch only where that tier can run (E4M3, within its
+        // limits); a call above MOE_GEMV_MAX_M tokens outside them is
+        // refused by moe_expert_ffn
         if (max_M > MOE_GEMV_MAX_M) {
             const size_t g = ffn_bytes(max_M, S, num_experts, hidden, inter, fmt, MOE_MODE_GEMM_A8);
             ffn = g > ffn ? g : ffn;
         }
     } else {
         ffn = ffn_bytes(max_M, S, num_experts, hidden, inter, fmt, mode);
+        if (ffn == 0) return 0;
     }
     return moe::route_region_bytes(S, num_experts) + ffn;
 }
@@ -261,6 +274,11 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
     const int32_t tier = resolve(M, fmt, mode);
     if (tier == MOE_MODE_GEMM_A8 && fmt != MOE_W_E4M3_B128)
         return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: the FP8 GEMM tier serves E4M3 banks only");
+    if (tier == MOE_MODE_GEMM_A8 && !gemm_dims_ok(M, (int64_t)M * k, hidden, inter))
+        return fail(MOE_ERR_SHAPE,
+                    "moe_expert_ffn: GEMM tier needs hidden, inter <= %d and M*hidden, "
+                    "M*top_k*inter < 2^31 (M=%d top_k=%d hidden=%d inter=%d)",
+                    MOE_GEMM_MAX_K, M, k, hidden, inter);
     const size_t need = moe_workspace_bytes(M, k, E, hidden, inter, fmt, tier);
     if (ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu bytes < %zu", ws_bytes, need);

@@ -80,6 +80,8 @@ enum {
 
 #define MOE_GEMV_MAX_M 16
 #define MOE_MAX_EXPERTS 512
+/* Largest hidden and inter the GEMM tier takes (128 K blocks of 128). */
+#define MOE_GEMM_MAX_K 16384
 
 /* One projection bank holding every expert, expert-major (host struct of
  * device pointers).  n_out x k_in is the matrix shape per expert:
@@ -158,8 +160,9 @@ moe_status_t moe_route_pack(const int32_t *topk_ids, int32_t M, int32_t top_k,
  * moe_route_pack on this same `ws`.
  * Rules: hidden % 128 == 0, inter % 128 == 0; gate/up are inter x hidden,
  * down is hidden x inter; all banks share one format and num_experts;
- * GEMM_A8 needs E4M3 banks; ws_bytes >= moe_workspace_bytes(route->M, ...,
- * mode). */
+ * GEMM_A8 needs E4M3 banks, hidden and inter <= MOE_GEMM_MAX_K, and
+ * M*hidden and M*top_k*inter < 2^31 (MOE_ERR_SHAPE otherwise);
+ * ws_bytes >= moe_workspace_bytes(route->M, ..., mode). */
 moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up,
                             const moe_bank_t *down, const uint16_t *x_bf16,
                             const moe_route_t *route, int32_t hidden,

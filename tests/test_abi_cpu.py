@@ -65,10 +65,26 @@ def test_workspace_bytes_hand_computed():
     (1, 8, 256, 6144, 1664, 2, 0),      # NVFP4 needs % 256
     (1, 8, 256, 7168, 2048, 3, 0),      # unknown format
     (1, 8, 256, 7168, 2048, 1, 7),      # unknown mode
+    (64, 8, 256, 16512, 2048, 1, 2),    # GEMM tier: hidden > MOE_GEMM_MAX_K
+    (131072, 8, 256, 16384, 2048, 1, 2),  # GEMM tier: M * hidden = 2^31
+    (32768, 8, 256, 7168, 8192, 1, 2),  # GEMM tier: M * top_k * inter = 2^31
 ])
 def test_workspace_bytes_rejects_bad_sizes(args):
     from fp4_block_scaled_amd import binding as B
     assert B.lib.moe_workspace_bytes(*args) == 0
+
+
+def test_auto_workspace_skips_a_gemm_tier_that_cannot_run():
+    from fp4_block_scaled_amd import binding as B
+    L = B.lib
+    # NVFP4 banks have no GEMM tier: AUTO sizes the GEMV scratch (for up to
+    # MOE_GEMV_MAX_M tokens) and the route region for max_M
+    auto = L.moe_workspace_bytes(20, 8, 20, 1024, 512, B.MOE_W_NVFP4_B16, B.MOE_MODE_AUTO)
+    gemv = L.moe_workspace_bytes(16, 8, 20, 1024, 512, B.MOE_W_NVFP4_B16, B.MOE_MODE_GEMV_A16)
+    assert auto > 0 and auto >= gemv
+    # same for E4M3 beyond the GEMM tier's K limit
+    assert L.moe_workspace_bytes(64, 8, 256, 7168, 16512, B.MOE_W_E4M3_B128, B.MOE_MODE_AUTO) > 0
+    assert L.moe_workspace_bytes(64, 8, 256, 7168, 16512, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMM_A8) == 0
 
 
 def test_resolve_mode():
@@ -131,6 +147,12 @@ def test_ffn_error_contract_on_host():
     # bad limit, unknown mode
     assert _ffn(B, g, u, d, r, ws, limit=0.0) == B.MOE_ERR_ARG
     assert _ffn(B, g, u, d, r, ws, mode=5) == B.MOE_ERR_ARG
+    # beyond the GEMM tier's limits (it takes K <= MOE_GEMM_MAX_K)
+    big = 16512
+    rg = _route(B, ws, M=32)
+    assert _ffn(B, _bank(B, n=128, k=big), _bank(B, n=128, k=big), _bank(B, n=big, k=128), rg, ws,
+                hidden=big, inter=128, mode=2) == B.MOE_ERR_SHAPE
+    assert "GEMM tier" in B.moe_last_error()
 
 
 def test_route_pack_and_combine_error_contract_on_host():
