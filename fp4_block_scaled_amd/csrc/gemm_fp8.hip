@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t *__restri
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t *__restrict__ offsets,
                                                           int32_t E, int32_t tmax,
-                                                          int2 *__restrict__ tiles,
+                                                          int4 *__restrict__ tiles,
                                                           int32_t *__restrict__ ntiles)
 {
     __shared__ int32_t wsum[16];
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t *__restr
     const int first = base + inc - nt;
     if (e < E) {
         const int p0 = offsets[e];
-        for (int m = 0; m < nt && first + m < tmax; ++m) tiles[first + m] = make_int2(e, p0 + m * BM);
+        for (int m = 0; m < nt && first + m < tmax; ++m) tiles[first + m] = make_int4(e, p0 + m * BM, first, nt);
     }
     if (tid == 1023) *ntiles = min(base + inc, tmax);
 }
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t *__restr
 // instruction fills bytes 16i..16i+15 of a 1 KB run = 8 rows x 128 bytes),
 // three LDS stages deep, so two K steps of loads are always in flight without
 // holding any VGPRs.  Inside a stage a row's eight 16-byte chunks are stored
-// XOR-swizzled by (row >> 1) & 7: the 16 lanes that feed one MFMA operand
-// half (16 rows, same K chunk) then hit 16 distinct bank groups.  Each wave
+// XOR-swizzled (swz below), so the lanes that feed one MFMA operand half (16
+// rows, same K chunk) read without bank conflicts.  Each wave
 // loads the activation scales of its own 64 rows into its own 256-byte slot.
 // Every wave issues the same number of DMA instructions per stage, so an
 // immediate vmcnt wait tells a wave its share of a stage has landed; one
@@ -144,7 +144,7 @@ struct GemmArgs {
     const uint8_t *w0, *w1;    // gate and up codes (down: w0 only), [E][N][K]
     const float *ws0, *ws1;    // their block scales [E][N/128][K/128]
     const int32_t *offsets;
-    const int2 *tiles;
+    const int4 *tiles;         // (expert, first packed row, expert's first tile, its tile count)
     const int32_t *ntiles;
     uint8_t *hq;               // gate/up output codes [S][N]
     float *hs;                 // gate/up output scales [S][N/128]
@@ -152,6 +152,28 @@ struct GemmArgs {
     int32_t K, N, ntn;         // N: h columns (gate/up) or outputs (down); ntn = N/128
     float limit;
 };
+
+// Block -> (tile, column block).  The hardware hands blocks to the 8 XCDs
+// round-robin (block b to XCD b % 8), each XCD with its own L2: give every
+// XCD one contiguous run of the W = tiles x column-blocks work items, so the
+// blocks running together on an XCD share A rows in its L2.  Within an
+// expert the items go column-block-major: its tiles read each weight block
+// at about the same time.  False for blocks past W.
+__device__ __forceinline__ bool gemm_item(const GemmArgs &a, int4 &tile, int &nb)
+{
+    const int W = moe::uniform(*a.ntiles) * a.ntn;
+    const int b = blockIdx.x;
+    if (b >= W) return false;
+    const int q = W >> 3, r = W & 7, x = b & 7;
+    const int L = x * q + min(x, r) + (b >> 3);
+    const int4 head = a.tiles[L / a.ntn];
+    const int f = moe::uniform(head.z), n = moe::uniform(head.w);
+    const int local = L - f * a.ntn;
+    nb = local / n;
+    const int4 tl = a.tiles[f + local % n];
+    tile = make_int4(moe::uniform(tl.x), moe::uniform(tl.y), f, n);
+    return true;
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -167,7 +189,13 @@ __device__ __forceinline__ float lane_f(float v, int l)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// Physical 16-byte chunk of logical chunk `chunk` in tile row `row`.  An
+// operand read has 16 consecutive rows read the same logical chunk; with
+// f(row) = (row & 7) ^ ((row >> 3) & 1) any 8 consecutive rows land on 8
+// distinct chunks of a 128-byte bank line, and the 8 rows of one parity among
+// 16 consecutive rows on 8 distinct chunks, so those reads are conflict-free
+// whether the LDS serves 128 or 256 bytes per clock.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
 
 // 32-byte MFMA operand of lane `lane` for tile row `row` (K chunks 2q, 2q+1, q = lane/16)
 // (one byte offset per 16-byte read, so every LDS access stays a direct
@@ -232,10 +260,10 @@ __global__ __launch_bounds__(kGuThreads, 1) void gemm_gateup_kernel(GemmArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int wm = wave & 3, wn = wave >> 2;
-    const int t = blockIdx.x / a.ntn, nb = blockIdx.x - t * a.ntn;
-    if (t >= *a.ntiles) return;
-    const int2 tile = a.tiles[t];
-    const int e = moe::uniform(tile.x), p0 = moe::uniform(tile.y);
+    int4 tile;
+    int nb;
+    if (!gemm_item(a, tile, nb)) return;
+    const int e = tile.x, p0 = tile.y;
     const int rows = moe::uniform(min(BM, a.offsets[e + 1] - p0));
     const int K = a.K, N = a.N, KB = K / BK;
     const int n0 = nb * 128;
@@ -399,10 +427,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_down_kernel(GemmArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
-    const int t = blockIdx.x / a.ntn, nb = blockIdx.x - t * a.ntn;
-    if (t >= *a.ntiles) return;
-    const int2 tile = a.tiles[t];
-    const int e = moe::uniform(tile.x), p0 = moe::uniform(tile.y);
+    int4 tile;
+    int nb;
+    if (!gemm_item(a, tile, nb)) return;
+    const int e = tile.x, p0 = tile.y;
     const int rows = moe::uniform(min(BM, a.offsets[e + 1] - p0));
     const int K = a.K, N = a.N, KB = K / BK;
     const int n0 = nb * 128;
@@ -505,7 +533,7 @@ hipError_t launch_quant_act(const uint16_t *x, int32_t M, int32_t hidden, uint8_
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_tiles(const int32_t *offsets, int32_t E, int32_t tmax, int2 *tiles,
+hipError_t launch_gemm_tiles(const int32_t *offsets, int32_t E, int32_t tmax, int4 *tiles,
                              int32_t *ntiles, hipStream_t st)
 {
     hipLaunchKernelGGL(gemm_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, E, tmax, tiles,
@@ -515,7 +543,7 @@ hipError_t launch_gemm_tiles(const int32_t *offsets, int32_t E, int32_t tmax, in
 
 hipError_t launch_gemm_gateup(const uint8_t *xq, const float *xs, const int32_t *sorted_token,
                               const uint8_t *gcodes, const float *gscales, const uint8_t *ucodes,
-                              const float *uscales, const int32_t *offsets, const int2 *tiles,
+                              const float *uscales, const int32_t *offsets, const int4 *tiles,
                               const int32_t *ntiles, int32_t tmax, int32_t hidden, int32_t inter,
                               float limit, uint8_t *hq, float *hs, hipStream_t st)
 {
@@ -529,7 +557,7 @@ hipError_t launch_gemm_gateup(const uint8_t *xq, const float *xs, const int32_t 
 }
 
 hipError_t launch_gemm_down(const uint8_t *hq, const float *hs, const uint8_t *dcodes,
-                            const float *dscales, const int32_t *offsets, const int2 *tiles,
+                            const float *dscales, const int32_t *offsets, const int4 *tiles,
                             const int32_t *ntiles, int32_t tmax, int32_t hidden, int32_t inter,
                             float *y, hipStream_t st)
 {

@@ -94,7 +94,7 @@ bool ffn_dims_ok(int32_t fmt, int32_t hidden, int32_t inter)
 struct GemmScratch {
     uint8_t *xq, *hq;
     float *xs, *hs;
-    int2 *tiles;
+    int4 *tiles;
     int32_t *ntiles;
 };
 
@@ -105,7 +105,7 @@ size_t gemm_scratch_bytes(int64_t M, int64_t S, int32_t E, int32_t hidden, int32
            moe::align256(sizeof(float) * (size_t)(M * (hidden / 128))) +  // xs
            moe::align256((size_t)(S * inter)) +                           // hq
            moe::align256(sizeof(float) * (size_t)(S * (inter / 128))) +   // hs
-           moe::align256(sizeof(int2) * (size_t)tmax) + 256;              // tiles, count
+           moe::align256(sizeof(int4) * (size_t)tmax) + 256;              // tiles, count
 }
 
 GemmScratch carve_gemm(char *p, int64_t M, int64_t S, int32_t E, int32_t hidden, int32_t inter)
@@ -116,7 +116,7 @@ GemmScratch carve_gemm(char *p, int64_t M, int64_t S, int32_t E, int32_t hidden,
     g.xs = (float *)p;    p += moe::align256(sizeof(float) * (size_t)(M * (hidden / 128)));
     g.hq = (uint8_t *)p;  p += moe::align256((size_t)(S * inter));
     g.hs = (float *)p;    p += moe::align256(sizeof(float) * (size_t)(S * (inter / 128)));
-    g.tiles = (int2 *)p;  p += moe::align256(sizeof(int2) * (size_t)tmax);
+    g.tiles = (int4 *)p;  p += moe::align256(sizeof(int4) * (size_t)tmax);
     g.ntiles = (int32_t *)p;
     return g;
 }

@@ -96,15 +96,15 @@ hipError_t launch_swiglu_partials(const float *partials, int32_t nks, int32_t S,
 int gemm_max_tiles(int32_t S, int32_t E);
 hipError_t launch_quant_act(const uint16_t *x, int32_t M, int32_t hidden, uint8_t *xq, float *xs,
                             hipStream_t st);
-hipError_t launch_gemm_tiles(const int32_t *offsets, int32_t E, int32_t tmax, int2 *tiles,
+hipError_t launch_gemm_tiles(const int32_t *offsets, int32_t E, int32_t tmax, int4 *tiles,
                              int32_t *ntiles, hipStream_t st);
 hipError_t launch_gemm_gateup(const uint8_t *xq, const float *xs, const int32_t *sorted_token,
                               const uint8_t *gcodes, const float *gscales, const uint8_t *ucodes,
-                              const float *uscales, const int32_t *offsets, const int2 *tiles,
+                              const float *uscales, const int32_t *offsets, const int4 *tiles,
                               const int32_t *ntiles, int32_t tmax, int32_t hidden, int32_t inter,
                               float limit, uint8_t *hq, float *hs, hipStream_t st);
 hipError_t launch_gemm_down(const uint8_t *hq, const float *hs, const uint8_t *dcodes,
-                            const float *dscales, const int32_t *offsets, const int2 *tiles,
+                            const float *dscales, const int32_t *offsets, const int4 *tiles,
                             const int32_t *ntiles, int32_t tmax, int32_t hidden, int32_t inter,
                             float *y, hipStream_t st);
 

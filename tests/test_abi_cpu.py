@@ -49,6 +49,15 @@ def test_workspace_bytes_hand_computed():
     route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
     gemv = a256(4 * 1 * S * 2 * I) + a256(4 * S * I) + a256(4 * 3 * S * H)
     assert B.moe_workspace_bytes(1, 2, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16) == route + gemv
+    # prefill, GEMM tier: H7168 I2048 E256 k8 M=4096 -> S=32768 slots; x codes
+    # + scales, h codes + scales, at most min(S,E) + S/128 tiles of 16 bytes,
+    # and the tile count
+    M, S, E, H, I = 4096, 32768, 256, 7168, 2048
+    route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
+    tmax = min(S, E) + S // 128
+    gemm = (a256(M * H) + a256(4 * M * (H // 128)) + a256(S * I) + a256(4 * S * (I // 128))
+            + a256(16 * tmax) + 256)
+    assert B.moe_workspace_bytes(M, 8, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMM_A8) == route + gemm
     # monotone in max_M
     sizes = [B.moe_workspace_bytes(m, 8, 256, 7168, 2048, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16)
              for m in (1, 2, 4, 8, 16)]
