@@ -143,7 +143,7 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True):
         if mode == B.MOE_MODE_GEMM_A8:
             names = ["route_pack", "act_quant_tiles", "gateup_gemm", "down_gemm", "combine"]
         else:
-            names = ["route_pack", "gateup_gemv", "swiglu", "down_gemv", "combine"]
+            names = ["route_pack", "gateup_gemv", "down_gemv", "combine"]
         acc = np.zeros(per - 1)
         for ev, _ in evs:
             for j in range(per - 1):

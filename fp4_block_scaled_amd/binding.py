@@ -31,7 +31,7 @@ MOE_MODE_GEMM_A8 = 2
 
 MOE_GEMV_MAX_M = 16
 MOE_MAX_EXPERTS = 512
-MOE_GEMM_MAX_K = 16384
+MOE_MAX_DIM = 16384
 
 EXPORTS = ("moe_workspace_bytes", "moe_resolve_mode", "moe_route_pack",
            "moe_expert_ffn", "moe_combine", "moe_set_stage_events", "moe_last_error")

@@ -16,12 +16,11 @@
 // LDS, scaled by the block scale once per 16 products, accumulated in FP32,
 // and reduced over the 8 lanes of a group with DPP.
 //
-//   gate+up: one launch covers both banks; K is cut into 1024-wide slices and
-//            each slice writes an FP32 partial row; the SwiGLU kernel adds the
-//            slices in a fixed order (deterministic, no atomics).
-//   down:    K (= inter) in slices of 2048; with one slice the rows go
-//            straight to y, otherwise slice partials are summed in order by a
-//            small reduction kernel.
+//   gate+up: one launch covers both banks and the whole of K; a block holds
+//            the gate and the up rows of the same 16 h rows and applies the
+//            clamped SwiGLU itself, so h leaves the kernel finished.
+//   down:    a block covers 32 output rows over the whole of K (= inter)
+//            and writes y rows directly.
 #include "moe_internal.h"
 
 namespace {
@@ -31,40 +30,28 @@ using moe::f32x2;
 
 constexpr int kThreads = 256;                    // 4 waves
 
-// Launch-shape constants (rows per wave = 8 * RG; slots per weight pass = ST).
-#ifndef MOE_E4M3_GU_RG
-#define MOE_E4M3_GU_RG 1
-#endif
-#ifndef MOE_E4M3_GU_ST
-#define MOE_E4M3_GU_ST 8
-#endif
-#ifndef MOE_E4M3_DN_RG
-#define MOE_E4M3_DN_RG 1
-#endif
-#ifndef MOE_E4M3_DN_ST
-#define MOE_E4M3_DN_ST 4
-#endif
-// minimum waves per SIMD the register allocation must allow
-#ifndef MOE_GEMV_MIN_WAVES
-#define MOE_GEMV_MIN_WAVES 1
-#endif
+// Most slots one weight pass serves (the pass size is also capped by the LDS
+// that holds the slots' activation rows).
+constexpr int MOE_E4M3_GU_ST = 8;
+constexpr int MOE_E4M3_DN_ST = 8;
 
 struct GateUpArgs {
     const uint8_t *gcodes, *ucodes;
     const float *gscales, *uscales;
     const uint16_t *x;
-    const int32_t *offsets, *sorted_token, *active, *num_active;
-    float *partials;
-    int32_t S, H, I, nks, ntiles, st;   // st: slots per weight pass (<= ST)
+    const int32_t *offsets, *sorted_token, *active;
+    float *h;                           // [S][I]
+    int32_t H, I, ntiles, st;           // st: slots per weight pass (<= ST)
+    float limit;
 };
 
 struct DownArgs {
     const uint8_t *codes;
     const float *scales;
-    const float *h;
-    const int32_t *offsets, *active, *num_active;
-    float *out;          // y [S][H] when nks == 1, else partials [nks][S][H]
-    int32_t S, H, I, nks, ntiles, st;   // st: slots per weight pass (<= ST)
+    const float *h;                     // [S][I]
+    const int32_t *offsets, *active;
+    float *y;                           // [S][H]
+    int32_t H, I, ntiles, st;           // st: slots per weight pass (<= ST)
 };
 
 // Weights are streamed once per call: non-temporal loads keep them from
@@ -93,96 +80,94 @@ __device__ __forceinline__ float dot2(bf16x2 a, uint32_t b, float c)
     return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// ---------------------------------------------------------------------------
-// gate + up
-// ---------------------------------------------------------------------------
-// SEGS: 128-wide K segments per slice (the slice width divides hidden);
-// RG: 8-row groups per wave; ST: slots per pass over the weights.  A wave
-// issues all RG*SEGS 16-byte loads of its rows before the first multiply, so
-// up to RG*SEGS KB per wave are in flight.  The block's 128 rows share one
-// 128-row scale block, so the SEGS scales are loaded once per block.
-template <int SEGS, int RG, int ST>
-__global__ __launch_bounds__(kThreads, MOE_GEMV_MIN_WAVES) void gemv_gateup_e4m3_kernel(GateUpArgs a)
+// silu(min(g, L)) * clamp(u, -L, L), silu(z) = z / (1 + e^-z)
+__device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 {
-    constexpr int RPW = RG * 8;
-    constexpr int RPB = RPW * (kThreads / 64);
-    static_assert(128 % RPB == 0, "block rows inside one 128-row scale block");
-    extern __shared__ uint4 lds_x[];                 // bf16 x slice per slot: [a.st][SEGS*16]
-    uint4 (*xs)[SEGS * 16] = reinterpret_cast<uint4 (*)[SEGS * 16]>(lds_x);
+    const float gc = fminf(g, L);
+    const float uc = fminf(fmaxf(u, -L), L);
+    return gc / (1.0f + expf(-gc)) * uc;
+}
+
+// ---------------------------------------------------------------------------
+// gate + up + SwiGLU
+// ---------------------------------------------------------------------------
+// One block = 16 h rows of one active expert over the whole of K: waves 0-1
+// stream those 16 rows of the gate bank, waves 2-3 the same 16 rows of the up
+// bank (8 rows per wave).  At the start of a pass the bf16 x rows of up to
+// a.st slots are copied to LDS for the whole of K; the K loop then only
+// streams weights, in chunks of CH segments, with the next two chunks' loads
+// in flight while the current one is multiplied (three register buffers).
+// With NCH > 0 (the chunk count known at compile time) the K loop is fully
+// unrolled: straight-line code lets the compiler wait for exactly the chunk
+// it multiplies; at most 128 VGPRs (4 waves per SIMD), so the 4 blocks of
+// 16 rows that a CU holds all stay resident.  NCH == 0 is the generic looped form (one chunk in flight,
+// an explicit wait at each step).  At the end the up sums go through LDS to
+// the gate waves, which apply the clamped SwiGLU and write h: no partial sums
+// leave the block.  The 16 rows lie in one 128-row scale block, so a wave
+// keeps the block scales of all K segments in two registers (lane l:
+// segments l and l + 64).
+template <int CH, int NCH, int ST>
+__global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArgs a)
+{
+    extern __shared__ uint4 xl[];                    // [a.st][H / 8] bf16 x rows, K order
+    __shared__ float ush[ST][16];                    // up sums of the 16 rows per slot
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int grp = lane >> 3, sub = lane & 7;
-    int bid = blockIdx.x;
-    const int ks = bid % a.nks;
-    bid /= a.nks;
-    const int tile = bid % a.ntiles;
-    const int ai = bid / a.ntiles;
-    const int e = a.active[ai];              // -1 past the active experts
+    const int tile = blockIdx.x % a.ntiles;
+    const int ai = blockIdx.x / a.ntiles;
+    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
     if (e < 0) return;
-    const int H = a.H, I = a.I;
-    const int half = a.ntiles >> 1;
-    const bool is_up = tile >= half;
-    const uint8_t *codes = (is_up ? a.ucodes : a.gcodes) + (size_t)e * I * H;
-    const int sc_cols = H >> 7;
-    const int row_b0 = (is_up ? tile - half : tile) * RPB;
-    const int col_b0 = (is_up ? I : 0) + row_b0;
-    const int k0 = ks * SEGS * 128;
-    const size_t pstride = (size_t)2 * I;
+    const int H = a.H, I = a.I, H8 = H >> 3;
+    const int nseg = H >> 7, nch = NCH > 0 ? NCH : nseg / CH;
+    const bool is_up = wave >= 2;
+    const int hrow0 = tile * 16;
+    const int hrow = hrow0 + (wave & 1) * 8 + grp;
+    // weight address = wave-uniform base (SGPRs) + fixed 32-bit lane offset
+    const uint8_t *wb0 = (is_up ? a.ucodes : a.gcodes) + ((size_t)e * I + hrow0 + (wave & 1) * 8) * H;
+    const uint32_t loff = (uint32_t)grp * H + sub * 16;
+    const float *scb = (is_up ? a.uscales : a.gscales) + ((size_t)e * (I >> 7) + (hrow0 >> 7)) * nseg;
+    const float sc_lo = lane < nseg ? scb[lane] : 0.0f;
+    const float sc_hi = lane + 64 < nseg ? scb[lane + 64] : 0.0f;
+    const int p0 = moe::uniform(a.offsets[e]);
+    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
 
-    // block scales of this slice: lane l holds scale (l % SEGS)
-    const float *sc_blk = (is_up ? a.uscales : a.gscales) + (size_t)e * (I >> 7) * sc_cols +
-                          (size_t)(row_b0 >> 7) * sc_cols + (k0 >> 7);
-    const float sc_lane = sc_blk[lane % SEGS];
+    for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
+        const int nt = min(a.st, ne - s0);
+        // opaque copies: the per-chunk address arithmetic stays inside the
+        // pass instead of being hoisted out of it into live registers
+        const uint8_t *wbp = wb0;
+        uint32_t lo = loff;
+        asm volatile("" : "+s"(wbp), "+v"(lo));
+        auto load_w = [&](uint4 (&wb)[CH], int c) {
+            const uint8_t *cb = wbp + c * CH * 128;
+#pragma unroll
+            for (int sg = 0; sg < CH; ++sg) wb[sg] = load16(cb + lo + sg * 128);
+        };
+        float acc[ST];
+#pragma unroll
+        for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
 
-    const uint8_t *rp = codes + (size_t)(row_b0 + wave * RPW + grp) * H + k0 + sub * 16;
-    // weight loads go out first; the slot range is read while they fly
-    int p0 = 0, ne = 1;
-    for (int st = 0; st < ne; st += a.st) {
-        uint4 w[RG][SEGS];
-#ifdef MOE_GEMV_X_FIRST
-        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
-        const int nt = min(a.st, ne - st);
-        for (int c = tid; c < nt * SEGS * 16; c += kThreads) {
-            const int j = c / (SEGS * 16), r = c - j * (SEGS * 16);
-            const int tok = a.sorted_token[p0 + st + j];
-            xs[j][r] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok * H + k0 + r * 8);
-        }
-#endif
+        auto mul_chunk = [&](const uint4 (&wc)[CH], int c) {
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) w[rg][sg] = load16(rp + (size_t)rg * 8 * H + sg * 128);
-#ifndef MOE_GEMV_X_FIRST
-        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
-        const int nt = min(a.st, ne - st);
-        for (int c = tid; c < nt * SEGS * 16; c += kThreads) {
-            const int j = c / (SEGS * 16), r = c - j * (SEGS * 16);
-            const int tok = a.sorted_token[p0 + st + j];
-            xs[j][r] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok * H + k0 + r * 8);
-        }
-#endif
-        __syncthreads();
-
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            float acc[ST];
-#pragma unroll
-            for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
-#pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) {
-                const float s = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_lane), sg));
+            for (int sg = 0; sg < CH; ++sg) {
+                const int seg = c * CH + sg;
+                const float s = seg < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, sc_lo), seg))
+                                         : __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, sc_hi), seg - 64));
+                const uint4 wv = wc[sg];
                 bf16x2 wb[8];
-                e4m3x4_to_bf16(w[rg][sg].x, wb[0], wb[1]);
-                e4m3x4_to_bf16(w[rg][sg].y, wb[2], wb[3]);
-                e4m3x4_to_bf16(w[rg][sg].z, wb[4], wb[5]);
-                e4m3x4_to_bf16(w[rg][sg].w, wb[6], wb[7]);
+                e4m3x4_to_bf16(wv.x, wb[0], wb[1]);
+                e4m3x4_to_bf16(wv.y, wb[2], wb[3]);
+                e4m3x4_to_bf16(wv.z, wb[4], wb[5]);
+                e4m3x4_to_bf16(wv.w, wb[6], wb[7]);
 #pragma unroll
                 for (int j = 0; j < ST; ++j) {
                     if (j < nt) {
-                        const uint4 xa = xs[j][sg * 16 + sub * 2];
-                        const uint4 xb = xs[j][sg * 16 + sub * 2 + 1];
+                        const uint4 xa = xl[j * H8 + seg * 16 + sub * 2];
+                        const uint4 xb = xl[j * H8 + seg * 16 + sub * 2 + 1];
                         float d = dot2(wb[0], xa.x, 0.0f);
                         d = dot2(wb[1], xa.y, d);
                         d = dot2(wb[2], xa.z, d);
@@ -194,148 +179,197 @@ __global__ __launch_bounds__(kThreads, MOE_GEMV_MIN_WAVES) void gemv_gateup_e4m3
                         acc[j] = fmaf(d, s, acc[j]);
                     }
                 }
+                if constexpr (NCH > 0) __builtin_amdgcn_sched_barrier(0);  // convert per segment
             }
+        };
+
+        // x rows to LDS (their loads go out first), with the first weight
+        // chunks in flight across the barrier
+        for (int f = tid; f < nt * H8; f += kThreads) {
+            const int j = f / H8, r = f - j * H8;
+            xl[f] = *reinterpret_cast<const uint4 *>(a.x + (size_t)a.sorted_token[p0 + s0 + j] * H + r * 8);
+        }
+        if constexpr (NCH > 0) {
+            uint4 w[3][CH];
+            load_w(w[0], 0);
+            if (NCH > 1) load_w(w[1], 1);
+            moe::lds_barrier();
 #pragma unroll
-            for (int j = 0; j < ST; ++j) {
-                if (j < nt) {
-                    const float v = moe::sum8_lanes(acc[j]);
-                    if (sub == 0)
-                        a.partials[((size_t)ks * a.S + p0 + st + j) * pstride + col_b0 + wave * RPW +
-                                   rg * 8 + grp] = v;
-                }
+            for (int c = 0; c < NCH; ++c) {
+                // the scheduling fences keep each chunk's loads where they are
+                // issued (two chunks ahead), not hoisted into a register spill
+                if (c + 2 < NCH) load_w(w[(c + 2) % 3], c + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                mul_chunk(w[c % 3], c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            uint4 w0[CH], w1[CH];
+            load_w(w0, 0);
+            moe::lds_barrier();
+            // wait for chunk c (the only loads in flight), start chunk c + 1,
+            // multiply chunk c; unrolled by two so both buffers stay static
+            auto step = [&](int c, uint4 (&wc)[CH], uint4 (&wn)[CH]) {
+                moe::wait_vm0();
+                if (c + 1 < nch) load_w(wn, c + 1);
+                mul_chunk(wc, c);
+            };
+            for (int c = 0; c < nch; c += 2) {
+                step(c, w0, w1);
+                if (c + 1 >= nch) break;
+                step(c + 1, w1, w0);
             }
         }
-        __syncthreads();
+
+        // up sums to LDS, then SwiGLU in the gate waves
+        float v[ST];
+#pragma unroll
+        for (int j = 0; j < ST; ++j) v[j] = j < nt ? moe::sum8_lanes(acc[j]) : 0.0f;
+        if (is_up && sub == 0) {
+#pragma unroll
+            for (int j = 0; j < ST; ++j)
+                if (j < nt) ush[j][(wave & 1) * 8 + grp] = v[j];
+        }
+        moe::lds_barrier();
+        if (!is_up && sub == 0) {
+#pragma unroll
+            for (int j = 0; j < ST; ++j)
+                if (j < nt)
+                    a.h[(size_t)(p0 + s0 + j) * I + hrow] =
+                        swiglu_clamp(v[j], ush[j][(wave & 1) * 8 + grp], a.limit);
+        }
+        moe::lds_barrier();                           // x and ush are reused by the next pass
     }
 }
 
 // ---------------------------------------------------------------------------
 // down
 // ---------------------------------------------------------------------------
-// h slice staged in LDS with the float4 of lane `sub`, part q of segment sg at
-// index sg*32 + q*8 + sub, so the 8 lanes of a group read 128 contiguous
-// bytes per LDS instruction (no bank conflicts).  The block's 64 rows lie in
-// one 128-row scale block.
-template <int SEGS, int RG, int ST>
-__global__ __launch_bounds__(kThreads, MOE_GEMV_MIN_WAVES) void gemv_down_e4m3_kernel(DownArgs a)
+// One block = 32 output rows of one active expert over the whole of K (=
+// inter), 8 rows per wave.  At the start of a pass the FP32 h rows of up to
+// a.st slots go to LDS (float4 q of lane sub in segment sg at sg*32 + q*8 +
+// sub, so the 8 lanes of a row read 128 contiguous bytes); the K loop then
+// streams weights in chunks of CH segments.  With NCH > 0 the loop is fully
+// unrolled with the next two chunks in flight; NCH == 0 is the looped form
+// with one chunk in flight.  The 32 rows lie in one 128-row scale block, so
+// a wave keeps the block scales of all K segments in two registers.  With
+// one slot per pass the kernel fits 72 VGPRs (7 waves per SIMD): the decode
+// grid of 8 experts x 224 row tiles is then one round of 7 blocks per CU.
+template <int CH, int NCH, int ST>
+__global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kernel(DownArgs a)
 {
-    constexpr int RPW = RG * 8;
-    constexpr int RPB = RPW * (kThreads / 64);
-    static_assert(128 % RPB == 0, "block rows inside one 128-row scale block");
-    extern __shared__ float4 lds_h[];                // FP32 h slice per slot: [a.st][SEGS*32]
-    float4 (*hs)[SEGS * 32] = reinterpret_cast<float4 (*)[SEGS * 32]>(lds_h);
+    extern __shared__ float4 hl[];                   // [a.st][I / 4], permuted per segment
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int grp = lane >> 3, sub = lane & 7;
-    int bid = blockIdx.x;
-    const int ks = bid % a.nks;
-    bid /= a.nks;
-    const int tile = bid % a.ntiles;
-    const int ai = bid / a.ntiles;
-    const int e = a.active[ai];              // -1 past the active experts
+    const int tile = blockIdx.x % a.ntiles;
+    const int ai = blockIdx.x / a.ntiles;
+    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
     if (e < 0) return;
-    const int H = a.H, I = a.I;
-    const uint8_t *codes = a.codes + (size_t)e * H * I;
-    const int sc_cols = I >> 7;
-    const int row_b0 = tile * RPB;
-    const int k0 = ks * SEGS * 128;
-    float *out = a.out + (size_t)ks * a.S * H;
+    const int H = a.H, I = a.I, I4 = I >> 2;
+    const int nseg = I >> 7, nch = NCH > 0 ? NCH : nseg / CH;
+    const int row0 = tile * 32;
+    const int row = row0 + wave * 8 + grp;
+    const uint8_t *wb0 = a.codes + ((size_t)e * H + row0 + wave * 8) * I;
+    const uint32_t loff = (uint32_t)grp * I + sub * 16;
+    const float *scb = a.scales + ((size_t)e * (H >> 7) + (row0 >> 7)) * nseg;
+    const float sc_lo = lane < nseg ? scb[lane] : 0.0f;
+    const float sc_hi = lane + 64 < nseg ? scb[lane + 64] : 0.0f;
+    const int p0 = moe::uniform(a.offsets[e]);
+    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
 
-    const float *sc_blk = a.scales + (size_t)e * (H >> 7) * sc_cols +
-                          (size_t)(row_b0 >> 7) * sc_cols + (k0 >> 7);
-    const float sc_lane = sc_blk[lane % SEGS];
-
-    const uint8_t *rp = codes + (size_t)(row_b0 + wave * RPW + grp) * I + k0 + sub * 16;
-    int p0 = 0, ne = 1;
-    for (int st = 0; st < ne; st += a.st) {
-        uint4 w[RG][SEGS];
-#ifdef MOE_GEMV_X_FIRST
-        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
-        const int nt = min(a.st, ne - st);
-        for (int c = tid; c < nt * SEGS * 32; c += kThreads) {
-            const int j = c / (SEGS * 32), f = c - j * (SEGS * 32);  // f = source float4 index
-            const int sg = f >> 5, r = f & 31, sb = r >> 2, q = r & 3;
-            hs[j][sg * 32 + q * 8 + sb] =
-                *reinterpret_cast<const float4 *>(a.h + (size_t)(p0 + st + j) * I + k0 + f * 4);
-        }
-#endif
+    for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
+        const int nt = min(a.st, ne - s0);
+        const uint8_t *wbp = wb0;
+        uint32_t lo = loff;
+        asm volatile("" : "+s"(wbp), "+v"(lo));      // keep per-chunk addresses inside the pass
+        auto load_w = [&](uint4 (&wb)[CH], int c) {
+            const uint8_t *cb = wbp + c * CH * 128;
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
+            for (int sg = 0; sg < CH; ++sg) wb[sg] = load16(cb + lo + sg * 128);
+        };
+        float acc[ST];
 #pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) w[rg][sg] = load16(rp + (size_t)rg * 8 * I + sg * 128);
-#ifndef MOE_GEMV_X_FIRST
-        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
-        const int nt = min(a.st, ne - st);
-        for (int c = tid; c < nt * SEGS * 32; c += kThreads) {
-            const int j = c / (SEGS * 32), f = c - j * (SEGS * 32);  // f = source float4 index
-            const int sg = f >> 5, r = f & 31, sb = r >> 2, q = r & 3;
-            hs[j][sg * 32 + q * 8 + sb] =
-                *reinterpret_cast<const float4 *>(a.h + (size_t)(p0 + st + j) * I + k0 + f * 4);
-        }
-#endif
-        __syncthreads();
-
+        for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
+        auto mul_chunk = [&](const uint4 (&wc)[CH], int c) {
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            float acc[ST];
+            for (int sg = 0; sg < CH; ++sg) {
+                const int seg = c * CH + sg;
+                const float s = seg < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, sc_lo), seg))
+                                         : __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, sc_hi), seg - 64));
+                const uint32_t dw[4] = {wc[sg].x, wc[sg].y, wc[sg].z, wc[sg].w};
+                float d[ST];
 #pragma unroll
-            for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
-#pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) {
-                const float s = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_lane), sg));
-                f32x2 wf[8];
-                const uint32_t dw[4] = {w[rg][sg].x, w[rg][sg].y, w[rg][sg].z, w[rg][sg].w};
+                for (int j = 0; j < ST; ++j) d[j] = 0.0f;
+                // one dword (4 weights) at a time keeps few temporaries live
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    wf[2 * q] = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[q], false);
-                    wf[2 * q + 1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[q], true);
-                }
+                    const f32x2 w01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[q], false);
+                    const f32x2 w23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[q], true);
 #pragma unroll
-                for (int j = 0; j < ST; ++j) {
-                    if (j < nt) {
-                        float d = 0.0f;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float4 hv = hs[j][sg * 32 + q * 8 + sub];
-                            d = fmaf(wf[2 * q].x, hv.x, d);
-                            d = fmaf(wf[2 * q].y, hv.y, d);
-                            d = fmaf(wf[2 * q + 1].x, hv.z, d);
-                            d = fmaf(wf[2 * q + 1].y, hv.w, d);
+                    for (int j = 0; j < ST; ++j) {
+                        if (j < nt) {
+                            const float4 hv = hl[j * I4 + seg * 32 + q * 8 + sub];
+                            d[j] = fmaf(w01.x, hv.x, d[j]);
+                            d[j] = fmaf(w01.y, hv.y, d[j]);
+                            d[j] = fmaf(w23.x, hv.z, d[j]);
+                            d[j] = fmaf(w23.y, hv.w, d[j]);
                         }
-                        acc[j] = fmaf(d, s, acc[j]);
                     }
+                    if constexpr (NCH > 0 && ST == 1) __builtin_amdgcn_sched_barrier(0);
                 }
-            }
 #pragma unroll
-            for (int j = 0; j < ST; ++j) {
-                if (j < nt) {
-                    const float v = moe::sum8_lanes(acc[j]);
-                    if (sub == 0)
-                        out[(size_t)(p0 + st + j) * H + row_b0 + wave * RPW + rg * 8 + grp] = v;
-                }
+                for (int j = 0; j < ST; ++j)
+                    if (j < nt) acc[j] = fmaf(d[j], s, acc[j]);
+                if constexpr (NCH > 0 && ST > 1) __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        for (int f = tid; f < nt * I4; f += kThreads) {
+            const int j = f / I4, r = f - j * I4;     // r: source float4 (4 K values)
+            const int sg = r >> 5, rr = r & 31;
+            hl[j * I4 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] =
+                *reinterpret_cast<const float4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
+        }
+        if constexpr (NCH > 0) {
+            uint4 w[3][CH];
+            load_w(w[0], 0);
+            if (NCH > 1) load_w(w[1], 1);
+            moe::lds_barrier();
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                if (c + 2 < NCH) load_w(w[(c + 2) % 3], c + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                mul_chunk(w[c % 3], c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            uint4 w0[CH], w1[CH];
+            load_w(w0, 0);
+            moe::lds_barrier();
+            auto step = [&](int c, uint4 (&wc)[CH], uint4 (&wn)[CH]) {
+                moe::wait_vm0();
+                if (c + 1 < nch) load_w(wn, c + 1);
+                mul_chunk(wc, c);
+            };
+            for (int c = 0; c < nch; c += 2) {
+                step(c, w0, w1);
+                if (c + 1 >= nch) break;
+                step(c + 1, w1, w0);
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            if (j < nt) {
+                const float v = moe::sum8_lanes(acc[j]);
+                if (sub == 0) a.y[(size_t)(p0 + s0 + j) * H + row] = v;
+            }
+        }
+        moe::lds_barrier();                           // h is reused by the next pass
     }
-}
-
-// y[p][m] = sum over slices of partials, slice order; rows p < offsets[E].
-__global__ __launch_bounds__(256) void sum_slices_kernel(const float *__restrict__ part, int32_t nks,
-                                                         int32_t S, int32_t H,
-                                                         const int32_t *__restrict__ offsets,
-                                                         int32_t E, float *__restrict__ y)
-{
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;    // float4 index
-    const size_t n4 = (size_t)offsets[E] * H / 4;
-    if (i >= n4) return;
-    float4 acc = reinterpret_cast<const float4 *>(part)[i];
-    for (int ks = 1; ks < nks; ++ks) {
-        const float4 v = reinterpret_cast<const float4 *>(part + (size_t)ks * S * H)[i];
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    reinterpret_cast<float4 *>(y)[i] = acc;
 }
 
 }  // namespace
@@ -345,83 +379,116 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float *__restrict
 // the host never needs the routing.
 namespace {
 
-template <int SEGS>
+template <int CH, int NCH, int ST>
 void gateup_launch(const GateUpArgs &a, int grid, hipStream_t st)
 {
-    const size_t lds = (size_t)a.st * SEGS * 16 * sizeof(uint4);
-    hipLaunchKernelGGL((gemv_gateup_e4m3_kernel<SEGS, MOE_E4M3_GU_RG, MOE_E4M3_GU_ST>), dim3(grid),
-                       dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_gateup_e4m3_kernel<CH, NCH, ST>), dim3(grid), dim3(kThreads),
+                       (size_t)a.st * a.H * 2, st, a);
 }
 
-template <int SEGS>
+// Unrolled kernels for 8-segment chunks (hidden a multiple of 1024), for the
+// chunk counts that fit 128 VGPRs at each pass size (up to 8 chunks with one
+// or two slots, 2 with more); every other shape runs the looped kernel.
+template <int ST, int MAXN, int N = 1>
+bool gateup_launch_unrolled(const GateUpArgs &a, int nch, int grid, hipStream_t st)
+{
+    if constexpr (N > MAXN) {
+        return false;
+    } else {
+        if (nch == N) {
+            gateup_launch<8, N, ST>(a, grid, st);
+            return true;
+        }
+        return gateup_launch_unrolled<ST, MAXN, N + 1>(a, nch, grid, st);
+    }
+}
+
+template <int CH, int NCH, int ST>
 void down_launch(const DownArgs &a, int grid, hipStream_t st)
 {
-    const size_t lds = (size_t)a.st * SEGS * 32 * sizeof(float4);
-    hipLaunchKernelGGL((gemv_down_e4m3_kernel<SEGS, MOE_E4M3_DN_RG, MOE_E4M3_DN_ST>), dim3(grid),
-                       dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_down_e4m3_kernel<CH, NCH, ST>), dim3(grid), dim3(kThreads),
+                       (size_t)a.st * a.I * 4, st, a);
+}
+
+// Unrolled kernels for 4-segment chunks, for the chunk counts that fit the
+// register budget of each pass size (up to 5 chunks, inter <= 2560, with one
+// slot; 8 with two; 3 with more); every other shape runs the looped kernel.
+template <int ST, int MAXN, int N = 1>
+bool down_launch_unrolled(const DownArgs &a, int nch, int grid, hipStream_t st)
+{
+    if constexpr (N > MAXN) {
+        return false;
+    } else {
+        if (nch == N) {
+            down_launch<4, N, ST>(a, grid, st);
+            return true;
+        }
+        return down_launch_unrolled<ST, MAXN, N + 1>(a, nch, grid, st);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
                                    const uint16_t *x, const MoeRouteDev &r, int32_t M, int32_t S,
-                                   int32_t E, int32_t hidden, int32_t inter, float *partials,
-                                   int32_t nks, hipStream_t st)
+                                   int32_t E, int32_t hidden, int32_t inter, float limit, float *h,
+                                   hipStream_t st)
 {
     GateUpArgs a;
-    a.st = M < MOE_E4M3_GU_ST ? M : MOE_E4M3_GU_ST;
+    a.st = gemv_gateup_pass_slots(M, hidden, MOE_E4M3_GU_ST);
     a.gcodes = gate.codes; a.ucodes = up.codes;
     a.gscales = (const float *)gate.scales; a.uscales = (const float *)up.scales;
     a.x = x; a.offsets = r.offsets; a.sorted_token = r.sorted_token; a.active = r.active;
-    a.num_active = r.num_active; a.partials = partials;
-    a.S = S; a.H = hidden; a.I = inter;
-    const int segs = gemv_segs_gateup(kFmtE4M3, hidden);
-    a.nks = gemv_gateup_slices(kFmtE4M3, hidden);
-    if (a.nks != nks) return hipErrorInvalidValue;
-    a.ntiles = 2 * (inter / (MOE_E4M3_GU_RG * 32));
-    const int grid = (S < E ? S : E) * a.ntiles * a.nks;
-    switch (segs) {
-    case 8: gateup_launch<8>(a, grid, st); break;
-    case 7: gateup_launch<7>(a, grid, st); break;
-    case 6: gateup_launch<6>(a, grid, st); break;
-    case 5: gateup_launch<5>(a, grid, st); break;
-    case 4: gateup_launch<4>(a, grid, st); break;
-    case 3: gateup_launch<3>(a, grid, st); break;
-    case 2: gateup_launch<2>(a, grid, st); break;
-    default: gateup_launch<1>(a, grid, st); break;
+    a.h = h; a.H = hidden; a.I = inter; a.limit = limit;
+    a.ntiles = inter / 16;
+    const int grid = (S < E ? S : E) * a.ntiles;
+    const int ch = gemv_chunk_segs(kFmtE4M3, hidden), nch = hidden / 128 / ch;
+    bool done = false;
+    if (ch == 8) {
+        if (a.st <= 1) done = gateup_launch_unrolled<1, 8>(a, nch, grid, st);
+        else if (a.st <= 2) done = gateup_launch_unrolled<2, 8>(a, nch, grid, st);
+        else done = gateup_launch_unrolled<MOE_E4M3_GU_ST, 2>(a, nch, grid, st);
+    }
+    if (!done) {
+        switch (ch) {
+        case 8: gateup_launch<8, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
+        case 7: gateup_launch<7, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
+        case 6: gateup_launch<6, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
+        case 5: gateup_launch<5, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
+        case 4: gateup_launch<4, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
+        case 3: gateup_launch<3, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
+        case 2: gateup_launch<2, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
+        default: gateup_launch<1, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
+        }
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
                                  int32_t M, int32_t S, int32_t E, int32_t hidden, int32_t inter,
-                                 float *y, float *slice_scratch, hipStream_t st)
+                                 float *y, hipStream_t st)
 {
     DownArgs a;
-    a.st = M < MOE_E4M3_DN_ST ? M : MOE_E4M3_DN_ST;
+    a.st = gemv_down_pass_slots(M, inter, MOE_E4M3_DN_ST);
     a.codes = down.codes; a.scales = (const float *)down.scales; a.h = h;
-    a.offsets = r.offsets; a.active = r.active; a.num_active = r.num_active;
-    a.S = S; a.H = hidden; a.I = inter;
-    const int segs = gemv_segs_down(kFmtE4M3, inter);
-    a.nks = gemv_down_slices(kFmtE4M3, inter);
-    a.out = a.nks == 1 ? y : slice_scratch;
-    a.ntiles = hidden / (MOE_E4M3_DN_RG * 32);
-    const int grid = (S < E ? S : E) * a.ntiles * a.nks;
-    switch (segs) {
-    case 16: down_launch<16>(a, grid, st); break;
-    case 8: down_launch<8>(a, grid, st); break;
-    case 7: down_launch<7>(a, grid, st); break;
-    case 6: down_launch<6>(a, grid, st); break;
-    case 5: down_launch<5>(a, grid, st); break;
-    case 4: down_launch<4>(a, grid, st); break;
-    case 3: down_launch<3>(a, grid, st); break;
-    case 2: down_launch<2>(a, grid, st); break;
-    default: down_launch<1>(a, grid, st); break;
+    a.offsets = r.offsets; a.active = r.active; a.y = y;
+    a.H = hidden; a.I = inter;
+    a.ntiles = hidden / 32;
+    const int grid = (S < E ? S : E) * a.ntiles;
+    const int ch = gemv_down_chunk_segs(kFmtE4M3, inter), nch = inter / 128 / ch;
+    bool done = false;
+    if (ch == 4) {
+        if (a.st <= 1) done = down_launch_unrolled<1, 5>(a, nch, grid, st);
+        else if (a.st <= 2) done = down_launch_unrolled<2, 8>(a, nch, grid, st);
+        else done = down_launch_unrolled<MOE_E4M3_DN_ST, 3>(a, nch, grid, st);
     }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.nks == 1) return err;
-    const size_t n4 = (size_t)S * hidden / 4;
-    hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
-                       slice_scratch, a.nks, S, hidden, r.offsets, E, y);
+    if (!done) {
+        switch (ch) {
+        case 4: down_launch<4, 0, MOE_E4M3_DN_ST>(a, grid, st); break;
+        case 3: down_launch<3, 0, MOE_E4M3_DN_ST>(a, grid, st); break;
+        case 2: down_launch<2, 0, MOE_E4M3_DN_ST>(a, grid, st); break;
+        default: down_launch<1, 0, MOE_E4M3_DN_ST>(a, grid, st); break;
+        }
+    }
     return hipGetLastError();
 }

@@ -6,7 +6,8 @@
 // and "spark_model glm5next_mlp/forward.rs", fn w4a16_gemv (the NVFP4 operand
 // triple, scale_2 by value).  Same work layout as the E4M3 GEMV: 8 lanes per
 // weight row, 16 code bytes (32 weights) per lane per 128-byte segment, one
-// pass over each active expert for all of its slots.
+// pass over each active expert for all of its slots; gate/up covers the
+// whole of K per block and ends in the clamped SwiGLU.
 //
 // Decode: gfx950 converts E2M1 pairs straight to bf16 (gate/up, against bf16
 // activations with v_dot2) or to f32 (down, against FP32 h); the E2M1 values
@@ -26,18 +27,19 @@ struct GateUpArgs {
     const uint8_t *gcodes, *ucodes, *gscales, *uscales;
     const float *gscale2, *uscale2;
     const uint16_t *x;
-    const int32_t *offsets, *sorted_token, *active, *num_active;
-    float *partials;
-    int32_t S, H, I, nks, ntiles, st;   // st: slots per weight pass (<= ST)
+    const int32_t *offsets, *sorted_token, *active;
+    float *h;                           // [S][I]
+    int32_t H, I, ntiles, st;           // st: slots per weight pass (<= ST)
+    float limit;
 };
 
 struct DownArgs {
     const uint8_t *codes, *scales;
     const float *scale2;
-    const float *h;
-    const int32_t *offsets, *active, *num_active;
-    float *out;
-    int32_t S, H, I, nks, ntiles, st;   // st: slots per weight pass (<= ST)
+    const float *h;                     // [S][I]
+    const int32_t *offsets, *active;
+    float *y;                           // [S][H]
+    int32_t H, I, ntiles, st;           // st: slots per weight pass (<= ST)
 };
 
 // Codes and group scales are streamed once per call (non-temporal loads).
@@ -82,279 +84,373 @@ __device__ __forceinline__ float dot8_fp4_f32(uint32_t c, float4 a, float4 b, fl
     return d;
 }
 
-// SEGS: 256-wide K segments per slice; RG: 8-row groups per wave; ST: slots
-// per pass.  All RG*SEGS code and scale loads of a wave are issued before the
-// first multiply.
-template <int SEGS, int RG, int ST>
-__global__ __launch_bounds__(kThreads) void gemv_gateup_nvfp4_kernel(GateUpArgs a)
+// silu(min(g, L)) * clamp(u, -L, L), silu(z) = z / (1 + e^-z)
+__device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 {
-    constexpr int RPW = RG * 8;
-    constexpr int RPB = RPW * (kThreads / 64);
-    // bf16 x slice per slot; uint4 q of lane sub in segment sg at sg*32 + q*8 + sub.
-    extern __shared__ uint4 lds_x[];                 // [a.st][SEGS*32]
-    uint4 (*xs)[SEGS * 32] = reinterpret_cast<uint4 (*)[SEGS * 32]>(lds_x);
+    const float gc = fminf(g, L);
+    const float uc = fminf(fmaxf(u, -L), L);
+    return gc / (1.0f + expf(-gc)) * uc;
+}
+
+// gate + up + SwiGLU: one block = 16 h rows of one active expert over the
+// whole of K; waves 0-1 stream those rows of the gate bank, waves 2-3 of the
+// up bank.  At the start of a pass the bf16 x rows of up to a.st slots go to
+// LDS for the whole of K (uint4 q of lane sub in segment sg at sg*32 + q*8 +
+// sub, so the 8 lanes of a row read 128 contiguous bytes); the K loop then
+// only streams codes and group scales, in chunks of CH 256-wide segments.
+// With NCH > 0 (chunk count known at compile time) the loop is fully
+// unrolled with the next two chunks in flight (straight-line code: the
+// compiler waits for exactly the chunk it multiplies); NCH == 0 is the
+// generic looped form with one chunk in flight.  The up sums reach the gate
+// waves through LDS; they apply scale_2, the clamped SwiGLU, and write h.
+template <int CH, int NCH, int ST>
+__global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpArgs a)
+{
+    extern __shared__ uint4 xl[];                    // [a.st][H / 8], permuted per segment
+    __shared__ float ush[ST][16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int grp = lane >> 3, sub = lane & 7;
-    int bid = blockIdx.x;
-    const int ks = bid % a.nks;
-    bid /= a.nks;
-    const int tile = bid % a.ntiles;
-    const int ai = bid / a.ntiles;
-    const int e = a.active[ai];              // -1 past the active experts
+    const int tile = blockIdx.x % a.ntiles;
+    const int ai = blockIdx.x / a.ntiles;
+    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
     if (e < 0) return;
-    const int H = a.H, I = a.I;
-    const int half = a.ntiles >> 1;
-    const bool is_up = tile >= half;
-    const size_t rowb = (size_t)H / 2, rows = (size_t)H / 16;
-    const int row_b0 = (is_up ? tile - half : tile) * RPB;
-    const int col_b0 = (is_up ? I : 0) + row_b0;
-    const int k0 = ks * SEGS * kSegK;
-    const size_t pstride = (size_t)2 * I;
+    const int H = a.H, I = a.I, H8 = H >> 3;
+    const int nch = NCH > 0 ? NCH : H / (kSegK * CH);
+    const bool is_up = wave >= 2;
+    const int hrow0 = tile * 16;
+    const int hrow = hrow0 + (wave & 1) * 8 + grp;
+    const int rowb = H / 2, rows = H / 16;
     const float s2 = (is_up ? a.uscale2 : a.gscale2)[e];
-    const size_t row0 = (size_t)e * I + row_b0 + wave * RPW + grp;
-    const uint8_t *rp = (is_up ? a.ucodes : a.gcodes) + row0 * rowb + k0 / 2 + sub * 16;
-    const uint8_t *sp = (is_up ? a.uscales : a.gscales) + row0 * rows + k0 / 16 + sub * 2;
+    // code and group-scale addresses = wave-uniform base + fixed lane offset
+    const size_t row0 = (size_t)e * I + hrow0 + (wave & 1) * 8;
+    const uint8_t *cb0 = (is_up ? a.ucodes : a.gcodes) + row0 * rowb;
+    const uint8_t *sb0 = (is_up ? a.uscales : a.gscales) + row0 * rows;
+    const uint32_t coff = (uint32_t)grp * rowb + sub * 16, soff = (uint32_t)grp * rows + sub * 2;
+    const int p0 = moe::uniform(a.offsets[e]);
+    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
 
-    // weight loads go out first; the slot range is read while they fly
-    int p0 = 0, ne = 1;
-    for (int st = 0; st < ne; st += a.st) {
-        uint4 w[RG][SEGS];
-        uint32_t sv[RG][SEGS];
+    for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
+        const int nt = min(a.st, ne - s0);
+        // opaque copies keep the per-chunk address arithmetic inside the pass
+        const uint8_t *cbp = cb0, *sbp = sb0;
+        uint32_t co = coff, so = soff;
+        asm volatile("" : "+s"(cbp), "+s"(sbp), "+v"(co), "+v"(so));
+        auto load_w = [&](uint4 (&wb)[CH], uint32_t (&sb)[CH], int c) {
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) {
-                w[rg][sg] = load16(rp + (size_t)rg * 8 * rowb + sg * 128);
-                sv[rg][sg] = load2(sp + (size_t)rg * 8 * rows + sg * 16);
+            for (int sg = 0; sg < CH; ++sg) {
+                wb[sg] = load16(cbp + (c * CH + sg) * 128 + co);
+                sb[sg] = load2(sbp + (c * CH + sg) * 16 + so);
             }
-        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
-        const int nt = min(a.st, ne - st);
-
-        for (int c = tid; c < nt * SEGS * 32; c += kThreads) {
-            const int j = c / (SEGS * 32), f = c - j * (SEGS * 32);
-            const int sg = f >> 5, r = f & 31, sb = r >> 2, q = r & 3;
-            const int tok = a.sorted_token[p0 + st + j];
-            xs[j][sg * 32 + q * 8 + sb] =
-                *reinterpret_cast<const uint4 *>(a.x + (size_t)tok * H + k0 + f * 8);
-        }
-        __syncthreads();
-
+        };
+        float acc[ST];
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            float acc[ST];
+        for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
+        auto mul_chunk = [&](const uint4 (&wc)[CH], const uint32_t (&vc)[CH], int c) {
 #pragma unroll
-            for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
-#pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) {
-                const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)sv[rg][sg], false);
+            for (int sg = 0; sg < CH; ++sg) {
+                const int seg = c * CH + sg;
+                const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)vc[sg], false);
+                const uint4 wv = wc[sg];
 #pragma unroll
                 for (int j = 0; j < ST; ++j) {
                     if (j < nt) {
-                        const uint4 *xv = &xs[j][sg * 32 + sub];
-                        float d0 = dot8_fp4_bf16(w[rg][sg].x, xv[0], 0.0f);
-                        d0 = dot8_fp4_bf16(w[rg][sg].y, xv[8], d0);
-                        float d1 = dot8_fp4_bf16(w[rg][sg].z, xv[16], 0.0f);
-                        d1 = dot8_fp4_bf16(w[rg][sg].w, xv[24], d1);
+                        const uint4 *xv = &xl[j * H8 + seg * 32 + sub];
+                        float d0 = dot8_fp4_bf16(wv.x, xv[0], 0.0f);
+                        d0 = dot8_fp4_bf16(wv.y, xv[8], d0);
+                        float d1 = dot8_fp4_bf16(wv.z, xv[16], 0.0f);
+                        d1 = dot8_fp4_bf16(wv.w, xv[24], d1);
                         acc[j] = fmaf(d0, sc.x, acc[j]);
                         acc[j] = fmaf(d1, sc.y, acc[j]);
                     }
                 }
+                if constexpr (NCH > 0) __builtin_amdgcn_sched_barrier(0);
             }
+        };
+
+        for (int f = tid; f < nt * H8; f += kThreads) {
+            const int j = f / H8, r = f - j * H8;     // r: source uint4 (8 K values)
+            const int sg = r >> 5, rr = r & 31;
+            xl[j * H8 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] =
+                *reinterpret_cast<const uint4 *>(a.x + (size_t)a.sorted_token[p0 + s0 + j] * H + r * 8);
+        }
+        if constexpr (NCH > 0) {
+            uint4 w[3][CH];
+            uint32_t v[3][CH];
+            load_w(w[0], v[0], 0);
+            if (NCH > 1) load_w(w[1], v[1], 1);
+            moe::lds_barrier();
 #pragma unroll
-            for (int j = 0; j < ST; ++j) {
-                if (j < nt) {
-                    const float v = moe::sum8_lanes(acc[j]) * s2;
-                    if (sub == 0)
-                        a.partials[((size_t)ks * a.S + p0 + st + j) * pstride + col_b0 + wave * RPW +
-                                   rg * 8 + grp] = v;
-                }
+            for (int c = 0; c < NCH; ++c) {
+                if (c + 2 < NCH) load_w(w[(c + 2) % 3], v[(c + 2) % 3], c + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                mul_chunk(w[c % 3], v[c % 3], c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            uint4 w0[CH], w1[CH];
+            uint32_t v0[CH], v1[CH];
+            load_w(w0, v0, 0);
+            moe::lds_barrier();
+            auto step = [&](int c, uint4 (&wc)[CH], uint32_t (&vc)[CH], uint4 (&wn)[CH],
+                            uint32_t (&vn)[CH]) {
+                moe::wait_vm0();
+                if (c + 1 < nch) load_w(wn, vn, c + 1);
+                mul_chunk(wc, vc, c);
+            };
+            for (int c = 0; c < nch; c += 2) {
+                step(c, w0, v0, w1, v1);
+                if (c + 1 >= nch) break;
+                step(c + 1, w1, v1, w0, v0);
             }
         }
-        __syncthreads();
+
+        float v[ST];
+#pragma unroll
+        for (int j = 0; j < ST; ++j) v[j] = j < nt ? moe::sum8_lanes(acc[j]) * s2 : 0.0f;
+        if (is_up && sub == 0) {
+#pragma unroll
+            for (int j = 0; j < ST; ++j)
+                if (j < nt) ush[j][(wave & 1) * 8 + grp] = v[j];
+        }
+        moe::lds_barrier();
+        if (!is_up && sub == 0) {
+#pragma unroll
+            for (int j = 0; j < ST; ++j)
+                if (j < nt)
+                    a.h[(size_t)(p0 + s0 + j) * I + hrow] =
+                        swiglu_clamp(v[j], ush[j][(wave & 1) * 8 + grp], a.limit);
+        }
+        moe::lds_barrier();                           // x and ush are reused by the next pass
     }
 }
 
-template <int SEGS, int RG, int ST>
+// down: one block = 32 output rows of one active expert over the whole of K
+// (= inter), 8 rows per wave.  At the start of a pass the FP32 h rows of up
+// to a.st slots go to LDS (float4 q of lane sub in segment sg at sg*64 + q*8
+// + sub); the K loop then streams codes and group scales in chunks of CH
+// 256-wide segments, fully unrolled with the next two chunks in flight when
+// NCH > 0, looped with one chunk in flight when NCH == 0.
+template <int CH, int NCH, int ST>
 __global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
 {
-    constexpr int RPW = RG * 8;
-    constexpr int RPB = RPW * (kThreads / 64);
-    // FP32 h slice per slot; float4 q of lane sub in segment sg at sg*64 + q*8 + sub.
-    extern __shared__ float4 lds_h[];                // [a.st][SEGS*64]
-    float4 (*hs)[SEGS * 64] = reinterpret_cast<float4 (*)[SEGS * 64]>(lds_h);
+    extern __shared__ float4 hl[];                   // [a.st][I / 4], permuted per segment
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int grp = lane >> 3, sub = lane & 7;
-    int bid = blockIdx.x;
-    const int ks = bid % a.nks;
-    bid /= a.nks;
-    const int tile = bid % a.ntiles;
-    const int ai = bid / a.ntiles;
-    const int e = a.active[ai];              // -1 past the active experts
+    const int tile = blockIdx.x % a.ntiles;
+    const int ai = blockIdx.x / a.ntiles;
+    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
     if (e < 0) return;
-    const int H = a.H, I = a.I;
-    const size_t rowb = (size_t)I / 2, rows = (size_t)I / 16;
+    const int H = a.H, I = a.I, I4 = I >> 2;
+    const int nch = NCH > 0 ? NCH : I / (kSegK * CH);
+    const int rowb = I / 2, rows = I / 16;
     const float s2 = a.scale2[e];
-    const int row_b0 = tile * RPB;
-    const int k0 = ks * SEGS * kSegK;
-    float *out = a.out + (size_t)ks * a.S * H;
-    const size_t row0 = (size_t)e * H + row_b0 + wave * RPW + grp;
-    const uint8_t *rp = a.codes + row0 * rowb + k0 / 2 + sub * 16;
-    const uint8_t *sp = a.scales + row0 * rows + k0 / 16 + sub * 2;
+    const int row0 = tile * 32;
+    const int row = row0 + wave * 8 + grp;
+    const size_t r0 = (size_t)e * H + row0 + wave * 8;
+    const uint8_t *cb0 = a.codes + r0 * rowb, *sb0 = a.scales + r0 * rows;
+    const uint32_t coff = (uint32_t)grp * rowb + sub * 16, soff = (uint32_t)grp * rows + sub * 2;
+    const int p0 = moe::uniform(a.offsets[e]);
+    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
 
-    // weight loads go out first; the slot range is read while they fly
-    int p0 = 0, ne = 1;
-    for (int st = 0; st < ne; st += a.st) {
-        uint4 w[RG][SEGS];
-        uint32_t sv[RG][SEGS];
+    for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
+        const int nt = min(a.st, ne - s0);
+        const uint8_t *cbp = cb0, *sbp = sb0;
+        uint32_t co = coff, so = soff;
+        asm volatile("" : "+s"(cbp), "+s"(sbp), "+v"(co), "+v"(so));
+        auto load_w = [&](uint4 (&wb)[CH], uint32_t (&sb)[CH], int c) {
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) {
-                w[rg][sg] = load16(rp + (size_t)rg * 8 * rowb + sg * 128);
-                sv[rg][sg] = load2(sp + (size_t)rg * 8 * rows + sg * 16);
+            for (int sg = 0; sg < CH; ++sg) {
+                wb[sg] = load16(cbp + (c * CH + sg) * 128 + co);
+                sb[sg] = load2(sbp + (c * CH + sg) * 16 + so);
             }
-        if (st == 0) { p0 = a.offsets[e]; ne = a.offsets[e + 1] - p0; }
-        const int nt = min(a.st, ne - st);
-
-        for (int c = tid; c < nt * SEGS * 64; c += kThreads) {
-            const int j = c / (SEGS * 64), f = c - j * (SEGS * 64);
-            const int sg = f >> 6, r = f & 63, sb = r >> 3, q = r & 7;
-            hs[j][sg * 64 + q * 8 + sb] =
-                *reinterpret_cast<const float4 *>(a.h + (size_t)(p0 + st + j) * I + k0 + f * 4);
-        }
-        __syncthreads();
-
+        };
+        float acc[ST];
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            float acc[ST];
+        for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
+        auto mul_chunk = [&](const uint4 (&wc)[CH], const uint32_t (&vc)[CH], int c) {
 #pragma unroll
-            for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
-#pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) {
-                const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)sv[rg][sg], false);
+            for (int sg = 0; sg < CH; ++sg) {
+                const int seg = c * CH + sg;
+                const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)vc[sg], false);
+                const uint4 wv = wc[sg];
 #pragma unroll
                 for (int j = 0; j < ST; ++j) {
                     if (j < nt) {
-                        const float4 *hv = &hs[j][sg * 64 + sub];
-                        float d0 = dot8_fp4_f32(w[rg][sg].x, hv[0], hv[8], 0.0f);
-                        d0 = dot8_fp4_f32(w[rg][sg].y, hv[16], hv[24], d0);
-                        float d1 = dot8_fp4_f32(w[rg][sg].z, hv[32], hv[40], 0.0f);
-                        d1 = dot8_fp4_f32(w[rg][sg].w, hv[48], hv[56], d1);
+                        const float4 *hv = &hl[j * I4 + seg * 64 + sub];
+                        float d0 = dot8_fp4_f32(wv.x, hv[0], hv[8], 0.0f);
+                        d0 = dot8_fp4_f32(wv.y, hv[16], hv[24], d0);
+                        float d1 = dot8_fp4_f32(wv.z, hv[32], hv[40], 0.0f);
+                        d1 = dot8_fp4_f32(wv.w, hv[48], hv[56], d1);
                         acc[j] = fmaf(d0, sc.x, acc[j]);
                         acc[j] = fmaf(d1, sc.y, acc[j]);
                     }
                 }
+                if constexpr (NCH > 0) __builtin_amdgcn_sched_barrier(0);
             }
+        };
+
+        for (int f = tid; f < nt * I4; f += kThreads) {
+            const int j = f / I4, r = f - j * I4;     // r: source float4 (4 K values)
+            const int sg = r >> 6, rr = r & 63;
+            hl[j * I4 + sg * 64 + (rr & 7) * 8 + (rr >> 3)] =
+                *reinterpret_cast<const float4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
+        }
+        if constexpr (NCH > 0) {
+            uint4 w[3][CH];
+            uint32_t v[3][CH];
+            load_w(w[0], v[0], 0);
+            if (NCH > 1) load_w(w[1], v[1], 1);
+            moe::lds_barrier();
 #pragma unroll
-            for (int j = 0; j < ST; ++j) {
-                if (j < nt) {
-                    const float v = moe::sum8_lanes(acc[j]) * s2;
-                    if (sub == 0)
-                        out[(size_t)(p0 + st + j) * H + row_b0 + wave * RPW + rg * 8 + grp] = v;
-                }
+            for (int c = 0; c < NCH; ++c) {
+                if (c + 2 < NCH) load_w(w[(c + 2) % 3], v[(c + 2) % 3], c + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                mul_chunk(w[c % 3], v[c % 3], c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            uint4 w0[CH], w1[CH];
+            uint32_t v0[CH], v1[CH];
+            load_w(w0, v0, 0);
+            moe::lds_barrier();
+            auto step = [&](int c, uint4 (&wc)[CH], uint32_t (&vc)[CH], uint4 (&wn)[CH],
+                            uint32_t (&vn)[CH]) {
+                moe::wait_vm0();
+                if (c + 1 < nch) load_w(wn, vn, c + 1);
+                mul_chunk(wc, vc, c);
+            };
+            for (int c = 0; c < nch; c += 2) {
+                step(c, w0, v0, w1, v1);
+                if (c + 1 >= nch) break;
+                step(c + 1, w1, v1, w0, v0);
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            if (j < nt) {
+                const float v = moe::sum8_lanes(acc[j]) * s2;
+                if (sub == 0) a.y[(size_t)(p0 + s0 + j) * H + row] = v;
+            }
+        }
+        moe::lds_barrier();                           // h is reused by the next pass
     }
-}
-
-__global__ __launch_bounds__(256) void sum_slices_kernel(const float *__restrict__ part, int32_t nks,
-                                                         int32_t S, int32_t H,
-                                                         const int32_t *__restrict__ offsets,
-                                                         int32_t E, float *__restrict__ y)
-{
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t n4 = (size_t)offsets[E] * H / 4;
-    if (i >= n4) return;
-    float4 acc = reinterpret_cast<const float4 *>(part)[i];
-    for (int ks = 1; ks < nks; ++ks) {
-        const float4 v = reinterpret_cast<const float4 *>(part + (size_t)ks * S * H)[i];
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    reinterpret_cast<float4 *>(y)[i] = acc;
 }
 
 }  // namespace
 
 namespace {
 
-constexpr int kGUST = 8, kDNST = 4;
+constexpr int kGUST = 8, kDNST = 8;
 
-template <int SEGS>
+template <int CH, int NCH, int ST>
 void gateup_launch(const GateUpArgs &a, int grid, hipStream_t st)
 {
-    const size_t lds = (size_t)a.st * SEGS * 32 * sizeof(uint4);
-    hipLaunchKernelGGL((gemv_gateup_nvfp4_kernel<SEGS, 1, kGUST>), dim3(grid), dim3(kThreads), lds,
-                       st, a);
+    hipLaunchKernelGGL((gemv_gateup_nvfp4_kernel<CH, NCH, ST>), dim3(grid), dim3(kThreads),
+                       (size_t)a.st * a.H * 2, st, a);
 }
 
-template <int SEGS>
+// Unrolled kernels for 4-segment chunks (hidden a multiple of 1024 up to
+// 8192) per pass size; every other shape runs the looped kernel.
+template <int ST>
+bool gateup_launch_unrolled(const GateUpArgs &a, int nch, int grid, hipStream_t st)
+{
+    switch (nch) {
+    case 1: gateup_launch<4, 1, ST>(a, grid, st); return true;
+    case 2: gateup_launch<4, 2, ST>(a, grid, st); return true;
+    case 3: gateup_launch<4, 3, ST>(a, grid, st); return true;
+    case 4: gateup_launch<4, 4, ST>(a, grid, st); return true;
+    case 5: gateup_launch<4, 5, ST>(a, grid, st); return true;
+    case 6: gateup_launch<4, 6, ST>(a, grid, st); return true;
+    case 7: gateup_launch<4, 7, ST>(a, grid, st); return true;
+    case 8: gateup_launch<4, 8, ST>(a, grid, st); return true;
+    default: return false;
+    }
+}
+
+template <int CH, int NCH, int ST>
 void down_launch(const DownArgs &a, int grid, hipStream_t st)
 {
-    const size_t lds = (size_t)a.st * SEGS * 64 * sizeof(float4);
-    hipLaunchKernelGGL((gemv_down_nvfp4_kernel<SEGS, 1, kDNST>), dim3(grid), dim3(kThreads), lds,
-                       st, a);
+    hipLaunchKernelGGL((gemv_down_nvfp4_kernel<CH, NCH, ST>), dim3(grid), dim3(kThreads),
+                       (size_t)a.st * a.I * 4, st, a);
 }
 
-#define MOE_SEGS_SWITCH(segs, fn, ...)        \
-    switch (segs) {                           \
-    case 8: fn<8>(__VA_ARGS__); break;        \
-    case 7: fn<7>(__VA_ARGS__); break;        \
-    case 6: fn<6>(__VA_ARGS__); break;        \
-    case 5: fn<5>(__VA_ARGS__); break;        \
-    case 4: fn<4>(__VA_ARGS__); break;        \
-    case 3: fn<3>(__VA_ARGS__); break;        \
-    case 2: fn<2>(__VA_ARGS__); break;        \
-    default: fn<1>(__VA_ARGS__); break;       \
+// Unrolled kernels for 2-segment chunks (inter a multiple of 512 up to 4096)
+// per pass size; every other shape runs the looped kernel.
+template <int ST>
+bool down_launch_unrolled(const DownArgs &a, int nch, int grid, hipStream_t st)
+{
+    switch (nch) {
+    case 1: down_launch<2, 1, ST>(a, grid, st); return true;
+    case 2: down_launch<2, 2, ST>(a, grid, st); return true;
+    case 3: down_launch<2, 3, ST>(a, grid, st); return true;
+    case 4: down_launch<2, 4, ST>(a, grid, st); return true;
+    case 5: down_launch<2, 5, ST>(a, grid, st); return true;
+    case 6: down_launch<2, 6, ST>(a, grid, st); return true;
+    case 7: down_launch<2, 7, ST>(a, grid, st); return true;
+    case 8: down_launch<2, 8, ST>(a, grid, st); return true;
+    default: return false;
     }
+}
 
 }  // namespace
 
 hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
                                     const uint16_t *x, const MoeRouteDev &r, int32_t M, int32_t S,
-                                    int32_t E, int32_t hidden, int32_t inter, float *partials,
-                                    int32_t nks, hipStream_t st)
+                                    int32_t E, int32_t hidden, int32_t inter, float limit, float *h,
+                                    hipStream_t st)
 {
     GateUpArgs a;
-    a.st = M < kGUST ? M : kGUST;
+    a.st = gemv_gateup_pass_slots(M, hidden, kGUST);
     a.gcodes = gate.codes; a.ucodes = up.codes;
     a.gscales = (const uint8_t *)gate.scales; a.uscales = (const uint8_t *)up.scales;
     a.gscale2 = gate.scale2; a.uscale2 = up.scale2;
     a.x = x; a.offsets = r.offsets; a.sorted_token = r.sorted_token; a.active = r.active;
-    a.num_active = r.num_active; a.partials = partials;
-    a.S = S; a.H = hidden; a.I = inter;
-    const int segs = gemv_segs_gateup(kFmtNVFP4, hidden);
-    a.nks = gemv_gateup_slices(kFmtNVFP4, hidden);
-    if (a.nks != nks) return hipErrorInvalidValue;
-    a.ntiles = 2 * (inter / 32);
-    const int grid = (S < E ? S : E) * a.ntiles * a.nks;
-    MOE_SEGS_SWITCH(segs, gateup_launch, a, grid, st)
+    a.h = h; a.H = hidden; a.I = inter; a.limit = limit;
+    a.ntiles = inter / 16;
+    const int grid = (S < E ? S : E) * a.ntiles;
+    const int ch = gemv_chunk_segs(kFmtNVFP4, hidden), nch = hidden / kSegK / ch;
+    bool done = false;
+    if (ch == 4) {
+        if (a.st <= 1) done = gateup_launch_unrolled<1>(a, nch, grid, st);
+        else if (a.st <= 2) done = gateup_launch_unrolled<2>(a, nch, grid, st);
+        else done = gateup_launch_unrolled<8>(a, nch, grid, st);
+    }
+    if (!done) {
+        switch (ch) {
+        case 4: gateup_launch<4, 0, kGUST>(a, grid, st); break;
+        case 3: gateup_launch<3, 0, kGUST>(a, grid, st); break;
+        case 2: gateup_launch<2, 0, kGUST>(a, grid, st); break;
+        default: gateup_launch<1, 0, kGUST>(a, grid, st); break;
+        }
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_down_nvfp4(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
                                   int32_t M, int32_t S, int32_t E, int32_t hidden, int32_t inter,
-                                  float *y, float *slice_scratch, hipStream_t st)
+                                  float *y, hipStream_t st)
 {
     DownArgs a;
-    a.st = M < kDNST ? M : kDNST;
+    a.st = gemv_down_pass_slots(M, inter, kDNST);
     a.codes = down.codes; a.scales = (const uint8_t *)down.scales; a.scale2 = down.scale2;
-    a.h = h; a.offsets = r.offsets; a.active = r.active; a.num_active = r.num_active;
-    a.S = S; a.H = hidden; a.I = inter;
-    const int segs = gemv_segs_down(kFmtNVFP4, inter);
-    a.nks = gemv_down_slices(kFmtNVFP4, inter);
-    a.out = a.nks == 1 ? y : slice_scratch;
+    a.h = h; a.offsets = r.offsets; a.active = r.active; a.y = y;
+    a.H = hidden; a.I = inter;
     a.ntiles = hidden / 32;
-    const int grid = (S < E ? S : E) * a.ntiles * a.nks;
-    MOE_SEGS_SWITCH(segs, down_launch, a, grid, st)
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.nks == 1) return err;
-    const size_t n4 = (size_t)S * hidden / 4;
-    hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
-                       slice_scratch, a.nks, S, hidden, r.offsets, E, y);
+    const int grid = (S < E ? S : E) * a.ntiles;
+    const int ch = gemv_down_chunk_segs(kFmtNVFP4, inter), nch = inter / kSegK / ch;
+    bool done = false;
+    if (ch == 2) {
+        if (a.st <= 1) done = down_launch_unrolled<1>(a, nch, grid, st);
+        else if (a.st <= 2) done = down_launch_unrolled<2>(a, nch, grid, st);
+        else done = down_launch_unrolled<kDNST>(a, nch, grid, st);
+    }
+    if (!done) {
+        if (ch == 2) down_launch<2, 0, kDNST>(a, grid, st);
+        else down_launch<1, 0, kDNST>(a, grid, st);
+    }
     return hipGetLastError();
 }

@@ -44,30 +44,10 @@ moe_status_t hip_fail(hipError_t e, const char *what)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 // FFN scratch of the GEMV tier for S slots.
-size_t gemv_scratch_bytes(int64_t S, int32_t hidden, int32_t inter, int32_t fmt)
+// FFN scratch of the GEMV tier: h, the SwiGLU output [S][inter].
+size_t gemv_scratch_bytes(int64_t S, int32_t inter)
 {
-    const int64_t nks = gemv_gateup_slices(fmt, hidden);
-    const int64_t nkd = gemv_down_slices(fmt, inter);
-    size_t b = moe::align256(sizeof(float) * (size_t)(nks * S * 2 * inter));   // gate/up partials
-    b += moe::align256(sizeof(float) * (size_t)(S * inter));                   // h
-    if (nkd > 1) b += moe::align256(sizeof(float) * (size_t)(nkd * S * hidden)); // down slices
-    return b;
-}
-
-struct GemvScratch {
-    float *partials, *h, *down_slices;
-};
-
-GemvScratch carve_gemv(char *base, int64_t S, int32_t hidden, int32_t inter, int32_t fmt)
-{
-    GemvScratch s;
-    const int64_t nks = gemv_gateup_slices(fmt, hidden);
-    s.partials = (float *)base;
-    base += moe::align256(sizeof(float) * (size_t)(nks * S * 2 * inter));
-    s.h = (float *)base;
-    base += moe::align256(sizeof(float) * (size_t)(S * inter));
-    s.down_slices = gemv_down_slices(fmt, inter) > 1 ? (float *)base : nullptr;
-    return s;
+    return moe::align256(sizeof(float) * (size_t)(S * inter));
 }
 
 bool sizes_ok(int32_t M, int32_t top_k, int32_t E)
@@ -86,6 +66,7 @@ int32_t resolve(int32_t M, int32_t fmt, int32_t requested)
 bool ffn_dims_ok(int32_t fmt, int32_t hidden, int32_t inter)
 {
     if (hidden <= 0 || inter <= 0 || hidden % 128 || inter % 128) return false;
+    if (hidden > MOE_MAX_DIM || inter > MOE_MAX_DIM) return false;
     if (fmt == MOE_W_NVFP4_B16 && (hidden % 256 || inter % 256)) return false;
     return true;
 }
@@ -121,19 +102,16 @@ GemmScratch carve_gemm(char *p, int64_t M, int64_t S, int32_t E, int32_t hidden,
     return g;
 }
 
-// The GEMM tier keeps the K-block weight scales of a column block in two
-// registers per lane (K <= 128 blocks of 128) and addresses activation rows
-// with 32-bit byte offsets (M * hidden and S * inter below 2^31).
+// The GEMM tier addresses activation rows with 32-bit byte offsets.
 bool gemm_dims_ok(int64_t M, int64_t S, int32_t hidden, int32_t inter)
 {
-    return hidden <= MOE_GEMM_MAX_K && inter <= MOE_GEMM_MAX_K && M * hidden < (int64_t(1) << 31) &&
-           S * inter < (int64_t(1) << 31);
+    return M * hidden < (int64_t(1) << 31) && S * inter < (int64_t(1) << 31);
 }
 
 size_t ffn_bytes(int64_t M, int64_t S, int32_t E, int32_t hidden, int32_t inter, int32_t fmt,
                  int32_t mode)
 {
-    if (mode == MOE_MODE_GEMV_A16) return gemv_scratch_bytes(S, hidden, inter, fmt);
+    if (mode == MOE_MODE_GEMV_A16) return gemv_scratch_bytes(S, inter);
     if (fmt != MOE_W_E4M3_B128 || !gemm_dims_ok(M, S, hidden, inter)) return 0;
     return gemm_scratch_bytes(M, S, E, hidden, inter);
 }
@@ -149,10 +127,10 @@ int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt,
 {
     g_stage_events = events;
     g_stage_n = events ? n_events : 0;
-    (void)fmt; (void)hidden; (void)inter; (void)mode;
-    // GEMV tier: gate/up GEMV, SwiGLU, down GEMV (with its slice sum, if any)
+    (void)fmt; (void)hidden; (void)inter;
+    // GEMV tier: gate/up GEMV with SwiGLU, down GEMV
     // GEMM tier: activation quantization + tile schedule, gate/up GEMM, down GEMM
-    return 3;
+    return mode == MOE_MODE_GEMV_A16 ? 2 : 3;
 }
 
 int32_t moe_resolve_mode(int32_t M, int32_t fmt, int32_t requested)
@@ -257,8 +235,8 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
         return fail(MOE_ERR_ARG, "moe_expert_ffn: unknown mode %d", mode);
     if (!ffn_dims_ok(fmt, hidden, inter))
         return fail(MOE_ERR_SHAPE,
-                    "moe_expert_ffn: hidden %d and inter %d must be positive multiples of %d",
-                    hidden, inter, fmt == MOE_W_NVFP4_B16 ? 256 : 128);
+                    "moe_expert_ffn: hidden %d and inter %d must be positive multiples of %d, "
+                    "at most %d", hidden, inter, fmt == MOE_W_NVFP4_B16 ? 256 : 128, MOE_MAX_DIM);
     if (route->expert_offsets != (int32_t *)ws || !sizes_ok(route->M, route->top_k, route->num_experts) ||
         route->num_slots != route->M * route->top_k)
         return fail(MOE_ERR_ARG, "moe_expert_ffn: route does not come from moe_route_pack on this ws");
@@ -276,9 +254,8 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
         return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: the FP8 GEMM tier serves E4M3 banks only");
     if (tier == MOE_MODE_GEMM_A8 && !gemm_dims_ok(M, (int64_t)M * k, hidden, inter))
         return fail(MOE_ERR_SHAPE,
-                    "moe_expert_ffn: GEMM tier needs hidden, inter <= %d and M*hidden, "
-                    "M*top_k*inter < 2^31 (M=%d top_k=%d hidden=%d inter=%d)",
-                    MOE_GEMM_MAX_K, M, k, hidden, inter);
+                    "moe_expert_ffn: GEMM tier needs M*hidden and M*top_k*inter < 2^31 "
+                    "(M=%d top_k=%d hidden=%d inter=%d)", M, k, hidden, inter);
     const size_t need = moe_workspace_bytes(M, k, E, hidden, inter, fmt, tier);
     if (ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu bytes < %zu", ws_bytes, need);
@@ -309,32 +286,24 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
         stage_mark(3, s);
         return MOE_OK;
     }
-    GemvScratch g = carve_gemv(scratch, S, hidden, inter, fmt);
+    float *h = (float *)scratch;
     GemvBankDev bg{gate->codes, gate->scales, gate->scale2};
     GemvBankDev bu{up->codes, up->scales, up->scale2};
     GemvBankDev bd{down->codes, down->scales, down->scale2};
-    const int32_t nks = gemv_gateup_slices(fmt, hidden);
     hipError_t e;
     stage_mark(0, s);
     if (fmt == MOE_W_E4M3_B128)
-        e = launch_gemv_gateup_e4m3(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, g.partials,
-                                    nks, s);
+        e = launch_gemv_gateup_e4m3(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, limit, h, s);
     else
-        e = launch_gemv_gateup_nvfp4(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, g.partials,
-                                     nks, s);
+        e = launch_gemv_gateup_nvfp4(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, limit, h, s);
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: gate/up GEMV launch");
     stage_mark(1, s);
-    e = launch_swiglu_partials(g.partials, nks, (int32_t)S, inter, r.offsets, E, limit, g.h, s);
-    if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: SwiGLU launch");
-    stage_mark(2, s);
     if (fmt == MOE_W_E4M3_B128)
-        e = launch_gemv_down_e4m3(bd, g.h, r, M, (int32_t)S, E, hidden, inter, y_packed,
-                                  g.down_slices, s);
+        e = launch_gemv_down_e4m3(bd, h, r, M, (int32_t)S, E, hidden, inter, y_packed, s);
     else
-        e = launch_gemv_down_nvfp4(bd, g.h, r, M, (int32_t)S, E, hidden, inter, y_packed,
-                                   g.down_slices, s);
+        e = launch_gemv_down_nvfp4(bd, h, r, M, (int32_t)S, E, hidden, inter, y_packed, s);
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: down GEMV launch");
-    stage_mark(3, s);
+    stage_mark(2, s);
     return MOE_OK;
 }
 

@@ -47,6 +47,24 @@ __device__ __forceinline__ float sum8_lanes(float v)
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Wait until at most N of this wave's vector memory loads are in flight
+// (vmcnt(N); expcnt and lgkmcnt not waited).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vm0() { wait_vm<0>(); }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt 0) but not for its global loads, which __syncthreads would drain.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0); vmcnt and expcnt not waited
+    asm volatile("s_barrier" ::: "memory");
+}
+
 }  // namespace moe
 
 // ---------------------------------------------------------------------------
@@ -67,30 +85,26 @@ struct GemvBankDev {
 };
 
 // M bounds the slots one expert usually holds (one per token); it sizes the
-// LDS slot tile.  Experts holding more slots are swept in several passes.
+// slot tile of a pass.  Experts holding more slots are swept in several
+// passes.  Gate/up covers the whole of K per block and writes h =
+// SwiGLU(gate x, up x) ([S][inter] floats) directly.
 hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
                                    const uint16_t *x, const MoeRouteDev &r, int32_t M,
                                    int32_t S, int32_t E, int32_t hidden, int32_t inter,
-                                   float *partials, int32_t nks, hipStream_t st);
-// Down projection; with more than one K slice the slices go to slice_scratch
-// ([gemv_down_slices(fmt, inter)][S][hidden] floats) and are summed in order
-// into y.
+                                   float limit, float *h, hipStream_t st);
+// Down projection: a block covers 32 output rows over the whole of K and
+// writes y ([S][hidden] floats) directly.
 hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
                                  int32_t M, int32_t S, int32_t E, int32_t hidden, int32_t inter,
-                                 float *y, float *slice_scratch, hipStream_t st);
+                                 float *y, hipStream_t st);
 
 hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
                                     const uint16_t *x, const MoeRouteDev &r, int32_t M,
                                     int32_t S, int32_t E, int32_t hidden, int32_t inter,
-                                    float *partials, int32_t nks, hipStream_t st);
+                                    float limit, float *h, hipStream_t st);
 hipError_t launch_gemv_down_nvfp4(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
                                   int32_t M, int32_t S, int32_t E, int32_t hidden, int32_t inter,
-                                  float *y, float *slice_scratch, hipStream_t st);
-
-// h[p][n] = swiglu_clamp(sum_ks P[ks][p][n], sum_ks P[ks][p][I + n]) for p < offsets[E].
-hipError_t launch_swiglu_partials(const float *partials, int32_t nks, int32_t S, int32_t inter,
-                                  const int32_t *offsets, int32_t E, float limit, float *h,
-                                  hipStream_t st);
+                                  float *y, hipStream_t st);
 
 // FP8 GEMM tier (E4M3 banks, wide M).
 int gemm_max_tiles(int32_t S, int32_t E);
@@ -111,11 +125,9 @@ hipError_t launch_gemm_down(const uint8_t *hq, const float *hs, const uint8_t *d
 hipError_t launch_combine(const float *y, const int32_t *token_to_perm, const float *w,
                           int32_t M, int32_t k, int32_t hidden, float *out, hipStream_t st);
 
-// K slicing of the GEMV tier.  A segment is the K span of one 128-byte row
-// chunk (128 values for E4M3, 256 for NVFP4); a slice is SEGS segments with
-// SEGS the largest divisor of the segment count not above the cap (8, or 16
-// for the E4M3 down projection when it divides).  Host sizing and launches
-// both use these.
+// K chunking of the GEMV tier.  A segment is the K span of one 128-byte row
+// chunk (128 values for E4M3, 256 for NVFP4); both projections stream the
+// whole of K per block, in chunks of a few segments.
 constexpr int kFmtE4M3 = 1, kFmtNVFP4 = 2;
 inline int gemv_seg_k(int fmt) { return fmt == kFmtNVFP4 ? 256 : 128; }
 inline int gemv_pick_segs(int nsegs, int cap)
@@ -124,18 +136,36 @@ inline int gemv_pick_segs(int nsegs, int cap)
         if (nsegs % d == 0) return d;
     return 1;
 }
-inline int gemv_segs_gateup(int fmt, int hidden) { return gemv_pick_segs(hidden / gemv_seg_k(fmt), 8); }
-inline int gemv_segs_down(int fmt, int inter)
+
+// Slots per weight pass of the gate/up GEMV: their bf16 x rows sit in LDS
+// for the whole of K, so the pass holds as many as fit in 32 KB (at least
+// one), at most cap and at most M.
+inline int gemv_gateup_pass_slots(int M, int hidden, int cap)
 {
-    const int n = inter / gemv_seg_k(fmt);
-    if (fmt == kFmtE4M3 && n % 16 == 0) return 16;
-    return gemv_pick_segs(n, 8);
+    int n = 32768 / (2 * hidden);
+    if (n < 1) n = 1;
+    if (n > cap) n = cap;
+    return n < M ? n : M;
 }
-inline int gemv_gateup_slices(int fmt, int hidden)
+
+// Same for the down GEMV, whose FP32 h rows sit in LDS: as many as fit in
+// 16 KB (at least one), at most cap and at most M.
+inline int gemv_down_pass_slots(int M, int inter, int cap)
 {
-    return hidden / gemv_seg_k(fmt) / gemv_segs_gateup(fmt, hidden);
+    int n = 16384 / (4 * inter);
+    if (n < 1) n = 1;
+    if (n > cap) n = cap;
+    return n < M ? n : M;
 }
-inline int gemv_down_slices(int fmt, int inter)
+
+// Segments per K chunk: the largest divisor of the segment count up to 8
+// (E4M3 gate/up), 4 (NVFP4 gate/up, E4M3 down) or 2 (NVFP4 down), so a chunk
+// spans at most 1024 K values for gate/up and 512 for down.
+inline int gemv_chunk_segs(int fmt, int hidden)
 {
-    return inter / gemv_seg_k(fmt) / gemv_segs_down(fmt, inter);
+    return gemv_pick_segs(hidden / gemv_seg_k(fmt), fmt == kFmtNVFP4 ? 4 : 8);
+}
+inline int gemv_down_chunk_segs(int fmt, int inter)
+{
+    return gemv_pick_segs(inter / gemv_seg_k(fmt), fmt == kFmtNVFP4 ? 2 : 4);
 }

@@ -80,8 +80,9 @@ enum {
 
 #define MOE_GEMV_MAX_M 16
 #define MOE_MAX_EXPERTS 512
-/* Largest hidden and inter the GEMM tier takes (128 K blocks of 128). */
-#define MOE_GEMM_MAX_K 16384
+/* Largest hidden and inter (128 blocks of 128 along K, and the bf16 x rows
+ * of a GEMV pass held in LDS). */
+#define MOE_MAX_DIM 16384
 
 /* One projection bank holding every expert, expert-major (host struct of
  * device pointers).  n_out x k_in is the matrix shape per expert:
@@ -158,10 +159,11 @@ moe_status_t moe_route_pack(const int32_t *topk_ids, int32_t M, int32_t top_k,
  * x_bf16: bf16 [M][hidden]; y_packed: float [M*top_k][hidden], rows past
  * expert_offsets[E] are left untouched.  `route` (host) must come from
  * moe_route_pack on this same `ws`.
- * Rules: hidden % 128 == 0, inter % 128 == 0; gate/up are inter x hidden,
+ * Rules: hidden % 128 == 0, inter % 128 == 0 (% 256 for NVFP4), both
+ * <= MOE_MAX_DIM; gate/up are inter x hidden,
  * down is hidden x inter; all banks share one format and num_experts;
- * GEMM_A8 needs E4M3 banks, hidden and inter <= MOE_GEMM_MAX_K, and
- * M*hidden and M*top_k*inter < 2^31 (MOE_ERR_SHAPE otherwise);
+ * hidden, inter <= MOE_MAX_DIM; GEMM_A8 needs E4M3 banks, and M*hidden
+ * and M*top_k*inter < 2^31 (MOE_ERR_SHAPE otherwise);
  * ws_bytes >= moe_workspace_bytes(route->M, ..., mode). */
 moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up,
                             const moe_bank_t *down, const uint16_t *x_bf16,
@@ -183,9 +185,10 @@ moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
  * moe_expert_ffn calls on this thread record events[0] on their stream before
  * the first kernel and events[i] after the i-th kernel, for at most
  * n_events events; NULL turns it off.  The handles are the caller's
- * hipEvent_t.  Returns the number of stages a tier records (3: GEMV tier
- * gate/up, SwiGLU, down; GEMM tier activation quantization + tile
- * schedule, gate/up with SwiGLU, down), so n_events = 4 covers them all.  Mirrors the
+ * hipEvent_t.  Returns the number of stages the tier `mode` records (2 for
+ * MOE_MODE_GEMV_A16: gate/up with SwiGLU, down; 3 otherwise, the GEMM tier's
+ * activation quantization + tile schedule, gate/up with SwiGLU, down), so
+ * n_events = 4 covers every tier.  Mirrors the
  * per-stage timers of "spark_model glm5next_mlp/forward.rs" (profile::start /
  * profile::end around the MoE stages). */
 int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt,

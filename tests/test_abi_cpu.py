@@ -34,20 +34,18 @@ def test_workspace_bytes_hand_computed():
     # decode: H7168 I2048 E256 k8 M=1, E4M3, GEMV tier
     S, E, H, I = 8, 256, 7168, 2048
     route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
-    nks = 7  # 1024-wide K slices of H
-    gemv = a256(4 * nks * S * 2 * I) + a256(4 * S * I)
+    # h only: both GEMVs cover the whole of K per block
+    gemv = a256(4 * S * I)
     assert B.moe_workspace_bytes(1, 8, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16) == route + gemv
-    # NVFP4 M=16: H6144 I1536 E160; 2048-wide K slices of H -> 3
+    # NVFP4 M=16: H6144 I1536 E160
     S, E, H, I = 128, 160, 6144, 1536
     route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
-    gemv = a256(4 * 3 * S * 2 * I) + a256(4 * S * I)
+    gemv = a256(4 * S * I)
     assert B.moe_workspace_bytes(16, 8, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_AUTO) == route + gemv
-    # inter = 2304 = 18 segments of 128: the down slice is 6 segments (the
-    # largest divisor <= 8, since 16 does not divide 18), so 3 slices and a
-    # slice buffer; hidden 256 = 2 segments -> one gate/up slice
+    # odd shapes need no extra scratch: both GEMVs cover the whole of K
     S, E, H, I = 2, 4, 256, 2304
     route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
-    gemv = a256(4 * 1 * S * 2 * I) + a256(4 * S * I) + a256(4 * 3 * S * H)
+    gemv = a256(4 * S * I)
     assert B.moe_workspace_bytes(1, 2, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16) == route + gemv
     # prefill, GEMM tier: H7168 I2048 E256 k8 M=4096 -> S=32768 slots; x codes
     # + scales, h codes + scales, at most min(S,E) + S/128 tiles of 16 bytes,
@@ -74,7 +72,8 @@ def test_workspace_bytes_hand_computed():
     (1, 8, 256, 6144, 1664, 2, 0),      # NVFP4 needs % 256
     (1, 8, 256, 7168, 2048, 3, 0),      # unknown format
     (1, 8, 256, 7168, 2048, 1, 7),      # unknown mode
-    (64, 8, 256, 16512, 2048, 1, 2),    # GEMM tier: hidden > MOE_GEMM_MAX_K
+    (64, 8, 256, 16512, 2048, 1, 2),    # hidden > MOE_MAX_DIM
+    (1, 8, 256, 7168, 16512, 1, 1),     # inter > MOE_MAX_DIM
     (131072, 8, 256, 16384, 2048, 1, 2),  # GEMM tier: M * hidden = 2^31
     (32768, 8, 256, 7168, 8192, 1, 2),  # GEMM tier: M * top_k * inter = 2^31
 ])
@@ -91,9 +90,9 @@ def test_auto_workspace_skips_a_gemm_tier_that_cannot_run():
     auto = L.moe_workspace_bytes(20, 8, 20, 1024, 512, B.MOE_W_NVFP4_B16, B.MOE_MODE_AUTO)
     gemv = L.moe_workspace_bytes(16, 8, 20, 1024, 512, B.MOE_W_NVFP4_B16, B.MOE_MODE_GEMV_A16)
     assert auto > 0 and auto >= gemv
-    # same for E4M3 beyond the GEMM tier's K limit
-    assert L.moe_workspace_bytes(64, 8, 256, 7168, 16512, B.MOE_W_E4M3_B128, B.MOE_MODE_AUTO) > 0
-    assert L.moe_workspace_bytes(64, 8, 256, 7168, 16512, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMM_A8) == 0
+    # same for E4M3 past the GEMM tier's 32-bit row offsets (M * hidden = 2^31)
+    assert L.moe_workspace_bytes(131072, 1, 256, 16384, 128, B.MOE_W_E4M3_B128, B.MOE_MODE_AUTO) > 0
+    assert L.moe_workspace_bytes(131072, 1, 256, 16384, 128, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMM_A8) == 0
 
 
 def test_resolve_mode():
@@ -148,7 +147,7 @@ def test_ffn_error_contract_on_host():
     assert _ffn(B, _bank(B, fmt=2, k=256, n=256), _bank(B, fmt=2, k=256, n=256),
                 _bank(B, fmt=2, n=256, k=256), r, ws, hidden=256, inter=256) == B.MOE_ERR_FORMAT
     # workspace too small
-    assert _ffn(B, g, u, d, r, ws, ws_bytes=4096) == B.MOE_ERR_WORKSPACE
+    assert _ffn(B, g, u, d, r, ws, ws_bytes=512) == B.MOE_ERR_WORKSPACE
     # route not from this workspace
     assert _ffn(B, g, u, d, _route(B, ws + 256), ws) == B.MOE_ERR_ARG
     # misaligned codes
@@ -156,12 +155,12 @@ def test_ffn_error_contract_on_host():
     # bad limit, unknown mode
     assert _ffn(B, g, u, d, r, ws, limit=0.0) == B.MOE_ERR_ARG
     assert _ffn(B, g, u, d, r, ws, mode=5) == B.MOE_ERR_ARG
-    # beyond the GEMM tier's limits (it takes K <= MOE_GEMM_MAX_K)
+    # hidden beyond MOE_MAX_DIM, any tier
     big = 16512
     rg = _route(B, ws, M=32)
     assert _ffn(B, _bank(B, n=128, k=big), _bank(B, n=128, k=big), _bank(B, n=big, k=128), rg, ws,
                 hidden=big, inter=128, mode=2) == B.MOE_ERR_SHAPE
-    assert "GEMM tier" in B.moe_last_error()
+    assert "at most 16384" in B.moe_last_error()
 
 
 def test_route_pack_and_combine_error_contract_on_host():
