@@ -38,6 +38,9 @@ def parse():
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="first run 3 device copies of this many MB (a plain copy kernel of known "
+                         "size, to scale HBM byte counters)")
     return ap.parse_args()
 
 
@@ -157,7 +160,7 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True):
     # dense-equivalent FLOPs of the valid slots: 2 (gate, up) + 1 (down) products of I*H
     flops = float(np.mean([6.0 * int(((s[0] >= 0) & (s[0] < wl.experts)).sum()) * wl.hidden * wl.inter
                            for s in sets]))
-    return dict(us_layer=us_layer, ms_total=total_ms, stable=stable, stages=stages,
+    return dict(name=wl.name, us_layer=us_layer, ms_total=total_ms, stable=stable, stages=stages,
                 alg_layer_bytes=alg_layer, alg_gateup_bytes=alg_gateup, unique_experts=uniq,
                 flops=flops, mode=mode, layer=layer, x=x, sets=sets)
 
@@ -192,6 +195,38 @@ def cpu_baseline(wl, banks, x, sets, budget_s):
                        f"selected experts copied to host before timing")
 
 
+# HBM bytes per launch of the roofline kernel, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+# counter reads for a plain 256 MB device copy in the same run: FETCH_SIZE
+# reads 131,088 KiB for it (x 2.0), WRITE_SIZE 262,144 KiB (x 1.0).  The
+# entry holds only while the kernel sources hash to `src` (first 16 hex
+# digits of the sha256 of the listed files, concatenated); otherwise the
+# traffic is reported as null.
+COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+TRAFFIC = {
+    "decode_e4m3_m1": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "moe_internal.h"],
+                       "src": "225a5797bf060326179d4e9e8c083606",
+                       "fetch_kib": 115065, "write_kib": 64},
+    "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "moe_internal.h"],
+                           "src": "3a2c3c224a614bf9179d4e9e8c083606",
+                           "fetch_kib": 4271567, "write_kib": 121954},
+}
+
+
+def measured_traffic(name):
+    import hashlib
+    t = TRAFFIC.get(name)
+    if t is None:
+        return None
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "fp4_block_scaled_amd", "csrc")
+    src = "".join(hashlib.sha256(open(os.path.join(d, f), "rb").read()).hexdigest()[:16]
+                  for f in t["files"])
+    if src != t["src"]:
+        return None
+    return round((t["fetch_kib"] * COUNTER_SCALE["FETCH_SIZE"] +
+                  t["write_kib"] * COUNTER_SCALE["WRITE_SIZE"]) * 1024)
+
+
 def roofline(r):
     """Roofline of the dominant kernel of the tier that ran: the gate/up GEMV
     against HBM bandwidth, or the gate/up FP8 GEMM against the FP8 MFMA peak."""
@@ -201,13 +236,14 @@ def roofline(r):
         tf = flop / (us * 1e-6) / 1e12
         return {"kernel": "gemm_gateup", "bound": "mfma", "achieved": round(tf, 1),
                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
-                "traffic": None, "alg_flop_per_launch": round(flop), "avg_launch_us": round(us, 3)}
+                "traffic": measured_traffic(r["name"]), "alg_flop_per_launch": round(flop),
+                "avg_launch_us": round(us, 3)}
     us = r["stages"]["gateup_gemv"]
     gbps = r["alg_gateup_bytes"] / (us * 1e-6) / 1e9
     return {"kernel": "gemv_gateup", "bound": "hbm", "achieved": round(gbps, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None, "alg_bytes_per_launch": round(r["alg_gateup_bytes"]),
-            "avg_launch_us": round(us, 3)}
+            "traffic": measured_traffic(r["name"]),
+            "alg_bytes_per_launch": round(r["alg_gateup_bytes"]), "avg_launch_us": round(us, 3)}
 
 
 def main():
@@ -223,6 +259,17 @@ def main():
     import workloads
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hip = Hip()
+
+    if args.copy_calib_mb > 0:
+        src = torch.empty(args.copy_calib_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"# copy calibration: 3 copies of {args.copy_calib_mb} MB", file=sys.stderr, flush=True)
 
     wl = workloads.WORKLOADS[args.workload]
     t0 = time.time()
