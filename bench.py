@@ -38,6 +38,8 @@ def parse():
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the one-launch fused layer rows")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="first run 3 device copies of this many MB (a plain copy kernel of known "
                          "size, to scale HBM byte counters)")
@@ -87,7 +89,7 @@ def algorithmic_bytes(wl, banks, ids):
     return len(used) * per_expert + io, len(used) * gu_per_expert + M * wl.hidden * 2, len(used)
 
 
-def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True):
+def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=False):
     import numpy as np
     import torch
 
@@ -100,8 +102,9 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True):
     ids_d = [torch.from_numpy(s[0]).cuda() for s in sets]
     w_d = [torch.from_numpy(s[1]).cuda() for s in sets]
     cb = [B.Bank.from_device_bank(b) for b in banks]
-    layer = MoeLayer(*cb, wl.hidden, wl.inter, wl.top_k, wl.M, wl.limit)
-    mode = B.moe_resolve_mode(wl.M, wl.fmt)
+    mode = B.MOE_MODE_FUSED if fused else B.moe_resolve_mode(wl.M, wl.fmt)
+    layer = MoeLayer(*cb, wl.hidden, wl.inter, wl.top_k, wl.M, wl.limit,
+                     mode=B.MOE_MODE_FUSED if fused else B.MOE_MODE_AUTO)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
@@ -145,6 +148,8 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True):
         torch.cuda.synchronize()
         if mode == B.MOE_MODE_GEMM_A8:
             names = ["route_pack", "act_quant_tiles", "gateup_gemm", "down_gemm", "combine"]
+        elif mode == B.MOE_MODE_FUSED:
+            names = ["host", "fused_layer", "tail"]
         else:
             names = ["route_pack", "gateup_gemv", "down_gemv", "combine"]
         acc = np.zeros(per - 1)
@@ -229,7 +234,15 @@ def measured_traffic(name):
 
 def roofline(r):
     """Roofline of the dominant kernel of the tier that ran: the gate/up GEMV
-    against HBM bandwidth, or the gate/up FP8 GEMM against the FP8 MFMA peak."""
+    against HBM bandwidth, the gate/up FP8 GEMM against the FP8 MFMA peak, or
+    the one-launch fused layer (all of the layer's bytes) against HBM."""
+    if r["mode"] == 3:
+        us = r["stages"]["fused_layer"]
+        gbps = r["alg_layer_bytes"] / (us * 1e-6) / 1e9
+        return {"kernel": "moe_fused_decode", "bound": "hbm", "achieved": round(gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(r["name"] + "/fused"),
+                "alg_bytes_per_launch": round(r["alg_layer_bytes"]), "avg_launch_us": round(us, 3)}
     if r["mode"] == 2:
         us = r["stages"]["gateup_gemm"]
         flop = r["flops"] * 2.0 / 3.0
@@ -306,6 +319,22 @@ def main():
     }
     if r["mode"] == 2:
         line["alg_TFLOPs"] = round(r["flops"] / (r["us_layer"] * 1e-6) / 1e12, 1)
+
+    def fused_row(w2, b2):
+        rf = measure(w2, b2, args.steps, args.warmup, args.route_sets, hip, fused=True)
+        gf = rf["alg_layer_bytes"] / (rf["us_layer"] * 1e-6) / 1e9
+        print(f"# {w2.name} fused: {rf['us_layer']:.2f} us/layer", file=sys.stderr, flush=True)
+        return {"us_layer": round(rf["us_layer"], 3), "weight_read_GBps": round(gf, 1),
+                "hbm_frac": round(gf / HBM_PEAK_GBPS, 4),
+                "tokens_per_s": round(w2.M / (rf["us_layer"] * 1e-6), 1),
+                "stages_us": {k: round(v, 3) for k, v in rf["stages"].items()},
+                "output_stable": rf["stable"], "roofline": roofline(rf)}
+
+    def fused_ok(w2):
+        return not args.no_fused and w2.fmt == 1 and w2.M * w2.top_k <= 256
+
+    if fused_ok(wl):
+        line["fused"] = fused_row(wl, banks)
     also = {}
     for name in [a for a in args.also.split(",") if a]:
         w2 = workloads.WORKLOADS[name]
@@ -321,6 +350,8 @@ def main():
                       "stages_us": {k: round(v, 3) for k, v in r2["stages"].items()},
                       "output_stable": r2["stable"]}
         also[name]["roofline"] = roofline(r2)
+        if fused_ok(w2):
+            also[name]["fused"] = fused_row(w2, b2)
         if r2["mode"] == 2:
             also[name].update({"tier": "fp8_mfma_grouped_gemm", "alg_TFLOPs": round(tf, 1),
                                "mfma_frac_fp8": round(tf / FP8_PEAK_TFLOPS, 4)})

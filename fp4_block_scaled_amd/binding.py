@@ -28,13 +28,16 @@ MOE_W_NVFP4_B16 = 2
 MOE_MODE_AUTO = 0
 MOE_MODE_GEMV_A16 = 1
 MOE_MODE_GEMM_A8 = 2
+MOE_MODE_FUSED = 3
 
 MOE_GEMV_MAX_M = 16
 MOE_MAX_EXPERTS = 512
 MOE_MAX_DIM = 16384
+MOE_FUSED_MAX_SLOTS = 256
 
 EXPORTS = ("moe_workspace_bytes", "moe_resolve_mode", "moe_route_pack",
-           "moe_expert_ffn", "moe_combine", "moe_set_stage_events", "moe_last_error")
+           "moe_expert_ffn", "moe_layer_fused", "moe_combine", "moe_set_stage_events",
+           "moe_last_error")
 
 
 class moe_bank_t(C.Structure):
@@ -72,6 +75,9 @@ def _load():
     L.moe_expert_ffn.argtypes = [C.POINTER(moe_bank_t)] * 3 + [
         P, C.POINTER(moe_route_t), i32, i32, C.c_float, i32, P, P, sz, P]
     L.moe_expert_ffn.restype = i32
+    L.moe_layer_fused.argtypes = [C.POINTER(moe_bank_t)] * 3 + [
+        P, P, P, i32, i32, i32, i32, C.c_float, P, P, P, sz, C.POINTER(moe_route_t), P]
+    L.moe_layer_fused.restype = i32
     L.moe_combine.argtypes = [P, C.POINTER(moe_route_t), P, i32, P, P]
     L.moe_combine.restype = i32
     L.moe_set_stage_events.argtypes = [P, i32, i32, i32, i32, i32]
@@ -145,6 +151,18 @@ def moe_expert_ffn(gate: Bank, up: Bank, down: Bank, x_bf16, route: moe_route_t,
     _check(lib.moe_expert_ffn(C.byref(gate.c), C.byref(up.c), C.byref(down.c), _ptr(x_bf16),
                               C.byref(route), hidden, inter, float(limit), mode, _ptr(y_packed),
                               _ptr(ws), nbytes, _stream(stream)))
+
+
+def moe_layer_fused(gate: Bank, up: Bank, down: Bank, x_bf16, topk_ids, topk_weights, M, top_k,
+                    hidden, inter, limit, y_packed, out, ws, ws_bytes=None,
+                    stream=None) -> moe_route_t:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    route = moe_route_t()
+    _check(lib.moe_layer_fused(C.byref(gate.c), C.byref(up.c), C.byref(down.c), _ptr(x_bf16),
+                               _ptr(topk_ids), _ptr(topk_weights), M, top_k, hidden, inter,
+                               float(limit), _ptr(y_packed), _ptr(out), _ptr(ws), nbytes,
+                               C.byref(route), _stream(stream)))
+    return route
 
 
 def moe_combine(y_packed, route: moe_route_t, topk_weights, hidden, out, stream=None) -> None:

@@ -106,19 +106,17 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 // leave the block.  The 16 rows lie in one 128-row scale block, so a wave
 // keeps the block scales of all K segments in two registers (lane l:
 // segments l and l + 64).
-template <int CH, int NCH, int ST>
-__global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArgs a)
+//
+// gateup_e4m3_item does one (expert e, 16-row tile) item for the ne slots of
+// e, whose packed rows start at p0 and whose tokens are tok[0..ne); xl is
+// the LDS x tile ([a.st][H / 8] uint4), ush the LDS up-sum exchange.
+template <int CH, int NCH, int ST, bool FUSED = false>
+__device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int tile, int p0, int ne,
+                                                 const int32_t *tok, uint4 *xl, float (*ush)[16])
 {
-    extern __shared__ uint4 xl[];                    // [a.st][H / 8] bf16 x rows, K order
-    __shared__ float ush[ST][16];                    // up sums of the 16 rows per slot
-
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int grp = lane >> 3, sub = lane & 7;
-    const int tile = blockIdx.x % a.ntiles;
-    const int ai = blockIdx.x / a.ntiles;
-    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
-    if (e < 0) return;
     const int H = a.H, I = a.I, H8 = H >> 3;
     const int nseg = H >> 7, nch = NCH > 0 ? NCH : nseg / CH;
     const bool is_up = wave >= 2;
@@ -130,14 +128,12 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
     const float *scb = (is_up ? a.uscales : a.gscales) + ((size_t)e * (I >> 7) + (hrow0 >> 7)) * nseg;
     const float sc_lo = lane < nseg ? scb[lane] : 0.0f;
     const float sc_hi = lane + 64 < nseg ? scb[lane + 64] : 0.0f;
-    const int p0 = moe::uniform(a.offsets[e]);
-    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
 
     for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
         const int nt = min(a.st, ne - s0);
         // opaque copies: the per-chunk address arithmetic stays inside the
         // pass instead of being hoisted out of it into live registers
-        const uint8_t *wbp = wb0;
+        const uint8_t *wbp = moe::uniform_ptr(wb0);
         uint32_t lo = loff;
         asm volatile("" : "+s"(wbp), "+v"(lo));
         auto load_w = [&](uint4 (&wb)[CH], int c) {
@@ -187,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
         // chunks in flight across the barrier
         for (int f = tid; f < nt * H8; f += kThreads) {
             const int j = f / H8, r = f - j * H8;
-            xl[f] = *reinterpret_cast<const uint4 *>(a.x + (size_t)a.sorted_token[p0 + s0 + j] * H + r * 8);
+            xl[f] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
         }
         if constexpr (NCH > 0) {
             uint4 w[3][CH];
@@ -234,12 +230,29 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
         if (!is_up && sub == 0) {
 #pragma unroll
             for (int j = 0; j < ST; ++j)
-                if (j < nt)
-                    a.h[(size_t)(p0 + s0 + j) * I + hrow] =
-                        swiglu_clamp(v[j], ush[j][(wave & 1) * 8 + grp], a.limit);
+                if (j < nt) {
+                    float *hp = a.h + (size_t)(p0 + s0 + j) * I + hrow;
+                    const float hv = swiglu_clamp(v[j], ush[j][(wave & 1) * 8 + grp], a.limit);
+                    if constexpr (FUSED) moe::store_dev(hp, hv);
+                    else *hp = hv;
+                }
         }
         moe::lds_barrier();                           // x and ush are reused by the next pass
     }
+}
+
+template <int CH, int NCH, int ST>
+__global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArgs a)
+{
+    extern __shared__ uint4 xl[];                    // [a.st][H / 8] bf16 x rows, K order
+    __shared__ float ush[ST][16];                    // up sums of the 16 rows per slot
+    const int tile = blockIdx.x % a.ntiles;
+    const int ai = blockIdx.x / a.ntiles;
+    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
+    if (e < 0) return;
+    const int p0 = moe::uniform(a.offsets[e]);
+    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
+    gateup_e4m3_item<CH, NCH, ST>(a, e, tile, p0, ne, a.sorted_token + p0, xl, ush);
 }
 
 // ---------------------------------------------------------------------------
@@ -255,18 +268,25 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
 // a wave keeps the block scales of all K segments in two registers.  With
 // one slot per pass the kernel fits 72 VGPRs (7 waves per SIMD): the decode
 // grid of 8 experts x 224 row tiles is then one round of 7 blocks per CU.
-template <int CH, int NCH, int ST>
-__global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kernel(DownArgs a)
-{
-    extern __shared__ float4 hl[];                   // [a.st][I / 4], permuted per segment
+//
+// down_e4m3_item does one (expert e, 32-row tile) item for the ne slots of e
+// (packed rows p0..p0+ne) with hl the LDS h tile ([a.st][I / 4] float4).
+// wait_h() runs once the first weight chunks are in flight and before h is
+// read (a no-op in the standalone kernel, the wait for the expert's h in the
+// fused one).  FUSED (the fused layer's item): the first chunks go out before
+// the wait and h and y move through device-coherent accesses; otherwise h is
+// staged before the first chunks go out.
+struct NoWait {
+    __device__ void operator()() const {}
+};
 
+template <int CH, int NCH, int ST, bool FUSED, class WaitH>
+__device__ __forceinline__ void down_e4m3_item(const DownArgs &a, int e, int tile, int p0, int ne,
+                                               float4 *hl, const WaitH &wait_h)
+{
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int grp = lane >> 3, sub = lane & 7;
-    const int tile = blockIdx.x % a.ntiles;
-    const int ai = blockIdx.x / a.ntiles;
-    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
-    if (e < 0) return;
     const int H = a.H, I = a.I, I4 = I >> 2;
     const int nseg = I >> 7, nch = NCH > 0 ? NCH : nseg / CH;
     const int row0 = tile * 32;
@@ -276,12 +296,10 @@ __global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kern
     const float *scb = a.scales + ((size_t)e * (H >> 7) + (row0 >> 7)) * nseg;
     const float sc_lo = lane < nseg ? scb[lane] : 0.0f;
     const float sc_hi = lane + 64 < nseg ? scb[lane + 64] : 0.0f;
-    const int p0 = moe::uniform(a.offsets[e]);
-    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
 
     for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
         const int nt = min(a.st, ne - s0);
-        const uint8_t *wbp = wb0;
+        const uint8_t *wbp = moe::uniform_ptr(wb0);
         uint32_t lo = loff;
         asm volatile("" : "+s"(wbp), "+v"(lo));      // keep per-chunk addresses inside the pass
         auto load_w = [&](uint4 (&wb)[CH], int c) {
@@ -328,16 +346,30 @@ __global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kern
             }
         };
 
-        for (int f = tid; f < nt * I4; f += kThreads) {
-            const int j = f / I4, r = f - j * I4;     // r: source float4 (4 K values)
-            const int sg = r >> 5, rr = r & 31;
-            hl[j * I4 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] =
-                *reinterpret_cast<const float4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
-        }
+        auto stage_h = [&]() {
+            for (int f = tid; f < nt * I4; f += kThreads) {
+                const int j = f / I4, r = f - j * I4; // r: source float4 (4 K values)
+                const int sg = r >> 5, rr = r & 31;
+                const float *hp = a.h + (size_t)(p0 + s0 + j) * I + r * 4;
+                float4 hv;
+                if constexpr (FUSED) {
+                    hv = make_float4(moe::load_dev(hp), moe::load_dev(hp + 1), moe::load_dev(hp + 2),
+                                     moe::load_dev(hp + 3));
+                } else {
+                    hv = *reinterpret_cast<const float4 *>(hp);
+                }
+                hl[j * I4 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = hv;
+            }
+        };
+        if constexpr (!FUSED) stage_h();
         if constexpr (NCH > 0) {
             uint4 w[3][CH];
             load_w(w[0], 0);
             if (NCH > 1) load_w(w[1], 1);
+            if constexpr (FUSED) {
+                wait_h();
+                stage_h();
+            }
             moe::lds_barrier();
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
@@ -349,6 +381,10 @@ __global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kern
         } else {
             uint4 w0[CH], w1[CH];
             load_w(w0, 0);
+            if constexpr (FUSED) {
+                wait_h();
+                stage_h();
+            }
             moe::lds_barrier();
             auto step = [&](int c, uint4 (&wc)[CH], uint4 (&wn)[CH]) {
                 moe::wait_vm0();
@@ -365,11 +401,231 @@ __global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kern
         for (int j = 0; j < ST; ++j) {
             if (j < nt) {
                 const float v = moe::sum8_lanes(acc[j]);
-                if (sub == 0) a.y[(size_t)(p0 + s0 + j) * H + row] = v;
+                float *yp = a.y + (size_t)(p0 + s0 + j) * H + row;
+                if (sub == 0) {
+                    if constexpr (FUSED) moe::store_dev(yp, v);
+                    else *yp = v;
+                }
             }
         }
         moe::lds_barrier();                           // h is reused by the next pass
     }
+}
+
+template <int CH, int NCH, int ST>
+__global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kernel(DownArgs a)
+{
+    extern __shared__ float4 hl[];                   // [a.st][I / 4], permuted per segment
+    const int tile = blockIdx.x % a.ntiles;
+    const int ai = blockIdx.x / a.ntiles;
+    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
+    if (e < 0) return;
+    const int p0 = moe::uniform(a.offsets[e]);
+    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
+    down_e4m3_item<CH, NCH, ST, false>(a, e, tile, p0, ne, hl, NoWait{});
+}
+
+// ---------------------------------------------------------------------------
+// fused decode layer: route pack, gate/up + SwiGLU, down and combine in one launch
+// ---------------------------------------------------------------------------
+// Every block is resident at once (the grid is sized by the occupancy API).
+// Each block first builds the route of the S <= kFusedMaxSlots slots in LDS
+// (the same stable pack as route_pack_kernel; block 0 also writes the route
+// tables).  Then it runs its share of the gate/up items (active expert x 16 h
+// rows); each finished item stores the call's epoch into its own
+// flag.  Then its share of the down items (32-row tile x active expert,
+// tile-major): the first weight chunks go out, the block waits until all the
+// gate/up flags of the expert hold the epoch, stages h and finishes the item,
+// and stores its own flag.  The down item of the last active expert of a
+// tile waits for the tile's other down flags and applies the top-k weights
+// for every token of that tile, in slot order (multiply, then add).
+//
+// No read-modify-write anywhere: each flag has one writer, and flags hold an
+// epoch no earlier call used, so a workspace needs no clearing and stale
+// contents cannot satisfy a wait.  A block does all its gate/up items before
+// it waits for anything and takes its down items in increasing index; the
+// combining item has the largest index of its tile, so it only waits on items
+// of smaller index.  With every block resident, each wait therefore ends; a
+// wait also gives up after a bounded spin and flags the call in route status.
+constexpr int kFusedMaxSlots = 256;
+constexpr uint32_t kFusedTimeoutFlag = 1u << 30;    // added to route status on a timed-out wait
+
+struct FusedArgs {
+    GateUpArgs gu;                   // offsets/sorted_token/active unused (route built in LDS)
+    DownArgs dn;                     // idem
+    const int32_t *ids;              // [M][k]
+    const float *w;                  // [M][k]
+    int32_t M, k, E, A;              // A = min(M*k, E): active-expert capacity
+    uint32_t epoch;
+    uint32_t *flag_gu;               // [A][inter / 16] per gate/up item
+    uint32_t *flag_dn;               // [hidden / 32][A] per down item
+    float *out;                      // [M][H]
+    MoeRouteDev r;                   // route tables written by block 0
+};
+
+struct FusedRoute {
+    int32_t ids[kFusedMaxSlots];
+    int32_t first[kFusedMaxSlots];   // 1: first slot of its (valid) expert
+    int32_t tok[kFusedMaxSlots];     // packed row -> token
+    int32_t t2p[kFusedMaxSlots];     // slot -> packed row, -1 if invalid
+    int32_t ae[kFusedMaxSlots];      // active experts, ascending
+    int32_t ap0[kFusedMaxSlots];     // their first packed row
+    int32_t acnt[kFusedMaxSlots];    // their slot counts
+    int32_t na, nvalid, ninvalid, flag;
+};
+
+// h and y move between blocks through device-coherent stores and loads
+// (written through to memory, read past the L2 of the reader's XCD); a
+// release or acquire at device scope would instead write back or invalidate
+// a whole L2 per item.  Each wave waits for its stores before the caller's
+// barrier; then one thread publishes the epoch in the item's flag.
+__device__ __forceinline__ void publish(uint32_t *flag, uint32_t epoch)
+{
+    __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// wave 0 waits until flags[0..n) all hold epoch; false on timeout.  The other
+// waves wait at the caller's barrier; the data behind the flags is then read
+// with device-coherent loads.
+__device__ __forceinline__ bool flags_wait(const uint32_t *flags, int n, uint32_t epoch)
+{
+    const int lane = threadIdx.x & 63;
+    for (int it = 0; it < (1 << 21); ++it) {
+        bool ok = true;
+        for (int i = lane; i < n; i += 64)
+            ok &= __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+        if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
+        __builtin_amdgcn_s_sleep(16);
+    }
+    return false;
+}
+
+// wave 0 waits for an expert's gate/up flags (flagging a timeout), then the block goes on
+struct FusedWait {
+    const uint32_t *flags;
+    int n;
+    uint32_t epoch;
+    int *flag;
+    __device__ void operator()() const
+    {
+        if (threadIdx.x < 64 && !flags_wait(flags, n, epoch) && threadIdx.x == 0) *flag = 1;
+        moe::lds_barrier();
+    }
+};
+
+// The route of the S slots in LDS, for any block; block 0 writes the tables.
+__device__ void fused_route(const FusedArgs &a, FusedRoute &R)
+{
+    const int tid = threadIdx.x, S = a.M * a.k, E = a.E;
+    if (tid == 0) { R.na = 0; R.nvalid = 0; R.ninvalid = 0; R.flag = 0; }
+    for (int s = tid; s < kFusedMaxSlots; s += kThreads) R.ids[s] = s < S ? a.ids[s] : -1;
+    __syncthreads();
+    const int id = tid < S ? R.ids[tid] : -1;
+    const bool valid = tid < S && id >= 0 && id < E;
+    int less = 0, before = 0, total = 0;
+    for (int q = 0; q < S; ++q) {
+        const int v = R.ids[q];
+        if (v >= 0 && v < E) {
+            less += v < id;
+            if (v == id) { ++total; before += q < tid; }
+        }
+    }
+    R.first[tid] = valid && before == 0;
+    if (tid < S && !valid && id != -1) atomicAdd(&R.ninvalid, 1);
+    if (valid) atomicAdd(&R.nvalid, 1);
+    __syncthreads();
+    int rank = 0;                                    // distinct valid experts below id
+    for (int q = 0; q < S; ++q) rank += R.first[q] && R.ids[q] < id;
+    const int p = less + before;
+    if (tid < S) R.t2p[tid] = valid ? p : -1;
+    if (valid) R.tok[p] = tid / a.k;
+    if (valid && before == 0) {
+        R.ae[rank] = id; R.ap0[rank] = less; R.acnt[rank] = total;
+        atomicAdd(&R.na, 1);
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {                           // the route tables, as route_pack writes them
+        for (int e = tid; e <= E; e += kThreads) {
+            int c = 0;
+            for (int q = 0; q < S; ++q) {
+                const int v = R.ids[q];
+                c += v >= 0 && v < e;
+            }
+            a.r.offsets[e] = c;
+        }
+        if (tid < S) {
+            a.r.token_to_perm[tid] = R.t2p[tid];
+            if (valid) { a.r.sorted_slot[p] = tid; a.r.sorted_token[p] = tid / a.k; }
+        }
+        const int A = S < E ? S : E;
+        for (int i = tid; i < A; i += kThreads) a.r.active[i] = i < R.na ? R.ae[i] : -1;
+        if (tid == 0) { *a.r.num_active = R.na; *a.r.status = R.ninvalid; }
+    }
+}
+
+// GCH/GNCH and DCH/DNCH: the chunking of the gate/up and down items (NCH > 0
+// fully unrolled, 0 looped).
+template <int GCH, int GNCH, int GST, int DCH, int DNCH, int DST>
+__global__ __launch_bounds__(kThreads, 4) void moe_fused_decode_e4m3_kernel(FusedArgs a)
+{
+    extern __shared__ uint4 dyn[];                   // x tile (gate/up), then h tile (down)
+    __shared__ FusedRoute R;
+    __shared__ float ush[GST][16];
+    const int tid = threadIdx.x;
+    fused_route(a, R);
+    const int na = moe::uniform(R.na);
+    const int H = a.dn.H, I = a.gu.I;
+    if (na == 0) {                                   // no valid slot: every output row is zero
+        for (size_t q = (size_t)blockIdx.x * kThreads + tid; q < (size_t)a.M * H;
+             q += (size_t)gridDim.x * kThreads)
+            a.out[q] = 0.0f;
+    }
+
+    // gate/up + SwiGLU items: expert-major
+    const int ntg = I / 16;
+    for (int it = blockIdx.x; it < na * ntg; it += gridDim.x) {
+        const int ai = it / ntg, tile = it - ai * ntg;
+        const int e = moe::uniform(R.ae[ai]), p0 = moe::uniform(R.ap0[ai]);
+        const int ne = moe::uniform(R.acnt[ai]);
+        gateup_e4m3_item<GCH, GNCH, GST, true>(a.gu, e, tile, p0, ne, R.tok + p0, dyn, ush);
+        moe::wait_vm0();                             // this wave's h stores are written
+        __syncthreads();
+        if (tid == 0) publish(a.flag_gu + it, a.epoch);
+    }
+
+    // down items: tile-major, so the experts of one row tile run together
+    const int ntd = H / 32;
+    for (int it = blockIdx.x; it < na * ntd; it += gridDim.x) {
+        const int tile = it / na, ai = it - tile * na;
+        const int e = moe::uniform(R.ae[ai]), p0 = moe::uniform(R.ap0[ai]);
+        const int ne = moe::uniform(R.acnt[ai]);
+        const FusedWait wait_h{a.flag_gu + ai * ntg, ntg, a.epoch, &R.flag};
+        down_e4m3_item<DCH, DNCH, DST, true>(a.dn, e, tile, p0, ne, reinterpret_cast<float4 *>(dyn),
+                                             wait_h);
+        moe::wait_vm0();                             // this wave's y stores are written
+        __syncthreads();
+        uint32_t *fl = a.flag_dn + (size_t)tile * a.A;
+        if (ai + 1 < na) {
+            if (tid == 0) publish(fl + ai, a.epoch);
+            continue;
+        }
+        // the tile's last expert: wait for the others' y rows, then combine rows
+        // tile*32 .. +32 of every token
+        const FusedWait wait_y{fl, na - 1, a.epoch, &R.flag};
+        wait_y();
+        for (int q = tid; q < a.M * 32; q += kThreads) {
+            const int t = q >> 5, m = tile * 32 + (q & 31);
+            float acc = 0.0f;
+            for (int j = 0; j < a.k; ++j) {
+                const int pr = R.t2p[t * a.k + j];
+                if (pr < 0) continue;
+                acc = __fadd_rn(acc, __fmul_rn(a.w[t * a.k + j], moe::load_dev(a.dn.y + (size_t)pr * H + m)));
+            }
+            a.out[(size_t)t * H + m] = acc;
+        }
+    }
+    __syncthreads();
+    if (tid == 0 && R.flag) atomicAdd(a.r.status, (int)kFusedTimeoutFlag);
 }
 
 }  // namespace
@@ -491,4 +747,75 @@ hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const 
         }
     }
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fused decode layer launch
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int GCH, int GNCH, int GST, int DCH, int DNCH, int DST>
+hipError_t fused_launch(const FusedArgs &a, size_t lds, hipStream_t st)
+{
+    auto kern = moe_fused_decode_e4m3_kernel<GCH, GNCH, GST, DCH, DNCH, DST>;
+    // one block per slot the occupancy allows: every block must be resident
+    // for the waits to end
+    static int per_cu = -1;
+    static size_t per_cu_lds = 0;
+    static int n_cu = 0;
+    if (per_cu < 0 || per_cu_lds != lds) {
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)kern, kThreads, lds);
+        if (e != hipSuccess) return e;
+        per_cu_lds = lds;
+    }
+    if (n_cu == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    if (per_cu < 1) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(per_cu * n_cu)), dim3(kThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+// Unrolled chunking for the pages' decode shape (hidden 7168 = 7 chunks of
+// 1024, inter 2048 = 4 chunks of 512); single-segment looped items otherwise.
+template <int GST, int DST>
+hipError_t fused_dispatch(const FusedArgs &a, size_t lds, hipStream_t st)
+{
+    if (a.gu.H == 7168 && a.gu.I == 2048) return fused_launch<8, 7, GST, 4, 4, DST>(a, lds, st);
+    return fused_launch<1, 0, GST, 1, 0, DST>(a, lds, st);
+}
+
+}  // namespace
+
+int fused_decode_max_slots() { return kFusedMaxSlots; }
+
+hipError_t launch_fused_decode_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
+                                    const GemvBankDev &down, const uint16_t *x, const int32_t *ids,
+                                    const float *w, int32_t M, int32_t k, int32_t E, int32_t hidden,
+                                    int32_t inter, float limit, const MoeRouteDev &r, float *h,
+                                    float *y, float *out, void *flags, uint32_t epoch,
+                                    hipStream_t st)
+{
+    FusedArgs a{};
+    a.gu.gcodes = gate.codes; a.gu.ucodes = up.codes;
+    a.gu.gscales = (const float *)gate.scales; a.gu.uscales = (const float *)up.scales;
+    a.gu.x = x; a.gu.h = h; a.gu.H = hidden; a.gu.I = inter; a.gu.limit = limit;
+    a.gu.st = gemv_gateup_pass_slots(M, hidden, 2);
+    a.dn.codes = down.codes; a.dn.scales = (const float *)down.scales; a.dn.h = h; a.dn.y = y;
+    a.dn.H = hidden; a.dn.I = inter;
+    a.dn.st = gemv_down_pass_slots(M, inter, 2);
+    a.ids = ids; a.w = w; a.M = M; a.k = k; a.E = E; a.epoch = epoch;
+    a.A = M * k < E ? M * k : E;
+    a.flag_gu = (uint32_t *)flags;
+    a.flag_dn = a.flag_gu + (size_t)a.A * (inter / 16);
+    a.out = out; a.r = r;
+    const size_t xl = (size_t)a.gu.st * hidden * 2, hl = (size_t)a.dn.st * inter * 4;
+    const size_t lds = xl > hl ? xl : hl;
+    if (a.gu.st == 1 && a.dn.st == 1) return fused_dispatch<1, 1>(a, lds, st);
+    if (a.gu.st == 1) return fused_dispatch<1, 2>(a, lds, st);
+    if (a.dn.st == 1) return fused_dispatch<2, 1>(a, lds, st);
+    return fused_dispatch<2, 2>(a, lds, st);
 }

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
         const int nt = min(a.st, ne - s0);
         // opaque copies keep the per-chunk address arithmetic inside the pass
-        const uint8_t *cbp = cb0, *sbp = sb0;
+        const uint8_t *cbp = moe::uniform_ptr(cb0), *sbp = moe::uniform_ptr(sb0);
         uint32_t co = coff, so = soff;
         asm volatile("" : "+s"(cbp), "+s"(sbp), "+v"(co), "+v"(so));
         auto load_w = [&](uint4 (&wb)[CH], uint32_t (&sb)[CH], int c) {
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
 
     for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
         const int nt = min(a.st, ne - s0);
-        const uint8_t *cbp = cb0, *sbp = sb0;
+        const uint8_t *cbp = moe::uniform_ptr(cb0), *sbp = moe::uniform_ptr(sb0);
         uint32_t co = coff, so = soff;
         asm volatile("" : "+s"(cbp), "+s"(sbp), "+v"(co), "+v"(so));
         auto load_w = [&](uint4 (&wb)[CH], uint32_t (&sb)[CH], int c) {

@@ -7,6 +7,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <chrono>
 #include <string>
 
 #include "../../include/moe.h"
@@ -58,7 +60,9 @@ bool sizes_ok(int32_t M, int32_t top_k, int32_t E)
 
 int32_t resolve(int32_t M, int32_t fmt, int32_t requested)
 {
-    if (requested == MOE_MODE_GEMV_A16 || requested == MOE_MODE_GEMM_A8) return requested;
+    if (requested == MOE_MODE_GEMV_A16 || requested == MOE_MODE_GEMM_A8 ||
+        requested == MOE_MODE_FUSED)
+        return requested;
     (void)fmt;
     return M <= MOE_GEMV_MAX_M ? MOE_MODE_GEMV_A16 : MOE_MODE_GEMM_A8;
 }
@@ -102,6 +106,35 @@ GemmScratch carve_gemm(char *p, int64_t M, int64_t S, int32_t E, int32_t hidden,
     return g;
 }
 
+// Scratch of moe_layer_fused after the route region: h [S][inter] FP32, then
+// the epoch flags, one 32-bit word per gate/up item (A x inter/16) and per
+// down item (hidden/32 x A), A = min(S, E).
+size_t fused_scratch_bytes(int64_t S, int32_t E, int32_t hidden, int32_t inter)
+{
+    const size_t A = (size_t)(S < E ? S : E);
+    return moe::align256(sizeof(float) * (size_t)(S * inter)) +
+           moe::align256(4 * A * (size_t)(inter / 16 + hidden / 32));
+}
+
+// Points *route at the route tables at the start of ws.
+void carve_route(void *ws, int32_t M, int32_t top_k, int32_t E, moe_route_t *route)
+{
+    const int64_t S = (int64_t)M * top_k;
+    const int64_t A = S < E ? S : E;
+    char *p = (char *)ws;
+    route->M = M;
+    route->top_k = top_k;
+    route->num_experts = E;
+    route->num_slots = (int32_t)S;
+    route->expert_offsets = (int32_t *)p; p += moe::align256(sizeof(int32_t) * (E + 1));
+    route->sorted_slot = (int32_t *)p;    p += moe::align256(sizeof(int32_t) * S);
+    route->sorted_token = (int32_t *)p;   p += moe::align256(sizeof(int32_t) * S);
+    route->token_to_perm = (int32_t *)p;  p += moe::align256(sizeof(int32_t) * S);
+    route->active_experts = (int32_t *)p; p += moe::align256(sizeof(int32_t) * (A > 0 ? A : 1));
+    route->num_active = (int32_t *)p;
+    route->status = (int32_t *)p + 1;
+}
+
 // The GEMM tier addresses activation rows with 32-bit byte offsets.
 bool gemm_dims_ok(int64_t M, int64_t S, int32_t hidden, int32_t inter)
 {
@@ -129,8 +162,9 @@ int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt,
     g_stage_n = events ? n_events : 0;
     (void)fmt; (void)hidden; (void)inter;
     // GEMV tier: gate/up GEMV with SwiGLU, down GEMV
+    // fused layer: its one launch
     // GEMM tier: activation quantization + tile schedule, gate/up GEMM, down GEMM
-    return mode == MOE_MODE_GEMV_A16 ? 2 : 3;
+    return mode == MOE_MODE_GEMV_A16 ? 2 : mode == MOE_MODE_FUSED ? 1 : 3;
 }
 
 int32_t moe_resolve_mode(int32_t M, int32_t fmt, int32_t requested)
@@ -143,9 +177,13 @@ size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts, in
 {
     if (!sizes_ok(max_M, top_k, num_experts)) return 0;
     if (fmt != MOE_W_E4M3_B128 && fmt != MOE_W_NVFP4_B16) return 0;
-    if (mode < MOE_MODE_AUTO || mode > MOE_MODE_GEMM_A8) return 0;
+    if (mode < MOE_MODE_AUTO || mode > MOE_MODE_FUSED) return 0;
     if (!ffn_dims_ok(fmt, hidden, inter)) return 0;
     const int64_t S = (int64_t)max_M * top_k;
+    if (mode == MOE_MODE_FUSED) {
+        if (fmt != MOE_W_E4M3_B128 || S > MOE_FUSED_MAX_SLOTS) return 0;
+        return moe::route_region_bytes(S, num_experts) + fused_scratch_bytes(S, num_experts, hidden, inter);
+    }
     size_t ffn;
     if (mode == MOE_MODE_AUTO) {
         const int64_t mg = max_M < MOE_GEMV_MAX_M ? max_M : MOE_GEMV_MAX_M;
@@ -179,19 +217,7 @@ moe_status_t moe_route_pack(const int32_t *topk_ids, int32_t M, int32_t top_k, i
         return fail(MOE_ERR_WORKSPACE, "moe_route_pack: workspace %zu bytes < %zu", ws_bytes, need);
     if (((uintptr_t)ws & 255) != 0) return fail(MOE_ERR_ARG, "moe_route_pack: ws not 256-byte aligned");
 
-    char *p = (char *)ws;
-    const int64_t A = S < num_experts ? S : num_experts;
-    route->M = M;
-    route->top_k = top_k;
-    route->num_experts = num_experts;
-    route->num_slots = (int32_t)S;
-    route->expert_offsets = (int32_t *)p; p += moe::align256(sizeof(int32_t) * (num_experts + 1));
-    route->sorted_slot = (int32_t *)p;    p += moe::align256(sizeof(int32_t) * S);
-    route->sorted_token = (int32_t *)p;   p += moe::align256(sizeof(int32_t) * S);
-    route->token_to_perm = (int32_t *)p;  p += moe::align256(sizeof(int32_t) * S);
-    route->active_experts = (int32_t *)p; p += moe::align256(sizeof(int32_t) * (A > 0 ? A : 1));
-    route->num_active = (int32_t *)p;
-    route->status = (int32_t *)p + 1;
+    carve_route(ws, M, top_k, num_experts, route);
 
     MoeRouteDev r{route->expert_offsets, route->sorted_slot, route->sorted_token,
                   route->token_to_perm, route->active_experts, route->num_active, route->status};
@@ -200,24 +226,24 @@ moe_status_t moe_route_pack(const int32_t *topk_ids, int32_t M, int32_t top_k, i
     return MOE_OK;
 }
 
-static moe_status_t check_bank(const moe_bank_t *b, const char *name, int32_t fmt, int32_t E,
-                               int32_t n_out, int32_t k_in)
+static moe_status_t check_bank(const char *fn, const moe_bank_t *b, const char *name, int32_t fmt,
+                               int32_t E, int32_t n_out, int32_t k_in)
 {
     if (!b || !b->codes || !b->scales)
-        return fail(MOE_ERR_ARG, "moe_expert_ffn: %s bank or its codes/scales is null", name);
+        return fail(MOE_ERR_ARG, "%s: %s bank or its codes/scales is null", fn, name);
     if (b->fmt != fmt)
-        return fail(MOE_ERR_FORMAT, "moe_expert_ffn: %s bank format %d differs from gate's %d",
-                    name, b->fmt, fmt);
+        return fail(MOE_ERR_FORMAT, "%s: %s bank format %d differs from gate's %d",
+                    fn, name, b->fmt, fmt);
     if (fmt == MOE_W_E4M3_B128 && b->scale2)
-        return fail(MOE_ERR_FORMAT, "moe_expert_ffn: %s bank: scale2 must be NULL for E4M3", name);
+        return fail(MOE_ERR_FORMAT, "%s: %s bank: scale2 must be NULL for E4M3", fn, name);
     if (fmt == MOE_W_NVFP4_B16 && !b->scale2)
-        return fail(MOE_ERR_FORMAT, "moe_expert_ffn: %s bank: NVFP4 needs scale2", name);
+        return fail(MOE_ERR_FORMAT, "%s: %s bank: NVFP4 needs scale2", fn, name);
     if (b->num_experts != E || b->n_out != n_out || b->k_in != k_in)
         return fail(MOE_ERR_SHAPE,
-                    "moe_expert_ffn: %s bank is E=%d %dx%d, expected E=%d %dx%d", name,
+                    "%s: %s bank is E=%d %dx%d, expected E=%d %dx%d", fn, name,
                     b->num_experts, b->n_out, b->k_in, E, n_out, k_in);
     if (!aligned16(b->codes))
-        return fail(MOE_ERR_ARG, "moe_expert_ffn: %s codes not 16-byte aligned", name);
+        return fail(MOE_ERR_ARG, "%s: %s codes not 16-byte aligned", fn, name);
     return MOE_OK;
 }
 
@@ -232,7 +258,8 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
     if (fmt != MOE_W_E4M3_B128 && fmt != MOE_W_NVFP4_B16)
         return fail(MOE_ERR_FORMAT, "moe_expert_ffn: unknown weight format %d", fmt);
     if (mode < MOE_MODE_AUTO || mode > MOE_MODE_GEMM_A8)
-        return fail(MOE_ERR_ARG, "moe_expert_ffn: unknown mode %d", mode);
+        return fail(MOE_ERR_ARG, "moe_expert_ffn: unknown mode %d%s", mode,
+                    mode == MOE_MODE_FUSED ? " (the fused layer is moe_layer_fused)" : "");
     if (!ffn_dims_ok(fmt, hidden, inter))
         return fail(MOE_ERR_SHAPE,
                     "moe_expert_ffn: hidden %d and inter %d must be positive multiples of %d, "
@@ -242,9 +269,9 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
         return fail(MOE_ERR_ARG, "moe_expert_ffn: route does not come from moe_route_pack on this ws");
     const int32_t E = route->num_experts;
     moe_status_t st;
-    if ((st = check_bank(gate, "gate", fmt, E, inter, hidden))) return st;
-    if ((st = check_bank(up, "up", fmt, E, inter, hidden))) return st;
-    if ((st = check_bank(down, "down", fmt, E, hidden, inter))) return st;
+    if ((st = check_bank("moe_expert_ffn", gate, "gate", fmt, E, inter, hidden))) return st;
+    if ((st = check_bank("moe_expert_ffn", up, "up", fmt, E, inter, hidden))) return st;
+    if ((st = check_bank("moe_expert_ffn", down, "down", fmt, E, hidden, inter))) return st;
     if (!aligned16(x_bf16) || !aligned16(y_packed))
         return fail(MOE_ERR_ARG, "moe_expert_ffn: x and y must be 16-byte aligned");
     if (!(limit > 0.0f)) return fail(MOE_ERR_ARG, "moe_expert_ffn: limit must be > 0");
@@ -304,6 +331,66 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
         e = launch_gemv_down_nvfp4(bd, h, r, M, (int32_t)S, E, hidden, inter, y_packed, s);
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: down GEMV launch");
     stage_mark(2, s);
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
+                             const uint16_t *x_bf16, const int32_t *topk_ids,
+                             const float *topk_weights, int32_t M, int32_t top_k, int32_t hidden,
+                             int32_t inter, float limit, float *y_packed, float *out, void *ws,
+                             size_t ws_bytes, moe_route_t *route, void *stream)
+{
+    static const char *fn = "moe_layer_fused";
+    if (!gate || !up || !down || !x_bf16 || !topk_ids || !topk_weights || !y_packed || !out ||
+        !ws || !route)
+        return fail(MOE_ERR_ARG, "%s: null pointer", fn);
+    const int32_t fmt = gate->fmt, E = gate->num_experts;
+    if (fmt != MOE_W_E4M3_B128 && fmt != MOE_W_NVFP4_B16)
+        return fail(MOE_ERR_FORMAT, "%s: unknown weight format %d", fn, fmt);
+    if (!sizes_ok(M, top_k, E))
+        return fail(MOE_ERR_SHAPE, "%s: need M >= 1, 1 <= top_k <= num_experts <= %d (M=%d top_k=%d E=%d)",
+                    fn, MOE_MAX_EXPERTS, M, top_k, E);
+    if ((int64_t)M * top_k > MOE_FUSED_MAX_SLOTS)
+        return fail(MOE_ERR_SHAPE, "%s: M*top_k = %lld > %d", fn, (long long)M * top_k,
+                    MOE_FUSED_MAX_SLOTS);
+    if (!ffn_dims_ok(fmt, hidden, inter))
+        return fail(MOE_ERR_SHAPE, "%s: hidden %d and inter %d must be positive multiples of %d, "
+                    "at most %d", fn, hidden, inter, fmt == MOE_W_NVFP4_B16 ? 256 : 128, MOE_MAX_DIM);
+    moe_status_t st;
+    if ((st = check_bank(fn, gate, "gate", fmt, E, inter, hidden))) return st;
+    if ((st = check_bank(fn, up, "up", fmt, E, inter, hidden))) return st;
+    if ((st = check_bank(fn, down, "down", fmt, E, hidden, inter))) return st;
+    if (fmt != MOE_W_E4M3_B128)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: the fused layer serves E4M3 banks only", fn);
+    if (!aligned16(x_bf16) || !aligned16(y_packed) || !aligned16(out))
+        return fail(MOE_ERR_ARG, "%s: x, y and out must be 16-byte aligned", fn);
+    if (!(limit > 0.0f)) return fail(MOE_ERR_ARG, "%s: limit must be > 0", fn);
+    if (((uintptr_t)ws & 255) != 0) return fail(MOE_ERR_ARG, "%s: ws not 256-byte aligned", fn);
+    const size_t need = moe_workspace_bytes(M, top_k, E, hidden, inter, fmt, MOE_MODE_FUSED);
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
+
+    carve_route(ws, M, top_k, E, route);
+    const int64_t S = (int64_t)M * top_k;
+    char *scratch = (char *)ws + moe::route_region_bytes(S, E);
+    float *h = (float *)scratch;
+    void *flags = scratch + moe::align256(sizeof(float) * (size_t)(S * inter));
+    // a fresh epoch per call: flags of any earlier call in this process never
+    // match it
+    static std::atomic<uint32_t> epoch{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() |
+                                       1u};
+    const uint32_t ep = epoch.fetch_add(1, std::memory_order_relaxed);
+    MoeRouteDev r{route->expert_offsets, route->sorted_slot, route->sorted_token,
+                  route->token_to_perm, route->active_experts, route->num_active, route->status};
+    GemvBankDev bg{gate->codes, gate->scales, gate->scale2};
+    GemvBankDev bu{up->codes, up->scales, up->scale2};
+    GemvBankDev bd{down->codes, down->scales, down->scale2};
+    hipStream_t s = (hipStream_t)stream;
+    stage_mark(0, s);
+    hipError_t e = launch_fused_decode_e4m3(bg, bu, bd, x_bf16, topk_ids, topk_weights, M, top_k, E,
+                                            hidden, inter, limit, r, h, y_packed, out, flags, ep, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_fused: launch");
+    stage_mark(1, s);
     return MOE_OK;
 }
 

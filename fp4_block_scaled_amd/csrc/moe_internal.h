@@ -47,6 +47,16 @@ __device__ __forceinline__ float sum8_lanes(float v)
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// A pointer every lane of the wave holds, made explicitly uniform (SGPRs).
+template <class T>
+__device__ __forceinline__ T *uniform_ptr(T *p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Wait until at most N of this wave's vector memory loads are in flight
 // (vmcnt(N); expcnt and lgkmcnt not waited).
 template <int N>
@@ -63,6 +73,20 @@ __device__ __forceinline__ void lds_barrier()
 {
     __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0); vmcnt and expcnt not waited
     asm volatile("s_barrier" ::: "memory");
+}
+
+// Device-coherent relaxed accesses (device-scope atomics): a store writes
+// through to memory and a load reads past this XCD's L2, so data handed
+// between blocks of one launch needs no whole-cache write-back or
+// invalidation.  The writer waits for its stores (wait_vm0) before it
+// publishes; the reader loads only after it has seen the publication.
+__device__ __forceinline__ void store_dev(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace moe
@@ -97,6 +121,18 @@ hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &u
 hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
                                  int32_t M, int32_t S, int32_t E, int32_t hidden, int32_t inter,
                                  float *y, hipStream_t st);
+
+// Fused decode layer (E4M3): route pack, gate/up + SwiGLU, down and combine
+// in one launch of resident blocks.  S = M*k <= fused_decode_max_slots();
+// flags: min(S, E) x (inter/16 + hidden/32) 32-bit words, any contents;
+// epoch: a value no earlier call on these flags used.
+int fused_decode_max_slots();
+hipError_t launch_fused_decode_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
+                                    const GemvBankDev &down, const uint16_t *x, const int32_t *ids,
+                                    const float *w, int32_t M, int32_t k, int32_t E, int32_t hidden,
+                                    int32_t inter, float limit, const MoeRouteDev &r, float *h,
+                                    float *y, float *out, void *flags, uint32_t epoch,
+                                    hipStream_t st);
 
 hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
                                     const uint16_t *x, const MoeRouteDev &r, int32_t M,

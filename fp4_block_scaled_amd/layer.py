@@ -1,8 +1,9 @@
 """Device buffers for one routed-MoE layer call sequence (plumbing only).
 
 Allocates the workspace, packed-y and output tensors once for a maximum M and
-runs moe_route_pack -> moe_expert_ffn -> moe_combine on the current stream.
-No arithmetic happens here."""
+runs moe_route_pack -> moe_expert_ffn -> moe_combine on the current stream, or
+moe_layer_fused (one launch) when built with mode MOE_MODE_FUSED.  No
+arithmetic happens here."""
 from __future__ import annotations
 
 import torch
@@ -31,6 +32,11 @@ class MoeLayer:
     def __call__(self, x_bf16, ids, weights, stream=None):
         M = int(ids.shape[0])
         assert M <= self.max_M and int(ids.shape[1]) == self.top_k
+        if self.mode == B.MOE_MODE_FUSED:
+            self.route = B.moe_layer_fused(self.gate, self.up, self.down, x_bf16, ids, weights, M,
+                                           self.top_k, self.hidden, self.inter, self.limit, self.y,
+                                           self.out, self.ws, stream=stream)
+            return self.out[:M]
         self.route = B.moe_route_pack(ids, M, self.top_k, self.E, self.ws, stream=stream)
         B.moe_expert_ffn(self.gate, self.up, self.down, x_bf16, self.route, self.hidden,
                          self.inter, self.limit, self.mode, self.y, self.ws, stream=stream)

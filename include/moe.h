@@ -75,10 +75,15 @@ enum {
      * quantized to E4M3 per 1x128 group ("spark_model glm5next_mlp/forward.rs",
      * grouped prefill arm of fn forward_moe; "memra-engine src/dsv4_ep.rs",
      * EpScratch xq/xs/hq/hs).  E4M3 banks only. */
-    MOE_MODE_GEMM_A8 = 2
+    MOE_MODE_GEMM_A8 = 2,
+    /* Not a tier of moe_expert_ffn: the workspace mode of moe_layer_fused
+     * (route pack, gate/up, SwiGLU, down and combine in one launch). */
+    MOE_MODE_FUSED = 3
 };
 
 #define MOE_GEMV_MAX_M 16
+/* Largest M * top_k moe_layer_fused takes. */
+#define MOE_FUSED_MAX_SLOTS 256
 #define MOE_MAX_EXPERTS 512
 /* Largest hidden and inter (128 blocks of 128 along K, and the bf16 x rows
  * of a GEMV pass held in LDS). */
@@ -181,14 +186,42 @@ moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
                          const float *topk_weights, int32_t hidden, float *out,
                          void *stream);
 
+/* Fused decode layer: moe_route_pack, moe_expert_ffn on the GEMV tier and
+ * moe_combine as ONE kernel launch of resident blocks ("spark_model
+ * glm5next_mlp/forward.rs", doc of forward_moe: the per-row MoE path without
+ * host round trips and its launch count; "memra-engine src/dsv4_ep.rs", fn
+ * chain: gate/up, activation, down and weighting as one chain per expert).
+ * Each block builds the route in LDS; gate/up items publish per expert, down
+ * items wait for their expert's h, and the last down item of each 32-row
+ * output tile applies the top-k weights for every token.
+ * Inputs and outputs as for the three calls: topk_ids int32 [M][top_k],
+ * topk_weights float [M][top_k], x bf16 [M][hidden]; y_packed float
+ * [M*top_k][hidden] (expert-sorted rows), out float [M][hidden]; *route
+ * (host) describes the route tables in ws, as moe_route_pack fills them.
+ * Rules: E4M3 banks (NVFP4: MOE_ERR_UNSUPPORTED); M*top_k <=
+ * MOE_FUSED_MAX_SLOTS; the moe_expert_ffn shape rules; num_experts is the
+ * banks'; ws_bytes >= moe_workspace_bytes(M, top_k, E, hidden, inter, fmt,
+ * MOE_MODE_FUSED), ws 256-byte aligned.  The workspace needs no clearing,
+ * and calls on one ws must be ordered on one stream.  The kernel assumes its
+ * blocks can all be resident on the GPU at once (no other kernel holding the
+ * CUs); a wait that does not end within about a second gives up and adds
+ * 2^30 to route->status. */
+moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
+                             const uint16_t *x_bf16, const int32_t *topk_ids,
+                             const float *topk_weights, int32_t M, int32_t top_k,
+                             int32_t hidden, int32_t inter, float limit, float *y_packed,
+                             float *out, void *ws, size_t ws_bytes, moe_route_t *route,
+                             void *stream);
+
 /* Stage timing (optional, thread-local).  With events != NULL, later
  * moe_expert_ffn calls on this thread record events[0] on their stream before
  * the first kernel and events[i] after the i-th kernel, for at most
  * n_events events; NULL turns it off.  The handles are the caller's
  * hipEvent_t.  Returns the number of stages the tier `mode` records (2 for
- * MOE_MODE_GEMV_A16: gate/up with SwiGLU, down; 3 otherwise, the GEMM tier's
- * activation quantization + tile schedule, gate/up with SwiGLU, down), so
- * n_events = 4 covers every tier.  Mirrors the
+ * MOE_MODE_GEMV_A16: gate/up with SwiGLU, down; 1 for MOE_MODE_FUSED, where
+ * moe_layer_fused records around its single launch; 3 otherwise, the GEMM
+ * tier's activation quantization + tile schedule, gate/up with SwiGLU,
+ * down), so n_events = 4 covers every tier.  Mirrors the
  * per-stage timers of "spark_model glm5next_mlp/forward.rs" (profile::start /
  * profile::end around the MoE stages). */
 int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt,

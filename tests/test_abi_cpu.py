@@ -181,3 +181,45 @@ def test_route_pack_and_combine_error_contract_on_host():
     empty = B.moe_route_t()
     empty.token_to_perm = FAKE
     assert L.moe_combine(FAKE, C.byref(empty), FAKE, 256, FAKE, None) == B.MOE_ERR_ARG
+
+
+def test_fused_workspace_and_error_contract_on_host():
+    from fp4_block_scaled_amd import binding as B
+    L = B.lib
+    # workspace: route region + h [S][I] FP32 + one 32-bit flag per gate/up
+    # item (A x I/16) and per down item (H/32 x A), A = min(S, E)
+    M, k, E, H, I = 1, 8, 256, 7168, 2048
+    S = M * k
+    route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
+    want = route + a256(4 * S * I) + a256(4 * min(S, E) * (I // 16 + H // 32))
+    assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_FUSED) == want
+    assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_FUSED) == 0
+    assert L.moe_workspace_bytes(33, 8, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_FUSED) == 0
+    assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_E4M3_B128, 4) == 0
+    assert B.moe_resolve_mode(1, B.MOE_W_E4M3_B128, B.MOE_MODE_FUSED) == B.MOE_MODE_FUSED
+
+    ws = FAKE + 0x100000
+    g, u, d = _bank(B), _bank(B), _bank(B, n=256, k=128)
+    r = B.moe_route_t()
+
+    def fused(gate=g, up=u, down=d, M=1, k=4, hidden=256, inter=128, ws_=ws, nbytes=1 << 30,
+              x=FAKE + 0x2000, limit=7.0):
+        return L.moe_layer_fused(C.byref(gate), C.byref(up), C.byref(down), x, FAKE + 0x4000,
+                                 FAKE + 0x5000, M, k, hidden, inter, limit, FAKE + 0x3000,
+                                 FAKE + 0x6000, ws_, nbytes, C.byref(r), None)
+
+    assert fused(x=None) == B.MOE_ERR_ARG
+    assert fused(M=80, k=4) == B.MOE_ERR_SHAPE                 # S = 320 > 256
+    assert "256" in B.moe_last_error()
+    assert fused(hidden=200) == B.MOE_ERR_SHAPE
+    assert fused(gate=_bank(B, E=8)) == B.MOE_ERR_SHAPE
+    nv = _bank(B, fmt=2, k=256, n=256, scale2=FAKE)
+    assert fused(gate=nv, up=nv, down=_bank(B, fmt=2, n=256, k=256, scale2=FAKE), hidden=256,
+                 inter=256) == B.MOE_ERR_UNSUPPORTED
+    assert fused(nbytes=512) == B.MOE_ERR_WORKSPACE
+    assert fused(ws_=ws + 64) == B.MOE_ERR_ARG
+    assert fused(limit=-1.0) == B.MOE_ERR_ARG
+    # moe_expert_ffn points the fused mode at moe_layer_fused
+    rr = _route(B, ws)
+    assert _ffn(B, g, u, d, rr, ws, mode=B.MOE_MODE_FUSED) == B.MOE_ERR_ARG
+    assert "moe_layer_fused" in B.moe_last_error()

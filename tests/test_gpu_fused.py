@@ -1,0 +1,139 @@
+"""GPU tests of moe_layer_fused, the one-launch decode layer: route tables bit
+for bit against the oracle's route pack, layer outputs against the oracle
+(max|err| <= 2e-3 * max|ref|, relative L2 <= 1e-3), and bit identity with the
+three-call path (moe_route_pack, moe_expert_ffn, moe_combine), whose kernels
+do the same arithmetic in the same order."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from fp4_block_scaled_amd import binding as B
+from moe_cases import GpuCase, check_fp, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def get_case(wl):
+    key = (wl.name, wl.hidden, wl.inter, wl.experts, wl.top_k, wl.fmt, wl.seed)
+    if key not in _cache:
+        _cache.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+        _cache[key] = GpuCase(wl)
+    return _cache[key]
+
+
+def assert_route_equal(tabs, ids, E):
+    ref = oracle.route_pack(ids, E)
+    nv = int(ref["expert_offsets"][-1])
+    assert np.array_equal(tabs["expert_offsets"], ref["expert_offsets"])
+    assert np.array_equal(tabs["sorted_slot"][:nv], ref["sorted_slot"])
+    assert np.array_equal(tabs["sorted_token"][:nv], ref["sorted_token"])
+    assert np.array_equal(tabs["token_to_perm"], ref["token_to_perm"])
+    assert int(tabs["num_active"][0]) == ref["num_active"]
+    assert np.array_equal(tabs["active_experts"][:ref["num_active"]], ref["active_experts"])
+    assert np.all(tabs["active_experts"][ref["num_active"]:] == -1)
+    return ref
+
+
+def fused_vs_three_call(case, ids, w, label, x=None):
+    """Run the fused layer and the three-call path on the same inputs; check the
+    route, the oracle parity, and bit identity of out and the valid y rows."""
+    wl = case.wl
+    M = ids.shape[0]
+    Lf = case.layer(max_M=M, mode=B.MOE_MODE_FUSED)
+    Lf.y.fill_(float("nan"))
+    out_f, y_f, tabs, _ = case.run(ids, w, x=x, layer=Lf)
+    ref = assert_route_equal(tabs, ids, wl.experts)
+    assert int(tabs["status"][0]) == ref["invalid"], "status (a timed-out wait adds 2^30)"
+    nv = int(ref["expert_offsets"][-1])
+    assert np.all(np.isnan(y_f[nv:])), f"{label}: fused layer wrote y rows past the valid slots"
+    out_3, y_3, _, _ = case.run(ids, w, B.MOE_MODE_GEMV_A16, x=x)
+    assert np.array_equal(out_f.view(np.uint32), out_3.view(np.uint32)), f"{label}: out differs"
+    assert np.array_equal(y_f[:nv].view(np.uint32), y_3[:nv].view(np.uint32)), f"{label}: y differs"
+    xx = case.x if x is None else x
+    ref_out, _ = oracle_layer(case.banks, xx, ids, w, wl.limit, False)
+    return check_fp(out_f, ref_out, f"{label} out")
+
+
+@pytest.mark.parametrize("name", ["tiny_e4m3_m1", "decode_e4m3_m1", "verify_e4m3_m8"])
+@pytest.mark.parametrize("route_set", [0, 1])
+def test_fused_layer_workloads(name, route_set):
+    wl = workloads.WORKLOADS[name]
+    print(f"fused {name} set {route_set}", flush=True)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, route_set)
+    r = fused_vs_three_call(case, ids, w, f"{name}/{route_set}")
+    print(f"  max err frac {r[0]:.2e}, rel L2 {r[1]:.2e}", flush=True)
+
+
+REDUCED = [
+    ("f_h384_i256", dict(hidden=384, inter=256, experts=8, top_k=3), [1, 3, 16]),
+    ("f_h1152_i384", dict(hidden=1152, inter=384, experts=6, top_k=2), [1, 7]),
+    ("f_h256_i2304", dict(hidden=256, inter=2304, experts=4, top_k=2), [1, 5]),
+    ("f_h1024_i512_k16", dict(hidden=1024, inter=512, experts=64, top_k=16), [16]),
+]
+
+
+@pytest.mark.parametrize("name,over,Ms", REDUCED, ids=[r[0] for r in REDUCED])
+def test_fused_layer_reduced_shapes(name, over, Ms):
+    wl = workloads.with_shape(workloads.WORKLOADS["tiny_e4m3_m1"], name=name, M=max(Ms), **over)
+    case = get_case(wl)
+    for M in Ms:
+        ids, w, _ = workloads.make_routes(wl, 0, M=M)
+        print(f"fused {name} M={M} S={ids.size}", flush=True)
+        fused_vs_three_call(case, ids, w, f"{name} M={M}")
+
+
+def test_fused_crowded_expert_and_invalid_ids():
+    # 16 tokens, 12 of them on one expert (several weight passes), plus
+    # unfilled and out-of-range ids
+    wl = workloads.with_shape(workloads.WORKLOADS["tiny_e4m3_m1"], name="f_crowded",
+                              hidden=512, inter=256, experts=5, top_k=2, M=16)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 0)
+    ids[:12, 0] = 3
+    ids[ids[:, 1] == 3, 1] = 1
+    ids[2, 1] = -1
+    ids[5, 1] = wl.experts + 4
+    ids[7, 1] = -3
+    print("fused crowded/invalid", flush=True)
+    fused_vs_three_call(case, ids, w, "crowded")
+
+
+def test_fused_all_ids_invalid_gives_zero_rows():
+    wl = workloads.with_shape(workloads.WORKLOADS["tiny_e4m3_m1"], name="f_none", M=3)
+    case = get_case(wl)
+    ids = np.full((3, wl.top_k), -1, np.int32)
+    ids[1, 2] = wl.experts
+    w = np.ones(ids.shape, np.float32)
+    L = case.layer(max_M=3, mode=B.MOE_MODE_FUSED)
+    L.out.fill_(float("nan"))
+    out, _, tabs, _ = case.run(ids, w, layer=L)
+    assert np.all(out == 0.0)
+    assert int(tabs["num_active"][0]) == 0 and int(tabs["status"][0]) == 1
+
+
+def test_fused_back_to_back_calls_on_one_workspace():
+    # the epoch counters need no clearing: successive calls with different
+    # routes (and stale counter words in between) stay exact
+    wl = workloads.WORKLOADS["tiny_e4m3_m1"]
+    wl = workloads.with_shape(wl, name="f_epochs", M=4, experts=16, top_k=4)
+    case = get_case(wl)
+    L = case.layer(max_M=4, mode=B.MOE_MODE_FUSED)
+    L.ws.fill_(0xFF)                                  # garbage counters
+    for r in range(4):
+        ids, w, _ = workloads.make_routes(wl, r)
+        out_f, _, tabs, _ = case.run(ids, w, layer=L)
+        assert int(tabs["status"][0]) == 0
+        out_3, _, _, _ = case.run(ids, w, B.MOE_MODE_GEMV_A16)
+        assert np.array_equal(out_f.view(np.uint32), out_3.view(np.uint32)), r
+    # and the same call twice gives the same bits
+    again, _, _, _ = case.run(ids, w, layer=L)
+    assert np.array_equal(again.view(np.uint32), out_f.view(np.uint32))
