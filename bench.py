@@ -89,7 +89,77 @@ def algorithmic_bytes(wl, banks, ids):
     return len(used) * per_expert + io, len(used) * gu_per_expert + M * wl.hidden * 2, len(used)
 
 
-def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=False):
+def nearest_rank(v, q):
+    """q-th percentile of v by nearest rank (1-based rank ceil(q/100 * n))."""
+    import math
+    v = sorted(v)
+    return v[max(1, math.ceil(q / 100.0 * len(v))) - 1]
+
+
+def percentiles(us):
+    return {"mean": round(sum(us) / len(us), 3), "min": round(min(us), 3),
+            "p50": round(nearest_rank(us, 50), 3), "p90": round(nearest_rank(us, 90), 3),
+            "p99": round(nearest_rank(us, 99), 3)}
+
+
+def graph_replay(layer, x, ids_d, w_d, steps, hip):
+    """One HIP graph of len(ids_d) layers (one per route set), replayed until
+    at least `steps` layers ran.  Every replay's output is checked bit for bit
+    against the eager layer of the last route set, with eager work and a
+    synchronization between replays."""
+    import torch
+    R = len(ids_d)
+    want = layer(x, ids_d[R - 1], w_d[R - 1]).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(R):
+            layer(x, ids_d[i], w_d[i])
+    torch.cuda.synchronize()
+    ok = True
+    for _ in range(3):                       # checked replays, eager work in between
+        layer(x, ids_d[0], w_d[0])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ok &= bool(torch.equal(layer.out.view(torch.int32), want.view(torch.int32)))
+    reps = max(1, (steps + R - 1) // R)
+    sh = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.events(2)
+    torch.cuda.synchronize()
+    hip.record(e0, sh)
+    for _ in range(reps):
+        g.replay()
+    hip.record(e1, sh)
+    torch.cuda.synchronize()
+    us = hip.ms(e0, e1) * 1000.0 / (reps * R)
+    ok &= bool(torch.equal(layer.out.view(torch.int32), want.view(torch.int32)))
+    del g
+    return {"us_layer": round(us, 3), "layers": reps * R, "replays_match_eager": ok}
+
+
+def cold_layers(layer, x, ids_d, w_d, steps, hip):
+    """Each layer timed on its own after a 1 GiB device write (outside the
+    events) that evicts the last-level cache."""
+    import torch
+    R = len(ids_d)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    evs = [hip.events(2) for _ in range(steps)]
+    for i in range(steps):
+        flush.fill_(float(i))
+        hip.record(evs[i][0], sh)
+        layer(x, ids_d[i % R], w_d[i % R])
+        hip.record(evs[i][1], sh)
+    torch.cuda.synchronize()
+    us = [hip.ms(a, b) * 1000.0 for a, b in evs]
+    del flush
+    torch.cuda.empty_cache()
+    return percentiles(us)
+
+
+def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=False,
+            graph=True, cold=False):
     import numpy as np
     import torch
 
@@ -125,16 +195,28 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=F
     total_ms = hip.ms(e0, e1)
     us_layer = total_ms * 1000.0 / steps
 
+    # per-layer times: two events around each layer, nothing else in between
+    pev = [hip.events(2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        hip.record(pev[i][0], sh)
+        layer(x, ids_d[i % route_sets], w_d[i % route_sets])
+        hip.record(pev[i][1], sh)
+    torch.cuda.synchronize()
+    pct = percentiles([hip.ms(a, b) * 1000.0 for a, b in pev])
+
     # output must not drift across runs (deterministic kernels)
     again = layer(x, ids_d[0], w_d[0])
     torch.cuda.synchronize()
     stable = bool(torch.equal(again.view(torch.int32), ref.view(torch.int32)))
 
     stages = None
+    sums_stable = None
     if want_stages:
         nst = B.moe_set_stage_events(None, wl.fmt, wl.hidden, wl.inter, mode)
         per = nst + 3       # route start, ffn stage marks (nst+1), combine end
         evs = [hip.events(per) for _ in range(steps)]
+        sums = []
         torch.cuda.synchronize()
         for i in range(steps):
             ev = evs[i]
@@ -142,10 +224,14 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=F
             evs[i] = (ev, sub)
             hip.record(ev[0], sh)
             B.moe_set_stage_events(sub, wl.fmt, wl.hidden, wl.inter, mode)
-            layer(x, ids_d[i % route_sets], w_d[i % route_sets])
+            out = layer(x, ids_d[i % route_sets], w_d[i % route_sets])
             hip.record(ev[per - 1], sh)
+            # checksum of the output bits, outside the events
+            sums.append(out.view(torch.int32).to(torch.int64).sum())
         B.moe_set_stage_events(None, wl.fmt, wl.hidden, wl.inter, mode)
         torch.cuda.synchronize()
+        sums = [int(v) for v in sums]
+        sums_stable = all(sums[i] == sums[i % route_sets] for i in range(steps))
         if mode == B.MOE_MODE_GEMM_A8:
             names = ["route_pack", "act_quant_tiles", "gateup_gemm", "down_gemm", "combine"]
         elif mode == B.MOE_MODE_FUSED:
@@ -165,7 +251,13 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=F
     # dense-equivalent FLOPs of the valid slots: 2 (gate, up) + 1 (down) products of I*H
     flops = float(np.mean([6.0 * int(((s[0] >= 0) & (s[0] < wl.experts)).sum()) * wl.hidden * wl.inter
                            for s in sets]))
+    if fused:       # the one-launch layer refuses graph capture (a fresh epoch per call)
+        gr = {"unsupported": "moe_layer_fused takes a fresh epoch per call and refuses capture"}
+    else:
+        gr = graph_replay(layer, x, ids_d, w_d, steps, hip) if graph else None
+    cl = cold_layers(layer, x, ids_d, w_d, steps, hip) if cold else None
     return dict(name=wl.name, us_layer=us_layer, ms_total=total_ms, stable=stable, stages=stages,
+                percentiles=pct, checksums_stable=sums_stable, graph=gr, cold=cl,
                 alg_layer_bytes=alg_layer, alg_gateup_bytes=alg_gateup, unique_experts=uniq,
                 flops=flops, mode=mode, layer=layer, x=x, sets=sets)
 
@@ -259,6 +351,17 @@ def roofline(r):
             "alg_bytes_per_launch": round(r["alg_gateup_bytes"]), "avg_launch_us": round(us, 3)}
 
 
+def extra_rows(r):
+    """Per-layer percentiles, the output checksum check, HIP-graph replay and
+    the cold-cache row of one measured workload."""
+    out = {"layer_us_percentiles": r["percentiles"], "checksums_stable": r["checksums_stable"]}
+    if r["graph"] is not None:
+        out["graph"] = r["graph"]
+    if r["cold"] is not None:
+        out["cold_us_percentiles"] = r["cold"]
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -289,7 +392,7 @@ def main():
     banks = workloads.make_banks(wl, "cuda")
     torch.cuda.synchronize()
     print(f"# banks for {wl.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    r = measure(wl, banks, args.steps, args.warmup, args.route_sets, hip)
+    r = measure(wl, banks, args.steps, args.warmup, args.route_sets, hip, cold=wl.M <= 16)
     print(f"# {wl.name}: {r['us_layer']:.2f} us/layer, stages {r['stages']}", file=sys.stderr,
           flush=True)
 
@@ -317,18 +420,20 @@ def main():
         "output_stable": r["stable"],
         "roofline": roofline(r),
     }
+    line.update(extra_rows(r))
     if r["mode"] == 2:
         line["alg_TFLOPs"] = round(r["flops"] / (r["us_layer"] * 1e-6) / 1e12, 1)
 
     def fused_row(w2, b2):
-        rf = measure(w2, b2, args.steps, args.warmup, args.route_sets, hip, fused=True)
+        rf = measure(w2, b2, args.steps, args.warmup, args.route_sets, hip, fused=True,
+                     cold=w2.M <= 16)
         gf = rf["alg_layer_bytes"] / (rf["us_layer"] * 1e-6) / 1e9
         print(f"# {w2.name} fused: {rf['us_layer']:.2f} us/layer", file=sys.stderr, flush=True)
         return {"us_layer": round(rf["us_layer"], 3), "weight_read_GBps": round(gf, 1),
                 "hbm_frac": round(gf / HBM_PEAK_GBPS, 4),
                 "tokens_per_s": round(w2.M / (rf["us_layer"] * 1e-6), 1),
                 "stages_us": {k: round(v, 3) for k, v in rf["stages"].items()},
-                "output_stable": rf["stable"], "roofline": roofline(rf)}
+                "output_stable": rf["stable"], "roofline": roofline(rf), **extra_rows(rf)}
 
     def fused_ok(w2):
         return not args.no_fused and w2.fmt == 1 and w2.M * w2.top_k <= 256
@@ -340,7 +445,8 @@ def main():
         w2 = workloads.WORKLOADS[name]
         same = (w2.hidden, w2.inter, w2.experts, w2.fmt) == (wl.hidden, wl.inter, wl.experts, wl.fmt)
         b2 = banks if same else workloads.make_banks(w2, "cuda")
-        r2 = measure(w2, b2, max(20, args.steps // 2), args.warmup, args.route_sets, hip)
+        r2 = measure(w2, b2, max(20, args.steps // 2), args.warmup, args.route_sets, hip,
+                     cold=w2.M <= 16)
         g2 = r2["alg_layer_bytes"] / (r2["us_layer"] * 1e-6) / 1e9
         tf = r2["flops"] / (r2["us_layer"] * 1e-6) / 1e12
         also[name] = {"us_layer": round(r2["us_layer"], 3), "weight_read_GBps": round(g2, 1),
@@ -350,6 +456,7 @@ def main():
                       "stages_us": {k: round(v, 3) for k, v in r2["stages"].items()},
                       "output_stable": r2["stable"]}
         also[name]["roofline"] = roofline(r2)
+        also[name].update(extra_rows(r2))
         if fused_ok(w2):
             also[name]["fused"] = fused_row(w2, b2)
         if r2["mode"] == 2:

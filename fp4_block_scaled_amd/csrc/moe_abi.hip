@@ -370,6 +370,17 @@ moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const
     if (ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
 
+    hipStream_t s = (hipStream_t)stream;
+    // the epoch is a launch argument: a captured launch would replay with the
+    // same epoch, and flags left by an earlier replay could then end a wait
+    // before the data behind them is written
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t ce = hipStreamIsCapturing(s, &cap);
+    if (ce != hipSuccess) return hip_fail(ce, "moe_layer_fused: hipStreamIsCapturing");
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: cannot be captured into a HIP graph (each call needs a "
+                    "fresh epoch); capture moe_route_pack + moe_expert_ffn + moe_combine instead", fn);
+
     carve_route(ws, M, top_k, E, route);
     const int64_t S = (int64_t)M * top_k;
     char *scratch = (char *)ws + moe::route_region_bytes(S, E);
@@ -385,7 +396,6 @@ moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const
     GemvBankDev bg{gate->codes, gate->scales, gate->scale2};
     GemvBankDev bu{up->codes, up->scales, up->scale2};
     GemvBankDev bd{down->codes, down->scales, down->scale2};
-    hipStream_t s = (hipStream_t)stream;
     stage_mark(0, s);
     hipError_t e = launch_fused_decode_e4m3(bg, bu, bd, x_bf16, topk_ids, topk_weights, M, top_k, E,
                                             hidden, inter, limit, r, h, y_packed, out, flags, ep, s);

@@ -205,7 +205,10 @@ moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
  * and calls on one ws must be ordered on one stream.  The kernel assumes its
  * blocks can all be resident on the GPU at once (no other kernel holding the
  * CUs); a wait that does not end within about a second gives up and adds
- * 2^30 to route->status. */
+ * 2^30 to route->status.  Each call takes a fresh epoch on the host, so the
+ * call cannot be captured into a HIP graph: on a capturing stream it returns
+ * MOE_ERR_UNSUPPORTED and launches nothing (the three calls above can be
+ * captured). */
 moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
                              const uint16_t *x_bf16, const int32_t *topk_ids,
                              const float *topk_weights, int32_t M, int32_t top_k,
