@@ -70,6 +70,8 @@ def lib():
             P, P, i32, i32, i32, i32, f32, i32, P, i32, P, P, P, P]
         L.oracle_expert_slots.restype = None
         L.oracle_combine.argtypes = [P, P, P, i32, i32, i32, P]
+        L.oracle_router_topk.argtypes = [P, i32, i32, i32, i32, P, f32, i32, P, P]
+        L.oracle_router_topk.restype = i32
         L.oracle_combine.restype = None
         _lib = L
     return _lib
@@ -273,3 +275,33 @@ def moe_layer(gate: Bank, up: Bank, down: Bank, x_bf16: np.ndarray,
     res = expert_slots(gate, up, down, x_bf16, ids, limit, act_fp8)
     valid = ((ids >= 0) & (ids < E)).astype(np.int32).ravel()
     return combine(res["y"], w, valid), res["y"]
+
+
+# --------------------------------------------------------------------------
+# router
+# --------------------------------------------------------------------------
+
+ROUTER_SOFTMAX = 0
+ROUTER_SIGMOID = 1
+
+
+def router_topk(logits: np.ndarray, top_k: int, kind: int = ROUTER_SOFTMAX,
+                bias: Optional[np.ndarray] = None, routed_scale: float = 1.0,
+                renormalize: bool = True):
+    """(ids int32 [M, k], weights float32 [M, k]) of the softmax or sigmoid
+    top-k router on binary32 logits [M, E].
+
+    Pinned: a brute-force ranking of the keys in numpy, scipy's softmax and
+    logistic functions on the chosen experts, hand-worked rows where the
+    selection bias changes the choice, ties, and non-finite logits."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    M, E = logits.shape
+    ids = np.empty((M, top_k), np.int32)
+    w = np.empty((M, top_k), np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    rc = lib().oracle_router_topk(_ptr(logits), M, E, top_k, kind,
+                                  None if b is None else _ptr(b), float(routed_scale),
+                                  int(bool(renormalize)), _ptr(ids), _ptr(w))
+    if rc != 0:
+        raise ValueError("oracle_router_topk: bad arguments")
+    return ids, w

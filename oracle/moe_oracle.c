@@ -33,10 +33,16 @@
  *     "spark_model glm5next_mlp/forward.rs", fn w4a16_gemv);
  *   - per 1x128 group FP8 quantization of activations for the wide-M tier
  *     ("memra-engine src/dsv4_ep.rs", EpScratch xq/xs and the act_quant_fp8
- *     step of fn chain).
+ *     step of fn chain);
+ *   - the router before the layer: softmax, or sigmoid with a selection bias,
+ *     top-k per token, renormalized and scaled weights ("spark_model
+ *     glm5next_mlp/forward.rs", the router launch of fn forward_moe;
+ *     "memra-engine src/bin/ep_step_fp8_gate.rs", the full-layer gate's
+ *     sigmoid top-k router).
  * Readings of points the pages leave open are listed beside the function
  * that takes them.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -359,4 +365,102 @@ void oracle_combine(const double *y_by_slot, const float *w,
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router: the top-k experts of each token and their weights                 */
+/* ------------------------------------------------------------------------ */
+
+/* Two routers are defined.
+ *   kind 0, softmax (the routing of the benchmark workloads):
+ *     p[e] = exp(l[e] - m) / sum_e' exp(l[e'] - m),  m = max_e l[e];
+ *     the k experts with the largest p are chosen.  p is strictly increasing
+ *     in the logit, so the order is the order of the logits themselves.
+ *     Weights: renormalized, w[j] = exp(l[j] - l[0]) / sum_{i<k} exp(l[i] - l[0])
+ *     (this is p[j] / sum of the chosen p), else w[j] = p[j].
+ *   kind 1, sigmoid with a selection bias ("memra-engine
+ *     src/bin/ep_step_fp8_gate.rs", the full-layer gate's sigmoid top-k router
+ *     with router bias, router scale and route norm; "spark_model
+ *     glm5next_mlp/forward.rs", the router launch in fn forward_moe with its
+ *     bias, routed_scale and renormalize arguments):
+ *     s[e] = 1 / (1 + exp(-l[e])); the key is binary32(s[e]) + bias[e], one
+ *     binary32 addition; the k largest keys are chosen.  The bias only
+ *     selects: w[j] = s[j], renormalized by the sum of the chosen s if asked.
+ * Both: w[j] is then multiplied by routed_scale and rounded once to binary32.
+ * Readings where the pages are silent:
+ *   - ties in the key go to the lower expert id, and slot j holds rank j;
+ *   - a NaN logit counts as -FLT_MAX and an infinite one as +-FLT_MAX, so
+ *     every key and weight is finite;
+ *   - sums over the chosen experts run in rank order, the softmax
+ *     denominator over e ascending, all in double. */
+typedef struct {
+    float key;
+    int32_t id;
+} router_key_t;
+
+static int router_key_cmp(const void *pa, const void *pb)
+{
+    const router_key_t *a = pa, *b = pb;
+    if (a->key > b->key) return -1;
+    if (a->key < b->key) return 1;
+    return (a->id > b->id) - (a->id < b->id);
+}
+
+static double router_logit(float v)
+{
+    if (isnan(v)) return -(double)FLT_MAX;
+    if (v > FLT_MAX) return (double)FLT_MAX;
+    if (v < -FLT_MAX) return -(double)FLT_MAX;
+    return (double)v;
+}
+
+int oracle_router_topk(const float *logits, int32_t M, int32_t E, int32_t k,
+                       int32_t kind, const float *bias, float routed_scale,
+                       int32_t renormalize, int32_t *ids, float *w)
+{
+    if (M < 1 || k < 1 || k > E || (kind != 0 && kind != 1)) return -1;
+    double *l = malloc(sizeof(double) * (size_t)E);
+    double *s = malloc(sizeof(double) * (size_t)E);
+    router_key_t *keys = malloc(sizeof(router_key_t) * (size_t)E);
+    for (int64_t t = 0; t < M; ++t) {
+        for (int32_t e = 0; e < E; ++e) l[e] = router_logit(logits[t * E + e]);
+        if (kind == 0) {
+            double m = l[0];
+            for (int32_t e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+            double den = 0.0;
+            for (int32_t e = 0; e < E; ++e) den += exp(l[e] - m);
+            for (int32_t e = 0; e < E; ++e) {
+                s[e] = exp(l[e] - m) / den;
+                keys[e].key = (float)l[e];
+                keys[e].id = e;
+            }
+        } else {
+            for (int32_t e = 0; e < E; ++e) {
+                s[e] = 1.0 / (1.0 + exp(-l[e]));
+                float b = bias ? bias[e] : 0.0f;
+                volatile float sk = (float)s[e];      /* one rounding, then one addition */
+                keys[e].key = sk + b;
+                keys[e].id = e;
+            }
+        }
+        qsort(keys, (size_t)E, sizeof(router_key_t), router_key_cmp);
+        double sum = 0.0;
+        if (renormalize) {
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t e = keys[j].id;
+                sum += kind == 0 ? exp(l[e] - l[keys[0].id]) : s[e];
+            }
+        }
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = keys[j].id;
+            double v;
+            if (!renormalize) v = s[e];
+            else if (kind == 0) v = exp(l[e] - l[keys[0].id]) / sum;
+            else v = s[e] / sum;
+            ids[t * k + j] = e;
+            w[t * k + j] = (float)(v * (double)routed_scale);
+        }
+    }
+    free(l); free(s); free(keys);
+    return 0;
 }

@@ -223,8 +223,8 @@ def calibrate_rho(seed: int, M: int, E: int, k: int, shared: float = 0.30) -> fl
     return float(best)
 
 
-def make_routes(wl: Workload, route_set: int = 0, M: Optional[int] = None):
-    """(ids int32 [M, k], weights float32 [M, k], info dict)."""
+def make_logits(wl: Workload, route_set: int = 0, M: Optional[int] = None):
+    """(router logits float64 [M, E], info dict) of one route set."""
     M = wl.M if M is None else M
     seed = wl.seed * 100 + route_set
     rng = np.random.default_rng(seed)
@@ -240,6 +240,12 @@ def make_routes(wl: Workload, route_set: int = 0, M: Optional[int] = None):
         info["rho"] = rho
     else:
         raise ValueError(wl.route)
+    return logits, info
+
+
+def make_routes(wl: Workload, route_set: int = 0, M: Optional[int] = None):
+    """(ids int32 [M, k], weights float32 [M, k], info dict)."""
+    logits, info = make_logits(wl, route_set, M)
     ids, w = topk_softmax(logits, wl.top_k)
     info["unique_experts"] = int(len(np.unique(ids)))
     counts = np.bincount(ids.ravel(), minlength=wl.experts)
