@@ -391,6 +391,9 @@ void oracle_combine(const double *y_by_slot, const float *w,
  *   - ties in the key go to the lower expert id, and slot j holds rank j;
  *   - a NaN logit counts as -FLT_MAX and an infinite one as +-FLT_MAX, so
  *     every key and weight is finite;
+ *   - the sigmoid weights renormalize by the sum of the chosen s; where that
+ *     sum is 0 (every chosen s underflows, logits below about -745) the
+ *     weights are 0.  The softmax sum is at least 1;
  *   - sums over the chosen experts run in rank order, the softmax
  *     denominator over e ascending, all in double. */
 typedef struct {
@@ -456,7 +459,7 @@ int oracle_router_topk(const float *logits, int32_t M, int32_t E, int32_t k,
             double v;
             if (!renormalize) v = s[e];
             else if (kind == 0) v = exp(l[e] - l[keys[0].id]) / sum;
-            else v = s[e] / sum;
+            else v = sum > 0.0 ? s[e] / sum : 0.0;
             ids[t * k + j] = e;
             w[t * k + j] = (float)(v * (double)routed_scale);
         }

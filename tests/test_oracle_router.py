@@ -121,6 +121,11 @@ def test_non_finite_logits():
     assert w[0, 0] == np.float32(1.0) and np.all(w[0, 1:] == 0)
     ids, w = oracle.router_topk(l, 2, ROUTER_SIGMOID)
     assert ids.tolist() == [[2, 1]] and np.all(np.isfinite(w))
+    # every chosen sigmoid is 0: nothing to renormalize, the weights are 0
+    ids, w = oracle.router_topk(np.full((1, 4), nan, np.float32), 2, ROUTER_SIGMOID)
+    assert ids.tolist() == [[0, 1]] and np.all(w == 0)
+    ids, w = oracle.router_topk(np.full((1, 4), -1000.0, np.float32), 2, ROUTER_SIGMOID)
+    assert np.all(w == 0)
 
 
 def test_shift_invariance_of_the_softmax():
