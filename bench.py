@@ -351,6 +351,59 @@ def roofline(r):
             "alg_bytes_per_launch": round(r["alg_gateup_bytes"]), "avg_launch_us": round(us, 3)}
 
 
+def router_rows(wl, banks, steps, route_sets, hip, M=None):
+    """moe_router_topk (softmax, renormalized) alone on [M, E] logits, and, at
+    the workload's own M, router + the three layer calls with no host hop."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from fp4_block_scaled_amd import binding as B
+    from fp4_block_scaled_amd.layer import MoeLayer
+
+    M = wl.M if M is None else M
+    logits = [torch.from_numpy(workloads.make_logits(wl, r, M)[0].astype(np.float32)).cuda()
+              for r in range(route_sets)]
+    ids = torch.empty((M, wl.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, wl.top_k), dtype=torch.float32, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def router(i):
+        B.moe_router_topk(logits[i % route_sets], M, wl.experts, wl.top_k, B.MOE_ROUTER_SOFTMAX,
+                          None, 1.0, 1, ids, w)
+
+    for i in range(3):
+        router(i)
+    e0, e1 = hip.events(2)
+    torch.cuda.synchronize()
+    hip.record(e0, sh)
+    for i in range(steps):
+        router(i)
+    hip.record(e1, sh)
+    torch.cuda.synchronize()
+    out = {"rows": M, "experts": wl.experts, "top_k": wl.top_k,
+           "router_us": round(hip.ms(e0, e1) * 1000.0 / steps, 3)}
+    if M == wl.M:
+        cb = [B.Bank.from_device_bank(b) for b in banks]
+        layer = MoeLayer(*cb, wl.hidden, wl.inter, wl.top_k, wl.M, wl.limit)
+        x = workloads.make_x(wl, "cuda")
+        for i in range(3):
+            router(i)
+            layer(x, ids, w)
+        torch.cuda.synchronize()
+        hip.record(e0, sh)
+        for i in range(steps):
+            router(i)
+            layer(x, ids, w)
+        hip.record(e1, sh)
+        torch.cuda.synchronize()
+        out["router_plus_layer_us"] = round(hip.ms(e0, e1) * 1000.0 / steps, 3)
+        del layer
+    del logits
+    torch.cuda.empty_cache()
+    return out
+
+
 def extra_rows(r):
     """Per-layer percentiles, the output checksum check, HIP-graph replay and
     the cold-cache row of one measured workload."""
@@ -440,6 +493,7 @@ def main():
 
     if fused_ok(wl):
         line["fused"] = fused_row(wl, banks)
+    line["router"] = router_rows(wl, banks, args.steps, args.route_sets, hip)
     also = {}
     for name in [a for a in args.also.split(",") if a]:
         w2 = workloads.WORKLOADS[name]
@@ -459,6 +513,9 @@ def main():
         also[name].update(extra_rows(r2))
         if fused_ok(w2):
             also[name]["fused"] = fused_row(w2, b2)
+        if w2.M > 16:
+            also[name]["router"] = router_rows(w2, b2, max(20, args.steps // 2), args.route_sets,
+                                               hip)
         if r2["mode"] == 2:
             also[name].update({"tier": "fp8_mfma_grouped_gemm", "alg_TFLOPs": round(tf, 1),
                                "mfma_frac_fp8": round(tf / FP8_PEAK_TFLOPS, 4)})

@@ -30,12 +30,15 @@ MOE_MODE_GEMV_A16 = 1
 MOE_MODE_GEMM_A8 = 2
 MOE_MODE_FUSED = 3
 
+MOE_ROUTER_SOFTMAX = 0
+MOE_ROUTER_SIGMOID = 1
+
 MOE_GEMV_MAX_M = 16
 MOE_MAX_EXPERTS = 512
 MOE_MAX_DIM = 16384
 MOE_FUSED_MAX_SLOTS = 256
 
-EXPORTS = ("moe_workspace_bytes", "moe_resolve_mode", "moe_route_pack",
+EXPORTS = ("moe_workspace_bytes", "moe_resolve_mode", "moe_router_topk", "moe_route_pack",
            "moe_expert_ffn", "moe_layer_fused", "moe_combine", "moe_set_stage_events",
            "moe_last_error")
 
@@ -70,6 +73,8 @@ def _load():
     L.moe_workspace_bytes.restype = sz
     L.moe_resolve_mode.argtypes = [i32, i32, i32]
     L.moe_resolve_mode.restype = i32
+    L.moe_router_topk.argtypes = [P, i32, i32, i32, i32, P, C.c_float, i32, P, P, P]
+    L.moe_router_topk.restype = i32
     L.moe_route_pack.argtypes = [P, i32, i32, i32, P, sz, C.POINTER(moe_route_t), P]
     L.moe_route_pack.restype = i32
     L.moe_expert_ffn.argtypes = [C.POINTER(moe_bank_t)] * 3 + [
@@ -135,6 +140,13 @@ class Bank:
     @classmethod
     def from_device_bank(cls, b):
         return cls(b.fmt, b.codes, b.scales, b.scale2)
+
+
+def moe_router_topk(logits, M, num_experts, top_k, kind, bias, routed_scale, renormalize,
+                    topk_ids, topk_weights, stream=None) -> None:
+    _check(lib.moe_router_topk(_ptr(logits), M, num_experts, top_k, kind, _ptr(bias),
+                               float(routed_scale), int(renormalize), _ptr(topk_ids),
+                               _ptr(topk_weights), _stream(stream)))
 
 
 def moe_route_pack(topk_ids, M, top_k, num_experts, ws, ws_bytes=None, stream=None) -> moe_route_t:

@@ -404,6 +404,30 @@ moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const
     return MOE_OK;
 }
 
+moe_status_t moe_router_topk(const float *logits, int32_t M, int32_t num_experts, int32_t top_k,
+                             int32_t kind, const float *bias, float routed_scale,
+                             int32_t renormalize, int32_t *topk_ids, float *topk_weights,
+                             void *stream)
+{
+    static const char *fn = "moe_router_topk";
+    if (!logits || !topk_ids || !topk_weights) return fail(MOE_ERR_ARG, "%s: null pointer", fn);
+    if (!sizes_ok(M, top_k, num_experts))
+        return fail(MOE_ERR_SHAPE, "%s: need M >= 1, 1 <= top_k <= num_experts <= %d (M=%d top_k=%d E=%d)",
+                    fn, MOE_MAX_EXPERTS, M, top_k, num_experts);
+    if (kind != MOE_ROUTER_SOFTMAX && kind != MOE_ROUTER_SIGMOID)
+        return fail(MOE_ERR_ARG, "%s: unknown router kind %d", fn, kind);
+    if (kind == MOE_ROUTER_SOFTMAX && bias)
+        return fail(MOE_ERR_ARG, "%s: the softmax router takes no bias", fn);
+    if (!(routed_scale > 0.0f) || !(routed_scale <= 3.4028234663852886e38f))
+        return fail(MOE_ERR_ARG, "%s: routed_scale must be finite and > 0", fn);
+    if (renormalize != 0 && renormalize != 1)
+        return fail(MOE_ERR_ARG, "%s: renormalize must be 0 or 1", fn);
+    hipError_t e = launch_router_topk(logits, M, num_experts, top_k, kind, bias, routed_scale,
+                                      renormalize, topk_ids, topk_weights, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_router_topk: launch");
+    return MOE_OK;
+}
+
 moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
                          const float *topk_weights, int32_t hidden, float *out, void *stream)
 {

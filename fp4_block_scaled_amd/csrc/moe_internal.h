@@ -98,6 +98,11 @@ struct MoeRouteDev {
     int32_t *offsets, *sorted_slot, *sorted_token, *token_to_perm, *active, *num_active, *status;
 };
 
+// Router: one wave per token row (router.hip).
+hipError_t launch_router_topk(const float *logits, int32_t M, int32_t E, int32_t k, int32_t kind,
+                              const float *bias, float routed_scale, int32_t renormalize,
+                              int32_t *ids, float *w, hipStream_t st);
+
 hipError_t launch_route_pack(const int32_t *ids, int32_t M, int32_t k, int32_t E,
                              const MoeRouteDev &r, hipStream_t st);
 

@@ -81,6 +81,16 @@ enum {
     MOE_MODE_FUSED = 3
 };
 
+/* Routers of moe_router_topk. */
+enum {
+    /* p = softmax(logits) over the experts; the top_k largest p, which are
+     * the top_k largest logits. */
+    MOE_ROUTER_SOFTMAX = 0,
+    /* s = sigmoid(logits); the top_k largest binary32(s) + bias (one binary32
+     * addition); the bias only selects, the weights come from s. */
+    MOE_ROUTER_SIGMOID = 1
+};
+
 #define MOE_GEMV_MAX_M 16
 /* Largest M * top_k moe_layer_fused takes. */
 #define MOE_FUSED_MAX_SLOTS 256
@@ -144,6 +154,38 @@ typedef struct {
 size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts,
                            int32_t hidden, int32_t inter, int32_t fmt,
                            int32_t mode);
+
+/* Router: the top_k experts of every token row and their weights, all rows
+ * in one launch ("spark_model glm5next_mlp/forward.rs", fn forward_moe: one
+ * top-k launch for every row, with router bias, routed_scale, renormalize and
+ * one expert group; "memra-engine src/bin/ep_step_fp8_gate.rs", the full-layer
+ * gate's sigmoid top-k router with router bias, router scale and route norm).
+ * Its outputs feed moe_route_pack directly, with no host round trip.
+ *   logits        float [M][num_experts], row-major (device)
+ *   bias          float [num_experts] (device) for MOE_ROUTER_SIGMOID, or NULL
+ *                 (no bias); must be NULL for MOE_ROUTER_SOFTMAX; its values
+ *                 must be finite (a NaN bias leaves the order undefined)
+ *   topk_ids      int32 [M][top_k] out (device): slot j holds rank j
+ *   topk_weights  float [M][top_k] out (device)
+ * Definition, per row (l = the row's logits; a NaN counts as -FLT_MAX and
+ * +-inf as +-FLT_MAX):
+ *   SOFTMAX: choose the top_k largest l; renormalize != 0:
+ *            w[j] = exp(l[j] - l[0]) / sum_{i<top_k} exp(l[i] - l[0]), which is
+ *            p[j] / sum of the chosen p; renormalize == 0: w[j] = p[j] (the
+ *            full softmax, denominator summed over experts in ascending order).
+ *   SIGMOID: s = 1 / (1 + exp(-l)); choose the top_k largest binary32(s) + bias;
+ *            w[j] = s[j], divided by sum_{i<top_k} s[i] if renormalize != 0
+ *            (all 0 if that sum is 0: every chosen s underflowed).
+ *   Equal keys go to the lower expert id.  w[j] is then multiplied by
+ *   routed_scale and rounded once to binary32; everything before that is
+ *   double, and sums over the chosen experts run in rank order.
+ * Rules: M >= 1, 1 <= top_k <= num_experts <= MOE_MAX_EXPERTS, routed_scale
+ * finite and > 0, renormalize 0 or 1; else MOE_ERR_SHAPE / MOE_ERR_ARG, with
+ * nothing launched.  Allocates nothing; capturable in a HIP graph. */
+moe_status_t moe_router_topk(const float *logits, int32_t M, int32_t num_experts, int32_t top_k,
+                             int32_t kind, const float *bias, float routed_scale,
+                             int32_t renormalize, int32_t *topk_ids, float *topk_weights,
+                             void *stream);
 
 /* The tier moe_expert_ffn runs for `requested` at M tokens (AUTO resolves by
  * M).  Needs no GPU. */

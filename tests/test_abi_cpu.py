@@ -223,3 +223,28 @@ def test_fused_workspace_and_error_contract_on_host():
     rr = _route(B, ws)
     assert _ffn(B, g, u, d, rr, ws, mode=B.MOE_MODE_FUSED) == B.MOE_ERR_ARG
     assert "moe_layer_fused" in B.moe_last_error()
+
+
+def test_router_error_contract_on_host():
+    from fp4_block_scaled_amd import binding as B
+    L = B.lib
+    FAKE = 0x7F0000000000
+
+    def router(logits=FAKE, M=4, E=16, k=4, kind=B.MOE_ROUTER_SOFTMAX, bias=None, scale=1.0,
+               renorm=1, ids=FAKE + 0x1000, w=FAKE + 0x2000):
+        return L.moe_router_topk(logits, M, E, k, kind, bias, scale, renorm, ids, w, None)
+
+    assert router(logits=None) == B.MOE_ERR_ARG
+    assert router(ids=None) == B.MOE_ERR_ARG
+    assert router(w=None) == B.MOE_ERR_ARG
+    assert router(M=0) == B.MOE_ERR_SHAPE
+    assert router(k=0) == B.MOE_ERR_SHAPE
+    assert router(k=17) == B.MOE_ERR_SHAPE
+    assert router(E=B.MOE_MAX_EXPERTS + 1, k=2) == B.MOE_ERR_SHAPE
+    assert router(kind=2) == B.MOE_ERR_ARG
+    assert router(bias=FAKE) == B.MOE_ERR_ARG              # softmax takes no bias
+    assert "bias" in B.moe_last_error()
+    assert router(scale=0.0) == B.MOE_ERR_ARG
+    assert router(scale=float("inf")) == B.MOE_ERR_ARG
+    assert router(scale=float("nan")) == B.MOE_ERR_ARG
+    assert router(renorm=2) == B.MOE_ERR_ARG
