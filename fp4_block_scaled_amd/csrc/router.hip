@@ -66,13 +66,15 @@ __device__ __forceinline__ void wave_lds_sync()
 }
 
 // Per wave in dynamic LDS, k entries each: the chosen experts in id order
-// (key, id, value), then the ids and values in rank order.
+// (key, id, value), then the ids and values in rank order; for the softmax
+// without renormalization also exp(l - m) of every expert.
 struct RouterLds {
     uint32_t *key;
     int32_t *id;
     double *val;
     int32_t *rid;
     double *rval;
+    double *all;
 };
 
 __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(RouterArgs a)
@@ -91,7 +93,9 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(RouterArgs 
         L.key = reinterpret_cast<uint32_t *>(base + 2 * k);
         L.id = reinterpret_cast<int32_t *>(L.key + k);
         L.rid = reinterpret_cast<int32_t *>(dyn + (size_t)kRowsPerBlock * 3 * k) + wave * k;
+        L.all = dyn + (size_t)kRowsPerBlock * 3 * k + ((size_t)kRowsPerBlock * k + 1) / 2 + (size_t)wave * E;
     }
+    const bool full_softmax = a.kind == 0 && !a.renorm;
 
     float l[kPerLane];                               // canonical logits
     double s[kPerLane];                              // sigmoid, or exp(l - m) for the softmax
@@ -112,10 +116,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(RouterArgs 
     }
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
+        s[q] = 0.0;
+        key[q] = 0;
+        if (64 * q >= E) continue;                   // uniform: no expert in this slot
         const int e = lane + 64 * q;
         float kf;
         if (a.kind == 0) {
-            s[q] = exp((double)l[q] - (double)m);
+            if (full_softmax) s[q] = exp((double)l[q] - (double)m);
             kf = l[q];
         } else {
             s[q] = 1.0 / (1.0 + exp(-(double)l[q]));
@@ -125,7 +132,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(RouterArgs 
     }
 
     // T = the k-th largest key: the largest value with at least k keys >= it,
-    // found bit by bit from the top with ballots
+    // found bit by bit from the top with ballots.  Once exactly k keys are >= T
+    // the choice is made (it is those k) and the remaining bits change nothing.
     uint32_t T = 0;
     for (int b = 31; b >= 0; --b) {
         const uint32_t cand = T | (1u << b);
@@ -133,7 +141,10 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(RouterArgs 
 #pragma unroll
         for (int q = 0; q < kPerLane; ++q)
             if (64 * q < E) cnt += __popcll(__ballot(ok[q] && key[q] >= cand));
-        if (cnt >= k) T = cand;
+        if (cnt >= k) {
+            T = cand;
+            if (cnt == k) break;
+        }
     }
     // chosen: every key above T, then keys equal to T by ascending id; each
     // chosen entry gets its place in id order
@@ -177,13 +188,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(RouterArgs 
 
     // softmax without renormalization: the denominator over every expert, e ascending
     double den = 1.0;
-    if (a.kind == 0 && !a.renorm) {
-        den = 0.0;
+    if (full_softmax) {
 #pragma unroll
-        for (int q = 0; q < kPerLane; ++q) {
-            const int n = min(64, E - 64 * q);
-            for (int src = 0; src < n; ++src) den += __shfl(s[q], src, 64);
-        }
+        for (int q = 0; q < kPerLane; ++q)
+            if (ok[q]) L.all[lane + 64 * q] = s[q];
+        wave_lds_sync();
+        den = 0.0;
+        for (int e = 0; e < E; ++e) den += L.all[e];
     }
     // raw value per rank, then the chosen sum in rank order
     const double l0 = L.rval[0];
@@ -215,7 +226,10 @@ hipError_t launch_router_topk(const float *logits, int32_t M, int32_t E, int32_t
     RouterArgs a{logits, bias, ids, w, M, E, k, kind, renormalize ? 1 : 0, routed_scale};
     const int grid = (M + kRowsPerBlock - 1) / kRowsPerBlock;
     // per wave: val, rval (double) and key, id (32-bit) for k entries, then rid
-    const size_t lds = (size_t)kRowsPerBlock * k * (3 * sizeof(double) + sizeof(int32_t));
+    // (rounded up to whole doubles), then E doubles for the full softmax
+    size_t lds = (size_t)kRowsPerBlock * 3 * k * sizeof(double) +
+                 (((size_t)kRowsPerBlock * k + 1) / 2) * sizeof(double);
+    if (kind == 0 && !renormalize) lds += (size_t)kRowsPerBlock * E * sizeof(double);
     hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(kRouterThreads), lds, st, a);
     return hipGetLastError();
 }
