@@ -513,13 +513,16 @@ struct FusedWait {
     }
 };
 
-// The route of the S slots in LDS, for any block; block 0 writes the tables.
-__device__ void fused_route(const FusedArgs &a, FusedRoute &R)
+// The route of the S slots in LDS, for any block.  id_in is this thread's
+// slot id (slot tid; -1 past S), loaded by the caller; the barriers inside are
+// LDS-only, so global loads the caller has in flight stay in flight.
+static_assert(kFusedMaxSlots == kThreads, "one slot per thread");
+__device__ void fused_route(const FusedArgs &a, FusedRoute &R, int id_in)
 {
     const int tid = threadIdx.x, S = a.M * a.k, E = a.E;
     if (tid == 0) { R.na = 0; R.nvalid = 0; R.ninvalid = 0; R.flag = 0; }
-    for (int s = tid; s < kFusedMaxSlots; s += kThreads) R.ids[s] = s < S ? a.ids[s] : -1;
-    __syncthreads();
+    R.ids[tid] = id_in;
+    moe::lds_barrier();
     const int id = tid < S ? R.ids[tid] : -1;
     const bool valid = tid < S && id >= 0 && id < E;
     int less = 0, before = 0, total = 0;
@@ -533,7 +536,7 @@ __device__ void fused_route(const FusedArgs &a, FusedRoute &R)
     R.first[tid] = valid && before == 0;
     if (tid < S && !valid && id != -1) atomicAdd(&R.ninvalid, 1);
     if (valid) atomicAdd(&R.nvalid, 1);
-    __syncthreads();
+    moe::lds_barrier();
     int rank = 0;                                    // distinct valid experts below id
     for (int q = 0; q < S; ++q) rank += R.first[q] && R.ids[q] < id;
     const int p = less + before;
@@ -543,24 +546,38 @@ __device__ void fused_route(const FusedArgs &a, FusedRoute &R)
         R.ae[rank] = id; R.ap0[rank] = less; R.acnt[rank] = total;
         atomicAdd(&R.na, 1);
     }
-    __syncthreads();
-    if (blockIdx.x == 0) {                           // the route tables, as route_pack writes them
-        for (int e = tid; e <= E; e += kThreads) {
-            int c = 0;
-            for (int q = 0; q < S; ++q) {
-                const int v = R.ids[q];
-                c += v >= 0 && v < e;
-            }
-            a.r.offsets[e] = c;
+    moe::lds_barrier();
+}
+
+// Block 0 writes the other route tables, as route_pack writes them.  Nothing
+// in the launch reads them, so this runs at the end, off the critical path.
+__device__ void fused_route_tables(const FusedArgs &a, const FusedRoute &R)
+{
+    if (blockIdx.x != 0) return;
+    const int tid = threadIdx.x, S = a.M * a.k, E = a.E;
+    for (int e = tid; e <= E; e += kThreads) {
+        int c = 0;
+        for (int q = 0; q < S; ++q) {
+            const int v = R.ids[q];
+            c += v >= 0 && v < e;
         }
-        if (tid < S) {
-            a.r.token_to_perm[tid] = R.t2p[tid];
-            if (valid) { a.r.sorted_slot[p] = tid; a.r.sorted_token[p] = tid / a.k; }
-        }
-        const int A = S < E ? S : E;
-        for (int i = tid; i < A; i += kThreads) a.r.active[i] = i < R.na ? R.ae[i] : -1;
-        if (tid == 0) { *a.r.num_active = R.na; *a.r.status = R.ninvalid; }
+        a.r.offsets[e] = c;
     }
+    if (tid < S) {
+        const int p = R.t2p[tid];
+        a.r.token_to_perm[tid] = p;
+        if (p >= 0) { a.r.sorted_slot[p] = tid; a.r.sorted_token[p] = tid / a.k; }
+    }
+    const int A = S < E ? S : E;
+    for (int i = tid; i < A; i += kThreads) a.r.active[i] = i < R.na ? R.ae[i] : -1;
+    if (tid == 0) *a.r.num_active = R.na;
+}
+
+// Block 0 sets the route status right after the route: a wait that times out
+// later adds its flag to it.
+__device__ __forceinline__ void fused_route_status(const FusedArgs &a, const FusedRoute &R)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.r.status = R.ninvalid;
 }
 
 // GCH/GNCH and DCH/DNCH: the chunking of the gate/up and down items (NCH > 0
@@ -572,7 +589,8 @@ __global__ __launch_bounds__(kThreads, 4) void moe_fused_decode_e4m3_kernel(Fuse
     __shared__ FusedRoute R;
     __shared__ float ush[GST][16];
     const int tid = threadIdx.x;
-    fused_route(a, R);
+    fused_route(a, R, tid < a.M * a.k ? a.ids[tid] : -1);
+    fused_route_status(a, R);
     const int na = moe::uniform(R.na);
     const int H = a.dn.H, I = a.gu.I;
     if (na == 0) {                                   // no valid slot: every output row is zero
@@ -624,6 +642,166 @@ __global__ __launch_bounds__(kThreads, 4) void moe_fused_decode_e4m3_kernel(Fuse
             a.out[(size_t)t * H + m] = acc;
         }
     }
+    fused_route_tables(a, R);
+    __syncthreads();
+    if (tid == 0 && R.flag) atomicAdd(a.r.status, (int)kFusedTimeoutFlag);
+}
+
+// ---------------------------------------------------------------------------
+// fused decode layer for one token (M == 1)
+// ---------------------------------------------------------------------------
+// The same phases with gate/up items of 2 h rows: wave w streams row
+// 2r + (w & 1) of the gate (w < 2) or up (w >= 2) bank of one expert over the
+// whole of K, 64 lanes x 16 bytes per load (1 KB, 8 K segments).  Every block
+// walks the experts in order (block b takes rows 2b, 2b+1, then 2(b+grid), ...
+// of expert 0, then of expert 1, ...), so the experts' h are completed one
+// after another rather than all at the end; the down items (32 rows of one
+// expert) run expert-major, so those of the first experts overlap the gate/up
+// of the last.  The token's x row sits in LDS for the whole gate/up phase;
+// each item's weights are in flight while the previous item is multiplied.
+// Gate/up flags are per item ([A][inter/2]).  Products are summed per lane
+// over its K segments, then over the 64 lanes, so g and u agree with the
+// three-call path to rounding, not bit for bit.
+template <int NJ>
+__device__ __forceinline__ void thin_issue(const FusedArgs &a, const FusedRoute &R, bool is_up,
+                                           int wave, int lane, int ai, int r, uint4 (&w)[NJ],
+                                           float &sc)
+{
+    const int H = a.gu.H, I = a.gu.I;
+    const int e = moe::uniform(R.ae[ai]);
+    const int row = 2 * r + (wave & 1);
+    const uint8_t *rp = moe::uniform_ptr((is_up ? a.gu.ucodes : a.gu.gcodes) + ((size_t)e * I + row) * H);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) w[j] = load16(rp + j * 1024 + lane * 16);
+    const int nseg = H >> 7;
+    const float *sp = (is_up ? a.gu.uscales : a.gu.gscales) + ((size_t)e * (I >> 7) + (row >> 7)) * nseg;
+    sc = lane < nseg ? sp[lane] : 0.0f;
+}
+
+// one row's sum over K, every lane of the wave ends with it
+template <int NJ>
+__device__ __forceinline__ float thin_row(const uint4 (&w)[NJ], float sc, const uint4 *xl, int lane)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const float s = __shfl(sc, j * 8 + (lane >> 3), 64);
+        bf16x2 wb[8];
+        e4m3x4_to_bf16(w[j].x, wb[0], wb[1]);
+        e4m3x4_to_bf16(w[j].y, wb[2], wb[3]);
+        e4m3x4_to_bf16(w[j].z, wb[4], wb[5]);
+        e4m3x4_to_bf16(w[j].w, wb[6], wb[7]);
+        const uint4 xa = xl[j * 128 + lane * 2];
+        const uint4 xb = xl[j * 128 + lane * 2 + 1];
+        float d = dot2(wb[0], xa.x, 0.0f);
+        d = dot2(wb[1], xa.y, d);
+        d = dot2(wb[2], xa.z, d);
+        d = dot2(wb[3], xa.w, d);
+        d = dot2(wb[4], xb.x, d);
+        d = dot2(wb[5], xb.y, d);
+        d = dot2(wb[6], xb.z, d);
+        d = dot2(wb[7], xb.w, d);
+        acc = fmaf(d, s, acc);
+    }
+    acc = moe::sum8_lanes(acc);
+    acc += __shfl_xor(acc, 8, 64);
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    return acc;
+}
+
+template <int NJ, int DCH, int DNCH, int DST>
+__global__ __launch_bounds__(kThreads, 4) void moe_fused_decode1_e4m3_kernel(FusedArgs a)
+{
+    extern __shared__ uint4 dyn[];                   // x row (gate/up), then h tile (down)
+    __shared__ FusedRoute R;
+    __shared__ float ush[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = moe::uniform(tid >> 6);
+    const int H = a.dn.H, I = a.gu.I;
+    const int id_in = tid < a.k ? a.ids[tid] : -1;
+    fused_route(a, R, id_in);
+    fused_route_status(a, R);
+    const int na = moe::uniform(R.na);
+    if (na == 0) {                                   // no valid slot: the output row is zero
+        for (int q = blockIdx.x * kThreads + tid; q < H; q += gridDim.x * kThreads) a.out[q] = 0.0f;
+    }
+
+    // gate/up + SwiGLU items, expert by expert
+    const int nr = I >> 1;
+    const bool is_up = wave >= 2;
+    int ai = 0, r = blockIdx.x;
+    bool have = na > 0 && r < nr;
+    int pai = -1, pr = 0;                            // item whose h waits for its flag
+    uint4 w0[NJ], w1[NJ];
+    float sc0 = 0.0f, sc1 = 0.0f;
+    if (have) thin_issue<NJ>(a, R, is_up, wave, lane, ai, r, w0, sc0);
+    for (int f = tid; f < (H >> 3); f += kThreads)
+        dyn[f] = *reinterpret_cast<const uint4 *>(a.gu.x + (size_t)f * 8);
+    auto step = [&](uint4 (&wc)[NJ], float &scc, uint4 (&wn)[NJ], float &scn) {
+        moe::wait_vm0();                             // this item's weights, the last h stores
+        moe::lds_barrier();
+        if (tid == 0 && pai >= 0) publish(a.flag_gu + (size_t)pai * nr + pr, a.epoch);
+        int ai2 = ai, r2 = r + (int)gridDim.x;
+        if (r2 >= nr) { r2 = blockIdx.x; ++ai2; }
+        const bool have2 = ai2 < na;
+        if (have2) thin_issue<NJ>(a, R, is_up, wave, lane, ai2, r2, wn, scn);
+        const float v = thin_row<NJ>(wc, scc, dyn, lane);
+        if (is_up && lane == 0) ush[wave - 2] = v;
+        moe::lds_barrier();
+        if (!is_up && lane == 0) {
+            const float hv = swiglu_clamp(v, ush[wave], a.gu.limit);
+            const int p0 = R.ap0[ai], ne = R.acnt[ai];
+            const int row = 2 * r + wave;
+            for (int j = 0; j < ne; ++j) moe::store_dev(a.gu.h + (size_t)(p0 + j) * I + row, hv);
+        }
+        pai = ai; pr = r; ai = ai2; r = r2; have = have2;
+    };
+    if (have) {
+        for (;;) {
+            step(w0, sc0, w1, sc1);
+            if (!have) break;
+            step(w1, sc1, w0, sc0);
+            if (!have) break;
+        }
+        moe::wait_vm0();
+        moe::lds_barrier();
+        if (tid == 0) publish(a.flag_gu + (size_t)pai * nr + pr, a.epoch);
+    } else {
+        moe::lds_barrier();                          // x is in LDS before the down items
+    }
+
+    // down items, expert-major
+    const int ntd = H / 32, nd = na * ntd;
+    for (int d = blockIdx.x; d < nd; d += gridDim.x) {
+        const int dai = d / ntd, tile = d - dai * ntd;
+        const int e = moe::uniform(R.ae[dai]), p0 = moe::uniform(R.ap0[dai]);
+        const int ne = moe::uniform(R.acnt[dai]);
+        const FusedWait wait_h{a.flag_gu + (size_t)dai * nr, nr, a.epoch, &R.flag};
+        down_e4m3_item<DCH, DNCH, DST, true>(a.dn, e, tile, p0, ne, reinterpret_cast<float4 *>(dyn),
+                                             wait_h);
+        moe::wait_vm0();                             // this wave's y stores are written
+        __syncthreads();
+        uint32_t *fl = a.flag_dn + (size_t)tile * a.A;
+        if (dai + 1 < na) {
+            if (tid == 0) publish(fl + dai, a.epoch);
+            continue;
+        }
+        // the tile's last expert: wait for the others' y rows, then combine
+        const FusedWait wait_y{fl, na - 1, a.epoch, &R.flag};
+        wait_y();
+        for (int q = tid; q < 32; q += kThreads) {
+            const int m = tile * 32 + q;
+            float acc = 0.0f;
+            for (int j = 0; j < a.k; ++j) {
+                const int pr2 = R.t2p[j];
+                if (pr2 < 0) continue;
+                acc = __fadd_rn(acc, __fmul_rn(a.w[j], moe::load_dev(a.dn.y + (size_t)pr2 * H + m)));
+            }
+            a.out[m] = acc;
+        }
+    }
+    fused_route_tables(a, R);
     __syncthreads();
     if (tid == 0 && R.flag) atomicAdd(a.r.status, (int)kFusedTimeoutFlag);
 }
@@ -754,17 +932,16 @@ hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const 
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int GCH, int GNCH, int GST, int DCH, int DNCH, int DST>
-hipError_t fused_launch(const FusedArgs &a, size_t lds, hipStream_t st)
+// One block per slot the occupancy allows: every block must be resident for
+// the waits to end.  The occupancy and CU count are kept per kernel.
+template <auto Kern>
+hipError_t resident_launch(const FusedArgs &a, size_t lds, hipStream_t st)
 {
-    auto kern = moe_fused_decode_e4m3_kernel<GCH, GNCH, GST, DCH, DNCH, DST>;
-    // one block per slot the occupancy allows: every block must be resident
-    // for the waits to end
     static int per_cu = -1;
     static size_t per_cu_lds = 0;
     static int n_cu = 0;
     if (per_cu < 0 || per_cu_lds != lds) {
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)kern, kThreads, lds);
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)Kern, kThreads, lds);
         if (e != hipSuccess) return e;
         per_cu_lds = lds;
     }
@@ -775,8 +952,14 @@ hipError_t fused_launch(const FusedArgs &a, size_t lds, hipStream_t st)
         if (e != hipSuccess) return e;
     }
     if (per_cu < 1) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(per_cu * n_cu)), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL(Kern, dim3((unsigned)(per_cu * n_cu)), dim3(kThreads), lds, st, a);
     return hipGetLastError();
+}
+
+template <int GCH, int GNCH, int GST, int DCH, int DNCH, int DST>
+hipError_t fused_launch(const FusedArgs &a, size_t lds, hipStream_t st)
+{
+    return resident_launch<moe_fused_decode_e4m3_kernel<GCH, GNCH, GST, DCH, DNCH, DST>>(a, lds, st);
 }
 
 // Unrolled chunking for the pages' decode shape (hidden 7168 = 7 chunks of
@@ -786,6 +969,16 @@ hipError_t fused_dispatch(const FusedArgs &a, size_t lds, hipStream_t st)
 {
     if (a.gu.H == 7168 && a.gu.I == 2048) return fused_launch<8, 7, GST, 4, 4, DST>(a, lds, st);
     return fused_launch<1, 0, GST, 1, 0, DST>(a, lds, st);
+}
+
+// One token: 2-row gate/up items (H a multiple of 1024), unrolled down items
+// for the pages' decode shape.
+template <int NJ>
+hipError_t fused1_dispatch(const FusedArgs &a, size_t lds, hipStream_t st)
+{
+    if (a.gu.H == 7168 && a.gu.I == 2048)
+        return resident_launch<moe_fused_decode1_e4m3_kernel<NJ, 4, 4, 1>>(a, lds, st);
+    return resident_launch<moe_fused_decode1_e4m3_kernel<NJ, 1, 0, 1>>(a, lds, st);
 }
 
 }  // namespace
@@ -810,10 +1003,22 @@ hipError_t launch_fused_decode_e4m3(const GemvBankDev &gate, const GemvBankDev &
     a.ids = ids; a.w = w; a.M = M; a.k = k; a.E = E; a.epoch = epoch;
     a.A = M * k < E ? M * k : E;
     a.flag_gu = (uint32_t *)flags;
-    a.flag_dn = a.flag_gu + (size_t)a.A * (inter / 16);
+    a.flag_dn = a.flag_gu + (size_t)a.A * (inter / 2);
     a.out = out; a.r = r;
     const size_t xl = (size_t)a.gu.st * hidden * 2, hl = (size_t)a.dn.st * inter * 4;
     const size_t lds = xl > hl ? xl : hl;
+    if (M == 1 && hidden % 1024 == 0 && hidden <= 8192 && a.dn.st == 1) {
+        switch (hidden / 1024) {
+        case 1: return fused1_dispatch<1>(a, lds, st);
+        case 2: return fused1_dispatch<2>(a, lds, st);
+        case 3: return fused1_dispatch<3>(a, lds, st);
+        case 4: return fused1_dispatch<4>(a, lds, st);
+        case 5: return fused1_dispatch<5>(a, lds, st);
+        case 6: return fused1_dispatch<6>(a, lds, st);
+        case 7: return fused1_dispatch<7>(a, lds, st);
+        default: return fused1_dispatch<8>(a, lds, st);
+        }
+    }
     if (a.gu.st == 1 && a.dn.st == 1) return fused_dispatch<1, 1>(a, lds, st);
     if (a.gu.st == 1) return fused_dispatch<1, 2>(a, lds, st);
     if (a.dn.st == 1) return fused_dispatch<2, 1>(a, lds, st);

@@ -107,13 +107,14 @@ GemmScratch carve_gemm(char *p, int64_t M, int64_t S, int32_t E, int32_t hidden,
 }
 
 // Scratch of moe_layer_fused after the route region: h [S][inter] FP32, then
-// the epoch flags, one 32-bit word per gate/up item (A x inter/16) and per
-// down item (hidden/32 x A), A = min(S, E).
+// the epoch flags, one 32-bit word per gate/up item (A x inter/2: the
+// one-token kernel's 2-row items; the general kernel uses the first A x
+// inter/16) and per down item (hidden/32 x A), A = min(S, E).
 size_t fused_scratch_bytes(int64_t S, int32_t E, int32_t hidden, int32_t inter)
 {
     const size_t A = (size_t)(S < E ? S : E);
     return moe::align256(sizeof(float) * (size_t)(S * inter)) +
-           moe::align256(4 * A * (size_t)(inter / 16 + hidden / 32));
+           moe::align256(4 * A * (size_t)(inter / 2 + hidden / 32));
 }
 
 // Points *route at the route tables at the start of ws.

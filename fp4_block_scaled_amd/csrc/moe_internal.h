@@ -129,7 +129,7 @@ hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const 
 
 // Fused decode layer (E4M3): route pack, gate/up + SwiGLU, down and combine
 // in one launch of resident blocks.  S = M*k <= fused_decode_max_slots();
-// flags: min(S, E) x (inter/16 + hidden/32) 32-bit words, any contents;
+// flags: min(S, E) x (inter/2 + hidden/32) 32-bit words, any contents;
 // epoch: a value no earlier call on these flags used.
 int fused_decode_max_slots();
 hipError_t launch_fused_decode_e4m3(const GemvBankDev &gate, const GemvBankDev &up,

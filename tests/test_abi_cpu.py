@@ -187,11 +187,12 @@ def test_fused_workspace_and_error_contract_on_host():
     from fp4_block_scaled_amd import binding as B
     L = B.lib
     # workspace: route region + h [S][I] FP32 + one 32-bit flag per gate/up
-    # item (A x I/16) and per down item (H/32 x A), A = min(S, E)
+    # item (A x I/2, the one-token kernel's 2-row items) and per down item
+    # (H/32 x A), A = min(S, E)
     M, k, E, H, I = 1, 8, 256, 7168, 2048
     S = M * k
     route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
-    want = route + a256(4 * S * I) + a256(4 * min(S, E) * (I // 16 + H // 32))
+    want = route + a256(4 * S * I) + a256(4 * min(S, E) * (I // 2 + H // 32))
     assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_FUSED) == want
     assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_FUSED) == 0
     assert L.moe_workspace_bytes(33, 8, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_FUSED) == 0
