@@ -489,7 +489,9 @@ def main():
                 "output_stable": rf["stable"], "roofline": roofline(rf), **extra_rows(rf)}
 
     def fused_ok(w2):
-        return not args.no_fused and w2.fmt == 1 and w2.M * w2.top_k <= 256
+        if args.no_fused or w2.M * w2.top_k > 256:
+            return False
+        return w2.fmt == 1 or (w2.M == 1 and w2.hidden % 2048 == 0 and w2.hidden <= 16384)
 
     if fused_ok(wl):
         line["fused"] = fused_row(wl, banks)

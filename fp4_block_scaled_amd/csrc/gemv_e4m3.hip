@@ -22,6 +22,7 @@
 //   down:    a block covers 32 output rows over the whole of K (= inter)
 //            and writes y rows directly.
 #include "moe_internal.h"
+#include "fused_common.h"
 
 namespace {
 
@@ -428,157 +429,10 @@ __global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kern
 // ---------------------------------------------------------------------------
 // fused decode layer: route pack, gate/up + SwiGLU, down and combine in one launch
 // ---------------------------------------------------------------------------
-// Every block is resident at once (the grid is sized by the occupancy API).
-// Each block first builds the route of the S <= kFusedMaxSlots slots in LDS
-// (the same stable pack as route_pack_kernel; block 0 also writes the route
-// tables).  Then it runs its share of the gate/up items (active expert x 16 h
-// rows); each finished item stores the call's epoch into its own
-// flag.  Then its share of the down items (32-row tile x active expert,
-// tile-major): the first weight chunks go out, the block waits until all the
-// gate/up flags of the expert hold the epoch, stages h and finishes the item,
-// and stores its own flag.  The down item of the last active expert of a
-// tile waits for the tile's other down flags and applies the top-k weights
-// for every token of that tile, in slot order (multiply, then add).
-//
-// No read-modify-write anywhere: each flag has one writer, and flags hold an
-// epoch no earlier call used, so a workspace needs no clearing and stale
-// contents cannot satisfy a wait.  A block does all its gate/up items before
-// it waits for anything and takes its down items in increasing index; the
-// combining item has the largest index of its tile, so it only waits on items
-// of smaller index.  With every block resident, each wait therefore ends; a
-// wait also gives up after a bounded spin and flags the call in route status.
-constexpr int kFusedMaxSlots = 256;
-constexpr uint32_t kFusedTimeoutFlag = 1u << 30;    // added to route status on a timed-out wait
-
-struct FusedArgs {
-    GateUpArgs gu;                   // offsets/sorted_token/active unused (route built in LDS)
-    DownArgs dn;                     // idem
-    const int32_t *ids;              // [M][k]
-    const float *w;                  // [M][k]
-    int32_t M, k, E, A;              // A = min(M*k, E): active-expert capacity
-    uint32_t epoch;
-    uint32_t *flag_gu;               // [A][inter / 16] per gate/up item
-    uint32_t *flag_dn;               // [hidden / 32][A] per down item
-    float *out;                      // [M][H]
-    MoeRouteDev r;                   // route tables written by block 0
-};
-
-struct FusedRoute {
-    int32_t ids[kFusedMaxSlots];
-    int32_t first[kFusedMaxSlots];   // 1: first slot of its (valid) expert
-    int32_t tok[kFusedMaxSlots];     // packed row -> token
-    int32_t t2p[kFusedMaxSlots];     // slot -> packed row, -1 if invalid
-    int32_t ae[kFusedMaxSlots];      // active experts, ascending
-    int32_t ap0[kFusedMaxSlots];     // their first packed row
-    int32_t acnt[kFusedMaxSlots];    // their slot counts
-    int32_t na, nvalid, ninvalid, flag;
-};
-
-// h and y move between blocks through device-coherent stores and loads
-// (written through to memory, read past the L2 of the reader's XCD); a
-// release or acquire at device scope would instead write back or invalidate
-// a whole L2 per item.  Each wave waits for its stores before the caller's
-// barrier; then one thread publishes the epoch in the item's flag.
-__device__ __forceinline__ void publish(uint32_t *flag, uint32_t epoch)
-{
-    __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// wave 0 waits until flags[0..n) all hold epoch; false on timeout.  The other
-// waves wait at the caller's barrier; the data behind the flags is then read
-// with device-coherent loads.
-__device__ __forceinline__ bool flags_wait(const uint32_t *flags, int n, uint32_t epoch)
-{
-    const int lane = threadIdx.x & 63;
-    for (int it = 0; it < (1 << 21); ++it) {
-        bool ok = true;
-        for (int i = lane; i < n; i += 64)
-            ok &= __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-        if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
-        __builtin_amdgcn_s_sleep(16);
-    }
-    return false;
-}
-
-// wave 0 waits for an expert's gate/up flags (flagging a timeout), then the block goes on
-struct FusedWait {
-    const uint32_t *flags;
-    int n;
-    uint32_t epoch;
-    int *flag;
-    __device__ void operator()() const
-    {
-        if (threadIdx.x < 64 && !flags_wait(flags, n, epoch) && threadIdx.x == 0) *flag = 1;
-        moe::lds_barrier();
-    }
-};
-
-// The route of the S slots in LDS, for any block.  id_in is this thread's
-// slot id (slot tid; -1 past S), loaded by the caller; the barriers inside are
-// LDS-only, so global loads the caller has in flight stay in flight.
-static_assert(kFusedMaxSlots == kThreads, "one slot per thread");
-__device__ void fused_route(const FusedArgs &a, FusedRoute &R, int id_in)
-{
-    const int tid = threadIdx.x, S = a.M * a.k, E = a.E;
-    if (tid == 0) { R.na = 0; R.nvalid = 0; R.ninvalid = 0; R.flag = 0; }
-    R.ids[tid] = id_in;
-    moe::lds_barrier();
-    const int id = tid < S ? R.ids[tid] : -1;
-    const bool valid = tid < S && id >= 0 && id < E;
-    int less = 0, before = 0, total = 0;
-    for (int q = 0; q < S; ++q) {
-        const int v = R.ids[q];
-        if (v >= 0 && v < E) {
-            less += v < id;
-            if (v == id) { ++total; before += q < tid; }
-        }
-    }
-    R.first[tid] = valid && before == 0;
-    if (tid < S && !valid && id != -1) atomicAdd(&R.ninvalid, 1);
-    if (valid) atomicAdd(&R.nvalid, 1);
-    moe::lds_barrier();
-    int rank = 0;                                    // distinct valid experts below id
-    for (int q = 0; q < S; ++q) rank += R.first[q] && R.ids[q] < id;
-    const int p = less + before;
-    if (tid < S) R.t2p[tid] = valid ? p : -1;
-    if (valid) R.tok[p] = tid / a.k;
-    if (valid && before == 0) {
-        R.ae[rank] = id; R.ap0[rank] = less; R.acnt[rank] = total;
-        atomicAdd(&R.na, 1);
-    }
-    moe::lds_barrier();
-}
-
-// Block 0 writes the other route tables, as route_pack writes them.  Nothing
-// in the launch reads them, so this runs at the end, off the critical path.
-__device__ void fused_route_tables(const FusedArgs &a, const FusedRoute &R)
-{
-    if (blockIdx.x != 0) return;
-    const int tid = threadIdx.x, S = a.M * a.k, E = a.E;
-    for (int e = tid; e <= E; e += kThreads) {
-        int c = 0;
-        for (int q = 0; q < S; ++q) {
-            const int v = R.ids[q];
-            c += v >= 0 && v < e;
-        }
-        a.r.offsets[e] = c;
-    }
-    if (tid < S) {
-        const int p = R.t2p[tid];
-        a.r.token_to_perm[tid] = p;
-        if (p >= 0) { a.r.sorted_slot[p] = tid; a.r.sorted_token[p] = tid / a.k; }
-    }
-    const int A = S < E ? S : E;
-    for (int i = tid; i < A; i += kThreads) a.r.active[i] = i < R.na ? R.ae[i] : -1;
-    if (tid == 0) *a.r.num_active = R.na;
-}
-
-// Block 0 sets the route status right after the route: a wait that times out
-// later adds its flag to it.
-__device__ __forceinline__ void fused_route_status(const FusedArgs &a, const FusedRoute &R)
-{
-    if (blockIdx.x == 0 && threadIdx.x == 0) *a.r.status = R.ninvalid;
-}
+// The route, flags, waits and launch are in fused_common.h; the items below
+// are this file's gate/up and down items.
+static_assert(kThreads == kFusedThreads, "fused kernels use the GEMV block size");
+using FusedArgs = FusedArgsT<GateUpArgs, DownArgs>;
 
 // GCH/GNCH and DCH/DNCH: the chunking of the gate/up and down items (NCH > 0
 // fully unrolled, 0 looped).
@@ -652,10 +506,10 @@ __global__ __launch_bounds__(kThreads, 4) void moe_fused_decode_e4m3_kernel(Fuse
 // ---------------------------------------------------------------------------
 // The same phases with gate/up items of 2 h rows: wave w streams row
 // 2r + (w & 1) of the gate (w < 2) or up (w >= 2) bank of one expert over the
-// whole of K, 64 lanes x 16 bytes per load (1 KB, 8 K segments).  Every block
-// walks the experts in order (block b takes rows 2b, 2b+1, then 2(b+grid), ...
-// of expert 0, then of expert 1, ...), so the experts' h are completed one
-// after another rather than all at the end; the down items (32 rows of one
+// whole of K, 64 lanes x 16 bytes per load (1 KB, 8 K segments).  Items are
+// numbered expert-major (q = expert * inter/2 + r) and block b takes q = b,
+// b + grid, ..., so every block walks the experts in order and the experts'
+// h are completed one after another rather than all at the end; the down items (32 rows of one
 // expert) run expert-major, so those of the first experts overlap the gate/up
 // of the last.  The token's x row sits in LDS for the whole gate/up phase;
 // each item's weights are in flight while the previous item is multiplied.
@@ -730,9 +584,10 @@ __global__ __launch_bounds__(kThreads, 4) void moe_fused_decode1_e4m3_kernel(Fus
     // gate/up + SwiGLU items, expert by expert
     const int nr = I >> 1;
     const bool is_up = wave >= 2;
-    int ai = 0, r = blockIdx.x;
-    bool have = na > 0 && r < nr;
-    int pai = -1, pr = 0;                            // item whose h waits for its flag
+    const int nq = na * nr;                          // item q: expert q / nr, rows 2(q % nr), +1
+    int q = blockIdx.x, ai = q / nr, r = q - ai * nr;
+    bool have = q < nq;
+    int pq = -1;                                     // item whose h waits for its flag
     uint4 w0[NJ], w1[NJ];
     float sc0 = 0.0f, sc1 = 0.0f;
     if (have) thin_issue<NJ>(a, R, is_up, wave, lane, ai, r, w0, sc0);
@@ -741,10 +596,9 @@ __global__ __launch_bounds__(kThreads, 4) void moe_fused_decode1_e4m3_kernel(Fus
     auto step = [&](uint4 (&wc)[NJ], float &scc, uint4 (&wn)[NJ], float &scn) {
         moe::wait_vm0();                             // this item's weights, the last h stores
         moe::lds_barrier();
-        if (tid == 0 && pai >= 0) publish(a.flag_gu + (size_t)pai * nr + pr, a.epoch);
-        int ai2 = ai, r2 = r + (int)gridDim.x;
-        if (r2 >= nr) { r2 = blockIdx.x; ++ai2; }
-        const bool have2 = ai2 < na;
+        if (tid == 0 && pq >= 0) publish(a.flag_gu + pq, a.epoch);
+        const int q2 = q + (int)gridDim.x, ai2 = q2 / nr, r2 = q2 - ai2 * nr;
+        const bool have2 = q2 < nq;
         if (have2) thin_issue<NJ>(a, R, is_up, wave, lane, ai2, r2, wn, scn);
         const float v = thin_row<NJ>(wc, scc, dyn, lane);
         if (is_up && lane == 0) ush[wave - 2] = v;
@@ -755,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 4) void moe_fused_decode1_e4m3_kernel(Fus
             const int row = 2 * r + wave;
             for (int j = 0; j < ne; ++j) moe::store_dev(a.gu.h + (size_t)(p0 + j) * I + row, hv);
         }
-        pai = ai; pr = r; ai = ai2; r = r2; have = have2;
+        pq = q; q = q2; ai = ai2; r = r2; have = have2;
     };
     if (have) {
         for (;;) {
@@ -766,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 4) void moe_fused_decode1_e4m3_kernel(Fus
         }
         moe::wait_vm0();
         moe::lds_barrier();
-        if (tid == 0) publish(a.flag_gu + (size_t)pai * nr + pr, a.epoch);
+        if (tid == 0) publish(a.flag_gu + pq, a.epoch);
     } else {
         moe::lds_barrier();                          // x is in LDS before the down items
     }
@@ -931,30 +785,6 @@ hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const 
 // fused decode layer launch
 // ---------------------------------------------------------------------------
 namespace {
-
-// One block per slot the occupancy allows: every block must be resident for
-// the waits to end.  The occupancy and CU count are kept per kernel.
-template <auto Kern>
-hipError_t resident_launch(const FusedArgs &a, size_t lds, hipStream_t st)
-{
-    static int per_cu = -1;
-    static size_t per_cu_lds = 0;
-    static int n_cu = 0;
-    if (per_cu < 0 || per_cu_lds != lds) {
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)Kern, kThreads, lds);
-        if (e != hipSuccess) return e;
-        per_cu_lds = lds;
-    }
-    if (n_cu == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-    }
-    if (per_cu < 1) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(Kern, dim3((unsigned)(per_cu * n_cu)), dim3(kThreads), lds, st, a);
-    return hipGetLastError();
-}
 
 template <int GCH, int GNCH, int GST, int DCH, int DNCH, int DST>
 hipError_t fused_launch(const FusedArgs &a, size_t lds, hipStream_t st)

@@ -14,6 +14,7 @@
 // are exact in both.  The two E4M3 group scales of a lane's 32 weights are
 // applied once per 16 products; scale_2 once per output.
 #include "moe_internal.h"
+#include "fused_common.h"
 
 namespace {
 
@@ -232,18 +233,22 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
 // + sub); the K loop then streams codes and group scales in chunks of CH
 // 256-wide segments, fully unrolled with the next two chunks in flight when
 // NCH > 0, looped with one chunk in flight when NCH == 0.
-template <int CH, int NCH, int ST>
-__global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
-{
-    extern __shared__ float4 hl[];                   // [a.st][I / 4], permuted per segment
+// down_nvfp4_item does one (expert e, 32-row tile) item for the ne slots of
+// e (packed rows p0..p0+ne) with hl the LDS h tile ([a.st][I / 4] float4).
+// FUSED (the one-launch layer's item): the first weight chunks go out, then
+// wait_h() runs (the wait for the expert's h), and h and y move through
+// device-coherent accesses; otherwise h is staged before the first chunks.
+struct NoWait {
+    __device__ void operator()() const {}
+};
 
+template <int CH, int NCH, int ST, bool FUSED, class WaitH>
+__device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int tile, int p0, int ne,
+                                                float4 *hl, const WaitH &wait_h)
+{
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int grp = lane >> 3, sub = lane & 7;
-    const int tile = blockIdx.x % a.ntiles;
-    const int ai = blockIdx.x / a.ntiles;
-    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
-    if (e < 0) return;
     const int H = a.H, I = a.I, I4 = I >> 2;
     const int nch = NCH > 0 ? NCH : I / (kSegK * CH);
     const int rowb = I / 2, rows = I / 16;
@@ -253,8 +258,6 @@ __global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
     const size_t r0 = (size_t)e * H + row0 + wave * 8;
     const uint8_t *cb0 = a.codes + r0 * rowb, *sb0 = a.scales + r0 * rows;
     const uint32_t coff = (uint32_t)grp * rowb + sub * 16, soff = (uint32_t)grp * rows + sub * 2;
-    const int p0 = moe::uniform(a.offsets[e]);
-    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
 
     for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
         const int nt = min(a.st, ne - s0);
@@ -292,18 +295,32 @@ __global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
                 if constexpr (NCH > 0) __builtin_amdgcn_sched_barrier(0);
             }
         };
+        auto stage_h = [&]() {
+            for (int f = tid; f < nt * I4; f += kThreads) {
+                const int j = f / I4, r = f - j * I4; // r: source float4 (4 K values)
+                const int sg = r >> 6, rr = r & 63;
+                const float *hp = a.h + (size_t)(p0 + s0 + j) * I + r * 4;
+                float4 hv;
+                if constexpr (FUSED) {
+                    hv = make_float4(moe::load_dev(hp), moe::load_dev(hp + 1), moe::load_dev(hp + 2),
+                                     moe::load_dev(hp + 3));
+                } else {
+                    hv = *reinterpret_cast<const float4 *>(hp);
+                }
+                hl[j * I4 + sg * 64 + (rr & 7) * 8 + (rr >> 3)] = hv;
+            }
+        };
 
-        for (int f = tid; f < nt * I4; f += kThreads) {
-            const int j = f / I4, r = f - j * I4;     // r: source float4 (4 K values)
-            const int sg = r >> 6, rr = r & 63;
-            hl[j * I4 + sg * 64 + (rr & 7) * 8 + (rr >> 3)] =
-                *reinterpret_cast<const float4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
-        }
+        if constexpr (!FUSED) stage_h();
         if constexpr (NCH > 0) {
             uint4 w[3][CH];
             uint32_t v[3][CH];
             load_w(w[0], v[0], 0);
             if (NCH > 1) load_w(w[1], v[1], 1);
+            if constexpr (FUSED) {
+                wait_h();
+                stage_h();
+            }
             moe::lds_barrier();
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
@@ -316,6 +333,10 @@ __global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
             uint4 w0[CH], w1[CH];
             uint32_t v0[CH], v1[CH];
             load_w(w0, v0, 0);
+            if constexpr (FUSED) {
+                wait_h();
+                stage_h();
+            }
             moe::lds_barrier();
             auto step = [&](int c, uint4 (&wc)[CH], uint32_t (&vc)[CH], uint4 (&wn)[CH],
                             uint32_t (&vn)[CH]) {
@@ -333,11 +354,200 @@ __global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
         for (int j = 0; j < ST; ++j) {
             if (j < nt) {
                 const float v = moe::sum8_lanes(acc[j]) * s2;
-                if (sub == 0) a.y[(size_t)(p0 + s0 + j) * H + row] = v;
+                float *yp = a.y + (size_t)(p0 + s0 + j) * H + row;
+                if (sub == 0) {
+                    if constexpr (FUSED) moe::store_dev(yp, v);
+                    else *yp = v;
+                }
             }
         }
         moe::lds_barrier();                           // h is reused by the next pass
     }
+}
+
+template <int CH, int NCH, int ST>
+__global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
+{
+    extern __shared__ float4 hl[];                   // [a.st][I / 4], permuted per segment
+    const int tile = blockIdx.x % a.ntiles;
+    const int ai = blockIdx.x / a.ntiles;
+    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
+    if (e < 0) return;
+    const int p0 = moe::uniform(a.offsets[e]);
+    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
+    down_nvfp4_item<CH, NCH, ST, false>(a, e, tile, p0, ne, hl, NoWait{});
+}
+
+// ---------------------------------------------------------------------------
+// fused decode layer for one token (M == 1), NVFP4 banks
+// ---------------------------------------------------------------------------
+// The one-launch layer of fused_common.h with gate/up items of 2 h rows: wave
+// w streams row 2r + (w & 1) of the gate (w < 2) or up (w >= 2) bank over the
+// whole of K, 64 lanes x 16 code bytes per load (2048 K values); every block
+// walks the experts in order, so their h complete one after another; the down
+// items (32 rows of one expert) run expert-major.  The token's x row stays in
+// LDS, permuted so that the lanes of one load read consecutive 16-byte words:
+// word q (q < 4) of lane l in load j sits at j*256 + q*64 + l.  A lane's two
+// group scales of a load come from one dword of the row's scale bytes, read
+// once per item (lane l holds dwords l, l + 64, ...).  The gate/up sums run in
+// another order than the three-call path's (per lane over its K, then over 64
+// lanes), so they agree with it to rounding.
+using FusedArgs = FusedArgsT<GateUpArgs, DownArgs>;
+static_assert(kThreads == kFusedThreads, "fused kernels use the GEMV block size");
+
+template <int NJ>
+__device__ __forceinline__ void thin_issue_nv(const FusedArgs &a, const FusedRoute &R, bool is_up,
+                                              int wave, int lane, int ai, int r, uint4 (&w)[NJ],
+                                              uint32_t (&sd)[(NJ + 1) / 2])
+{
+    const int H = a.gu.H, I = a.gu.I;
+    const int e = moe::uniform(R.ae[ai]);
+    const size_t rr = (size_t)e * I + 2 * r + (wave & 1);
+    const uint8_t *cp = moe::uniform_ptr((is_up ? a.gu.ucodes : a.gu.gcodes) + rr * (H / 2));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) w[j] = load16(cp + j * 1024 + lane * 16);
+    const uint32_t *sp = reinterpret_cast<const uint32_t *>(
+        moe::uniform_ptr((is_up ? a.gu.uscales : a.gu.gscales) + rr * (H / 16)));
+    const int ndw = H / 64;                          // scale dwords of the row
+#pragma unroll
+    for (int q = 0; q < (NJ + 1) / 2; ++q) {
+        const int d = lane + 64 * q;
+        sd[q] = d < ndw ? __builtin_nontemporal_load(sp + d) : 0u;
+    }
+}
+
+// one row's sum over K (before scale_2), every lane of the wave ends with it
+template <int NJ>
+__device__ __forceinline__ float thin_row_nv(const uint4 (&w)[NJ], const uint32_t (&sd)[(NJ + 1) / 2],
+                                             const uint4 *xl, int lane)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        // group scales of K j*2048 + lane*32 .. +32: bytes j*128 + 2*lane, +1
+        const uint32_t dw = __shfl(sd[j / 2], (j * 32 + (lane >> 1)) & 63, 64);
+        const uint32_t s16 = (lane & 1) ? (dw >> 16) : (dw & 0xFFFFu);
+        const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)s16, false);
+        const uint4 *xv = xl + j * 256 + lane;
+        float d0 = dot8_fp4_bf16(w[j].x, xv[0], 0.0f);
+        d0 = dot8_fp4_bf16(w[j].y, xv[64], d0);
+        float d1 = dot8_fp4_bf16(w[j].z, xv[128], 0.0f);
+        d1 = dot8_fp4_bf16(w[j].w, xv[192], d1);
+        acc = fmaf(d0, sc.x, acc);
+        acc = fmaf(d1, sc.y, acc);
+    }
+    acc = moe::sum8_lanes(acc);
+    acc += __shfl_xor(acc, 8, 64);
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    return acc;
+}
+
+template <int NJ, int DCH, int DNCH>
+__global__ __launch_bounds__(kThreads, 4) void moe_fused_decode1_nvfp4_kernel(FusedArgs a)
+{
+    extern __shared__ uint4 dyn[];                   // x row (gate/up), then h tile (down)
+    __shared__ FusedRoute R;
+    __shared__ float ush[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = moe::uniform(tid >> 6);
+    const int H = a.dn.H, I = a.gu.I;
+    fused_route(a, R, tid < a.k ? a.ids[tid] : -1);
+    fused_route_status(a, R);
+    const int na = moe::uniform(R.na);
+    if (na == 0) {                                   // no valid slot: the output row is zero
+        for (int q = blockIdx.x * kThreads + tid; q < H; q += gridDim.x * kThreads) a.out[q] = 0.0f;
+    }
+
+    // gate/up + SwiGLU items, expert by expert
+    const int nr = I >> 1;
+    const bool is_up = wave >= 2;
+    const int nq = na * nr;                          // item q: expert q / nr, rows 2(q % nr), +1
+    int q = blockIdx.x, ai = q / nr, r = q - ai * nr;
+    bool have = q < nq;
+    int pq = -1;                                     // item whose h waits for its flag
+    uint4 w0[NJ], w1[NJ];
+    uint32_t s0[(NJ + 1) / 2], s1[(NJ + 1) / 2];
+    if (have) thin_issue_nv<NJ>(a, R, is_up, wave, lane, ai, r, w0, s0);
+    for (int u = tid; u < (H >> 3); u += kThreads)   // x, permuted per load
+        dyn[(u & ~255) + (u & 3) * 64 + ((u & 255) >> 2)] =
+            *reinterpret_cast<const uint4 *>(a.gu.x + (size_t)u * 8);
+    auto step = [&](uint4 (&wc)[NJ], uint32_t (&sc)[(NJ + 1) / 2], uint4 (&wn)[NJ],
+                    uint32_t (&sn)[(NJ + 1) / 2]) {
+        moe::wait_vm0();                             // this item's weights, the last h stores
+        moe::lds_barrier();
+        if (tid == 0 && pq >= 0) publish(a.flag_gu + pq, a.epoch);
+        const int q2 = q + (int)gridDim.x, ai2 = q2 / nr, r2 = q2 - ai2 * nr;
+        const bool have2 = q2 < nq;
+        if (have2) thin_issue_nv<NJ>(a, R, is_up, wave, lane, ai2, r2, wn, sn);
+        const int e = moe::uniform(R.ae[ai]);
+        const float v = thin_row_nv<NJ>(wc, sc, dyn, lane) * (is_up ? a.gu.uscale2 : a.gu.gscale2)[e];
+        if (is_up && lane == 0) ush[wave - 2] = v;
+        moe::lds_barrier();
+        if (!is_up && lane == 0) {
+            const float hv = swiglu_clamp(v, ush[wave], a.gu.limit);
+            const int p0 = R.ap0[ai], ne = R.acnt[ai];
+            const int row = 2 * r + wave;
+            for (int j = 0; j < ne; ++j) moe::store_dev(a.gu.h + (size_t)(p0 + j) * I + row, hv);
+        }
+        pq = q; q = q2; ai = ai2; r = r2; have = have2;
+    };
+    if (have) {
+        for (;;) {
+            step(w0, s0, w1, s1);
+            if (!have) break;
+            step(w1, s1, w0, s0);
+            if (!have) break;
+        }
+        moe::wait_vm0();
+        moe::lds_barrier();
+        if (tid == 0) publish(a.flag_gu + pq, a.epoch);
+    } else {
+        moe::lds_barrier();                          // x is in LDS before the down items
+    }
+
+    // down items, expert-major
+    const int ntd = H / 32, nd = na * ntd;
+    for (int d = blockIdx.x; d < nd; d += gridDim.x) {
+        const int dai = d / ntd, tile = d - dai * ntd;
+        const int e = moe::uniform(R.ae[dai]), p0 = moe::uniform(R.ap0[dai]);
+        const int ne = moe::uniform(R.acnt[dai]);
+        const FusedWait wait_h{a.flag_gu + (size_t)dai * nr, nr, a.epoch, &R.flag};
+        down_nvfp4_item<DCH, DNCH, 1, true>(a.dn, e, tile, p0, ne, reinterpret_cast<float4 *>(dyn),
+                                            wait_h);
+        moe::wait_vm0();                             // this wave's y stores are written
+        __syncthreads();
+        uint32_t *fl = a.flag_dn + (size_t)tile * a.A;
+        if (dai + 1 < na) {
+            if (tid == 0) publish(fl + dai, a.epoch);
+            continue;
+        }
+        // the tile's last expert: wait for the others' y rows, then combine
+        const FusedWait wait_y{fl, na - 1, a.epoch, &R.flag};
+        wait_y();
+        for (int q = tid; q < 32; q += kThreads) {
+            const int m = tile * 32 + q;
+            float acc = 0.0f;
+            for (int j = 0; j < a.k; ++j) {
+                const int pr2 = R.t2p[j];
+                if (pr2 < 0) continue;
+                acc = __fadd_rn(acc, __fmul_rn(a.w[j], moe::load_dev(a.dn.y + (size_t)pr2 * H + m)));
+            }
+            a.out[m] = acc;
+        }
+    }
+    fused_route_tables(a, R);
+    __syncthreads();
+    if (tid == 0 && R.flag) atomicAdd(a.r.status, (int)kFusedTimeoutFlag);
+}
+
+// Unrolled down items for the pages' NVFP4 shape (inter 1536 = 3 chunks of
+// 2 segments), looped single-segment items otherwise.
+template <int NJ>
+hipError_t fused1_nv_dispatch(const FusedArgs &a, size_t lds, hipStream_t st)
+{
+    if (a.dn.I == 1536) return resident_launch<moe_fused_decode1_nvfp4_kernel<NJ, 2, 3>>(a, lds, st);
+    return resident_launch<moe_fused_decode1_nvfp4_kernel<NJ, 1, 0>>(a, lds, st);
 }
 
 }  // namespace
@@ -453,4 +663,38 @@ hipError_t launch_gemv_down_nvfp4(const GemvBankDev &down, const float *h, const
         else down_launch<1, 0, kDNST>(a, grid, st);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_fused_decode_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
+                                     const GemvBankDev &down, const uint16_t *x, const int32_t *ids,
+                                     const float *w, int32_t M, int32_t k, int32_t E, int32_t hidden,
+                                     int32_t inter, float limit, const MoeRouteDev &r, float *h,
+                                     float *y, float *out, void *flags, uint32_t epoch,
+                                     hipStream_t st)
+{
+    if (M != 1 || hidden % 2048 != 0 || hidden > 16384) return hipErrorInvalidValue;
+    FusedArgs a{};
+    a.gu.gcodes = gate.codes; a.gu.ucodes = up.codes;
+    a.gu.gscales = (const uint8_t *)gate.scales; a.gu.uscales = (const uint8_t *)up.scales;
+    a.gu.gscale2 = gate.scale2; a.gu.uscale2 = up.scale2;
+    a.gu.x = x; a.gu.h = h; a.gu.H = hidden; a.gu.I = inter; a.gu.limit = limit; a.gu.st = 1;
+    a.dn.codes = down.codes; a.dn.scales = (const uint8_t *)down.scales; a.dn.scale2 = down.scale2;
+    a.dn.h = h; a.dn.y = y; a.dn.H = hidden; a.dn.I = inter; a.dn.st = 1;
+    a.ids = ids; a.w = w; a.M = M; a.k = k; a.E = E; a.epoch = epoch;
+    a.A = k < E ? k : E;
+    a.flag_gu = (uint32_t *)flags;
+    a.flag_dn = a.flag_gu + (size_t)a.A * (inter / 2);
+    a.out = out; a.r = r;
+    const size_t xl = (size_t)hidden * 2, hl = (size_t)inter * 4;
+    const size_t lds = xl > hl ? xl : hl;
+    switch (hidden / 2048) {
+    case 1: return fused1_nv_dispatch<1>(a, lds, st);
+    case 2: return fused1_nv_dispatch<2>(a, lds, st);
+    case 3: return fused1_nv_dispatch<3>(a, lds, st);
+    case 4: return fused1_nv_dispatch<4>(a, lds, st);
+    case 5: return fused1_nv_dispatch<5>(a, lds, st);
+    case 6: return fused1_nv_dispatch<6>(a, lds, st);
+    case 7: return fused1_nv_dispatch<7>(a, lds, st);
+    default: return fused1_nv_dispatch<8>(a, lds, st);
+    }
 }

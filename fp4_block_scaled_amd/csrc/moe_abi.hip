@@ -117,6 +117,13 @@ size_t fused_scratch_bytes(int64_t S, int32_t E, int32_t hidden, int32_t inter)
            moe::align256(4 * A * (size_t)(inter / 2 + hidden / 32));
 }
 
+// The fused layer serves NVFP4 banks for one token with hidden a multiple of
+// 2048 (one 1 KB code load per 2048 K values) up to 16384.
+bool nvfp4_fused_ok(int64_t M, int32_t hidden)
+{
+    return M == 1 && hidden % 2048 == 0 && hidden <= 16384;
+}
+
 // Points *route at the route tables at the start of ws.
 void carve_route(void *ws, int32_t M, int32_t top_k, int32_t E, moe_route_t *route)
 {
@@ -182,7 +189,8 @@ size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts, in
     if (!ffn_dims_ok(fmt, hidden, inter)) return 0;
     const int64_t S = (int64_t)max_M * top_k;
     if (mode == MOE_MODE_FUSED) {
-        if (fmt != MOE_W_E4M3_B128 || S > MOE_FUSED_MAX_SLOTS) return 0;
+        if (S > MOE_FUSED_MAX_SLOTS) return 0;
+        if (fmt == MOE_W_NVFP4_B16 && !nvfp4_fused_ok(max_M, hidden)) return 0;
         return moe::route_region_bytes(S, num_experts) + fused_scratch_bytes(S, num_experts, hidden, inter);
     }
     size_t ffn;
@@ -361,8 +369,9 @@ moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const
     if ((st = check_bank(fn, gate, "gate", fmt, E, inter, hidden))) return st;
     if ((st = check_bank(fn, up, "up", fmt, E, inter, hidden))) return st;
     if ((st = check_bank(fn, down, "down", fmt, E, hidden, inter))) return st;
-    if (fmt != MOE_W_E4M3_B128)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: the fused layer serves E4M3 banks only", fn);
+    if (fmt == MOE_W_NVFP4_B16 && !nvfp4_fused_ok(M, hidden))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: NVFP4 banks need M = 1 and hidden a multiple of 2048 "
+                    "up to 16384 (M=%d hidden=%d)", fn, M, hidden);
     if (!aligned16(x_bf16) || !aligned16(y_packed) || !aligned16(out))
         return fail(MOE_ERR_ARG, "%s: x, y and out must be 16-byte aligned", fn);
     if (!(limit > 0.0f)) return fail(MOE_ERR_ARG, "%s: limit must be > 0", fn);
@@ -398,8 +407,11 @@ moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const
     GemvBankDev bu{up->codes, up->scales, up->scale2};
     GemvBankDev bd{down->codes, down->scales, down->scale2};
     stage_mark(0, s);
-    hipError_t e = launch_fused_decode_e4m3(bg, bu, bd, x_bf16, topk_ids, topk_weights, M, top_k, E,
-                                            hidden, inter, limit, r, h, y_packed, out, flags, ep, s);
+    hipError_t e = fmt == MOE_W_E4M3_B128
+        ? launch_fused_decode_e4m3(bg, bu, bd, x_bf16, topk_ids, topk_weights, M, top_k, E, hidden,
+                                   inter, limit, r, h, y_packed, out, flags, ep, s)
+        : launch_fused_decode_nvfp4(bg, bu, bd, x_bf16, topk_ids, topk_weights, M, top_k, E, hidden,
+                                    inter, limit, r, h, y_packed, out, flags, ep, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer_fused: launch");
     stage_mark(1, s);
     return MOE_OK;

@@ -139,6 +139,15 @@ hipError_t launch_fused_decode_e4m3(const GemvBankDev &gate, const GemvBankDev &
                                     float *y, float *out, void *flags, uint32_t epoch,
                                     hipStream_t st);
 
+// Fused decode layer for NVFP4 banks: one token (M == 1), hidden a multiple
+// of 2048 up to 16384; flags and epoch as for launch_fused_decode_e4m3.
+hipError_t launch_fused_decode_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
+                                     const GemvBankDev &down, const uint16_t *x, const int32_t *ids,
+                                     const float *w, int32_t M, int32_t k, int32_t E, int32_t hidden,
+                                     int32_t inter, float limit, const MoeRouteDev &r, float *h,
+                                     float *y, float *out, void *flags, uint32_t epoch,
+                                     hipStream_t st);
+
 hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
                                     const uint16_t *x, const MoeRouteDev &r, int32_t M,
                                     int32_t S, int32_t E, int32_t hidden, int32_t inter,

@@ -235,13 +235,19 @@ moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
  * chain: gate/up, activation, down and weighting as one chain per expert).
  * Each block builds the route in LDS; gate/up items publish per expert, down
  * items wait for their expert's h, and the last down item of each 32-row
- * output tile applies the top-k weights for every token.
+ * output tile applies the top-k weights for every token.  One token (M = 1,
+ * hidden a multiple of 1024 for E4M3, 2048 for NVFP4) runs gate/up items of
+ * two h rows taken expert by expert; their sums run in another order than
+ * the three calls', so outputs agree with those to rounding.  Otherwise
+ * (E4M3 only) the items are the three-call path's and outputs are
+ * bit-identical to it.
  * Inputs and outputs as for the three calls: topk_ids int32 [M][top_k],
  * topk_weights float [M][top_k], x bf16 [M][hidden]; y_packed float
  * [M*top_k][hidden] (expert-sorted rows), out float [M][hidden]; *route
  * (host) describes the route tables in ws, as moe_route_pack fills them.
- * Rules: E4M3 banks (NVFP4: MOE_ERR_UNSUPPORTED); M*top_k <=
- * MOE_FUSED_MAX_SLOTS; the moe_expert_ffn shape rules; num_experts is the
+ * Rules: E4M3 banks with M*top_k <= MOE_FUSED_MAX_SLOTS, or NVFP4 banks
+ * with M = 1 and hidden a multiple of 2048 up to 16384 (other NVFP4 sizes:
+ * MOE_ERR_UNSUPPORTED); the moe_expert_ffn shape rules; num_experts is the
  * banks'; ws_bytes >= moe_workspace_bytes(M, top_k, E, hidden, inter, fmt,
  * MOE_MODE_FUSED), ws 256-byte aligned.  The workspace needs no clearing,
  * and calls on one ws must be ordered on one stream.  The kernel assumes its

@@ -194,7 +194,11 @@ def test_fused_workspace_and_error_contract_on_host():
     route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
     want = route + a256(4 * S * I) + a256(4 * min(S, E) * (I // 2 + H // 32))
     assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_FUSED) == want
+    # NVFP4: one token with hidden a multiple of 2048 (7168 is not)
     assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_FUSED) == 0
+    assert L.moe_workspace_bytes(1, k, E, 6144, 1536, B.MOE_W_NVFP4_B16, B.MOE_MODE_FUSED) == \
+        route + a256(4 * S * 1536) + a256(4 * min(S, E) * (1536 // 2 + 6144 // 32))
+    assert L.moe_workspace_bytes(2, k, E, 6144, 1536, B.MOE_W_NVFP4_B16, B.MOE_MODE_FUSED) == 0
     assert L.moe_workspace_bytes(33, 8, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_FUSED) == 0
     assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_E4M3_B128, 4) == 0
     assert B.moe_resolve_mode(1, B.MOE_W_E4M3_B128, B.MOE_MODE_FUSED) == B.MOE_MODE_FUSED
@@ -217,6 +221,10 @@ def test_fused_workspace_and_error_contract_on_host():
     nv = _bank(B, fmt=2, k=256, n=256, scale2=FAKE)
     assert fused(gate=nv, up=nv, down=_bank(B, fmt=2, n=256, k=256, scale2=FAKE), hidden=256,
                  inter=256) == B.MOE_ERR_UNSUPPORTED
+    nv2 = _bank(B, fmt=2, k=2048, n=256, scale2=FAKE)      # hidden 2048 fits, but M = 2 does not
+    assert fused(gate=nv2, up=nv2, down=_bank(B, fmt=2, n=2048, k=256, scale2=FAKE), hidden=2048,
+                 inter=256, M=2, k=4) == B.MOE_ERR_UNSUPPORTED
+    assert "M = 1" in B.moe_last_error()
     assert fused(nbytes=512) == B.MOE_ERR_WORKSPACE
     assert fused(ws_=ws + 64) == B.MOE_ERR_ARG
     assert fused(limit=-1.0) == B.MOE_ERR_ARG

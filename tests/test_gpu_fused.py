@@ -46,7 +46,9 @@ def assert_route_equal(tabs, ids, E):
     return ref
 
 
-def one_token_kernel(M, hidden):
+def one_token_kernel(M, hidden, fmt=workloads.E4M3_B128):
+    if fmt == workloads.NVFP4_B16:
+        return True                      # the only NVFP4 fused path (M = 1, hidden % 2048 == 0)
     return M == 1 and hidden % 1024 == 0 and hidden <= 8192
 
 
@@ -64,7 +66,7 @@ def fused_vs_three_call(case, ids, w, label, x=None):
     nv = int(ref["expert_offsets"][-1])
     assert np.all(np.isnan(y_f[nv:])), f"{label}: fused layer wrote y rows past the valid slots"
     out_3, y_3, _, _ = case.run(ids, w, B.MOE_MODE_GEMV_A16, x=x)
-    if one_token_kernel(M, wl.hidden):
+    if one_token_kernel(M, wl.hidden, wl.fmt):
         check_fp(out_f, out_3, f"{label} out vs three-call")
         check_fp(y_f[:nv], y_3[:nv], f"{label} y vs three-call")
     else:
@@ -76,7 +78,7 @@ def fused_vs_three_call(case, ids, w, label, x=None):
     return check_fp(out_f, ref_out, f"{label} out")
 
 
-@pytest.mark.parametrize("name", ["tiny_e4m3_m1", "decode_e4m3_m1", "verify_e4m3_m8"])
+@pytest.mark.parametrize("name", ["tiny_e4m3_m1", "decode_e4m3_m1", "verify_e4m3_m8", "nvfp4_m1"])
 @pytest.mark.parametrize("route_set", [0, 1])
 def test_fused_layer_workloads(name, route_set):
     wl = workloads.WORKLOADS[name]
@@ -178,6 +180,47 @@ def test_one_token_kernel_edge_routes():
     w = np.array([[0.25, 0.125, 0.2, 0.1, 0.15, 0.175]], np.float32)
     print("one-token duplicates/invalid", flush=True)
     fused_vs_three_call(case, ids, w, "one-token duplicates")
+    ids = np.array([[-1, wl.experts, -1, -5, -1, -1]], np.int32)
+    L.out.fill_(float("nan"))
+    out, _, tabs, _ = case.run(ids, w, layer=L)
+    assert np.all(out == 0.0)
+    assert int(tabs["num_active"][0]) == 0 and int(tabs["status"][0]) == 2
+
+
+NVFP4_REDUCED = [
+    ("nf_h2048_i256", dict(hidden=2048, inter=256, experts=12, top_k=4)),    # 1 load per row
+    ("nf_h4096_i512", dict(hidden=4096, inter=512, experts=20, top_k=8)),    # 2 loads per row
+]
+
+
+@pytest.mark.parametrize("name,over", NVFP4_REDUCED, ids=[r[0] for r in NVFP4_REDUCED])
+def test_fused_nvfp4_reduced_shapes(name, over):
+    wl = workloads.with_shape(workloads.WORKLOADS["nvfp4_m1"], name=name, M=1, **over)
+    case = get_case(wl)
+    for r in range(2):
+        ids, w, _ = workloads.make_routes(wl, r)
+        print(f"fused nvfp4 {name} set {r}", flush=True)
+        fused_vs_three_call(case, ids, w, f"{name}/{r}")
+
+
+def test_fused_nvfp4_edge_routes():
+    wl = workloads.with_shape(workloads.WORKLOADS["nvfp4_m1"], name="nf_edge", hidden=2048,
+                              inter=512, experts=16, top_k=6, M=1)
+    case = get_case(wl)
+    L = case.layer(max_M=1, mode=B.MOE_MODE_FUSED)
+    L.ws.fill_(0xFF)
+    for r in range(3):
+        ids, w, _ = workloads.make_routes(wl, r)
+        print(f"nvfp4 one-token back-to-back {r}", flush=True)
+        out_f, _, tabs, _ = case.run(ids, w, layer=L)
+        assert_route_equal(tabs, ids, wl.experts)
+        assert int(tabs["status"][0]) == 0
+        ref, _ = oracle_layer(case.banks, case.x, ids, w, wl.limit, False)
+        check_fp(out_f, ref, f"nvfp4 one-token epoch {r}")
+    ids = np.array([[3, 3, 7, -1, wl.experts + 2, 5]], np.int32)
+    w = np.array([[0.25, 0.125, 0.2, 0.1, 0.15, 0.175]], np.float32)
+    print("nvfp4 one-token duplicates/invalid", flush=True)
+    fused_vs_three_call(case, ids, w, "nvfp4 duplicates")
     ids = np.array([[-1, wl.experts, -1, -5, -1, -1]], np.int32)
     L.out.fill_(float("nan"))
     out, _, tabs, _ = case.run(ids, w, layer=L)
