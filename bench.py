@@ -302,11 +302,11 @@ def cpu_baseline(wl, banks, x, sets, budget_s):
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC = {
     "decode_e4m3_m1": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "moe_internal.h"],
-                       "src": "225a5797bf060326179d4e9e8c083606",
-                       "fetch_kib": 115065, "write_kib": 64},
+        "src": "493ea8e72758718f29dda69f4e84aaaf", "fetch_kib": 115063, "write_kib": 64},
+    "decode_e4m3_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_e4m3.hip", "moe_internal.h", "fused_common.h"],
+        "src": "493ea8e72758718f29dda69f4e84aaaf98f66700d679828b", "fetch_kib": 173063, "write_kib": 1070},
     "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "moe_internal.h"],
-                           "src": "3a2c3c224a614bf9179d4e9e8c083606",
-                           "fetch_kib": 4271567, "write_kib": 121954},
+        "src": "3a2c3c224a614bf929dda69f4e84aaaf", "fetch_kib": 4279075, "write_kib": 122082},
 }
 
 
