@@ -72,6 +72,10 @@ def lib():
         L.oracle_combine.argtypes = [P, P, P, i32, i32, i32, P]
         L.oracle_router_topk.argtypes = [P, i32, i32, i32, i32, P, f32, i32, P, P]
         L.oracle_router_topk.restype = i32
+        L.oracle_shared_expert.argtypes = [P, P, P, P, i32, i32, i32, f32, P]
+        L.oracle_shared_expert.restype = None
+        L.oracle_combine_residual.argtypes = [P, P, P, P, P, i32, i32, i32, P]
+        L.oracle_combine_residual.restype = None
         L.oracle_combine.restype = None
         _lib = L
     return _lib
@@ -305,3 +309,47 @@ def router_topk(logits: np.ndarray, top_k: int, kind: int = ROUTER_SOFTMAX,
     if rc != 0:
         raise ValueError("oracle_router_topk: bad arguments")
     return ids, w
+
+
+# --------------------------------------------------------------------------
+# shared expert and residual
+# --------------------------------------------------------------------------
+
+def shared_expert(gate_bf16: np.ndarray, up_bf16: np.ndarray, down_bf16: np.ndarray,
+                  x_bf16: np.ndarray, limit: float) -> np.ndarray:
+    """The shared expert's output [M, H] (FP64) for bf16 bit arrays gate, up
+    [W, H], down [H, W] and x [M, H].
+
+    Pinned: numpy FP64 matmuls of the bf16-decoded weights, a diagonal MLP
+    with a closed form, and zero rows."""
+    gate_bf16 = np.ascontiguousarray(gate_bf16, np.uint16)
+    up_bf16 = np.ascontiguousarray(up_bf16, np.uint16)
+    down_bf16 = np.ascontiguousarray(down_bf16, np.uint16)
+    x_bf16 = np.ascontiguousarray(x_bf16, np.uint16)
+    W, H = gate_bf16.shape
+    M = x_bf16.shape[0]
+    assert up_bf16.shape == (W, H) and down_bf16.shape == (H, W) and x_bf16.shape[1] == H
+    out = np.empty((M, H), np.float64)
+    lib().oracle_shared_expert(_ptr(gate_bf16), _ptr(up_bf16), _ptr(down_bf16), _ptr(x_bf16),
+                               M, H, W, float(limit), _ptr(out))
+    return out
+
+
+def combine_residual(y_by_slot: np.ndarray, w: np.ndarray, valid: np.ndarray,
+                     shared: Optional[np.ndarray], residual: Optional[np.ndarray]) -> np.ndarray:
+    """((sum_j w[t, j] * y[t*k + j]) + shared[t]) + residual[t] (FP64).
+
+    Pinned: the pages' worked combine example extended by hand, reduction
+    to the plain combine, and linearity."""
+    w = np.ascontiguousarray(w, np.float32)
+    M, k = w.shape
+    y_by_slot = np.ascontiguousarray(y_by_slot, np.float64)
+    hidden = y_by_slot.shape[1]
+    valid = np.ascontiguousarray(valid, np.int32).reshape(-1)
+    sh = None if shared is None else np.ascontiguousarray(shared, np.float64)
+    rs = None if residual is None else np.ascontiguousarray(residual, np.float32)
+    out = np.empty((M, hidden), np.float64)
+    lib().oracle_combine_residual(_ptr(y_by_slot), _ptr(w), _ptr(valid),
+                                  None if sh is None else _ptr(sh),
+                                  None if rs is None else _ptr(rs), M, k, hidden, _ptr(out))
+    return out

@@ -34,6 +34,10 @@
  *   - per 1x128 group FP8 quantization of activations for the wide-M tier
  *     ("memra-engine src/dsv4_ep.rs", EpScratch xq/xs and the act_quant_fp8
  *     step of fn chain);
+ *   - the shared expert (a dense bf16 SwiGLU MLP applied to every token) and
+ *     the final add order routed, then shared, then residual ("spark_model
+ *     glm5next_mlp/forward.rs", fn forward_dense; "memra-engine
+ *     src/bin/ep_step_fp8_gate.rs", the full-layer gate);
  *   - the router before the layer: softmax, or sigmoid with a selection bias,
  *     top-k per token, renormalized and scaled weights ("spark_model
  *     glm5next_mlp/forward.rs", the router launch of fn forward_moe;
@@ -466,4 +470,64 @@ int oracle_router_topk(const float *logits, int32_t M, int32_t E, int32_t k,
     }
     free(l); free(s); free(keys);
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Shared expert and residual                                                */
+/* ------------------------------------------------------------------------ */
+
+/* The shared expert: a dense SwiGLU MLP of width W with bf16 weights, applied
+ * to every token with weight 1 ("spark_model glm5next_mlp/forward.rs",
+ * fn forward_dense: down(clamped_swiglu(gate(x), up(x))), the same math as a
+ * routed expert with its own clamp, and the shared-expert step of
+ * fn forward_moe, not routed-scaled).  For each token t:
+ *   g = Wg x[t], u = Wu x[t]   (FP64 sums over decoded bf16 values)
+ *   h = swiglu_clamp(g, u, L)  (FP64)
+ *   out[t] = Wd h
+ * gate, up: bf16 [W][H]; down: bf16 [H][W]; x: bf16 [M][H]; out [M][H]. */
+void oracle_shared_expert(const uint16_t *gate, const uint16_t *up,
+                          const uint16_t *down, const uint16_t *x, int32_t M,
+                          int32_t H, int32_t W, float limit, double *out)
+{
+    double *xv = malloc(sizeof(double) * (size_t)H);
+    double *h = malloc(sizeof(double) * (size_t)W);
+    for (int64_t t = 0; t < M; ++t) {
+        for (int64_t i = 0; i < H; ++i) xv[i] = oracle_bf16_value(x[t * H + i]);
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < W; ++n) {
+            double g = 0.0, u = 0.0;
+            for (int64_t i = 0; i < H; ++i) {
+                g += oracle_bf16_value(gate[n * H + i]) * xv[i];
+                u += oracle_bf16_value(up[n * H + i]) * xv[i];
+            }
+            h[n] = oracle_swiglu_clamp(g, u, (double)limit);
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < H; ++m) {
+            double y = 0.0;
+            for (int64_t n = 0; n < W; ++n) y += oracle_bf16_value(down[m * W + n]) * h[n];
+            out[t * H + m] = y;
+        }
+    }
+    free(xv); free(h);
+}
+
+/* out[t][m] = ((sum_j w[t][j] * y[t*k + j][m]) + shared[t][m]) + residual[t][m]:
+ * the routed combine in slot order, then the shared expert's row, then the
+ * residual ("memra-engine src/bin/ep_step_fp8_gate.rs", the full-layer gate's
+ * final add order routed-plus-shared-then-residual).  Rows of slots whose
+ * valid[] flag is 0 contribute nothing; shared or residual may be NULL. */
+void oracle_combine_residual(const double *y_by_slot, const float *w,
+                             const int32_t *valid, const double *shared,
+                             const float *residual, int32_t M, int32_t k,
+                             int32_t hidden, double *out)
+{
+    oracle_combine(y_by_slot, w, valid, M, k, hidden, out);
+    for (int64_t t = 0; t < M; ++t)
+        for (int64_t m = 0; m < hidden; ++m) {
+            double v = out[t * hidden + m];
+            if (shared) v += shared[t * hidden + m];
+            if (residual) v += (double)residual[t * hidden + m];
+            out[t * hidden + m] = v;
+        }
 }
