@@ -404,6 +404,71 @@ def router_rows(wl, banks, steps, route_sets, hip, M=None):
     return out
 
 
+def shared_rows(wl, banks, steps, hip):
+    """The shared expert (bf16 SwiGLU MLP as wide as one routed expert) on the
+    workload's M tokens alone, and the whole layer with it: route pack, expert
+    FFN, shared expert, then the combine with the shared row and a residual."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from fp4_block_scaled_amd import binding as B
+    from fp4_block_scaled_amd.layer import MoeLayer
+
+    M, H, W = wl.M, wl.hidden, wl.inter
+    gate, up, down = workloads.make_shared_expert(H, W, wl.seed * 10 + 11, "cuda")
+    x = workloads.make_x(wl, "cuda")
+    sh = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.moe_shared_workspace_bytes(M, H, W), dtype=torch.uint8, device="cuda")
+    res = workloads.make_residual(M, H, wl.seed + 5, "cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.events(2)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        hip.record(e0, st)
+        for _ in range(steps):
+            fn()
+        hip.record(e1, st)
+        torch.cuda.synchronize()
+        return hip.ms(e0, e1) * 1000.0 / steps
+
+    def shared():
+        B.moe_shared_expert(gate, up, down, x, M, H, W, wl.limit, sh, ws)
+
+    us_sh = timed(shared)
+    nbytes = 3 * W * H * 2 + M * H * 2 + M * H * 4
+    cb = [B.Bank.from_device_bank(b) for b in banks]
+    layer = MoeLayer(*cb, H, W, wl.top_k, M, wl.limit)
+    ids, w, _ = workloads.make_routes(wl)
+    ids_d = torch.from_numpy(ids).cuda()
+    w_d = torch.from_numpy(w).cuda()
+    out = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    layer(x, ids_d, w_d)
+
+    def combine_res():
+        B.moe_combine_residual(layer.y, layer.route, w_d, sh, res, H, out)
+
+    us_cr = timed(combine_res)
+
+    def full():
+        r = B.moe_route_pack(ids_d, M, wl.top_k, layer.E, layer.ws)
+        B.moe_expert_ffn(layer.gate, layer.up, layer.down, x, r, H, W, wl.limit, B.MOE_MODE_AUTO,
+                         layer.y, layer.ws)
+        shared()
+        B.moe_combine_residual(layer.y, r, w_d, sh, res, H, out)
+
+    us_full = timed(full)
+    del layer
+    torch.cuda.empty_cache()
+    return {"shared_width": W, "shared_us": round(us_sh, 3),
+            "shared_hbm_frac": round(nbytes / (us_sh * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "combine_residual_us": round(us_cr, 3),
+            "layer_with_shared_and_residual_us": round(us_full, 3)}
+
+
 def extra_rows(r):
     """Per-layer percentiles, the output checksum check, HIP-graph replay and
     the cold-cache row of one measured workload."""
@@ -496,6 +561,8 @@ def main():
     if fused_ok(wl):
         line["fused"] = fused_row(wl, banks)
     line["router"] = router_rows(wl, banks, args.steps, args.route_sets, hip)
+    if wl.M <= 16:
+        line["shared_expert"] = shared_rows(wl, banks, args.steps, hip)
     also = {}
     for name in [a for a in args.also.split(",") if a]:
         w2 = workloads.WORKLOADS[name]
@@ -515,6 +582,8 @@ def main():
         also[name].update(extra_rows(r2))
         if fused_ok(w2):
             also[name]["fused"] = fused_row(w2, b2)
+        if w2.M <= 16:
+            also[name]["shared_expert"] = shared_rows(w2, b2, max(20, args.steps // 2), hip)
         if w2.M > 16:
             also[name]["router"] = router_rows(w2, b2, max(20, args.steps // 2), args.route_sets,
                                                hip)

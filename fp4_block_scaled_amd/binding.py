@@ -39,8 +39,8 @@ MOE_MAX_DIM = 16384
 MOE_FUSED_MAX_SLOTS = 256
 
 EXPORTS = ("moe_workspace_bytes", "moe_resolve_mode", "moe_router_topk", "moe_route_pack",
-           "moe_expert_ffn", "moe_layer_fused", "moe_combine", "moe_set_stage_events",
-           "moe_last_error")
+           "moe_expert_ffn", "moe_layer_fused", "moe_combine", "moe_shared_workspace_bytes",
+           "moe_shared_expert", "moe_combine_residual", "moe_set_stage_events", "moe_last_error")
 
 
 class moe_bank_t(C.Structure):
@@ -85,6 +85,12 @@ def _load():
     L.moe_layer_fused.restype = i32
     L.moe_combine.argtypes = [P, C.POINTER(moe_route_t), P, i32, P, P]
     L.moe_combine.restype = i32
+    L.moe_combine_residual.argtypes = [P, C.POINTER(moe_route_t), P, P, P, i32, P, P]
+    L.moe_combine_residual.restype = i32
+    L.moe_shared_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_shared_workspace_bytes.restype = sz
+    L.moe_shared_expert.argtypes = [P, P, P, P, i32, i32, i32, C.c_float, P, P, sz, P]
+    L.moe_shared_expert.restype = i32
     L.moe_set_stage_events.argtypes = [P, i32, i32, i32, i32, i32]
     L.moe_set_stage_events.restype = i32
     L.moe_last_error.argtypes = []
@@ -180,6 +186,25 @@ def moe_layer_fused(gate: Bank, up: Bank, down: Bank, x_bf16, topk_ids, topk_wei
 def moe_combine(y_packed, route: moe_route_t, topk_weights, hidden, out, stream=None) -> None:
     _check(lib.moe_combine(_ptr(y_packed), C.byref(route), _ptr(topk_weights), hidden, _ptr(out),
                            _stream(stream)))
+
+
+def moe_combine_residual(y_packed, route: moe_route_t, topk_weights, shared_out, residual, hidden,
+                         out, stream=None) -> None:
+    _check(lib.moe_combine_residual(_ptr(y_packed), C.byref(route), _ptr(topk_weights),
+                                    _ptr(shared_out), _ptr(residual), hidden, _ptr(out),
+                                    _stream(stream)))
+
+
+def moe_shared_workspace_bytes(max_M, hidden, shared_width) -> int:
+    return int(lib.moe_shared_workspace_bytes(max_M, hidden, shared_width))
+
+
+def moe_shared_expert(gate_bf16, up_bf16, down_bf16, x_bf16, M, hidden, shared_width, limit,
+                      shared_out, ws, ws_bytes=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib.moe_shared_expert(_ptr(gate_bf16), _ptr(up_bf16), _ptr(down_bf16), _ptr(x_bf16), M,
+                                 hidden, shared_width, float(limit), _ptr(shared_out), _ptr(ws),
+                                 nbytes, _stream(stream)))
 
 
 def moe_set_stage_events(events, fmt, hidden, inter, mode) -> int:

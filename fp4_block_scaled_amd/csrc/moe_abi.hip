@@ -453,8 +453,66 @@ moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
     if (!aligned16(y_packed) || !aligned16(out))
         return fail(MOE_ERR_ARG, "moe_combine: y and out must be 16-byte aligned");
     hipError_t e = launch_combine(y_packed, route->token_to_perm, topk_weights, route->M,
-                                  route->top_k, hidden, out, (hipStream_t)stream);
+                                  route->top_k, hidden, nullptr, nullptr, out, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "moe_combine: launch");
+    return MOE_OK;
+}
+
+moe_status_t moe_combine_residual(const float *y_packed, const moe_route_t *route,
+                                  const float *topk_weights, const float *shared_out,
+                                  const float *residual, int32_t hidden, float *out, void *stream)
+{
+    static const char *fn = "moe_combine_residual";
+    if (!y_packed || !route || !topk_weights || !out || !route->token_to_perm)
+        return fail(MOE_ERR_ARG, "%s: null pointer", fn);
+    if (!sizes_ok(route->M, route->top_k, route->num_experts))
+        return fail(MOE_ERR_ARG, "%s: route is not filled", fn);
+    if (hidden <= 0 || hidden % 4)
+        return fail(MOE_ERR_SHAPE, "%s: hidden %d must be a positive multiple of 4", fn, hidden);
+    if (!aligned16(y_packed) || !aligned16(out) || (shared_out && !aligned16(shared_out)) ||
+        (residual && !aligned16(residual)))
+        return fail(MOE_ERR_ARG, "%s: y, out, shared_out and residual must be 16-byte aligned", fn);
+    hipError_t e = launch_combine(y_packed, route->token_to_perm, topk_weights, route->M,
+                                  route->top_k, hidden, shared_out, residual, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_combine_residual: launch");
+    return MOE_OK;
+}
+
+size_t moe_shared_workspace_bytes(int32_t max_M, int32_t hidden, int32_t shared_width)
+{
+    if (max_M < 1 || max_M > MOE_GEMV_MAX_M || hidden <= 0 || shared_width <= 0 ||
+        hidden % 512 || shared_width % 512 || hidden > 8192 || shared_width > 8192)
+        return 0;
+    return moe::align256(sizeof(float) * (size_t)max_M * shared_width);
+}
+
+moe_status_t moe_shared_expert(const uint16_t *gate_bf16, const uint16_t *up_bf16,
+                               const uint16_t *down_bf16, const uint16_t *x_bf16, int32_t M,
+                               int32_t hidden, int32_t shared_width, float limit,
+                               float *shared_out, void *ws, size_t ws_bytes, void *stream)
+{
+    static const char *fn = "moe_shared_expert";
+    if (!gate_bf16 || !up_bf16 || !down_bf16 || !x_bf16 || !shared_out || !ws)
+        return fail(MOE_ERR_ARG, "%s: null pointer", fn);
+    if (M < 1) return fail(MOE_ERR_SHAPE, "%s: M must be >= 1 (M=%d)", fn, M);
+    if (M > MOE_GEMV_MAX_M)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: M = %d > %d (the shared expert runs the GEMV form only)",
+                    fn, M, MOE_GEMV_MAX_M);
+    if (hidden <= 0 || shared_width <= 0 || hidden % 512 || shared_width % 512 || hidden > 8192 ||
+        shared_width > 8192)
+        return fail(MOE_ERR_SHAPE, "%s: hidden %d and shared_width %d must be positive multiples of 512, "
+                    "at most 8192", fn, hidden, shared_width);
+    if (!(limit > 0.0f)) return fail(MOE_ERR_ARG, "%s: limit must be > 0", fn);
+    if (!aligned16(gate_bf16) || !aligned16(up_bf16) || !aligned16(down_bf16) || !aligned16(x_bf16) ||
+        !aligned16(shared_out))
+        return fail(MOE_ERR_ARG, "%s: weights, x and shared_out must be 16-byte aligned", fn);
+    if (((uintptr_t)ws & 255) != 0) return fail(MOE_ERR_ARG, "%s: ws not 256-byte aligned", fn);
+    const size_t need = moe_shared_workspace_bytes(M, hidden, shared_width);
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
+    hipError_t e = launch_shared_expert(gate_bf16, up_bf16, down_bf16, x_bf16, M, hidden, shared_width,
+                                        limit, (float *)ws, shared_out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_shared_expert: launch");
     return MOE_OK;
 }
 

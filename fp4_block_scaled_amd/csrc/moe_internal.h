@@ -172,8 +172,18 @@ hipError_t launch_gemm_down(const uint8_t *hq, const float *hs, const uint8_t *d
                             const int32_t *ntiles, int32_t tmax, int32_t hidden, int32_t inter,
                             float *y, hipStream_t st);
 
+// shared and residual ([M][hidden] FP32) may be null; each is added after
+// the routed sum, in that order.
 hipError_t launch_combine(const float *y, const int32_t *token_to_perm, const float *w,
-                          int32_t M, int32_t k, int32_t hidden, float *out, hipStream_t st);
+                          int32_t M, int32_t k, int32_t hidden, const float *shared,
+                          const float *residual, float *out, hipStream_t st);
+
+// Shared expert (dense bf16 SwiGLU MLP of width W) for M <= 16 tokens:
+// h [M][W] FP32 scratch, out [M][hidden] FP32.  hidden and W multiples of
+// 512 up to 8192.
+hipError_t launch_shared_expert(const uint16_t *gate, const uint16_t *up, const uint16_t *down,
+                                const uint16_t *x, int32_t M, int32_t hidden, int32_t W,
+                                float limit, float *h, float *out, hipStream_t st);
 
 // K chunking of the GEMV tier.  A segment is the K span of one 128-byte row
 // chunk (128 values for E4M3, 256 for NVFP4); both projections stream the

@@ -264,6 +264,40 @@ moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const
                              float *out, void *ws, size_t ws_bytes, moe_route_t *route,
                              void *stream);
 
+/* Shared expert: a dense SwiGLU MLP of width shared_width with bf16 weights,
+ * applied to every token with weight 1 ("spark_model
+ * glm5next_mlp/forward.rs", fn forward_dense: down(clamped_swiglu(gate(x),
+ * up(x))), the same math as a routed expert with its own clamp, and the
+ * shared-expert step of fn forward_moe, not routed-scaled).
+ *   gate_bf16, up_bf16  bf16 [shared_width][hidden]
+ *   down_bf16           bf16 [hidden][shared_width]
+ *   x_bf16              bf16 [M][hidden]
+ *   shared_out          float [M][hidden] out
+ *   ws                  >= moe_shared_workspace_bytes(M, hidden, shared_width)
+ *                       bytes, 256-byte aligned (h [M][shared_width] FP32)
+ * g, u, h and the outputs are FP32.  Rules: 1 <= M <= MOE_GEMV_MAX_M (wider M:
+ * MOE_ERR_UNSUPPORTED); hidden and shared_width positive multiples of 512 up
+ * to 8192; limit > 0; pointers 16-byte aligned.  Two launches on `stream`;
+ * allocates nothing. */
+size_t moe_shared_workspace_bytes(int32_t max_M, int32_t hidden, int32_t shared_width);
+moe_status_t moe_shared_expert(const uint16_t *gate_bf16, const uint16_t *up_bf16,
+                               const uint16_t *down_bf16, const uint16_t *x_bf16, int32_t M,
+                               int32_t hidden, int32_t shared_width, float limit,
+                               float *shared_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Combine with the shared expert and the residual:
+ *   out[t][m] = ((sum_j w[t][j] * y[perm(t, j)][m]) + shared_out[t][m]) + residual[t][m]
+ * the routed combine of moe_combine (slot order, multiply then add), then one
+ * rounded FP32 addition of the shared expert's row, then one of the residual
+ * ("memra-engine src/bin/ep_step_fp8_gate.rs", the full-layer gate's final
+ * add order routed-plus-shared-then-residual).  shared_out and residual are
+ * float [M][hidden] (device) and may each be NULL (not added); with both NULL
+ * this is moe_combine.  Same rules as moe_combine. */
+moe_status_t moe_combine_residual(const float *y_packed, const moe_route_t *route,
+                                  const float *topk_weights, const float *shared_out,
+                                  const float *residual, int32_t hidden, float *out,
+                                  void *stream);
+
 /* Stage timing (optional, thread-local).  With events != NULL, later
  * moe_expert_ffn calls on this thread record events[0] on their stream before
  * the first kernel and events[i] after the i-th kernel, for at most

@@ -257,3 +257,52 @@ def test_router_error_contract_on_host():
     assert router(scale=float("inf")) == B.MOE_ERR_ARG
     assert router(scale=float("nan")) == B.MOE_ERR_ARG
     assert router(renorm=2) == B.MOE_ERR_ARG
+
+
+def test_shared_expert_workspace_and_error_contract_on_host():
+    from fp4_block_scaled_amd import binding as B
+    L = B.lib
+    # h [M][W] FP32, rounded up to 256 bytes
+    assert L.moe_shared_workspace_bytes(1, 7168, 2048) == 4 * 2048
+    assert L.moe_shared_workspace_bytes(3, 512, 1536) == a256(4 * 3 * 1536)
+    assert L.moe_shared_workspace_bytes(16, 8192, 8192) == 4 * 16 * 8192
+    for args in [(0, 512, 512), (17, 512, 512), (1, 500, 512), (1, 512, 1000), (1, 8704, 512),
+                 (1, 512, 8704), (1, 0, 512)]:
+        assert L.moe_shared_workspace_bytes(*args) == 0, args
+
+    def shared(M=2, H=512, W=512, limit=7.0, ws=FAKE + 0x100000, nbytes=1 << 20, x=FAKE + 0x1000,
+               out=FAKE + 0x2000, gate=FAKE + 0x3000):
+        return L.moe_shared_expert(gate, FAKE + 0x4000, FAKE + 0x5000, x, M, H, W, limit, out, ws,
+                                   nbytes, None)
+
+    assert shared(x=None) == B.MOE_ERR_ARG
+    assert shared(out=None) == B.MOE_ERR_ARG
+    assert shared(ws=None) == B.MOE_ERR_ARG
+    assert shared(M=0) == B.MOE_ERR_SHAPE
+    assert shared(M=17) == B.MOE_ERR_UNSUPPORTED
+    assert shared(H=640) == B.MOE_ERR_SHAPE
+    assert shared(W=8704) == B.MOE_ERR_SHAPE
+    assert shared(limit=0.0) == B.MOE_ERR_ARG
+    assert shared(limit=float("nan")) == B.MOE_ERR_ARG
+    assert shared(gate=FAKE + 0x3008) == B.MOE_ERR_ARG
+    assert shared(ws=FAKE + 0x100040) == B.MOE_ERR_ARG
+    assert shared(nbytes=4 * 2 * 512 - 4) == B.MOE_ERR_WORKSPACE
+
+
+def test_combine_residual_error_contract_on_host():
+    from fp4_block_scaled_amd import binding as B
+    L = B.lib
+    rr = _route(B, FAKE + 0x100000)
+
+    def cr(y=FAKE, w=FAKE + 0x1000, sh=None, res=None, H=256, out=FAKE + 0x2000, route=rr):
+        return L.moe_combine_residual(y, C.byref(route), w, sh, res, H, out, None)
+
+    assert cr(y=None) == B.MOE_ERR_ARG
+    assert cr(w=None) == B.MOE_ERR_ARG
+    assert cr(out=None) == B.MOE_ERR_ARG
+    assert cr(H=258) == B.MOE_ERR_SHAPE
+    assert cr(sh=FAKE + 0x3004) == B.MOE_ERR_ARG
+    assert cr(res=FAKE + 0x3008) == B.MOE_ERR_ARG
+    empty = B.moe_route_t()
+    empty.token_to_perm = FAKE
+    assert cr(route=empty) == B.MOE_ERR_ARG

@@ -181,6 +181,35 @@ def make_x(wl: Workload, device, seed: Optional[int] = None, M: Optional[int] = 
 
 
 # --------------------------------------------------------------------------
+# shared expert and residual
+# --------------------------------------------------------------------------
+
+def make_shared_expert(hidden: int, width: int, seed: int, device, gate_std: float = 2.5):
+    """bf16 (gate [W, H], up [W, H], down [H, W]) of a shared expert.
+
+    Entries N(0, s^2) rounded to bf16, s = gate_std / sqrt(H) for gate and up
+    (so with N(0,1) activations g and u are about N(0, gate_std^2) and the
+    clamp at 7 is reached now and then) and 1 / sqrt(W) for down."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    sg = gate_std / hidden ** 0.5
+    gate = (torch.randn((width, hidden), generator=g, device=device) * sg).to(torch.bfloat16)
+    up = (torch.randn((width, hidden), generator=g, device=device) * sg).to(torch.bfloat16)
+    down = (torch.randn((hidden, width), generator=g, device=device) / width ** 0.5) \
+        .to(torch.bfloat16)
+    return gate.contiguous(), up.contiguous(), down.contiguous()
+
+
+def make_residual(M: int, hidden: int, seed: int, device) -> torch.Tensor:
+    """FP32 residual rows N(0, 1)."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn((M, hidden), generator=g, device=device, dtype=torch.float32)
+
+
+# --------------------------------------------------------------------------
 # routes (host, FP64)
 # --------------------------------------------------------------------------
 
