@@ -24,6 +24,7 @@ import time
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA (no sparsity)
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA (no sparsity)
 METRIC = "µs/MoE layer + weight-read GB/s (% HBM peak) at M=1; tokens/s at M=4096"
 
 
@@ -34,7 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_e4m3_m1")
     ap.add_argument("--route-sets", type=int, default=16)
-    ap.add_argument("--also", default="verify_e4m3_m8,nvfp4_m1,nvfp4_m16,prefill_e4m3_m4096",
+    ap.add_argument("--also", default="verify_e4m3_m8,nvfp4_m1,nvfp4_m16,prefill_e4m3_m4096,nvfp4_m4096",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -234,6 +235,8 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=F
         sums_stable = all(sums[i] == sums[i % route_sets] for i in range(steps))
         if mode == B.MOE_MODE_GEMM_A8:
             names = ["route_pack", "act_quant_tiles", "gateup_gemm", "down_gemm", "combine"]
+        elif mode == B.MOE_MODE_GEMM_A16:
+            names = ["route_pack", "tiles", "gateup_gemm", "down_gemm", "combine"]
         elif mode == B.MOE_MODE_FUSED:
             names = ["host", "fused_layer", "tail"]
         else:
@@ -341,6 +344,14 @@ def roofline(r):
         tf = flop / (us * 1e-6) / 1e12
         return {"kernel": "gemm_gateup", "bound": "mfma", "achieved": round(tf, 1),
                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(r["name"]), "alg_flop_per_launch": round(flop),
+                "avg_launch_us": round(us, 3)}
+    if r["mode"] == 4:
+        us = r["stages"]["gateup_gemm"]
+        flop = r["flops"] * 2.0 / 3.0
+        tf = flop / (us * 1e-6) / 1e12
+        return {"kernel": "gemm_gateup_nvfp4", "bound": "mfma", "achieved": round(tf, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(r["name"]), "alg_flop_per_launch": round(flop),
                 "avg_launch_us": round(us, 3)}
     us = r["stages"]["gateup_gemv"]
@@ -591,6 +602,10 @@ def main():
             also[name].update({"tier": "fp8_mfma_grouped_gemm", "alg_TFLOPs": round(tf, 1),
                                "mfma_frac_fp8": round(tf / FP8_PEAK_TFLOPS, 4)})
             line["prefill_tokens_per_s"] = also[name]["tokens_per_s"]
+        elif r2["mode"] == 4:
+            also[name].update({"tier": "bf16_mfma_grouped_gemm_w4a16", "alg_TFLOPs": round(tf, 1),
+                               "mfma_frac_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
+            line["nvfp4_prefill_tokens_per_s"] = also[name]["tokens_per_s"]
         print(f"# {name}: {r2['us_layer']:.2f} us/layer", file=sys.stderr, flush=True)
         if not same:
             del b2

@@ -29,6 +29,7 @@ MOE_MODE_AUTO = 0
 MOE_MODE_GEMV_A16 = 1
 MOE_MODE_GEMM_A8 = 2
 MOE_MODE_FUSED = 3
+MOE_MODE_GEMM_A16 = 4
 
 MOE_ROUTER_SOFTMAX = 0
 MOE_ROUTER_SIGMOID = 1

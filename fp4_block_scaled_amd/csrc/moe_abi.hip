@@ -61,10 +61,15 @@ bool sizes_ok(int32_t M, int32_t top_k, int32_t E)
 int32_t resolve(int32_t M, int32_t fmt, int32_t requested)
 {
     if (requested == MOE_MODE_GEMV_A16 || requested == MOE_MODE_GEMM_A8 ||
-        requested == MOE_MODE_FUSED)
+        requested == MOE_MODE_FUSED || requested == MOE_MODE_GEMM_A16)
         return requested;
-    (void)fmt;
-    return M <= MOE_GEMV_MAX_M ? MOE_MODE_GEMV_A16 : MOE_MODE_GEMM_A8;
+    if (M <= MOE_GEMV_MAX_M) return MOE_MODE_GEMV_A16;
+    return fmt == MOE_W_NVFP4_B16 ? MOE_MODE_GEMM_A16 : MOE_MODE_GEMM_A8;
+}
+
+bool valid_mode(int32_t mode)
+{
+    return mode >= MOE_MODE_AUTO && mode <= MOE_MODE_GEMM_A16;
 }
 
 bool ffn_dims_ok(int32_t fmt, int32_t hidden, int32_t inter)
@@ -143,16 +148,47 @@ void carve_route(void *ws, int32_t M, int32_t top_k, int32_t E, moe_route_t *rou
     route->status = (int32_t *)p + 1;
 }
 
-// The GEMM tier addresses activation rows with 32-bit byte offsets.
-bool gemm_dims_ok(int64_t M, int64_t S, int32_t hidden, int32_t inter)
+// The GEMM tiers address activation rows with 32-bit byte offsets (bf16
+// rows in the A16 tier: two bytes per element).
+bool gemm_dims_ok(int64_t M, int64_t S, int32_t hidden, int32_t inter, int32_t elem_bytes = 1)
 {
-    return M * hidden < (int64_t(1) << 31) && S * inter < (int64_t(1) << 31);
+    return M * hidden * elem_bytes < (int64_t(1) << 31) &&
+           S * inter * elem_bytes < (int64_t(1) << 31);
+}
+
+// Scratch of the bf16 GEMM tier: h hi and h lo bf16 [S][inter], the tiles.
+struct GemmA16Scratch {
+    uint16_t *hhi, *hlo;
+    int4 *tiles;
+    int32_t *ntiles;
+};
+
+size_t gemm_a16_scratch_bytes(int64_t S, int32_t E, int32_t inter)
+{
+    const int64_t tmax = gemm_max_tiles((int32_t)S, E);
+    return 2 * moe::align256(2 * (size_t)(S * inter)) +
+           moe::align256(sizeof(int4) * (size_t)tmax) + 256;
+}
+
+GemmA16Scratch carve_gemm_a16(char *p, int64_t S, int32_t E, int32_t inter)
+{
+    GemmA16Scratch g;
+    const int64_t tmax = gemm_max_tiles((int32_t)S, E);
+    g.hhi = (uint16_t *)p;  p += moe::align256(2 * (size_t)(S * inter));
+    g.hlo = (uint16_t *)p;  p += moe::align256(2 * (size_t)(S * inter));
+    g.tiles = (int4 *)p;    p += moe::align256(sizeof(int4) * (size_t)tmax);
+    g.ntiles = (int32_t *)p;
+    return g;
 }
 
 size_t ffn_bytes(int64_t M, int64_t S, int32_t E, int32_t hidden, int32_t inter, int32_t fmt,
                  int32_t mode)
 {
     if (mode == MOE_MODE_GEMV_A16) return gemv_scratch_bytes(S, inter);
+    if (mode == MOE_MODE_GEMM_A16) {
+        if (fmt != MOE_W_NVFP4_B16 || !gemm_dims_ok(M, S, hidden, inter, 2)) return 0;
+        return gemm_a16_scratch_bytes(S, E, inter);
+    }
     if (fmt != MOE_W_E4M3_B128 || !gemm_dims_ok(M, S, hidden, inter)) return 0;
     return gemm_scratch_bytes(M, S, E, hidden, inter);
 }
@@ -171,7 +207,8 @@ int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt,
     (void)fmt; (void)hidden; (void)inter;
     // GEMV tier: gate/up GEMV with SwiGLU, down GEMV
     // fused layer: its one launch
-    // GEMM tier: activation quantization + tile schedule, gate/up GEMM, down GEMM
+    // FP8 GEMM tier: activation quantization + tile schedule, gate/up GEMM, down GEMM
+    // bf16 GEMM tier: tile schedule, gate/up GEMM, down GEMM
     return mode == MOE_MODE_GEMV_A16 ? 2 : mode == MOE_MODE_FUSED ? 1 : 3;
 }
 
@@ -185,7 +222,7 @@ size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts, in
 {
     if (!sizes_ok(max_M, top_k, num_experts)) return 0;
     if (fmt != MOE_W_E4M3_B128 && fmt != MOE_W_NVFP4_B16) return 0;
-    if (mode < MOE_MODE_AUTO || mode > MOE_MODE_FUSED) return 0;
+    if (!valid_mode(mode)) return 0;
     if (!ffn_dims_ok(fmt, hidden, inter)) return 0;
     const int64_t S = (int64_t)max_M * top_k;
     if (mode == MOE_MODE_FUSED) {
@@ -201,7 +238,8 @@ size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts, in
         // limits); a call above MOE_GEMV_MAX_M tokens outside them is
         // refused by moe_expert_ffn
         if (max_M > MOE_GEMV_MAX_M) {
-            const size_t g = ffn_bytes(max_M, S, num_experts, hidden, inter, fmt, MOE_MODE_GEMM_A8);
+            const size_t g = ffn_bytes(max_M, S, num_experts, hidden, inter, fmt,
+                                       resolve(max_M, fmt, MOE_MODE_AUTO));
             ffn = g > ffn ? g : ffn;
         }
     } else {
@@ -266,7 +304,7 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
     const int32_t fmt = gate->fmt;
     if (fmt != MOE_W_E4M3_B128 && fmt != MOE_W_NVFP4_B16)
         return fail(MOE_ERR_FORMAT, "moe_expert_ffn: unknown weight format %d", fmt);
-    if (mode < MOE_MODE_AUTO || mode > MOE_MODE_GEMM_A8)
+    if (!valid_mode(mode) || mode == MOE_MODE_FUSED)
         return fail(MOE_ERR_ARG, "moe_expert_ffn: unknown mode %d%s", mode,
                     mode == MOE_MODE_FUSED ? " (the fused layer is moe_layer_fused)" : "");
     if (!ffn_dims_ok(fmt, hidden, inter))
@@ -292,6 +330,15 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
         return fail(MOE_ERR_SHAPE,
                     "moe_expert_ffn: GEMM tier needs M*hidden and M*top_k*inter < 2^31 "
                     "(M=%d top_k=%d hidden=%d inter=%d)", M, k, hidden, inter);
+    if (tier == MOE_MODE_GEMM_A16 && fmt != MOE_W_NVFP4_B16)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: the bf16 GEMM tier serves NVFP4 banks only");
+    if (tier == MOE_MODE_GEMM_A16 && !gemm_dims_ok(M, (int64_t)M * k, hidden, inter, 2))
+        return fail(MOE_ERR_SHAPE,
+                    "moe_expert_ffn: bf16 GEMM tier needs 2*M*hidden and 2*M*top_k*inter < 2^31 "
+                    "(M=%d top_k=%d hidden=%d inter=%d)", M, k, hidden, inter);
+    if (tier == MOE_MODE_GEMM_A16 && (((uintptr_t)gate->scales | (uintptr_t)up->scales |
+                                       (uintptr_t)down->scales) & 3))
+        return fail(MOE_ERR_ARG, "moe_expert_ffn: the bf16 GEMM tier needs 4-byte aligned scales");
     const size_t need = moe_workspace_bytes(M, k, E, hidden, inter, fmt, tier);
     if (ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu bytes < %zu", ws_bytes, need);
@@ -322,11 +369,28 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
         stage_mark(3, s);
         return MOE_OK;
     }
-    float *h = (float *)scratch;
     GemvBankDev bg{gate->codes, gate->scales, gate->scale2};
     GemvBankDev bu{up->codes, up->scales, up->scale2};
     GemvBankDev bd{down->codes, down->scales, down->scale2};
     hipError_t e;
+    if (tier == MOE_MODE_GEMM_A16) {
+        GemmA16Scratch gs = carve_gemm_a16(scratch, S, E, inter);
+        const int32_t tmax = gemm_max_tiles((int32_t)S, E);
+        stage_mark(0, s);
+        e = launch_gemm_tiles(r.offsets, E, tmax, gs.tiles, gs.ntiles, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: tile schedule launch");
+        stage_mark(1, s);
+        e = launch_gemm_gateup_nvfp4(x_bf16, r.sorted_token, bg, bu, r.offsets, gs.tiles, gs.ntiles,
+                                     tmax, hidden, inter, limit, gs.hhi, gs.hlo, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: gate/up GEMM launch");
+        stage_mark(2, s);
+        e = launch_gemm_down_nvfp4(gs.hhi, gs.hlo, bd, r.offsets, gs.tiles, gs.ntiles, tmax, hidden,
+                                   inter, y_packed, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: down GEMM launch");
+        stage_mark(3, s);
+        return MOE_OK;
+    }
+    float *h = (float *)scratch;
     stage_mark(0, s);
     if (fmt == MOE_W_E4M3_B128)
         e = launch_gemv_gateup_e4m3(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, limit, h, s);

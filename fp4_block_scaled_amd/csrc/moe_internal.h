@@ -172,6 +172,19 @@ hipError_t launch_gemm_down(const uint8_t *hq, const float *hs, const uint8_t *d
                             const int32_t *ntiles, int32_t tmax, int32_t hidden, int32_t inter,
                             float *y, hipStream_t st);
 
+// bf16 MFMA GEMM tier (NVFP4 banks, wide M): gate/up with SwiGLU writes h as
+// a pair of bf16 arrays (hi, lo) [S][inter]; down reads both.
+hipError_t launch_gemm_gateup_nvfp4(const uint16_t *x, const int32_t *sorted_token,
+                                    const GemvBankDev &gate, const GemvBankDev &up,
+                                    const int32_t *offsets, const int4 *tiles,
+                                    const int32_t *ntiles, int32_t tmax, int32_t hidden,
+                                    int32_t inter, float limit, uint16_t *hhi, uint16_t *hlo,
+                                    hipStream_t st);
+hipError_t launch_gemm_down_nvfp4(const uint16_t *hhi, const uint16_t *hlo, const GemvBankDev &down,
+                                  const int32_t *offsets, const int4 *tiles, const int32_t *ntiles,
+                                  int32_t tmax, int32_t hidden, int32_t inter, float *y,
+                                  hipStream_t st);
+
 // shared and residual ([M][hidden] FP32) may be null; each is added after
 // the routed sum, in that order.
 hipError_t launch_combine(const float *y, const int32_t *token_to_perm, const float *w,

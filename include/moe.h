@@ -65,7 +65,8 @@ enum {
 
 /* Execution tiers. */
 enum {
-    MOE_MODE_AUTO = 0,      /* GEMV_A16 for M <= MOE_GEMV_MAX_M, else GEMM_A8   */
+    MOE_MODE_AUTO = 0,      /* GEMV_A16 for M <= MOE_GEMV_MAX_M; above that
+                               GEMM_A8 for E4M3 banks, GEMM_A16 for NVFP4     */
     /* Dequant-GEMV, bf16 activations, each active expert's weights streamed
      * once for all slots routed to it ("spark_model glm5next_mlp/forward.rs",
      * fn w4a16_gemv_moe_batchm: the union of the rows' experts, each swept
@@ -78,7 +79,15 @@ enum {
     MOE_MODE_GEMM_A8 = 2,
     /* Not a tier of moe_expert_ffn: the workspace mode of moe_layer_fused
      * (route pack, gate/up, SwiGLU, down and combine in one launch). */
-    MOE_MODE_FUSED = 3
+    MOE_MODE_FUSED = 3,
+    /* Grouped bf16 MFMA GEMM over expert-sorted rows for NVFP4 banks: the
+     * pages' W4A16 form (bf16 activations as given; "spark_model
+     * glm5next_mlp/forward.rs", fn w4a16_gemv and its batched variant) at
+     * prefill widths.  Each E2M1 code times its E4M3 group scale is exact in
+     * bf16; scale_2 multiplies the FP32 sums.  h is kept as a bf16 pair
+     * (hi, lo) whose sum is the FP32 h to about 2^-16.  NVFP4 banks only;
+     * scales must be 4-byte aligned. */
+    MOE_MODE_GEMM_A16 = 4
 };
 
 /* Routers of moe_router_topk. */
@@ -210,7 +219,10 @@ moe_status_t moe_route_pack(const int32_t *topk_ids, int32_t M, int32_t top_k,
  * <= MOE_MAX_DIM; gate/up are inter x hidden,
  * down is hidden x inter; all banks share one format and num_experts;
  * hidden, inter <= MOE_MAX_DIM; GEMM_A8 needs E4M3 banks, and M*hidden
- * and M*top_k*inter < 2^31 (MOE_ERR_SHAPE otherwise);
+ * and M*top_k*inter < 2^31 (MOE_ERR_SHAPE otherwise); GEMM_A16 needs NVFP4
+ * banks with 4-byte aligned scales, and 2*M*hidden and 2*M*top_k*inter
+ * < 2^31 (a tier that does not serve the banks' format returns
+ * MOE_ERR_UNSUPPORTED);
  * ws_bytes >= moe_workspace_bytes(route->M, ..., mode). */
 moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up,
                             const moe_bank_t *down, const uint16_t *x_bf16,
@@ -304,8 +316,9 @@ moe_status_t moe_combine_residual(const float *y_packed, const moe_route_t *rout
  * n_events events; NULL turns it off.  The handles are the caller's
  * hipEvent_t.  Returns the number of stages the tier `mode` records (2 for
  * MOE_MODE_GEMV_A16: gate/up with SwiGLU, down; 1 for MOE_MODE_FUSED, where
- * moe_layer_fused records around its single launch; 3 otherwise, the GEMM
- * tier's activation quantization + tile schedule, gate/up with SwiGLU,
+ * moe_layer_fused records around its single launch; 3 otherwise: for
+ * MOE_MODE_GEMM_A8 activation quantization + tile schedule, gate/up with
+ * SwiGLU, down; for MOE_MODE_GEMM_A16 tile schedule, gate/up with SwiGLU,
  * down), so n_events = 4 covers every tier.  Mirrors the
  * per-stage timers of "spark_model glm5next_mlp/forward.rs" (profile::start /
  * profile::end around the MoE stages). */

@@ -82,17 +82,31 @@ def test_workspace_bytes_rejects_bad_sizes(args):
     assert B.lib.moe_workspace_bytes(*args) == 0
 
 
-def test_auto_workspace_skips_a_gemm_tier_that_cannot_run():
+def test_auto_workspace_sizes_the_tier_each_format_runs():
     from fp4_block_scaled_amd import binding as B
     L = B.lib
-    # NVFP4 banks have no GEMM tier: AUTO sizes the GEMV scratch (for up to
-    # MOE_GEMV_MAX_M tokens) and the route region for max_M
-    auto = L.moe_workspace_bytes(20, 8, 20, 1024, 512, B.MOE_W_NVFP4_B16, B.MOE_MODE_AUTO)
-    gemv = L.moe_workspace_bytes(16, 8, 20, 1024, 512, B.MOE_W_NVFP4_B16, B.MOE_MODE_GEMV_A16)
-    assert auto > 0 and auto >= gemv
-    # same for E4M3 past the GEMM tier's 32-bit row offsets (M * hidden = 2^31)
+    # NVFP4 above MOE_GEMV_MAX_M tokens runs the bf16 GEMM tier: route region
+    # + max(GEMV scratch for 16 tokens, h hi + h lo bf16 [S][I] + tiles + count)
+    M, k, E, H, I = 20, 8, 20, 1024, 512
+    S = M * k
+    tmax = min(S, E) + (S + 127) // 128
+    route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
+    a16 = 2 * a256(2 * S * I) + a256(16 * tmax) + 256
+    assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_GEMM_A16) == route + a16
+    gemv16 = a256(4 * 16 * k * I)
+    assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_AUTO) == \
+        route + max(a16, gemv16)
+    # each GEMM tier serves one format
+    assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMM_A16) == 0
+    assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_GEMM_A8) == 0
+    assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_NVFP4_B16, 5) == 0
+    # E4M3 past the FP8 GEMM tier's 32-bit row offsets (M * hidden = 2^31):
+    # AUTO sizes the GEMV scratch only
     assert L.moe_workspace_bytes(131072, 1, 256, 16384, 128, B.MOE_W_E4M3_B128, B.MOE_MODE_AUTO) > 0
     assert L.moe_workspace_bytes(131072, 1, 256, 16384, 128, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMM_A8) == 0
+    # the bf16 tier's rows are 2 bytes an element: 2^30 elements is the limit
+    assert L.moe_workspace_bytes(65536, 1, 256, 16384, 256, B.MOE_W_NVFP4_B16, B.MOE_MODE_GEMM_A16) == 0
+    assert L.moe_workspace_bytes(65535, 1, 256, 16384, 256, B.MOE_W_NVFP4_B16, B.MOE_MODE_GEMM_A16) > 0
 
 
 def test_resolve_mode():
@@ -100,6 +114,9 @@ def test_resolve_mode():
     assert B.moe_resolve_mode(1, B.MOE_W_E4M3_B128) == B.MOE_MODE_GEMV_A16
     assert B.moe_resolve_mode(16, B.MOE_W_NVFP4_B16) == B.MOE_MODE_GEMV_A16
     assert B.moe_resolve_mode(17, B.MOE_W_E4M3_B128) == B.MOE_MODE_GEMM_A8
+    assert B.moe_resolve_mode(17, B.MOE_W_NVFP4_B16) == B.MOE_MODE_GEMM_A16
+    assert B.moe_resolve_mode(4096, B.MOE_W_NVFP4_B16) == B.MOE_MODE_GEMM_A16
+    assert B.moe_resolve_mode(8, B.MOE_W_NVFP4_B16, B.MOE_MODE_GEMM_A16) == B.MOE_MODE_GEMM_A16
     assert B.moe_resolve_mode(4096, B.MOE_W_E4M3_B128, B.MOE_MODE_GEMV_A16) == B.MOE_MODE_GEMV_A16
 
 
@@ -155,6 +172,15 @@ def test_ffn_error_contract_on_host():
     # bad limit, unknown mode
     assert _ffn(B, g, u, d, r, ws, limit=0.0) == B.MOE_ERR_ARG
     assert _ffn(B, g, u, d, r, ws, mode=5) == B.MOE_ERR_ARG
+    # each GEMM tier serves one format; the bf16 tier reads scales as dwords
+    assert _ffn(B, g, u, d, r, ws, mode=B.MOE_MODE_GEMM_A16) == B.MOE_ERR_UNSUPPORTED
+    nv = _bank(B, fmt=2, k=256, n=256, scale2=FAKE)
+    assert _ffn(B, nv, nv, nv, r, ws, hidden=256, inter=256,
+                mode=B.MOE_MODE_GEMM_A8) == B.MOE_ERR_UNSUPPORTED
+    odd = B.moe_bank_t(2, 16, 256, 256, FAKE, FAKE + 0x1002, FAKE)
+    assert _ffn(B, nv, odd, nv, r, ws, hidden=256, inter=256,
+                mode=B.MOE_MODE_GEMM_A16) == B.MOE_ERR_ARG
+    assert "4-byte" in B.moe_last_error()
     # hidden beyond MOE_MAX_DIM, any tier
     big = 16512
     rg = _route(B, ws, M=32)

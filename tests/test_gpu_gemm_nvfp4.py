@@ -1,0 +1,117 @@
+"""GPU parity of the bf16 MFMA grouped-GEMM tier for NVFP4 banks (wide M)
+against the oracle.
+
+The tier keeps the GEMV tier's numerics: x is bf16 as given, every weight
+(E2M1 code x E4M3 group scale) is exact in bf16, scale_2 multiplies the FP32
+sums, and h travels as a bf16 pair whose sum is the FP32 h to about 2^-16.
+So the layer's tolerance (max|err| <= 2e-3 * max|ref|, relative L2 <= 1e-3)
+is checked against the oracle's plain FP64 layer, on the whole output and on
+every packed y row: reduced shapes with several full and partial 128-row
+tiles per expert and K loops of 4 to 20 steps, one expert taking every
+token, invalid ids, the tier forced at a handful of tokens (against the GEMV
+tier too), and the prefill size M=4096 on sampled tokens."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from fp4_block_scaled_amd import binding as B
+from moe_cases import GpuCase, check_fp, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+A16 = B.MOE_MODE_GEMM_A16
+_cache = {}
+
+
+def get_case(wl):
+    key = (wl.name, wl.hidden, wl.inter, wl.experts, wl.top_k, wl.seed)
+    if key not in _cache:
+        _cache.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+        _cache[key] = GpuCase(wl)
+    return _cache[key]
+
+
+def run_a16(case, ids, w, tokens=None, label="", mode=A16):
+    wl = case.wl
+    assert B.moe_resolve_mode(ids.shape[0], wl.fmt, mode) == A16
+    out, y, tabs, _ = case.run(ids, w, mode)
+    ref_out, ref_y = oracle_layer(case.banks, case.x, ids, w, wl.limit, act_fp8=False, tokens=tokens)
+    sel = np.arange(ids.shape[0]) if tokens is None else np.asarray(tokens)
+    r = check_fp(out[sel], ref_out, f"{label} out")
+    t2p = tabs["token_to_perm"].reshape(ids.shape)
+    pairs = [(t2p[t, j], i * ids.shape[1] + j) for i, t in enumerate(sel)
+             for j in range(ids.shape[1]) if t2p[t, j] >= 0]
+    if pairs:
+        p, s = np.array(pairs).T
+        check_fp(y[p], ref_y[s], f"{label} y rows")
+    print(f"  {label}: max err frac {r[0]:.2e}, rel L2 {r[1]:.2e}", flush=True)
+    return out
+
+
+REDUCED = [
+    # name, overrides, M: K loops of 4..20 steps of 64, 1..5 tiles per expert
+    ("nv_h512_i256_e8_k2", dict(hidden=512, inter=256, experts=8, top_k=2), 300),
+    ("nv_h256_i768_e5_k3", dict(hidden=256, inter=768, experts=5, top_k=3), 100),
+    ("nv_h1280_i512_e16_k4", dict(hidden=1280, inter=512, experts=16, top_k=4), 77),
+    ("nv_h768_i256_e3_k1", dict(hidden=768, inter=256, experts=3, top_k=1), 20),
+    ("nv_h2048_i1536_e12_k8", dict(hidden=2048, inter=1536, experts=12, top_k=8), 64),
+]
+
+
+@pytest.mark.parametrize("name,over,M", REDUCED, ids=[r[0] for r in REDUCED])
+def test_a16_tier_reduced_shapes_full_oracle(name, over, M):
+    base = workloads.WORKLOADS["nvfp4_m4096"]
+    wl = workloads.with_shape(base, name=name, M=M, **over)
+    case = get_case(wl)
+    ids, w, info = workloads.make_routes(wl, 0)
+    print(f"A16 tier {name} M={M} max load {info['max_load']}", flush=True)
+    run_a16(case, ids, w, label=name, mode=B.MOE_MODE_AUTO)
+
+
+def test_a16_tier_skewed_and_invalid_ids():
+    base = workloads.WORKLOADS["nvfp4_m4096"]
+    wl = workloads.with_shape(base, name="nv_skew", hidden=512, inter=512, experts=6, top_k=2, M=400)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 0)
+    ids[:, 0] = 2                      # one expert takes every token: 4 tiles
+    ids[5, 1] = -1
+    ids[9, 1] = 99
+    ids[ids[:, 1] == 2, 1] = 3
+    print("A16 tier skewed", flush=True)
+    run_a16(case, ids, w, label="skewed")
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_a16_tier_forced_at_few_tokens_matches_gemv(M):
+    base = workloads.WORKLOADS["nvfp4_m4096"]
+    wl = workloads.with_shape(base, name="nv_few", hidden=1024, inter=768, experts=10, top_k=4, M=16)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 0, M=M)
+    print(f"A16 tier forced M={M}", flush=True)
+    out = run_a16(case, ids, w, label=f"forced M{M}")
+    gemv, _, _, _ = case.run(ids, w, B.MOE_MODE_GEMV_A16)
+    check_fp(out[:M], gemv[:M], f"A16 vs GEMV M{M}", max_frac=1e-4, rel_l2=1e-5)
+
+
+def test_a16_tier_prefill_full_size_sampled_tokens():
+    wl = workloads.WORKLOADS["nvfp4_m4096"]
+    case = get_case(wl)
+    ids, w, info = workloads.make_routes(wl, 0)
+    counts = np.bincount(ids.ravel(), minlength=wl.experts)
+    heavy = int(np.argmax(counts))
+    rng = np.random.default_rng(11)
+    toks = set(rng.choice(wl.M, 5, replace=False).tolist())
+    toks |= {0, wl.M - 1}
+    toks.add(int(np.nonzero((ids == heavy).any(axis=1))[0][-1]))
+    tokens = np.array(sorted(toks))
+    print(f"NVFP4 prefill M=4096: max load {info['max_load']} (expert {heavy}), mean "
+          f"{info['mean_load']:.1f}, checking tokens {tokens.tolist()}", flush=True)
+    out = run_a16(case, ids, w, tokens=tokens, label="nvfp4 prefill", mode=B.MOE_MODE_AUTO)
+    # run to run bit identity
+    out2, _, _, _ = case.run(ids, w, B.MOE_MODE_AUTO)
+    assert np.array_equal(out, out2)

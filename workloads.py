@@ -70,6 +70,9 @@ WORKLOADS = {
     "nvfp4_m16": Workload(
         "nvfp4_m16", 6144, 1536, 160, 8, 16, NVFP4_B16, "uniform2", "softmax",
         seed=1004, note="NVFP4 experts, M=16"),
+    "nvfp4_m4096": Workload(
+        "nvfp4_m4096", 6144, 1536, 160, 8, 4096, NVFP4_B16, "uniform2", "softmax",
+        seed=1004, note="NVFP4 experts, prefill M=4096 (the M=1/16 draws at prefill width)"),
 }
 
 
