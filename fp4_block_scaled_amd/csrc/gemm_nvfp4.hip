@@ -40,7 +40,6 @@ using moe::f32x4;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr int TM = 128;      // rows per tile
 constexpr int KS = 64;       // K per step (128 bytes of a bf16 row)
 
@@ -117,82 +116,140 @@ __device__ __forceinline__ uint32_t bf16_rne(float f)
     return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-// vmcnt wait that leaves `ahead` stages of `per` DMA instructions in flight
-#define NV_WAIT_AHEAD(kb, KB, per)                        \
-    do {                                                  \
-        if ((kb) + 2 < (KB)) MOE_WAIT_VM(2 * (per));      \
-        else if ((kb) + 1 < (KB)) MOE_WAIT_VM(per);       \
-        else MOE_WAIT_VM(0);                              \
-    } while (0)
+// vmcnt wait that leaves min(n, N) stages of PER DMA instructions in flight
+template <int PER, int N>
+__device__ __forceinline__ void wait_stages(int n)
+{
+    if constexpr (N == 0) {
+        MOE_WAIT_VM(0);
+    } else {
+        if (n >= N) MOE_WAIT_VM(N * PER);
+        else wait_stages<PER, N - 1>(n);
+    }
+}
+
+// Ring of NST LDS stages: K step kb lives in stage kb % NST.  The DMA for
+// step kb + NST - 1 goes out once every wave has passed the barrier of step
+// kb, i.e. is done reading stage (kb - 1) % NST; before that barrier each
+// wave waits until its own share of stage kb has landed, leaving the later
+// stages in flight.
+template <int NST, int PER, class Issue, class Compute>
+__device__ __forceinline__ void k_loop(int KB, uint8_t *sm, int stage_bytes, const Issue &issue,
+                                       const Compute &compute)
+{
+    MOE_WAIT_VM(0);    // retire the set-up loads before the DMA starts
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j)
+        if (j < KB) issue(j, sm + j * stage_bytes);
+    int cs = 0, is = NST - 1;
+    for (int kb = 0; kb < KB; ++kb) {
+        wait_stages<PER, NST - 2>(KB - 1 - kb);
+        MOE_WAIT_LGKM0();
+        MOE_BARRIER();
+        if (kb + NST - 1 < KB) issue(kb + NST - 1, sm + is * stage_bytes);
+        compute(sm + cs * stage_bytes);
+        cs = cs + 1 == NST ? 0 : cs + 1;
+        is = is + 1 == NST ? 0 : is + 1;
+    }
+    MOE_WAIT_VM(0);
+}
 
 // ---------------------------------------------------------------------------
 // gate + up (+ SwiGLU, h as hi/lo bf16)
 // ---------------------------------------------------------------------------
-// Stage: A [128 rows][128 B] | B codes [128 rows][32 B] (0-63 gate, 64-127 up)
-//        | B scales [4 runs][256 B]
-constexpr int GA = 0, GC = TM * 128, GS = GC + 128 * 32, GSTAGE = GS + 4 * 256;
-constexpr int G_DMA = 4 + 1 + 1;   // DMA instructions per wave per stage
+// Block: W waves; wave w = all 128 rows x h columns 32w..32w+31 of both gate
+// and up, so each decoded B operand feeds 8 MFMAs (one per 16-row group).
+// The tile is 128 rows x 32W h columns: 64W B rows, gate rows first, then up
+// rows; wave w loads B rows 64w..64w+63.
+// Stage: A [128][128 B] | B codes [64W][32 B] | B scales [64W][4 B]
+template <int W>
+struct GuLayout {
+    static constexpr int threads = 64 * W;
+    static constexpr int cols = 32 * W;
+    static constexpr int A = 0, C = TM * 128, S = C + 64 * W * 32, STAGE = S + 64 * W * 4;
+    static constexpr int arun = 16 / W;          // A runs of 8 rows per wave
+    static constexpr int dma = arun + 2 + 1;     // DMA instructions per wave per stage
+};
 
-__global__ __launch_bounds__(kThreads, 1) void gemm_gateup_nvfp4_kernel(NvGemmArgs a)
+// B operand of lane `lane` for B row `br` and K half ks, scales stored one
+// dword per row
+__device__ __forceinline__ bf16x8 b_op_lin(const uint8_t *codes, const uint8_t *scales, int br,
+                                           int ks, int lane)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t st0[GSTAGE], st1[GSTAGE], st2[GSTAGE], st3[GSTAGE];
+    const uint32_t c = *reinterpret_cast<const uint32_t *>(codes + br * 32 + ks * 16 + (lane >> 4) * 4);
+    const uint32_t sd = *reinterpret_cast<const uint32_t *>(scales + br * 4);
+    const uint32_t sb = sd >> ((lane >> 5) * 8);
+    const float sc = ks == 0 ? __builtin_amdgcn_cvt_f32_fp8((int)sb, 0)
+                             : __builtin_amdgcn_cvt_f32_fp8((int)sb, 2);
+    return dequant8(c, sc);
+}
+
+template <int W, int NST, int OCC>
+__global__ __launch_bounds__(GuLayout<W>::threads, OCC) void gemm_gateup_nvfp4_kernel(NvGemmArgs a)
+{
+    using Lo = GuLayout<W>;
+    __shared__ __attribute__((aligned(16))) uint8_t sm[NST * Lo::STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
     int4 tile;
     int nb;
     if (!gemm_item(a, tile, nb)) return;
     const int e = tile.x, p0 = tile.y;
     const int rows = moe::uniform(min(TM, a.offsets[e + 1] - p0));
     const int K = a.K, N = a.N, KB = K / KS;
-    const int n0 = nb * 64;
+    const int n0 = nb * Lo::cols;
     const float sg = a.g0[e], su = a.g1[e];
 
-    // A: four runs of 8 rows per wave (rows past the tile read its first row
-    // and are never stored)
-    uint32_t aoff[4];
+    // A: runs of 8 rows (rows past the tile read its first row and are
+    // never stored)
+    uint32_t aoff[Lo::arun];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = (wave * 4 + j) * 8 + (lane >> 3);
+    for (int j = 0; j < Lo::arun; ++j) {
+        const int r = (wave * Lo::arun + j) * 8 + (lane >> 3);
         const int tok = a.sorted_token[p0 + (r < rows ? r : 0)];
         aoff[j] = (uint32_t)tok * (uint32_t)(K * 2) + swz(r, lane & 7) * 16;
     }
-    // B: wave w loads B rows 32w..32w+31 (gate rows n0 + 32w.. for w < 2, up
-    // rows n0 + 32(w-2).. otherwise): codes 16 bytes per lane, scales one
-    // dword per lane (lanes 32-63 repeat lanes 0-31)
-    const size_t brow = (size_t)e * N + n0 + (wave & 1) * 32;
-    const uint8_t *cbase = (wave < 2 ? a.c0 : a.c1) + brow * (K / 2);
-    const uint8_t *sbase = (wave < 2 ? a.s0 : a.s1) + brow * (K / 16);
-    const uint32_t coff = (uint32_t)(lane >> 1) * (K / 2) + (lane & 1) * 16;
-    const uint32_t soff = (uint32_t)(lane & 31) * (K / 16);
+    // B rows 64w..64w+63: the first W/2 waves gate rows n0 + 64w.., the
+    // others up rows n0 + 64(w - W/2)..; codes in two runs of 32 rows (16
+    // bytes per lane), scales one dword per lane
+    const bool gate_rows = wave < W / 2;
+    const size_t brow = (size_t)e * N + n0 + (gate_rows ? wave : wave - W / 2) * 64;
+    const uint8_t *cbase = (gate_rows ? a.c0 : a.c1) + brow * (K / 2);
+    const uint8_t *sbase = (gate_rows ? a.s0 : a.s1) + brow * (K / 16);
+    const uint32_t coff0 = (uint32_t)(lane >> 1) * (K / 2) + (lane & 1) * 16;
+    const uint32_t coff1 = coff0 + 32 * (uint32_t)(K / 2);
+    const uint32_t soff = (uint32_t)lane * (K / 16);
 
     auto issue = [&](int kb, uint8_t *st) {
         const uint8_t *ab = reinterpret_cast<const uint8_t *>(a.a) + (size_t)kb * 128;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(ab, aoff[j], lds_addr(st + GA + (wave * 4 + j) * 1024));
-        dma16(cbase + (size_t)kb * 32, coff, lds_addr(st + GC + wave * 1024));
-        dma4(sbase + (size_t)kb * 4, soff, lds_addr(st + GS + wave * 256));
+        for (int j = 0; j < Lo::arun; ++j)
+            dma16(ab, aoff[j], lds_addr(st + Lo::A + (wave * Lo::arun + j) * 1024));
+        const uint8_t *cb = cbase + (size_t)kb * 32;
+        dma16(cb, coff0, lds_addr(st + Lo::C + wave * 2048));
+        dma16(cb, coff1, lds_addr(st + Lo::C + wave * 2048 + 1024));
+        dma4(sbase + (size_t)kb * 4, soff, lds_addr(st + Lo::S + wave * 256));
     };
 
-    f32x4 accg[4][2], accu[4][2];
+    f32x4 accg[8][2], accu[8][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) { accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f}; accu[i][j] = accg[i][j]; }
 
     auto compute = [&](const uint8_t *st) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 av[4];
+            bf16x8 av[8];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) av[mt] = a_op(st + GA, wm * 64 + mt * 16 + (lane & 15), ks, lane);
+            for (int mt = 0; mt < 8; ++mt) av[mt] = a_op(st + Lo::A, mt * 16 + (lane & 15), ks, lane);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const int rg = wn * 32 + nt * 16 + (lane & 15);
-                const bf16x8 bg = b_op(st + GC, st + GS, rg, ks, lane);
-                const bf16x8 bu = b_op(st + GC, st + GS, 64 + rg, ks, lane);
+                const int rg = wave * 32 + nt * 16 + (lane & 15);
+                const bf16x8 bg = b_op_lin(st + Lo::C, st + Lo::S, rg, ks, lane);
+                const bf16x8 bu = b_op_lin(st + Lo::C, st + Lo::S, Lo::cols + rg, ks, lane);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
+                for (int mt = 0; mt < 8; ++mt) {
                     accg[mt][nt] = mfma_bf16(av[mt], bg, accg[mt][nt]);
                     accu[mt][nt] = mfma_bf16(av[mt], bu, accu[mt][nt]);
                 }
@@ -200,55 +257,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_gateup_nvfp4_kernel(NvGemmAr
         }
     };
 
-    auto step = [&](int kb, const uint8_t *cur, uint8_t *later) {
-        NV_WAIT_AHEAD(kb, KB, G_DMA);
-        MOE_WAIT_LGKM0();
-        MOE_BARRIER();
-        if (kb + 3 < KB) issue(kb + 3, later);
-        compute(cur);
-    };
-
-    MOE_WAIT_VM(0);    // retire the offset and scale_2 loads above before the DMA starts
-    issue(0, st0);
-    if (KB > 1) issue(1, st1);
-    if (KB > 2) issue(2, st2);
-    for (int kb = 0; kb < KB; kb += 4) {
-        step(kb, st0, st3);
-        if (kb + 1 >= KB) break;
-        step(kb + 1, st1, st0);
-        if (kb + 2 >= KB) break;
-        step(kb + 2, st2, st1);
-        if (kb + 3 >= KB) break;
-        step(kb + 3, st3, st2);
-    }
-    MOE_WAIT_VM(0);
+    k_loop<NST, Lo::dma>(KB, sm, Lo::STAGE, issue, compute);
     __syncthreads();
 
-    // epilogue: h = SwiGLU(sg g, su u) -> hi, lo tiles [128][64] bf16 in LDS,
-    // then 16-byte stores of the valid rows
-    uint16_t *th = reinterpret_cast<uint16_t *>(st0);
-    uint16_t *tl = reinterpret_cast<uint16_t *>(st1);
+    // epilogue: h = SwiGLU(sg g, su u) -> hi, lo tiles [128][128] bf16 in LDS
+    // (rows padded to 136 elements), then 16-byte stores of the valid rows
+    constexpr int C = Lo::cols, CP = C + 8;
+    static_assert(2 * TM * CP * 2 <= NST * Lo::STAGE, "h tiles exceed the stages");
+    uint16_t *th = reinterpret_cast<uint16_t *>(sm);
+    uint16_t *tl = th + TM * CP;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = wm * 64 + mt * 16 + (lane >> 4) * 4 + i;
-                const int c = wn * 32 + nt * 16 + (lane & 15);
+                const int r = mt * 16 + (lane >> 4) * 4 + i;
+                const int c = wave * 32 + nt * 16 + (lane & 15);
                 const float h = swiglu_clamp(accg[mt][nt][i] * sg, accu[mt][nt][i] * su, a.limit);
                 const uint32_t hi = bf16_rne(h);
-                th[r * 64 + c] = (uint16_t)hi;
-                tl[r * 64 + c] = (uint16_t)bf16_rne(h - __uint_as_float(hi << 16));
+                th[r * CP + c] = (uint16_t)hi;
+                tl[r * CP + c] = (uint16_t)bf16_rne(h - __uint_as_float(hi << 16));
             }
     __syncthreads();
+    constexpr int cpr = C / 8;                        // 16-byte chunks per row
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int ch = tid + kThreads * j, r = ch >> 3, part = ch & 7;
+    for (int j = 0; j < TM * cpr / Lo::threads; ++j) {
+        const int ch = tid + Lo::threads * j, r = ch / cpr, part = ch % cpr;
         if (r < rows) {
             const size_t o = (size_t)(p0 + r) * N + n0 + part * 8;
-            *reinterpret_cast<uint4 *>(a.hhi + o) = *reinterpret_cast<const uint4 *>(th + r * 64 + part * 8);
-            *reinterpret_cast<uint4 *>(a.hlo + o) = *reinterpret_cast<const uint4 *>(tl + r * 64 + part * 8);
+            *reinterpret_cast<uint4 *>(a.hhi + o) = *reinterpret_cast<const uint4 *>(th + r * CP + part * 8);
+            *reinterpret_cast<uint4 *>(a.hlo + o) = *reinterpret_cast<const uint4 *>(tl + r * CP + part * 8);
         }
     }
 }
@@ -256,13 +295,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_gateup_nvfp4_kernel(NvGemmAr
 // ---------------------------------------------------------------------------
 // down
 // ---------------------------------------------------------------------------
-// Stage: A hi [128][128 B] | A lo [128][128 B] | B codes [128][32 B] | B scales
-constexpr int DA = 0, DA2 = TM * 128, DC = 2 * TM * 128, DS = DC + 128 * 32, DSTAGE = DS + 4 * 256;
-constexpr int D_DMA = 8 + 1 + 1;
+// Block: 2 x NW waves, wave (wm, wn) = 64 rows x 64 outputs; the tile is
+// 128 rows x 64 NW outputs.  Wave w loads B rows 32w..32w+31.
+// Stage: A hi [128][128 B] | A lo [128][128 B] | B codes [64 NW][32 B] | B scales
+template <int NW>
+struct DnLayout {
+    static constexpr int threads = 128 * NW;
+    static constexpr int cols = 64 * NW;
+    static constexpr int A = 0, A2 = TM * 128, C = 2 * TM * 128, S = C + 64 * NW * 32,
+                         STAGE = S + 2 * NW * 256;
+    static constexpr int arun = 8 / NW;          // runs of 8 rows per wave, for hi and for lo
+    static constexpr int dma = 2 * arun + 2;
+};
 
-__global__ __launch_bounds__(kThreads, 1) void gemm_down_nvfp4_kernel(NvGemmArgs a)
+template <int NW, int NST, int OCC>
+__global__ __launch_bounds__(DnLayout<NW>::threads, OCC) void gemm_down_nvfp4_kernel(NvGemmArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t st0[DSTAGE], st1[DSTAGE], st2[DSTAGE], st3[DSTAGE];
+    using Lo = DnLayout<NW>;
+    __shared__ __attribute__((aligned(16))) uint8_t sm[NST * Lo::STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
@@ -272,13 +322,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_down_nvfp4_kernel(NvGemmArgs
     const int e = tile.x, p0 = tile.y;
     const int rows = moe::uniform(min(TM, a.offsets[e + 1] - p0));
     const int K = a.K, N = a.N, KB = K / KS;
-    const int n0 = nb * 128;
+    const int n0 = nb * Lo::cols;
     const float sd = a.g0[e];
 
-    uint32_t aoff[4];
+    uint32_t aoff[Lo::arun];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = (wave * 4 + j) * 8 + (lane >> 3);
+    for (int j = 0; j < Lo::arun; ++j) {
+        const int r = (wave * Lo::arun + j) * 8 + (lane >> 3);
         aoff[j] = (uint32_t)(p0 + (r < rows ? r : 0)) * (uint32_t)(K * 2) + swz(r, lane & 7) * 16;
     }
     const size_t brow = (size_t)e * N + n0 + wave * 32;
@@ -291,11 +341,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_down_nvfp4_kernel(NvGemmArgs
         const uint8_t *ab = reinterpret_cast<const uint8_t *>(a.a) + (size_t)kb * 128;
         const uint8_t *ab2 = reinterpret_cast<const uint8_t *>(a.a2) + (size_t)kb * 128;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(ab, aoff[j], lds_addr(st + DA + (wave * 4 + j) * 1024));
+        for (int j = 0; j < Lo::arun; ++j)
+            dma16(ab, aoff[j], lds_addr(st + Lo::A + (wave * Lo::arun + j) * 1024));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(ab2, aoff[j], lds_addr(st + DA2 + (wave * 4 + j) * 1024));
-        dma16(cbase + (size_t)kb * 32, coff, lds_addr(st + DC + wave * 1024));
-        dma4(sbase + (size_t)kb * 4, soff, lds_addr(st + DS + wave * 256));
+        for (int j = 0; j < Lo::arun; ++j)
+            dma16(ab2, aoff[j], lds_addr(st + Lo::A2 + (wave * Lo::arun + j) * 1024));
+        dma16(cbase + (size_t)kb * 32, coff, lds_addr(st + Lo::C + wave * 1024));
+        dma4(sbase + (size_t)kb * 4, soff, lds_addr(st + Lo::S + wave * 256));
     };
 
     f32x4 acc[4][4];
@@ -311,12 +363,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_down_nvfp4_kernel(NvGemmArgs
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const int r = wm * 64 + mt * 16 + (lane & 15);
-                ah[mt] = a_op(st + DA, r, ks, lane);
-                al[mt] = a_op(st + DA2, r, ks, lane);
+                ah[mt] = a_op(st + Lo::A, r, ks, lane);
+                al[mt] = a_op(st + Lo::A2, r, ks, lane);
             }
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                const bf16x8 b = b_op(st + DC, st + DS, wn * 64 + nt * 16 + (lane & 15), ks, lane);
+                const bf16x8 b = b_op(st + Lo::C, st + Lo::S, wn * 64 + nt * 16 + (lane & 15), ks, lane);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     acc[mt][nt] = mfma_bf16(ah[mt], b, acc[mt][nt]);
@@ -326,27 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_down_nvfp4_kernel(NvGemmArgs
         }
     };
 
-    auto step = [&](int kb, const uint8_t *cur, uint8_t *later) {
-        NV_WAIT_AHEAD(kb, KB, D_DMA);
-        MOE_WAIT_LGKM0();
-        MOE_BARRIER();
-        if (kb + 3 < KB) issue(kb + 3, later);
-        compute(cur);
-    };
-
-    MOE_WAIT_VM(0);
-    issue(0, st0);
-    if (KB > 1) issue(1, st1);
-    if (KB > 2) issue(2, st2);
-    for (int kb = 0; kb < KB; kb += 4) {
-        step(kb, st0, st3);
-        if (kb + 1 >= KB) break;
-        step(kb + 1, st1, st0);
-        if (kb + 2 >= KB) break;
-        step(kb + 2, st2, st1);
-        if (kb + 3 >= KB) break;
-        step(kb + 3, st3, st2);
-    }
+    k_loop<NST, Lo::dma>(KB, sm, Lo::STAGE, issue, compute);
 
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -361,6 +393,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_down_nvfp4_kernel(NvGemmArgs
         }
 }
 
+// launch shapes: gate/up 4 waves (128 h columns) over 3 stages, down 4 waves
+// (128 outputs) over 2 stages, two blocks of each per CU (the LDS of both
+// within the 160 KB of a CU), so every SIMD runs waves of two blocks whose
+// barriers and waits do not line up
+constexpr int GU_W = 4, GU_NST = 3, GU_OCC = 2, DN_NW = 2, DN_NST = 2, DN_OCC = 2;
+static_assert(GU_OCC * GU_NST * GuLayout<GU_W>::STAGE <= 160 * 1024, "gate/up stages exceed LDS");
+static_assert(DN_OCC * DN_NST * DnLayout<DN_NW>::STAGE <= 160 * 1024, "down stages exceed LDS");
+
 }  // namespace
 
 hipError_t launch_gemm_gateup_nvfp4(const uint16_t *x, const int32_t *sorted_token,
@@ -370,14 +410,17 @@ hipError_t launch_gemm_gateup_nvfp4(const uint16_t *x, const int32_t *sorted_tok
                                     int32_t inter, float limit, uint16_t *hhi, uint16_t *hlo,
                                     hipStream_t st)
 {
+    using Lo = GuLayout<GU_W>;
+    if (inter % Lo::cols || hidden % KS) return hipErrorInvalidValue;
     NvGemmArgs a{};
     a.a = x; a.sorted_token = sorted_token;
     a.c0 = gate.codes; a.c1 = up.codes;
     a.s0 = (const uint8_t *)gate.scales; a.s1 = (const uint8_t *)up.scales;
     a.g0 = gate.scale2; a.g1 = up.scale2;
     a.offsets = offsets; a.tiles = tiles; a.ntiles = ntiles;
-    a.hhi = hhi; a.hlo = hlo; a.K = hidden; a.N = inter; a.ntn = inter / 64; a.limit = limit;
-    hipLaunchKernelGGL(gemm_gateup_nvfp4_kernel, dim3((unsigned)(tmax * a.ntn)), dim3(kThreads), 0, st, a);
+    a.hhi = hhi; a.hlo = hlo; a.K = hidden; a.N = inter; a.ntn = inter / Lo::cols; a.limit = limit;
+    hipLaunchKernelGGL((gemm_gateup_nvfp4_kernel<GU_W, GU_NST, GU_OCC>), dim3((unsigned)(tmax * a.ntn)),
+                       dim3(Lo::threads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -386,11 +429,14 @@ hipError_t launch_gemm_down_nvfp4(const uint16_t *hhi, const uint16_t *hlo, cons
                                   int32_t tmax, int32_t hidden, int32_t inter, float *y,
                                   hipStream_t st)
 {
+    using Lo = DnLayout<DN_NW>;
+    if (hidden % Lo::cols || inter % KS) return hipErrorInvalidValue;
     NvGemmArgs a{};
     a.a = hhi; a.a2 = hlo;
     a.c0 = down.codes; a.s0 = (const uint8_t *)down.scales; a.g0 = down.scale2;
     a.offsets = offsets; a.tiles = tiles; a.ntiles = ntiles;
-    a.y = y; a.K = inter; a.N = hidden; a.ntn = hidden / 128;
-    hipLaunchKernelGGL(gemm_down_nvfp4_kernel, dim3((unsigned)(tmax * a.ntn)), dim3(kThreads), 0, st, a);
+    a.y = y; a.K = inter; a.N = hidden; a.ntn = hidden / Lo::cols;
+    hipLaunchKernelGGL((gemm_down_nvfp4_kernel<DN_NW, DN_NST, DN_OCC>), dim3((unsigned)(tmax * a.ntn)),
+                       dim3(Lo::threads), 0, st, a);
     return hipGetLastError();
 }
