@@ -125,12 +125,78 @@ __global__ __launch_bounds__(kThreads) void route_pack_kernel(
     if (tid == 0) *status = s_invalid;
 }
 
+// Small routes (S <= 64: decode and speculative verify), one wave and no
+// LDS: lane s holds slot s.  With key = id for a valid slot and INT_MAX
+// otherwise, the packed position of a valid slot is
+//   #{j : key_j < key_s} + #{j < s : key_j == key_s}
+// (expert offset plus stable rank), and expert_offsets[e] = #{j : key_j < e};
+// both are counted by broadcasting each slot's key in turn.  Same tables,
+// bit for bit, as the general kernel.
+__global__ __launch_bounds__(64) void route_pack_small_kernel(
+    const int32_t *__restrict__ ids, int32_t S, int32_t k, int32_t E,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
+    int32_t *__restrict__ sorted_token, int32_t *__restrict__ token_to_perm,
+    int32_t *__restrict__ active, int32_t *__restrict__ num_active,
+    int32_t *__restrict__ status)
+{
+    const int lane = threadIdx.x;
+    const int id = lane < S ? ids[lane] : -1;
+    const bool valid = id >= 0 && id < E;
+    const int key = valid ? id : 0x7FFFFFFF;
+    const uint64_t bad = __ballot(lane < S && !valid && id != -1);
+
+    // packed position of this lane's slot
+    int below = 0, before = 0;
+    for (int j = 0; j < S; ++j) {
+        const int kj = __builtin_amdgcn_readlane(key, j);
+        below += kj < key;
+        before += (j < lane) & (kj == key);
+    }
+    if (lane < S) {
+        const int pos = below + before;
+        token_to_perm[lane] = valid ? pos : -1;
+        if (valid) {
+            sorted_slot[pos] = lane;
+            sorted_token[pos] = lane / k;
+        }
+    }
+
+    // expert offsets and the ascending active list, 64 experts per pass
+    const int A = S < E ? S : E;
+    int na = 0;
+    for (int e0 = 0; e0 <= E; e0 += 64) {
+        const int e = e0 + lane;
+        int lt = 0, le = 0;                       // slots with key < e, key <= e
+        for (int j = 0; j < S; ++j) {
+            const int kj = __builtin_amdgcn_readlane(key, j);
+            lt += kj < e;
+            le += kj <= e;
+        }
+        if (e <= E) offsets[e] = lt;
+        const bool act = e < E && le > lt;
+        const uint64_t m = __ballot(act);
+        if (act) active[na + __popcll(m & ((1ull << lane) - 1))] = e;
+        na += __popcll(m);
+    }
+    for (int i = na + lane; i < A; i += 64) active[i] = -1;
+    if (lane == 0) {
+        *num_active = na;
+        *status = __popcll(bad);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route_pack(const int32_t *ids, int32_t M, int32_t k, int32_t E,
                              const MoeRouteDev &r, hipStream_t st)
 {
     const int32_t S = M * k;
+    if (S <= 64) {
+        hipLaunchKernelGGL(route_pack_small_kernel, dim3(1), dim3(64), 0, st, ids, S, k, E, r.offsets,
+                           r.sorted_slot, r.sorted_token, r.token_to_perm, r.active, r.num_active,
+                           r.status);
+        return hipGetLastError();
+    }
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const size_t lds = sizeof(int32_t) * (size_t)E * (2 + kWaves);

@@ -99,6 +99,37 @@ def test_route_pack_bit_exact_adversarial(case):
     assert_pack_equal(gpu_pack(ids, E), oracle.route_pack(ids, E), ids.size)
 
 
+@pytest.mark.parametrize("case", ["s1", "s8_invalid", "s63_dups", "s64_e512", "e1", "all_invalid",
+                                  "k_eq_E", "one_expert", "neg_ids"])
+def test_route_pack_bit_exact_small_routes(case):
+    """Routes of at most 64 slots run a one-wave kernel of their own."""
+    rng = np.random.default_rng(29)
+    if case == "s1":
+        ids, E = np.array([[5]], np.int32), 16
+    elif case == "s8_invalid":
+        ids, E = np.array([[3, -1, 17, 3, 200, 0, -1, 16]], np.int32), 17
+    elif case == "s63_dups":
+        ids, E = rng.integers(0, 4, (21, 3)).astype(np.int32), 4
+    elif case == "s64_e512":
+        E = 512
+        ids = np.stack([rng.choice(E, 8, replace=False) for _ in range(8)]).astype(np.int32)
+    elif case == "e1":
+        ids, E = np.zeros((7, 1), np.int32), 1
+    elif case == "all_invalid":
+        ids, E = np.full((4, 4), -1, np.int32), 8
+        ids[1, 2] = 8
+    elif case == "k_eq_E":
+        E = 8
+        ids = np.stack([rng.permutation(E) for _ in range(8)]).astype(np.int32)
+    elif case == "one_expert":
+        ids, E = np.full((16, 4), 9, np.int32), 10
+    else:
+        ids, E = rng.integers(-3, 40, (5, 12)).astype(np.int32), 37
+    assert ids.size <= 64
+    print(f"route_pack small {case} S={ids.size} E={E}", flush=True)
+    assert_pack_equal(gpu_pack(ids, E), oracle.route_pack(ids, E), ids.size)
+
+
 # --------------------------------------------------------------------------
 # layer parity
 # --------------------------------------------------------------------------
