@@ -44,6 +44,11 @@ struct GateUpArgs {
     float *h;                           // [S][I]
     int32_t H, I, ntiles, st;           // st: slots per weight pass (<= ST)
     float limit;
+    // route built inside the launch (small routes): ids [M][k], and the
+    // tables block 0 writes for the launches after it
+    const int32_t *ids;
+    int32_t M, k, E;
+    MoeRouteDev r;
 };
 
 struct DownArgs {
@@ -242,18 +247,35 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
     }
 }
 
-template <int CH, int NCH, int ST>
+// ROUTE: the route of the S <= kFusedMaxSlots slots is built in LDS by every
+// block from the ids (the same stable pack as route_pack), instead of read
+// from the tables of a route pack launched before; block 0 writes the
+// tables for the down and combine launches that follow.
+template <int CH, int NCH, int ST, bool ROUTE>
 __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArgs a)
 {
     extern __shared__ uint4 xl[];                    // [a.st][H / 8] bf16 x rows, K order
     __shared__ float ush[ST][16];                    // up sums of the 16 rows per slot
     const int tile = blockIdx.x % a.ntiles;
     const int ai = blockIdx.x / a.ntiles;
-    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
-    if (e < 0) return;
-    const int p0 = moe::uniform(a.offsets[e]);
-    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
-    gateup_e4m3_item<CH, NCH, ST>(a, e, tile, p0, ne, a.sorted_token + p0, xl, ush);
+    if constexpr (ROUTE) {
+        __shared__ FusedRoute R;
+        const int id_in = (int)threadIdx.x < a.M * a.k ? a.ids[threadIdx.x] : -1;
+        fused_route(a, R, id_in);
+        fused_route_status(a, R);
+        if (ai < moe::uniform(R.na)) {
+            const int e = moe::uniform(R.ae[ai]), p0 = moe::uniform(R.ap0[ai]);
+            const int ne = moe::uniform(R.acnt[ai]);
+            gateup_e4m3_item<CH, NCH, ST>(a, e, tile, p0, ne, R.tok + p0, xl, ush);
+        }
+        fused_route_tables(a, R);
+    } else {
+        const int e = moe::uniform(a.active[ai]);   // -1 past the active experts
+        if (e < 0) return;
+        const int p0 = moe::uniform(a.offsets[e]);
+        const int ne = moe::uniform(a.offsets[e + 1]) - p0;
+        gateup_e4m3_item<CH, NCH, ST>(a, e, tile, p0, ne, a.sorted_token + p0, xl, ush);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -667,27 +689,51 @@ __global__ __launch_bounds__(kThreads, 4) void moe_fused_decode1_e4m3_kernel(Fus
 // the host never needs the routing.
 namespace {
 
-template <int CH, int NCH, int ST>
+template <int CH, int NCH, int ST, bool ROUTE>
 void gateup_launch(const GateUpArgs &a, int grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((gemv_gateup_e4m3_kernel<CH, NCH, ST>), dim3(grid), dim3(kThreads),
+    hipLaunchKernelGGL((gemv_gateup_e4m3_kernel<CH, NCH, ST, ROUTE>), dim3(grid), dim3(kThreads),
                        (size_t)a.st * a.H * 2, st, a);
 }
 
 // Unrolled kernels for 8-segment chunks (hidden a multiple of 1024), for the
 // chunk counts that fit 128 VGPRs at each pass size (up to 8 chunks with one
 // or two slots, 2 with more); every other shape runs the looped kernel.
-template <int ST, int MAXN, int N = 1>
+template <int ST, int MAXN, bool ROUTE, int N = 1>
 bool gateup_launch_unrolled(const GateUpArgs &a, int nch, int grid, hipStream_t st)
 {
     if constexpr (N > MAXN) {
         return false;
     } else {
         if (nch == N) {
-            gateup_launch<8, N, ST>(a, grid, st);
+            gateup_launch<8, N, ST, ROUTE>(a, grid, st);
             return true;
         }
-        return gateup_launch_unrolled<ST, MAXN, N + 1>(a, nch, grid, st);
+        return gateup_launch_unrolled<ST, MAXN, ROUTE, N + 1>(a, nch, grid, st);
+    }
+}
+
+template <bool ROUTE>
+void gateup_dispatch(const GateUpArgs &a, int grid, hipStream_t st)
+{
+    const int ch = gemv_chunk_segs(kFmtE4M3, a.H), nch = a.H / 128 / ch;
+    bool done = false;
+    if (ch == 8) {
+        if (a.st <= 1) done = gateup_launch_unrolled<1, 8, ROUTE>(a, nch, grid, st);
+        else if (a.st <= 2) done = gateup_launch_unrolled<2, 8, ROUTE>(a, nch, grid, st);
+        else done = gateup_launch_unrolled<MOE_E4M3_GU_ST, 2, ROUTE>(a, nch, grid, st);
+    }
+    if (!done) {
+        switch (ch) {
+        case 8: gateup_launch<8, 0, MOE_E4M3_GU_ST, ROUTE>(a, grid, st); break;
+        case 7: gateup_launch<7, 0, MOE_E4M3_GU_ST, ROUTE>(a, grid, st); break;
+        case 6: gateup_launch<6, 0, MOE_E4M3_GU_ST, ROUTE>(a, grid, st); break;
+        case 5: gateup_launch<5, 0, MOE_E4M3_GU_ST, ROUTE>(a, grid, st); break;
+        case 4: gateup_launch<4, 0, MOE_E4M3_GU_ST, ROUTE>(a, grid, st); break;
+        case 3: gateup_launch<3, 0, MOE_E4M3_GU_ST, ROUTE>(a, grid, st); break;
+        case 2: gateup_launch<2, 0, MOE_E4M3_GU_ST, ROUTE>(a, grid, st); break;
+        default: gateup_launch<1, 0, MOE_E4M3_GU_ST, ROUTE>(a, grid, st); break;
+        }
     }
 }
 
@@ -720,34 +766,22 @@ bool down_launch_unrolled(const DownArgs &a, int nch, int grid, hipStream_t st)
 hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
                                    const uint16_t *x, const MoeRouteDev &r, int32_t M, int32_t S,
                                    int32_t E, int32_t hidden, int32_t inter, float limit, float *h,
-                                   hipStream_t st)
+                                   hipStream_t st, const int32_t *route_ids, int32_t top_k)
 {
-    GateUpArgs a;
+    GateUpArgs a{};
     a.st = gemv_gateup_pass_slots(M, hidden, MOE_E4M3_GU_ST);
     a.gcodes = gate.codes; a.ucodes = up.codes;
     a.gscales = (const float *)gate.scales; a.uscales = (const float *)up.scales;
     a.x = x; a.offsets = r.offsets; a.sorted_token = r.sorted_token; a.active = r.active;
     a.h = h; a.H = hidden; a.I = inter; a.limit = limit;
     a.ntiles = inter / 16;
+    a.ids = route_ids; a.M = M; a.k = top_k; a.E = E; a.r = r;
     const int grid = (S < E ? S : E) * a.ntiles;
-    const int ch = gemv_chunk_segs(kFmtE4M3, hidden), nch = hidden / 128 / ch;
-    bool done = false;
-    if (ch == 8) {
-        if (a.st <= 1) done = gateup_launch_unrolled<1, 8>(a, nch, grid, st);
-        else if (a.st <= 2) done = gateup_launch_unrolled<2, 8>(a, nch, grid, st);
-        else done = gateup_launch_unrolled<MOE_E4M3_GU_ST, 2>(a, nch, grid, st);
-    }
-    if (!done) {
-        switch (ch) {
-        case 8: gateup_launch<8, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
-        case 7: gateup_launch<7, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
-        case 6: gateup_launch<6, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
-        case 5: gateup_launch<5, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
-        case 4: gateup_launch<4, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
-        case 3: gateup_launch<3, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
-        case 2: gateup_launch<2, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
-        default: gateup_launch<1, 0, MOE_E4M3_GU_ST>(a, grid, st); break;
-        }
+    if (route_ids) {
+        if (S > kFusedMaxSlots) return hipErrorInvalidValue;
+        gateup_dispatch<true>(a, grid, st);
+    } else {
+        gateup_dispatch<false>(a, grid, st);
     }
     return hipGetLastError();
 }

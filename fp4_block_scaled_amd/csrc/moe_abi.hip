@@ -294,10 +294,13 @@ static moe_status_t check_bank(const char *fn, const moe_bank_t *b, const char *
     return MOE_OK;
 }
 
-moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
-                            const uint16_t *x_bf16, const moe_route_t *route, int32_t hidden,
-                            int32_t inter, float limit, int32_t mode, float *y_packed, void *ws,
-                            size_t ws_bytes, void *stream)
+// The expert FFN of moe_expert_ffn.  With route_ids, the route tables of
+// `route` (carved, not yet filled) are built by the gate/up launch itself
+// from the ids: only for the GEMV tier with E4M3 banks and S <= 64.
+static moe_status_t expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
+                               const uint16_t *x_bf16, const moe_route_t *route, int32_t hidden,
+                               int32_t inter, float limit, int32_t mode, float *y_packed, void *ws,
+                               size_t ws_bytes, void *stream, const int32_t *route_ids)
 {
     if (!gate || !up || !down || !x_bf16 || !route || !y_packed || !ws)
         return fail(MOE_ERR_ARG, "moe_expert_ffn: null pointer");
@@ -393,7 +396,8 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
     float *h = (float *)scratch;
     stage_mark(0, s);
     if (fmt == MOE_W_E4M3_B128)
-        e = launch_gemv_gateup_e4m3(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, limit, h, s);
+        e = launch_gemv_gateup_e4m3(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, limit, h, s,
+                                    route_ids, k);
     else
         e = launch_gemv_gateup_nvfp4(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, limit, h, s);
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: gate/up GEMV launch");
@@ -405,6 +409,52 @@ moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const 
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: down GEMV launch");
     stage_mark(2, s);
     return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
+                            const uint16_t *x_bf16, const moe_route_t *route, int32_t hidden,
+                            int32_t inter, float limit, int32_t mode, float *y_packed, void *ws,
+                            size_t ws_bytes, void *stream)
+{
+    return expert_ffn(gate, up, down, x_bf16, route, hidden, inter, limit, mode, y_packed, ws,
+                      ws_bytes, stream, nullptr);
+}
+
+moe_status_t moe_layer(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
+                       const uint16_t *x_bf16, const int32_t *topk_ids, const float *topk_weights,
+                       int32_t M, int32_t top_k, int32_t hidden, int32_t inter, float limit,
+                       int32_t mode, float *y_packed, float *out, void *ws, size_t ws_bytes,
+                       moe_route_t *route, void *stream)
+{
+    static const char *fn = "moe_layer";
+    if (!gate || !up || !down || !x_bf16 || !topk_ids || !topk_weights || !y_packed || !out ||
+        !ws || !route)
+        return fail(MOE_ERR_ARG, "%s: null pointer", fn);
+    const int32_t fmt = gate->fmt, E = gate->num_experts;
+    if (!sizes_ok(M, top_k, E))
+        return fail(MOE_ERR_SHAPE, "%s: need M >= 1, 1 <= top_k <= num_experts <= %d (M=%d top_k=%d E=%d)",
+                    fn, MOE_MAX_EXPERTS, M, top_k, E);
+    if (!valid_mode(mode) || mode == MOE_MODE_FUSED)
+        return fail(MOE_ERR_ARG, "%s: unknown mode %d", fn, mode);
+    const int64_t S = (int64_t)M * top_k;
+    moe_status_t st;
+    if (S <= 64 && fmt == MOE_W_E4M3_B128 && resolve(M, fmt, mode) == MOE_MODE_GEMV_A16) {
+        // the route pack runs inside the gate/up launch
+        if (ws_bytes < moe::route_region_bytes(S, E))
+            return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes,
+                        moe::route_region_bytes(S, E));
+        if (((uintptr_t)ws & 255) != 0) return fail(MOE_ERR_ARG, "%s: ws not 256-byte aligned", fn);
+        carve_route(ws, M, top_k, E, route);
+        st = expert_ffn(gate, up, down, x_bf16, route, hidden, inter, limit, mode, y_packed, ws,
+                        ws_bytes, stream, topk_ids);
+    } else {
+        st = moe_route_pack(topk_ids, M, top_k, E, ws, ws_bytes, route, stream);
+        if (st == MOE_OK)
+            st = expert_ffn(gate, up, down, x_bf16, route, hidden, inter, limit, mode, y_packed, ws,
+                            ws_bytes, stream, nullptr);
+    }
+    if (st != MOE_OK) return st;
+    return moe_combine(y_packed, route, topk_weights, hidden, out, stream);
 }
 
 moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,

@@ -117,10 +117,14 @@ struct GemvBankDev {
 // slot tile of a pass.  Experts holding more slots are swept in several
 // passes.  Gate/up covers the whole of K per block and writes h =
 // SwiGLU(gate x, up x) ([S][inter] floats) directly.
+// With route_ids (S <= 256 slots of top_k each), the route is built inside
+// the launch from the ids and block 0 writes the tables of r; otherwise the
+// tables of r come from route_pack.
 hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
                                    const uint16_t *x, const MoeRouteDev &r, int32_t M,
                                    int32_t S, int32_t E, int32_t hidden, int32_t inter,
-                                   float limit, float *h, hipStream_t st);
+                                   float limit, float *h, hipStream_t st,
+                                   const int32_t *route_ids = nullptr, int32_t top_k = 0);
 // Down projection: a block covers 32 output rows over the whole of K and
 // writes y ([S][hidden] floats) directly.
 hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const MoeRouteDev &r,

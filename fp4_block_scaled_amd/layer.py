@@ -1,9 +1,10 @@
 """Device buffers for one routed-MoE layer call sequence (plumbing only).
 
 Allocates the workspace, packed-y and output tensors once for a maximum M and
-runs moe_route_pack -> moe_expert_ffn -> moe_combine on the current stream, or
-moe_layer_fused (one launch) when built with mode MOE_MODE_FUSED.  No
-arithmetic happens here."""
+runs the layer on the current stream: moe_layer (route pack, expert FFN and
+combine in one call), or moe_route_pack -> moe_expert_ffn -> moe_combine as
+three calls with single_call=False, or moe_layer_fused (one launch) when
+built with mode MOE_MODE_FUSED.  No arithmetic happens here."""
 from __future__ import annotations
 
 import torch
@@ -14,13 +15,14 @@ from . import binding as B
 class MoeLayer:
     def __init__(self, gate: B.Bank, up: B.Bank, down: B.Bank, hidden: int, inter: int,
                  top_k: int, max_M: int, limit: float = 7.0, mode: int = B.MOE_MODE_AUTO,
-                 device="cuda"):
+                 device="cuda", single_call: bool = True):
         self.gate, self.up, self.down = gate, up, down
         self.hidden, self.inter, self.top_k = hidden, inter, top_k
         self.E = gate.c.num_experts
         self.fmt = gate.c.fmt
         self.limit, self.mode = limit, mode
         self.max_M = max_M
+        self.single_call = single_call
         nbytes = B.moe_workspace_bytes(max_M, top_k, self.E, hidden, inter, self.fmt, mode)
         if nbytes == 0:
             raise B.MoeError(B.MOE_ERR_SHAPE, "moe_workspace_bytes rejected the sizes")
@@ -36,6 +38,11 @@ class MoeLayer:
             self.route = B.moe_layer_fused(self.gate, self.up, self.down, x_bf16, ids, weights, M,
                                            self.top_k, self.hidden, self.inter, self.limit, self.y,
                                            self.out, self.ws, stream=stream)
+            return self.out[:M]
+        if self.single_call:
+            self.route = B.moe_layer(self.gate, self.up, self.down, x_bf16, ids, weights, M,
+                                     self.top_k, self.hidden, self.inter, self.limit, self.mode,
+                                     self.y, self.out, self.ws, stream=stream)
             return self.out[:M]
         self.route = B.moe_route_pack(ids, M, self.top_k, self.E, self.ws, stream=stream)
         B.moe_expert_ffn(self.gate, self.up, self.down, x_bf16, self.route, self.hidden,

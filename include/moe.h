@@ -240,6 +240,23 @@ moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
                          const float *topk_weights, int32_t hidden, float *out,
                          void *stream);
 
+/* The whole layer in one call: the route pack, the expert FFN of tier `mode`
+ * and the combine, with the outputs (route tables in *route, y_packed, out)
+ * of moe_route_pack + moe_expert_ffn + moe_combine, bit for bit.  For the
+ * GEMV tier with E4M3 banks and M*top_k <= 64 slots the route pack runs
+ * inside the gate/up launch (every block builds the route of the slots from
+ * the ids in LDS; block 0 writes the tables for the down and combine
+ * launches), so the layer is three launches; otherwise the three calls'
+ * launches run in sequence.  No host state: capturable in a HIP graph.
+ * Rules and workspace: those of the three calls (ws_bytes >=
+ * moe_workspace_bytes(M, top_k, E, hidden, inter, fmt, mode)); a failed
+ * check launches nothing of the failing call. */
+moe_status_t moe_layer(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
+                       const uint16_t *x_bf16, const int32_t *topk_ids, const float *topk_weights,
+                       int32_t M, int32_t top_k, int32_t hidden, int32_t inter, float limit,
+                       int32_t mode, float *y_packed, float *out, void *ws, size_t ws_bytes,
+                       moe_route_t *route, void *stream);
+
 /* Fused decode layer: moe_route_pack, moe_expert_ffn on the GEMV tier and
  * moe_combine as ONE kernel launch of resident blocks ("spark_model
  * glm5next_mlp/forward.rs", doc of forward_moe: the per-row MoE path without

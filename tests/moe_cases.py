@@ -74,6 +74,8 @@ class GpuCase:
 
     def run(self, ids: np.ndarray, w: np.ndarray, mode=B.MOE_MODE_AUTO, x=None, layer=None):
         x = self.x if x is None else x
+        # the kernels read x rows of every token: never hand them fewer rows
+        assert x.shape[0] >= ids.shape[0], (x.shape, ids.shape)
         L = layer or self.layer(max_M=ids.shape[0], mode=mode)
         ids_d = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
         w_d = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()

@@ -332,3 +332,30 @@ def test_combine_residual_error_contract_on_host():
     empty = B.moe_route_t()
     empty.token_to_perm = FAKE
     assert cr(route=empty) == B.MOE_ERR_ARG
+
+
+def test_single_call_layer_error_contract_on_host():
+    from fp4_block_scaled_amd import binding as B
+    L = B.lib
+    ws = FAKE + 0x100000
+    g, u, d = _bank(B), _bank(B), _bank(B, n=256, k=128)
+    r = B.moe_route_t()
+
+    def layer(gate=g, up=u, down=d, M=1, k=4, hidden=256, inter=128, mode=0, ws_=ws,
+              nbytes=1 << 30, ids=FAKE + 0x4000, limit=7.0):
+        return L.moe_layer(C.byref(gate), C.byref(up), C.byref(down), FAKE + 0x2000, ids,
+                           FAKE + 0x5000, M, k, hidden, inter, limit, mode, FAKE + 0x3000,
+                           FAKE + 0x6000, ws_, nbytes, C.byref(r), None)
+
+    assert layer(ids=None) == B.MOE_ERR_ARG
+    assert layer(k=17) == B.MOE_ERR_SHAPE
+    assert layer(mode=B.MOE_MODE_FUSED) == B.MOE_ERR_ARG
+    assert layer(mode=7) == B.MOE_ERR_ARG
+    assert layer(nbytes=256) == B.MOE_ERR_WORKSPACE            # route region alone is larger
+    assert layer(ws_=ws + 64) == B.MOE_ERR_ARG
+    assert layer(hidden=200) == B.MOE_ERR_SHAPE                # the FFN's checks apply
+    assert layer(limit=0.0) == B.MOE_ERR_ARG
+    assert layer(gate=_bank(B, E=8)) == B.MOE_ERR_SHAPE
+    # NVFP4 banks or more than 64 slots take the three calls' path: the route
+    # pack's and FFN's own checks still apply
+    assert layer(M=20, k=4, mode=B.MOE_MODE_GEMV_A16, nbytes=600) == B.MOE_ERR_WORKSPACE

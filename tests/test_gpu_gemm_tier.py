@@ -21,7 +21,7 @@ _cache = {}
 
 
 def get_case(wl):
-    key = (wl.name, wl.hidden, wl.inter, wl.experts, wl.top_k, wl.seed)
+    key = (wl.name, wl.hidden, wl.inter, wl.experts, wl.top_k, wl.seed, wl.M)
     if key not in _cache:
         _cache.clear()
         gc.collect()

@@ -160,7 +160,7 @@ _cache = {}
 
 def get_case(name_or_wl):
     wl = workloads.WORKLOADS[name_or_wl] if isinstance(name_or_wl, str) else name_or_wl
-    key = (wl.name, wl.hidden, wl.inter, wl.experts, wl.top_k, wl.fmt, wl.seed)
+    key = (wl.name, wl.hidden, wl.inter, wl.experts, wl.top_k, wl.fmt, wl.seed, wl.M)
     if key not in _cache:
         _cache.clear()
         gc.collect()
@@ -259,3 +259,44 @@ def test_grouping_rows_never_changes_a_row():
         x1 = case.x[t:t + 1].contiguous()
         one, _, _, _ = case.run(ids[t:t + 1], w[t:t + 1], x=x1)
         assert np.array_equal(one[0].view(np.uint32), full[t].view(np.uint32)), t
+
+
+@pytest.mark.parametrize("name,M,mode", [
+    ("decode_e4m3_m1", 1, B.MOE_MODE_AUTO), ("verify_e4m3_m8", 8, B.MOE_MODE_AUTO),
+    ("verify_e4m3_m8", 16, B.MOE_MODE_AUTO), ("nvfp4_m1", 1, B.MOE_MODE_AUTO),
+    ("tiny_e4m3_m1", 1, B.MOE_MODE_AUTO), ("tiny_e4m3_m1", 40, B.MOE_MODE_GEMV_A16),
+    ("tiny_e4m3_m1", 20, B.MOE_MODE_AUTO),
+])
+def test_single_call_layer_matches_three_calls(name, M, mode):
+    """moe_layer (route pack inside the gate/up launch for small E4M3 routes)
+    gives the route tables, y rows and outputs of the three calls bit for bit,
+    also with invalid ids."""
+    from fp4_block_scaled_amd.layer import MoeLayer
+    wl = workloads.with_shape(workloads.WORKLOADS[name], M=max(M, workloads.WORKLOADS[name].M))
+    print(f"single call {name} M={M} mode={mode}", flush=True)
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 1, M=M)
+    if M > 1:
+        ids[1, 0] = -1
+        ids[M - 1, -1] = wl.experts + 3
+    res = []
+    for single in (True, False):
+        L = MoeLayer(*case.cbanks, wl.hidden, wl.inter, wl.top_k, M, wl.limit, mode, single_call=single)
+        L.ws.fill_(0x5A)
+        L.y.fill_(float("nan"))
+        ids_d = torch.from_numpy(np.ascontiguousarray(ids)).cuda()
+        w_d = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+        assert case.x.shape[0] >= M
+        out = L(case.x[:M], ids_d, w_d).clone()
+        torch.cuda.synchronize()
+        tabs = {k: v.cpu().numpy() for k, v in L.route_tables().items()}
+        nv = int(tabs["expert_offsets"][-1])
+        res.append((out.cpu().numpy(), L.y[:nv].cpu().numpy(), tabs))
+    (o1, y1, t1), (o2, y2, t2) = res
+    for key in t1:
+        a, b = t1[key], t2[key]
+        if key in ("sorted_slot", "sorted_token"):
+            a, b = a[:int(t1["expert_offsets"][-1])], b[:int(t2["expert_offsets"][-1])]
+        assert np.array_equal(a, b), f"route table {key} differs"
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
