@@ -261,22 +261,29 @@ def test_grouping_rows_never_changes_a_row():
         assert np.array_equal(one[0].view(np.uint32), full[t].view(np.uint32)), t
 
 
-@pytest.mark.parametrize("name,M,mode", [
-    ("decode_e4m3_m1", 1, B.MOE_MODE_AUTO), ("verify_e4m3_m8", 8, B.MOE_MODE_AUTO),
-    ("verify_e4m3_m8", 16, B.MOE_MODE_AUTO), ("nvfp4_m1", 1, B.MOE_MODE_AUTO),
-    ("tiny_e4m3_m1", 1, B.MOE_MODE_AUTO), ("tiny_e4m3_m1", 40, B.MOE_MODE_GEMV_A16),
-    ("tiny_e4m3_m1", 20, B.MOE_MODE_AUTO),
+@pytest.mark.parametrize("name,M,mode,invalid", [
+    ("decode_e4m3_m1", 1, B.MOE_MODE_AUTO, "some"), ("verify_e4m3_m8", 8, B.MOE_MODE_AUTO, "some"),
+    ("verify_e4m3_m8", 16, B.MOE_MODE_AUTO, "some"), ("nvfp4_m1", 1, B.MOE_MODE_AUTO, "some"),
+    ("tiny_e4m3_m1", 1, B.MOE_MODE_AUTO, "some"), ("tiny_e4m3_m1", 40, B.MOE_MODE_GEMV_A16, "some"),
+    ("tiny_e4m3_m1", 20, B.MOE_MODE_AUTO, "some"), ("tiny_e4m3_m1", 6, B.MOE_MODE_AUTO, "all"),
+    ("tiny_e4m3_m1", 5, B.MOE_MODE_AUTO, "token"),
 ])
-def test_single_call_layer_matches_three_calls(name, M, mode):
+def test_single_call_layer_matches_three_calls(name, M, mode, invalid):
     """moe_layer (route pack inside the gate/up launch for small E4M3 routes)
     gives the route tables, y rows and outputs of the three calls bit for bit,
-    also with invalid ids."""
+    also with invalid ids, a token with no valid slot, and no valid slot at
+    all (zero outputs)."""
     from fp4_block_scaled_amd.layer import MoeLayer
     wl = workloads.with_shape(workloads.WORKLOADS[name], M=max(M, workloads.WORKLOADS[name].M))
     print(f"single call {name} M={M} mode={mode}", flush=True)
     case = get_case(wl)
     ids, w, _ = workloads.make_routes(wl, 1, M=M)
-    if M > 1:
+    if invalid == "all":
+        ids[:] = -1
+        ids[0, 0] = wl.experts
+    elif invalid == "token":
+        ids[2, :] = -1
+    elif M > 1:
         ids[1, 0] = -1
         ids[M - 1, -1] = wl.experts + 3
     res = []
@@ -284,6 +291,7 @@ def test_single_call_layer_matches_three_calls(name, M, mode):
         L = MoeLayer(*case.cbanks, wl.hidden, wl.inter, wl.top_k, M, wl.limit, mode, single_call=single)
         L.ws.fill_(0x5A)
         L.y.fill_(float("nan"))
+        L.out.fill_(float("nan"))
         ids_d = torch.from_numpy(np.ascontiguousarray(ids)).cuda()
         w_d = torch.from_numpy(np.ascontiguousarray(w)).cuda()
         assert case.x.shape[0] >= M
@@ -300,3 +308,8 @@ def test_single_call_layer_matches_three_calls(name, M, mode):
         assert np.array_equal(a, b), f"route table {key} differs"
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.all(np.isfinite(o1))
+    if invalid == "all":
+        assert np.all(o1 == 0.0)
+    if invalid == "token":
+        assert np.all(o1[2] == 0.0)
