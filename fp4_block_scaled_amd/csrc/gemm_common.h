@@ -76,4 +76,42 @@ __device__ __forceinline__ void dma4(const void *base, uint32_t off, uint32_t ld
 #define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 #define MOE_BARRIER() asm volatile("s_barrier" ::: "memory")
 
+// vmcnt wait that leaves min(n, N) stages of PER DMA instructions in flight
+template <int PER, int N>
+__device__ __forceinline__ void wait_stages(int n)
+{
+    if constexpr (N == 0) {
+        MOE_WAIT_VM(0);
+    } else {
+        if (n >= N) MOE_WAIT_VM(N * PER);
+        else wait_stages<PER, N - 1>(n);
+    }
+}
+
+// Ring of NST LDS stages: K step kb lives in stage kb % NST.  The DMA for
+// step kb + NST - 1 goes out once every wave has passed the barrier of step
+// kb, i.e. is done reading stage (kb - 1) % NST; before that barrier each
+// wave waits until its own share of stage kb has landed, leaving the later
+// stages in flight.
+template <int NST, int PER, class Issue, class Compute>
+__device__ __forceinline__ void k_loop(int KB, uint8_t *sm, int stage_bytes, const Issue &issue,
+                                       const Compute &compute)
+{
+    MOE_WAIT_VM(0);    // retire the set-up loads before the DMA starts
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j)
+        if (j < KB) issue(j, sm + j * stage_bytes);
+    int cs = 0, is = NST - 1;
+    for (int kb = 0; kb < KB; ++kb) {
+        wait_stages<PER, NST - 2>(KB - 1 - kb);
+        MOE_WAIT_LGKM0();
+        MOE_BARRIER();
+        if (kb + NST - 1 < KB) issue(kb + NST - 1, sm + is * stage_bytes);
+        compute(sm + cs * stage_bytes, kb);
+        cs = cs + 1 == NST ? 0 : cs + 1;
+        is = is + 1 == NST ? 0 : is + 1;
+    }
+    MOE_WAIT_VM(0);
+}
+
 }  // namespace

@@ -188,9 +188,12 @@ constexpr int kGuThreads = 512;
 constexpr int GU_A = 0, GU_B = 128 * 128, GU_S = GU_B + 256 * 128, GU_STAGE = GU_S + 8 * 256;
 constexpr int GU_DMA = 2 + 4 + 1;   // DMA instructions per wave per stage
 
+constexpr int GU_NST = 3;           // LDS stages of the gate/up GEMM (2 K steps in flight)
+static_assert(GU_NST * GU_STAGE <= 160 * 1024, "gate/up stages exceed LDS");
+
 __global__ __launch_bounds__(kGuThreads, 1) void gemm_gateup_kernel(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t st0[GU_STAGE], st1[GU_STAGE], st2[GU_STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t sm[GU_NST * GU_STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int wm = wave & 3, wn = wave >> 2;
@@ -277,25 +280,7 @@ __global__ __launch_bounds__(kGuThreads, 1) void gemm_gateup_kernel(GemmArgs a)
         }
     };
 
-    auto step = [&](int kb, const uint8_t *cur, uint8_t *later) {
-        if (kb + 1 < KB) MOE_WAIT_VM(GU_DMA); else MOE_WAIT_VM(0);
-        MOE_WAIT_LGKM0();
-        MOE_BARRIER();
-        if (kb + 2 < KB) issue(kb + 2, later);
-        compute(cur, kb);
-    };
-
-    MOE_WAIT_VM(0);    // retire the offset and scale loads above before the DMA starts
-    issue(0, st0);
-    if (KB > 1) issue(1, st1);
-    for (int kb = 0; kb < KB; kb += 3) {
-        step(kb, st0, st2);
-        if (kb + 1 >= KB) break;
-        step(kb + 1, st1, st0);
-        if (kb + 2 >= KB) break;
-        step(kb + 2, st2, st1);
-    }
-    MOE_WAIT_VM(0);
+    k_loop<GU_NST, GU_DMA>(KB, sm, GU_STAGE, issue, compute);
     __syncthreads();
 
     // epilogue: h = SwiGLU(g, u); per-row amax over the block's 128 columns
@@ -315,7 +300,7 @@ __global__ __launch_bounds__(kGuThreads, 1) void gemm_gateup_kernel(GemmArgs a)
             for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
             rmax[mt][i] = m;
         }
-    float *xm = reinterpret_cast<float *>(st0);    // [2 column halves][128 rows]
+    float *xm = reinterpret_cast<float *>(sm);     // [2 column halves][128 rows]
     if ((lane & 15) == 0) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -323,7 +308,7 @@ __global__ __launch_bounds__(kGuThreads, 1) void gemm_gateup_kernel(GemmArgs a)
             for (int i = 0; i < 4; ++i) xm[wn * 128 + wm * 32 + mt * 16 + (lane >> 4) * 4 + i] = rmax[mt][i];
     }
     __syncthreads();
-    uint8_t *ct = st1;                             // codes tile [128][144]
+    uint8_t *ct = sm + GU_STAGE;                   // codes tile [128][144]
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -355,9 +340,12 @@ __global__ __launch_bounds__(kGuThreads, 1) void gemm_gateup_kernel(GemmArgs a)
 constexpr int DN_A = 0, DN_B = 128 * 128, DN_S = DN_B + 128 * 128, DN_STAGE = DN_S + 4 * 256;
 constexpr int DN_DMA = 4 + 4 + 1;
 
+constexpr int DN_NST = 3;           // LDS stages of the down GEMM (2 K steps in flight)
+static_assert(DN_NST * DN_STAGE <= 160 * 1024, "down stages exceed LDS");
+
 __global__ __launch_bounds__(kThreads, 1) void gemm_down_kernel(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t st0[DN_STAGE], st1[DN_STAGE], st2[DN_STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t sm[DN_NST * DN_STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
@@ -422,24 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_down_kernel(GemmArgs a)
                 for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(p[mt][nt][i], fa[mt][i], acc[mt][nt][i]);
     };
 
-    auto step = [&](int kb, const uint8_t *cur, uint8_t *later) {
-        if (kb + 1 < KB) MOE_WAIT_VM(DN_DMA); else MOE_WAIT_VM(0);
-        MOE_WAIT_LGKM0();
-        MOE_BARRIER();
-        if (kb + 2 < KB) issue(kb + 2, later);
-        compute(cur, kb);
-    };
-
-    MOE_WAIT_VM(0);    // retire the offset and scale loads above before the DMA starts
-    issue(0, st0);
-    if (KB > 1) issue(1, st1);
-    for (int kb = 0; kb < KB; kb += 3) {
-        step(kb, st0, st2);
-        if (kb + 1 >= KB) break;
-        step(kb + 1, st1, st0);
-        if (kb + 2 >= KB) break;
-        step(kb + 2, st2, st1);
-    }
+    k_loop<DN_NST, DN_DMA>(KB, sm, DN_STAGE, issue, compute);
 
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
