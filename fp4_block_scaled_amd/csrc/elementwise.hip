@@ -13,6 +13,24 @@
 
 namespace {
 
+// y rows are read once: non-temporal loads keep them out of the way.
+__device__ __forceinline__ float4 load_once(const float *p)
+{
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void add_row(float4 &acc, const float4 v)
+{
+    acc.x = __fadd_rn(acc.x, v.x); acc.y = __fadd_rn(acc.y, v.y);
+    acc.z = __fadd_rn(acc.z, v.z); acc.w = __fadd_rn(acc.w, v.w);
+}
+
+// KMAX > 0: top_k <= KMAX, the slot loop unrolled so that every y load is in
+// flight before the first product; KMAX == 0: any top_k, one slot at a time.
+// Either way the products are added in slot order.
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const int32_t *__restrict__ t2p,
                                                       const float *__restrict__ w, int32_t k,
@@ -25,27 +43,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const int m = ((blockIdx.x - t * bx) * 256 + threadIdx.x) * 4;
     if (m >= H) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const int p = t2p[(size_t)t * k + j];
-        if (p < 0) continue;
-        const float wt = w[(size_t)t * k + j];
-        const float4 v = *reinterpret_cast<const float4 *>(y + (size_t)p * H + m);
-        acc.x = __fadd_rn(acc.x, __fmul_rn(wt, v.x));
-        acc.y = __fadd_rn(acc.y, __fmul_rn(wt, v.y));
-        acc.z = __fadd_rn(acc.z, __fmul_rn(wt, v.z));
-        acc.w = __fadd_rn(acc.w, __fmul_rn(wt, v.w));
+    if constexpr (KMAX > 0) {
+        int p[KMAX];
+        float wt[KMAX];
+        float4 v[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            p[j] = j < k ? t2p[(size_t)t * k + j] : -1;
+            wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (p[j] >= 0) v[j] = load_once(y + (size_t)p[j] * H + m);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (p[j] >= 0)
+                add_row(acc, make_float4(__fmul_rn(wt[j], v[j].x), __fmul_rn(wt[j], v[j].y),
+                                         __fmul_rn(wt[j], v[j].z), __fmul_rn(wt[j], v[j].w)));
+    } else {
+        for (int j = 0; j < k; ++j) {
+            const int pj = t2p[(size_t)t * k + j];
+            if (pj < 0) continue;
+            const float wj = w[(size_t)t * k + j];
+            const float4 vj = load_once(y + (size_t)pj * H + m);
+            add_row(acc, make_float4(__fmul_rn(wj, vj.x), __fmul_rn(wj, vj.y), __fmul_rn(wj, vj.z),
+                                     __fmul_rn(wj, vj.w)));
+        }
     }
     const size_t o = (size_t)t * H + m;
-    if (shared) {
-        const float4 v = *reinterpret_cast<const float4 *>(shared + o);
-        acc.x = __fadd_rn(acc.x, v.x); acc.y = __fadd_rn(acc.y, v.y);
-        acc.z = __fadd_rn(acc.z, v.z); acc.w = __fadd_rn(acc.w, v.w);
-    }
-    if (residual) {
-        const float4 v = *reinterpret_cast<const float4 *>(residual + o);
-        acc.x = __fadd_rn(acc.x, v.x); acc.y = __fadd_rn(acc.y, v.y);
-        acc.z = __fadd_rn(acc.z, v.z); acc.w = __fadd_rn(acc.w, v.w);
-    }
+    if (shared) add_row(acc, *reinterpret_cast<const float4 *>(shared + o));
+    if (residual) add_row(acc, *reinterpret_cast<const float4 *>(residual + o));
     *reinterpret_cast<float4 *>(out + o) = acc;
 }
 
@@ -56,7 +83,12 @@ hipError_t launch_combine(const float *y, const int32_t *token_to_perm, const fl
                           float *out, hipStream_t st)
 {
     const int bx = (hidden / 4 + 255) / 256;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(bx * M)), dim3(256), 0, st, y, token_to_perm,
-                       w, k, hidden, bx, shared, residual, out);
+    const dim3 grid((unsigned)(bx * M));
+    if (k <= 8)
+        hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, st, y, token_to_perm, w, k, hidden,
+                           bx, shared, residual, out);
+    else
+        hipLaunchKernelGGL(combine_kernel<0>, grid, dim3(256), 0, st, y, token_to_perm, w, k, hidden,
+                           bx, shared, residual, out);
     return hipGetLastError();
 }
