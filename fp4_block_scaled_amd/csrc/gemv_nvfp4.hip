@@ -13,6 +13,8 @@
 // activations with v_dot2) or to f32 (down, against FP32 h); the E2M1 values
 // are exact in both.  The two E4M3 group scales of a lane's 32 weights are
 // applied once per 16 products; scale_2 once per output.
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "fused_common.h"
 
@@ -32,6 +34,11 @@ struct GateUpArgs {
     float *h;                           // [S][I]
     int32_t H, I, ntiles, st;           // st: slots per weight pass (<= ST)
     float limit;
+    // route built inside the launch (small routes): ids [M][k], and the
+    // tables block 0 writes for the launches after it
+    const int32_t *ids;
+    int32_t M, k, E;
+    MoeRouteDev r;
 };
 
 struct DownArgs {
@@ -104,19 +111,45 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 // compiler waits for exactly the chunk it multiplies); NCH == 0 is the
 // generic looped form with one chunk in flight.  The up sums reach the gate
 // waves through LDS; they apply scale_2, the clamped SwiGLU, and write h.
-template <int CH, int NCH, int ST>
+// ROUTE: the route of the S <= kFusedMaxSlots slots is built in LDS by every
+// block from the ids (the same stable pack as route_pack), instead of read
+// from the tables of a route pack launched before; block 0 writes the
+// tables for the down and combine launches that follow.
+struct NoRoute {};
+
+template <int CH, int NCH, int ST, bool ROUTE>
 __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpArgs a)
 {
     extern __shared__ uint4 xl[];                    // [a.st][H / 8], permuted per segment
     __shared__ float ush[ST][16];
+    __shared__ typename std::conditional<ROUTE, FusedRoute, NoRoute>::type R;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int grp = lane >> 3, sub = lane & 7;
     const int tile = blockIdx.x % a.ntiles;
     const int ai = blockIdx.x / a.ntiles;
-    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
-    if (e < 0) return;
+    int e, p0, ne;
+    const int32_t *tok;
+    if constexpr (ROUTE) {
+        const int id_in = tid < a.M * a.k ? a.ids[tid] : -1;
+        fused_route(a, R, id_in);
+        fused_route_status(a, R);
+        if (ai >= moe::uniform(R.na)) {
+            fused_route_tables(a, R);
+            return;
+        }
+        e = moe::uniform(R.ae[ai]);
+        p0 = moe::uniform(R.ap0[ai]);
+        ne = moe::uniform(R.acnt[ai]);
+        tok = R.tok + p0;
+    } else {
+        e = moe::uniform(a.active[ai]);              // -1 past the active experts
+        if (e < 0) return;
+        p0 = moe::uniform(a.offsets[e]);
+        ne = moe::uniform(a.offsets[e + 1]) - p0;
+        tok = a.sorted_token + p0;
+    }
     const int H = a.H, I = a.I, H8 = H >> 3;
     const int nch = NCH > 0 ? NCH : H / (kSegK * CH);
     const bool is_up = wave >= 2;
@@ -129,8 +162,6 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     const uint8_t *cb0 = (is_up ? a.ucodes : a.gcodes) + row0 * rowb;
     const uint8_t *sb0 = (is_up ? a.uscales : a.gscales) + row0 * rows;
     const uint32_t coff = (uint32_t)grp * rowb + sub * 16, soff = (uint32_t)grp * rows + sub * 2;
-    const int p0 = moe::uniform(a.offsets[e]);
-    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
 
     for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
         const int nt = min(a.st, ne - s0);
@@ -174,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
             const int j = f / H8, r = f - j * H8;     // r: source uint4 (8 K values)
             const int sg = r >> 5, rr = r & 31;
             xl[j * H8 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] =
-                *reinterpret_cast<const uint4 *>(a.x + (size_t)a.sorted_token[p0 + s0 + j] * H + r * 8);
+                *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
         }
         if constexpr (NCH > 0) {
             uint4 w[3][CH];
@@ -225,6 +256,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
         }
         moe::lds_barrier();                           // x and ush are reused by the next pass
     }
+    if constexpr (ROUTE) fused_route_tables(a, R);
 }
 
 // down: one block = 32 output rows of one active expert over the whole of K
@@ -556,28 +588,48 @@ namespace {
 
 constexpr int kGUST = 8, kDNST = 8;
 
-template <int CH, int NCH, int ST>
+template <int CH, int NCH, int ST, bool ROUTE>
 void gateup_launch(const GateUpArgs &a, int grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((gemv_gateup_nvfp4_kernel<CH, NCH, ST>), dim3(grid), dim3(kThreads),
+    hipLaunchKernelGGL((gemv_gateup_nvfp4_kernel<CH, NCH, ST, ROUTE>), dim3(grid), dim3(kThreads),
                        (size_t)a.st * a.H * 2, st, a);
 }
 
 // Unrolled kernels for 4-segment chunks (hidden a multiple of 1024 up to
 // 8192) per pass size; every other shape runs the looped kernel.
-template <int ST>
+template <int ST, bool ROUTE>
 bool gateup_launch_unrolled(const GateUpArgs &a, int nch, int grid, hipStream_t st)
 {
     switch (nch) {
-    case 1: gateup_launch<4, 1, ST>(a, grid, st); return true;
-    case 2: gateup_launch<4, 2, ST>(a, grid, st); return true;
-    case 3: gateup_launch<4, 3, ST>(a, grid, st); return true;
-    case 4: gateup_launch<4, 4, ST>(a, grid, st); return true;
-    case 5: gateup_launch<4, 5, ST>(a, grid, st); return true;
-    case 6: gateup_launch<4, 6, ST>(a, grid, st); return true;
-    case 7: gateup_launch<4, 7, ST>(a, grid, st); return true;
-    case 8: gateup_launch<4, 8, ST>(a, grid, st); return true;
+    case 1: gateup_launch<4, 1, ST, ROUTE>(a, grid, st); return true;
+    case 2: gateup_launch<4, 2, ST, ROUTE>(a, grid, st); return true;
+    case 3: gateup_launch<4, 3, ST, ROUTE>(a, grid, st); return true;
+    case 4: gateup_launch<4, 4, ST, ROUTE>(a, grid, st); return true;
+    case 5: gateup_launch<4, 5, ST, ROUTE>(a, grid, st); return true;
+    case 6: gateup_launch<4, 6, ST, ROUTE>(a, grid, st); return true;
+    case 7: gateup_launch<4, 7, ST, ROUTE>(a, grid, st); return true;
+    case 8: gateup_launch<4, 8, ST, ROUTE>(a, grid, st); return true;
     default: return false;
+    }
+}
+
+template <bool ROUTE>
+void gateup_dispatch(const GateUpArgs &a, int grid, hipStream_t st)
+{
+    const int ch = gemv_chunk_segs(kFmtNVFP4, a.H), nch = a.H / kSegK / ch;
+    bool done = false;
+    if (ch == 4) {
+        if (a.st <= 1) done = gateup_launch_unrolled<1, ROUTE>(a, nch, grid, st);
+        else if (a.st <= 2) done = gateup_launch_unrolled<2, ROUTE>(a, nch, grid, st);
+        else done = gateup_launch_unrolled<8, ROUTE>(a, nch, grid, st);
+    }
+    if (!done) {
+        switch (ch) {
+        case 4: gateup_launch<4, 0, kGUST, ROUTE>(a, grid, st); break;
+        case 3: gateup_launch<3, 0, kGUST, ROUTE>(a, grid, st); break;
+        case 2: gateup_launch<2, 0, kGUST, ROUTE>(a, grid, st); break;
+        default: gateup_launch<1, 0, kGUST, ROUTE>(a, grid, st); break;
+        }
     }
 }
 
@@ -611,9 +663,9 @@ bool down_launch_unrolled(const DownArgs &a, int nch, int grid, hipStream_t st)
 hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
                                     const uint16_t *x, const MoeRouteDev &r, int32_t M, int32_t S,
                                     int32_t E, int32_t hidden, int32_t inter, float limit, float *h,
-                                    hipStream_t st)
+                                    hipStream_t st, const int32_t *route_ids, int32_t top_k)
 {
-    GateUpArgs a;
+    GateUpArgs a{};
     a.st = gemv_gateup_pass_slots(M, hidden, kGUST);
     a.gcodes = gate.codes; a.ucodes = up.codes;
     a.gscales = (const uint8_t *)gate.scales; a.uscales = (const uint8_t *)up.scales;
@@ -621,21 +673,13 @@ hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &
     a.x = x; a.offsets = r.offsets; a.sorted_token = r.sorted_token; a.active = r.active;
     a.h = h; a.H = hidden; a.I = inter; a.limit = limit;
     a.ntiles = inter / 16;
+    a.ids = route_ids; a.M = M; a.k = top_k; a.E = E; a.r = r;
     const int grid = (S < E ? S : E) * a.ntiles;
-    const int ch = gemv_chunk_segs(kFmtNVFP4, hidden), nch = hidden / kSegK / ch;
-    bool done = false;
-    if (ch == 4) {
-        if (a.st <= 1) done = gateup_launch_unrolled<1>(a, nch, grid, st);
-        else if (a.st <= 2) done = gateup_launch_unrolled<2>(a, nch, grid, st);
-        else done = gateup_launch_unrolled<8>(a, nch, grid, st);
-    }
-    if (!done) {
-        switch (ch) {
-        case 4: gateup_launch<4, 0, kGUST>(a, grid, st); break;
-        case 3: gateup_launch<3, 0, kGUST>(a, grid, st); break;
-        case 2: gateup_launch<2, 0, kGUST>(a, grid, st); break;
-        default: gateup_launch<1, 0, kGUST>(a, grid, st); break;
-        }
+    if (route_ids) {
+        if (S > kFusedMaxSlots) return hipErrorInvalidValue;
+        gateup_dispatch<true>(a, grid, st);
+    } else {
+        gateup_dispatch<false>(a, grid, st);
     }
     return hipGetLastError();
 }

@@ -296,7 +296,7 @@ static moe_status_t check_bank(const char *fn, const moe_bank_t *b, const char *
 
 // The expert FFN of moe_expert_ffn.  With route_ids, the route tables of
 // `route` (carved, not yet filled) are built by the gate/up launch itself
-// from the ids: only for the GEMV tier with E4M3 banks and S <= 64.
+// from the ids: only for the GEMV tier and S <= 64.
 static moe_status_t expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
                                const uint16_t *x_bf16, const moe_route_t *route, int32_t hidden,
                                int32_t inter, float limit, int32_t mode, float *y_packed, void *ws,
@@ -399,7 +399,8 @@ static moe_status_t expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, con
         e = launch_gemv_gateup_e4m3(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, limit, h, s,
                                     route_ids, k);
     else
-        e = launch_gemv_gateup_nvfp4(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, limit, h, s);
+        e = launch_gemv_gateup_nvfp4(bg, bu, x_bf16, r, M, (int32_t)S, E, hidden, inter, limit, h, s,
+                                     route_ids, k);
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: gate/up GEMV launch");
     stage_mark(1, s);
     if (fmt == MOE_W_E4M3_B128)
@@ -438,7 +439,7 @@ moe_status_t moe_layer(const moe_bank_t *gate, const moe_bank_t *up, const moe_b
         return fail(MOE_ERR_ARG, "%s: unknown mode %d", fn, mode);
     const int64_t S = (int64_t)M * top_k;
     moe_status_t st;
-    if (S <= 64 && fmt == MOE_W_E4M3_B128 && resolve(M, fmt, mode) == MOE_MODE_GEMV_A16) {
+    if (S <= 64 && resolve(M, fmt, mode) == MOE_MODE_GEMV_A16) {
         // the route pack runs inside the gate/up launch
         if (ws_bytes < moe::route_region_bytes(S, E))
             return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes,

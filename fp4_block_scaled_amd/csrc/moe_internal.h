@@ -155,7 +155,8 @@ hipError_t launch_fused_decode_nvfp4(const GemvBankDev &gate, const GemvBankDev 
 hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
                                     const uint16_t *x, const MoeRouteDev &r, int32_t M,
                                     int32_t S, int32_t E, int32_t hidden, int32_t inter,
-                                    float limit, float *h, hipStream_t st);
+                                    float limit, float *h, hipStream_t st,
+                                    const int32_t *route_ids = nullptr, int32_t top_k = 0);
 hipError_t launch_gemv_down_nvfp4(const GemvBankDev &down, const float *h, const MoeRouteDev &r,
                                   int32_t M, int32_t S, int32_t E, int32_t hidden, int32_t inter,
                                   float *y, hipStream_t st);

@@ -243,7 +243,7 @@ moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
 /* The whole layer in one call: the route pack, the expert FFN of tier `mode`
  * and the combine, with the outputs (route tables in *route, y_packed, out)
  * of moe_route_pack + moe_expert_ffn + moe_combine, bit for bit.  For the
- * GEMV tier with E4M3 banks and M*top_k <= 64 slots the route pack runs
+ * GEMV tier (either format) and M*top_k <= 64 slots the route pack runs
  * inside the gate/up launch (every block builds the route of the slots from
  * the ids in LDS; block 0 writes the tables for the down and combine
  * launches), so the layer is three launches; otherwise the three calls'

@@ -266,10 +266,11 @@ def test_grouping_rows_never_changes_a_row():
     ("verify_e4m3_m8", 16, B.MOE_MODE_AUTO, "some"), ("nvfp4_m1", 1, B.MOE_MODE_AUTO, "some"),
     ("tiny_e4m3_m1", 1, B.MOE_MODE_AUTO, "some"), ("tiny_e4m3_m1", 40, B.MOE_MODE_GEMV_A16, "some"),
     ("tiny_e4m3_m1", 20, B.MOE_MODE_AUTO, "some"), ("tiny_e4m3_m1", 6, B.MOE_MODE_AUTO, "all"),
-    ("tiny_e4m3_m1", 5, B.MOE_MODE_AUTO, "token"),
+    ("tiny_e4m3_m1", 5, B.MOE_MODE_AUTO, "token"), ("nvfp4_m16", 8, B.MOE_MODE_AUTO, "some"),
+    ("nvfp4_m16", 16, B.MOE_MODE_AUTO, "some"),
 ])
 def test_single_call_layer_matches_three_calls(name, M, mode, invalid):
-    """moe_layer (route pack inside the gate/up launch for small E4M3 routes)
+    """moe_layer (route pack inside the gate/up launch for small routes)
     gives the route tables, y rows and outputs of the three calls bit for bit,
     also with invalid ids, a token with no valid slot, and no valid slot at
     all (zero outputs)."""
