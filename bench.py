@@ -304,17 +304,17 @@ def cpu_baseline(wl, banks, x, sets, budget_s):
 # traffic is reported as null.
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC = {
-    "decode_e4m3_m1": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_internal.h"],
-        "src": "bce16971a651f3e198f66700d679828bea648e35fbf0645b", "fetch_kib": 115074, "write_kib": 65},
-    "decode_e4m3_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_internal.h"],
-        "src": "bce16971a651f3e198f66700d679828bea648e35fbf0645b", "fetch_kib": 173072, "write_kib": 1070},
-    "nvfp4_m1": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "moe_internal.h"],
+    "decode_e4m3_m1": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
+        "src": "bce16971a651f3e198f66700d679828b80b4a18ccd74a69d", "fetch_kib": 115074, "write_kib": 65},
+    "decode_e4m3_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
+        "src": "bce16971a651f3e198f66700d679828b80b4a18ccd74a69d", "fetch_kib": 173072, "write_kib": 1070},
+    "nvfp4_m1": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "moe_device.h"],
         "src": "e701572306648d4eea648e35fbf0645b", "fetch_kib": 43302, "write_kib": 48},
-    "nvfp4_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_internal.h"],
+    "nvfp4_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
         "src": "e701572306648d4e98f66700d679828bea648e35fbf0645b", "fetch_kib": 64865, "write_kib": 835},
-    "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_internal.h"],
+    "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h"],
         "src": "8f7e2ad9dfe23eb6573655229e2b10f4ea648e35fbf0645b", "fetch_kib": 4279951, "write_kib": 122154},
-    "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_internal.h"],
+    "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
         "src": "42fff30e4b13f531573655229e2b10f4ea648e35fbf0645b", "fetch_kib": 2083942, "write_kib": 196608},
 }
 
