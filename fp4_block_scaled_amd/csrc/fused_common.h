@@ -136,6 +136,44 @@ __device__ void fused_route(const Args &a, FusedRoute &R, int id_in)
     moe::lds_barrier();
 }
 
+// The active expert of index ai of a route of S <= 64 slots, worked out by
+// each wave on its own from the ids (lane s holds slot s; no LDS, no
+// barrier), for a launch whose blocks each need only their own expert: e
+// (-1 when ai is past the active experts), its first packed row p0 (the
+// valid slots of smaller experts), its slot count ne and the mask of its
+// slots (bit s: slot s chose it), in slot order -- the stable pack.
+struct LightRoute {
+    int e, p0, ne;
+    uint64_t mask;
+};
+
+__device__ __forceinline__ LightRoute light_route(const int32_t *ids, int S, int E, int ai)
+{
+    const int lane = threadIdx.x & 63;
+    const int id = lane < S ? ids[lane] : -1;
+    const int key = id >= 0 && id < E ? id : 0x7FFFFFFF;
+    int dup_before = 0;
+    for (int j = 0; j < S; ++j) {
+        const int kj = __builtin_amdgcn_readlane(key, j);
+        dup_before += (j < lane) & (kj == key);
+    }
+    const bool first = key != 0x7FFFFFFF && dup_before == 0;
+    const uint64_t fm = __ballot(first);
+    int rank = 0;                                    // distinct valid experts below key
+    for (int j = 0; j < S; ++j) {
+        const int kj = __builtin_amdgcn_readlane(key, j);
+        rank += (int)((fm >> j) & 1) & (kj < key);
+    }
+    const uint64_t sel = __ballot(first && rank == ai);
+    LightRoute r{-1, 0, 0, 0};
+    if (sel == 0) return r;
+    r.e = __builtin_amdgcn_readlane(key, __ffsll((unsigned long long)sel) - 1);
+    r.p0 = __popcll(__ballot(key < r.e));
+    r.mask = __ballot(key == r.e);
+    r.ne = __popcll(r.mask);
+    return r;
+}
+
 // Block 0 writes the other route tables, as route_pack writes them.  Nothing
 // in the launch reads them, so this runs at the end, off the critical path.
 template <class Args>

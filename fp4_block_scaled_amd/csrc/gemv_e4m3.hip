@@ -247,10 +247,11 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
     }
 }
 
-// ROUTE: the route of the S <= kFusedMaxSlots slots is built in LDS by every
-// block from the ids (the same stable pack as route_pack), instead of read
-// from the tables of a route pack launched before; block 0 writes the
-// tables for the down and combine launches that follow.
+// ROUTE: the route of the S <= 64 slots comes from the ids inside the launch
+// (the same stable pack as route_pack) instead of from the tables of a route
+// pack launched before: every block works out its own expert; block 0 also
+// builds the whole route and writes the tables for the down and combine
+// launches that follow.
 template <int CH, int NCH, int ST, bool ROUTE>
 __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArgs a)
 {
@@ -259,16 +260,24 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
     const int tile = blockIdx.x % a.ntiles;
     const int ai = blockIdx.x / a.ntiles;
     if constexpr (ROUTE) {
-        __shared__ FusedRoute R;
-        const int id_in = (int)threadIdx.x < a.M * a.k ? a.ids[threadIdx.x] : -1;
-        fused_route(a, R, id_in);
-        fused_route_status(a, R);
-        if (ai < moe::uniform(R.na)) {
-            const int e = moe::uniform(R.ae[ai]), p0 = moe::uniform(R.ap0[ai]);
-            const int ne = moe::uniform(R.acnt[ai]);
-            gateup_e4m3_item<CH, NCH, ST>(a, e, tile, p0, ne, R.tok + p0, xl, ush);
+        // every wave finds this block's expert from the ids on its own; the
+        // tokens of its slots go to LDS; block 0 builds and writes the whole
+        // route tables after its item, off the critical path
+        __shared__ int32_t tokl[64];
+        const LightRoute lr = light_route(a.ids, a.M * a.k, a.E, ai);
+        if (lr.e >= 0 && threadIdx.x < 64 && ((lr.mask >> threadIdx.x) & 1))
+            tokl[__popcll(lr.mask & ((1ull << threadIdx.x) - 1))] = (int)threadIdx.x / a.k;
+        moe::lds_barrier();
+        if (lr.e >= 0)
+            gateup_e4m3_item<CH, NCH, ST>(a, moe::uniform(lr.e), tile, moe::uniform(lr.p0),
+                                          moe::uniform(lr.ne), tokl, xl, ush);
+        if (blockIdx.x == 0) {
+            __shared__ FusedRoute R;
+            const int id_in = (int)threadIdx.x < a.M * a.k ? a.ids[threadIdx.x] : -1;
+            fused_route(a, R, id_in);
+            fused_route_status(a, R);
+            fused_route_tables(a, R);
         }
-        fused_route_tables(a, R);
     } else {
         const int e = moe::uniform(a.active[ai]);   // -1 past the active experts
         if (e < 0) return;
@@ -778,7 +787,7 @@ hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &u
     a.ids = route_ids; a.M = M; a.k = top_k; a.E = E; a.r = r;
     const int grid = (S < E ? S : E) * a.ntiles;
     if (route_ids) {
-        if (S > kFusedMaxSlots) return hipErrorInvalidValue;
+        if (S > 64) return hipErrorInvalidValue;
         gateup_dispatch<true>(a, grid, st);
     } else {
         gateup_dispatch<false>(a, grid, st);

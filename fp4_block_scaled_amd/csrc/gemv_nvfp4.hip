@@ -111,11 +111,22 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 // compiler waits for exactly the chunk it multiplies); NCH == 0 is the
 // generic looped form with one chunk in flight.  The up sums reach the gate
 // waves through LDS; they apply scale_2, the clamped SwiGLU, and write h.
-// ROUTE: the route of the S <= kFusedMaxSlots slots is built in LDS by every
-// block from the ids (the same stable pack as route_pack), instead of read
-// from the tables of a route pack launched before; block 0 writes the
-// tables for the down and combine launches that follow.
+// ROUTE: the route of the S <= 64 slots comes from the ids inside the launch
+// (the same stable pack as route_pack) instead of from the tables of a route
+// pack launched before: every block works out its own expert; block 0 also
+// builds the whole route and writes the tables for the down and combine
+// launches that follow.
 struct NoRoute {};
+
+template <class Args, class Route>
+__device__ __forceinline__ void route_tables_block0(const Args &a, Route &R)
+{
+    if (blockIdx.x != 0) return;
+    const int id_in = (int)threadIdx.x < a.M * a.k ? a.ids[threadIdx.x] : -1;
+    fused_route(a, R, id_in);
+    fused_route_status(a, R);
+    fused_route_tables(a, R);
+}
 
 template <int CH, int NCH, int ST, bool ROUTE>
 __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpArgs a)
@@ -123,6 +134,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     extern __shared__ uint4 xl[];                    // [a.st][H / 8], permuted per segment
     __shared__ float ush[ST][16];
     __shared__ typename std::conditional<ROUTE, FusedRoute, NoRoute>::type R;
+    __shared__ int32_t tokl[ROUTE ? 64 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
@@ -132,17 +144,18 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     int e, p0, ne;
     const int32_t *tok;
     if constexpr (ROUTE) {
-        const int id_in = tid < a.M * a.k ? a.ids[tid] : -1;
-        fused_route(a, R, id_in);
-        fused_route_status(a, R);
-        if (ai >= moe::uniform(R.na)) {
-            fused_route_tables(a, R);
+        const LightRoute lr = light_route(a.ids, a.M * a.k, a.E, ai);
+        if (lr.e >= 0 && tid < 64 && ((lr.mask >> tid) & 1))
+            tokl[__popcll(lr.mask & ((1ull << tid) - 1))] = tid / a.k;
+        moe::lds_barrier();
+        if (lr.e < 0) {
+            route_tables_block0(a, R);
             return;
         }
-        e = moe::uniform(R.ae[ai]);
-        p0 = moe::uniform(R.ap0[ai]);
-        ne = moe::uniform(R.acnt[ai]);
-        tok = R.tok + p0;
+        e = moe::uniform(lr.e);
+        p0 = moe::uniform(lr.p0);
+        ne = moe::uniform(lr.ne);
+        tok = tokl;
     } else {
         e = moe::uniform(a.active[ai]);              // -1 past the active experts
         if (e < 0) return;
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
         }
         moe::lds_barrier();                           // x and ush are reused by the next pass
     }
-    if constexpr (ROUTE) fused_route_tables(a, R);
+    if constexpr (ROUTE) route_tables_block0(a, R);
 }
 
 // down: one block = 32 output rows of one active expert over the whole of K
@@ -676,7 +689,7 @@ hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &
     a.ids = route_ids; a.M = M; a.k = top_k; a.E = E; a.r = r;
     const int grid = (S < E ? S : E) * a.ntiles;
     if (route_ids) {
-        if (S > kFusedMaxSlots) return hipErrorInvalidValue;
+        if (S > 64) return hipErrorInvalidValue;
         gateup_dispatch<true>(a, grid, st);
     } else {
         gateup_dispatch<false>(a, grid, st);
