@@ -50,10 +50,13 @@ def parse():
 # --------------------------------------------------------------------------
 # HIP events on the stream the kernels run on (ctypes, no torch wrapper)
 # --------------------------------------------------------------------------
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000     # hipEventDisableSystemFence
+
+
 class Hip:
     def __init__(self):
         self.h = C.CDLL("libamdhip64.so")
-        self.h.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.h.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
         self.h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.h.hipEventSynchronize.argtypes = [C.c_void_p]
         self.h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
@@ -63,7 +66,10 @@ class Hip:
         arr = (C.c_void_p * n)()
         for i in range(n):
             p = C.c_void_p()
-            assert self.h.hipEventCreate(C.byref(p)) == 0
+            # timing events without the system-scope release a default
+            # event adds: nothing on the host reads the layer's output through
+            # an event, and torch's synchronize precedes every host read
+            assert self.h.hipEventCreateWithFlags(C.byref(p), HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0
             arr[i] = p.value
         return arr
 
@@ -213,13 +219,36 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=F
 
     stages = None
     sums_stable = None
+    host_ahead = None
     if want_stages:
         nst = B.moe_set_stage_events(None, wl.fmt, wl.hidden, wl.inter, mode)
         per = nst + 3       # route start, ffn stage marks (nst+1), combine end
         evs = [hip.events(per) for _ in range(steps)]
         sums = []
+        # The stage events time the GPU only if the host has queued a step's
+        # launches before the GPU reaches them: otherwise a host gap between
+        # an event and the next launch counts as kernel time.  So the steps
+        # go in batches, each queued behind a spin kernel that outlasts the
+        # host's queueing of the batch (checked below).
+        batch = 16
+        c0, c1 = hip.events(2)
+        torch.cuda.synchronize()
+        hip.record(c0, sh)
+        torch.cuda._sleep(1 << 20)
+        hip.record(c1, sh)
+        torch.cuda.synchronize()
+        us_per_cycle = hip.ms(c0, c1) * 1000.0 / (1 << 20)
+        hold_us = 4000.0
+        cycles = int(hold_us / max(us_per_cycle, 1e-6))
+        host_us = []
+        ref.view(torch.int32).to(torch.int64).sum()     # the checksum's kernels loaded once
         torch.cuda.synchronize()
         for i in range(steps):
+            if i % batch == 0:
+                if i:
+                    host_us.append((time.perf_counter() - t_b) * 1e6)
+                torch.cuda._sleep(cycles)
+                t_b = time.perf_counter()
             ev = evs[i]
             sub = (C.c_void_p * (nst + 1))(*[ev[1 + j] for j in range(nst + 1)])
             evs[i] = (ev, sub)
@@ -229,8 +258,12 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=F
             hip.record(ev[per - 1], sh)
             # checksum of the output bits, outside the events
             sums.append(out.view(torch.int32).to(torch.int64).sum())
+        host_us.append((time.perf_counter() - t_b) * 1e6)
         B.moe_set_stage_events(None, wl.fmt, wl.hidden, wl.inter, mode)
         torch.cuda.synchronize()
+        host_ahead = max(host_us) < hold_us
+        print(f"# {wl.name}: stage batches queued in {min(host_us):.0f}-{max(host_us):.0f} us "
+              f"behind a {hold_us:.0f} us spin", file=sys.stderr, flush=True)
         sums = [int(v) for v in sums]
         sums_stable = all(sums[i] == sums[i % route_sets] for i in range(steps))
         if mode == B.MOE_MODE_GEMM_A8:
@@ -260,7 +293,7 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=F
         gr = graph_replay(layer, x, ids_d, w_d, steps, hip) if graph else None
     cl = cold_layers(layer, x, ids_d, w_d, steps, hip) if cold else None
     return dict(name=wl.name, us_layer=us_layer, ms_total=total_ms, stable=stable, stages=stages,
-                percentiles=pct, checksums_stable=sums_stable, graph=gr, cold=cl,
+                percentiles=pct, checksums_stable=sums_stable, host_ahead=host_ahead, graph=gr, cold=cl,
                 alg_layer_bytes=alg_layer, alg_gateup_bytes=alg_gateup, unique_experts=uniq,
                 flops=flops, mode=mode, layer=layer, x=x, sets=sets)
 
@@ -305,17 +338,17 @@ def cpu_baseline(wl, banks, x, sets, budget_s):
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC = {
     "decode_e4m3_m1": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
-        "src": "bce16971a651f3e198f66700d679828b80b4a18ccd74a69d", "fetch_kib": 115074, "write_kib": 65},
+        "src": "c2d2d8e62f45df32d610978b517a952c80b4a18ccd74a69d", "fetch_kib": 115067, "write_kib": 65},
     "decode_e4m3_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
-        "src": "bce16971a651f3e198f66700d679828b80b4a18ccd74a69d", "fetch_kib": 173072, "write_kib": 1070},
-    "nvfp4_m1": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "moe_device.h"],
-        "src": "e701572306648d4eea648e35fbf0645b", "fetch_kib": 43302, "write_kib": 48},
+        "src": "c2d2d8e62f45df32d610978b517a952c80b4a18ccd74a69d", "fetch_kib": 173068, "write_kib": 1070},
+    "nvfp4_m1": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
+        "src": "80a699c1ab8c17d7d610978b517a952c80b4a18ccd74a69d", "fetch_kib": 43377, "write_kib": 49},
     "nvfp4_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "e701572306648d4e98f66700d679828bea648e35fbf0645b", "fetch_kib": 64865, "write_kib": 835},
+        "src": "80a699c1ab8c17d7d610978b517a952c80b4a18ccd74a69d", "fetch_kib": 64863, "write_kib": 835},
     "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h"],
-        "src": "8f7e2ad9dfe23eb6573655229e2b10f4ea648e35fbf0645b", "fetch_kib": 4279951, "write_kib": 122154},
+        "src": "0a5215434968026b46ff9d1401442f7f80b4a18ccd74a69d", "fetch_kib": 4245047, "write_kib": 69876},
     "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
-        "src": "42fff30e4b13f531573655229e2b10f4ea648e35fbf0645b", "fetch_kib": 2083942, "write_kib": 196608},
+        "src": "90d4f2b67c21b99a46ff9d1401442f7f80b4a18ccd74a69d", "fetch_kib": 2096609, "write_kib": 196608},
 }
 
 
@@ -487,9 +520,17 @@ def shared_rows(wl, banks, steps, hip):
 
 
 def extra_rows(r):
-    """Per-layer percentiles, the output checksum check, HIP-graph replay and
-    the cold-cache row of one measured workload."""
-    out = {"layer_us_percentiles": r["percentiles"], "checksums_stable": r["checksums_stable"]}
+    """Per-layer percentiles, the output checksum check, the routing's
+    statistics (expert loads over the route sets, rho of correlated
+    routing), HIP-graph replay and the cold-cache row of one measured
+    workload."""
+    infos = [s[2] for s in r["sets"]]
+    routing = {"max_expert_load": max(i["max_load"] for i in infos),
+               "mean_expert_load": round(float(sum(i["mean_load"] for i in infos) / len(infos)), 3)}
+    if "rho" in infos[0]:
+        routing["rho"] = [round(float(i["rho"]), 4) for i in infos]
+    out = {"layer_us_percentiles": r["percentiles"], "checksums_stable": r["checksums_stable"],
+           "routing": routing}
     if r["graph"] is not None:
         out["graph"] = r["graph"]
     if r["cold"] is not None:
@@ -552,6 +593,7 @@ def main():
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(wl.M / (r["us_layer"] * 1e-6), 1),
         "stages_us": {k: round(v, 3) for k, v in r["stages"].items()},
+        "stages_host_ahead": r["host_ahead"],
         "output_stable": r["stable"],
         "roofline": roofline(r),
     }
@@ -568,6 +610,7 @@ def main():
                 "hbm_frac": round(gf / HBM_PEAK_GBPS, 4),
                 "tokens_per_s": round(w2.M / (rf["us_layer"] * 1e-6), 1),
                 "stages_us": {k: round(v, 3) for k, v in rf["stages"].items()},
+                "stages_host_ahead": rf["host_ahead"],
                 "output_stable": rf["stable"], "roofline": roofline(rf), **extra_rows(rf)}
 
     def fused_ok(w2):
@@ -594,6 +637,7 @@ def main():
                       "tokens_per_s": round(w2.M / (r2["us_layer"] * 1e-6), 1),
                       "unique_experts": r2["unique_experts"],
                       "stages_us": {k: round(v, 3) for k, v in r2["stages"].items()},
+                      "stages_host_ahead": r2["host_ahead"],
                       "output_stable": r2["stable"]}
         also[name]["roofline"] = roofline(r2)
         also[name].update(extra_rows(r2))
