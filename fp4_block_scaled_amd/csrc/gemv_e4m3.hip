@@ -66,7 +66,7 @@ __device__ __forceinline__ uint4 load16(const uint8_t *p)
 {
 #ifndef MOE_GEMV_CACHED_LOADS
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    const u32x4 v = moe::load_nt_global<u32x4>(p);
     return make_uint4(v.x, v.y, v.z, v.w);
 #else
     return *reinterpret_cast<const uint4 *>(p);
@@ -185,15 +185,39 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
             }
         };
 
-        // x rows to LDS (their loads go out first), with the first weight
-        // chunks in flight across the barrier
-        for (int f = tid; f < nt * H8; f += kThreads) {
-            const int j = f / H8, r = f - j * H8;
-            xl[f] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
-        }
         if constexpr (NCH > 0) {
+            constexpr int H8C = NCH * CH * 16;       // uint4 per x row (H8)
+            constexpr int XV = (ST * H8C + kThreads - 1) / kThreads;
             uint4 w[3][CH];
-            load_w(w[0], 0);
+            if constexpr (XV <= 4 && ST == 1 && !FUSED) {   // (within the register budget)
+                // x rows to LDS: every x load goes out at once, then the first
+                // weight chunk; the LDS stores wait for the x loads only, so
+                // staging x costs one memory round trip, under the first chunk
+                moe::u32x4 xr[XV];                   // (native vectors stay in VGPRs)
+#pragma unroll
+                for (int i = 0; i < XV; ++i) {
+                    // past the pass's last uint4 a lane reloads that one (never stored)
+                    const int f = min(tid + i * kThreads, nt * H8C - 1);
+                    const int j = f / H8C, r = f - j * H8C;
+                    xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                load_w(w[0], 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < XV; ++i) {
+                    const int f = tid + i * kThreads;
+                    if (f < nt * H8C) reinterpret_cast<moe::u32x4 *>(xl)[f] = xr[i];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                // larger passes: x rows to LDS in a loop, then the first chunk
+                for (int f = tid; f < nt * H8; f += kThreads) {
+                    const int j = f / H8, r = f - j * H8;
+                    xl[f] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
+                }
+                load_w(w[0], 0);
+            }
             if (NCH > 1) load_w(w[1], 1);
             moe::lds_barrier();
 #pragma unroll
@@ -206,6 +230,12 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
+            // x rows to LDS, with the first weight chunk in flight across the
+            // barrier
+            for (int f = tid; f < nt * H8; f += kThreads) {
+                const int j = f / H8, r = f - j * H8;
+                xl[f] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
+            }
             uint4 w0[CH], w1[CH];
             load_w(w0, 0);
             moe::lds_barrier();
@@ -306,8 +336,9 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
 // wait_h() runs once the first weight chunks are in flight and before h is
 // read (a no-op in the standalone kernel, the wait for the expert's h in the
 // fused one).  FUSED (the fused layer's item): the first chunks go out before
-// the wait and h and y move through device-coherent accesses; otherwise h is
-// staged before the first chunks go out.
+// the wait and h and y move through device-coherent accesses; otherwise the
+// h loads go out first (in the unrolled form all of them, followed by the
+// first chunk's loads before h is written to LDS).
 struct NoWait {
     __device__ void operator()() const {}
 };
@@ -393,14 +424,44 @@ __device__ __forceinline__ void down_e4m3_item(const DownArgs &a, int e, int til
                 hl[j * I4 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = hv;
             }
         };
-        if constexpr (!FUSED) stage_h();
         if constexpr (NCH > 0) {
             uint4 w[3][CH];
-            load_w(w[0], 0);
-            if (NCH > 1) load_w(w[1], 1);
+            constexpr int I4C = NCH * CH * 32;       // float4 per h row (I4)
+            constexpr int HV = (ST * I4C + kThreads - 1) / kThreads;
             if constexpr (FUSED) {
+                load_w(w[0], 0);
+                if (NCH > 1) load_w(w[1], 1);
                 wait_h();
                 stage_h();
+            } else if constexpr (HV <= 2) {
+                // every h load goes out at once, then the first weight chunk;
+                // the LDS stores wait for the h loads only
+                moe::f32x4 hr[HV];                   // (native vectors stay in VGPRs)
+#pragma unroll
+                for (int i = 0; i < HV; ++i) {
+                    // past the pass's last float4 a lane reloads that one (never stored)
+                    const int f = min(tid + i * kThreads, nt * I4C - 1);
+                    const int j = f / I4C, r = f - j * I4C;
+                    hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                load_w(w[0], 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < HV; ++i) {
+                    const int f = tid + i * kThreads;
+                    if (f < nt * I4C) {
+                        const int j = f / I4C, r = f - j * I4C;
+                        const int sg = r >> 5, rr = r & 31;
+                        reinterpret_cast<moe::f32x4 *>(hl)[j * I4C + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = hr[i];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (NCH > 1) load_w(w[1], 1);
+            } else {
+                stage_h();
+                load_w(w[0], 0);
+                if (NCH > 1) load_w(w[1], 1);
             }
             moe::lds_barrier();
 #pragma unroll
@@ -411,6 +472,7 @@ __device__ __forceinline__ void down_e4m3_item(const DownArgs &a, int e, int til
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
+            if constexpr (!FUSED) stage_h();
             uint4 w0[CH], w1[CH];
             load_w(w0, 0);
             if constexpr (FUSED) {

@@ -54,13 +54,13 @@ struct DownArgs {
 __device__ __forceinline__ uint4 load16(const uint8_t *p)
 {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    const u32x4 v = moe::load_nt_global<u32x4>(p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 __device__ __forceinline__ uint32_t load2(const uint8_t *p)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+    return moe::load_nt_global<uint16_t>(p);
 }
 
 __device__ __forceinline__ float dot2(bf16x2 a, uint32_t b, float c)
@@ -214,16 +214,45 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
             }
         };
 
-        for (int f = tid; f < nt * H8; f += kThreads) {
-            const int j = f / H8, r = f - j * H8;     // r: source uint4 (8 K values)
-            const int sg = r >> 5, rr = r & 31;
-            xl[j * H8 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] =
-                *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
-        }
         if constexpr (NCH > 0) {
+            constexpr int H8C = NCH * CH * 32;       // uint4 per x row (H8)
+            constexpr int XV = (ST * H8C + kThreads - 1) / kThreads;
             uint4 w[3][CH];
             uint32_t v[3][CH];
-            load_w(w[0], v[0], 0);
+            if constexpr (XV <= 4) {
+                // x rows to LDS: every x load goes out at once, then the first
+                // weight chunk; the LDS stores wait for the x loads only
+                moe::u32x4 xr[XV];                   // (native vectors stay in VGPRs)
+#pragma unroll
+                for (int i = 0; i < XV; ++i) {
+                    // past the pass's last uint4 a lane reloads that one (never stored)
+                    const int f = min(tid + i * kThreads, nt * H8C - 1);
+                    const int j = f / H8C, r = f - j * H8C;
+                    xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                load_w(w[0], v[0], 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < XV; ++i) {
+                    const int f = tid + i * kThreads;
+                    if (f < nt * H8C) {
+                        const int j = f / H8C, r = f - j * H8C;
+                        const int sg = r >> 5, rr = r & 31;
+                        reinterpret_cast<moe::u32x4 *>(xl)[j * H8C + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = xr[i];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                // larger passes: x rows to LDS in a loop, then the first chunk
+                for (int f = tid; f < nt * H8; f += kThreads) {
+                    const int j = f / H8, r = f - j * H8;
+                    const int sg = r >> 5, rr = r & 31;
+                    xl[j * H8 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] =
+                        *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
+                }
+                load_w(w[0], v[0], 0);
+            }
             if (NCH > 1) load_w(w[1], v[1], 1);
             moe::lds_barrier();
 #pragma unroll
@@ -234,6 +263,12 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
+            for (int f = tid; f < nt * H8; f += kThreads) {
+                const int j = f / H8, r = f - j * H8; // r: source uint4 (8 K values)
+                const int sg = r >> 5, rr = r & 31;
+                xl[j * H8 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] =
+                    *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
+            }
             uint4 w0[CH], w1[CH];
             uint32_t v0[CH], v1[CH];
             load_w(w0, v0, 0);
@@ -282,7 +317,9 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
 // e (packed rows p0..p0+ne) with hl the LDS h tile ([a.st][I / 4] float4).
 // FUSED (the one-launch layer's item): the first weight chunks go out, then
 // wait_h() runs (the wait for the expert's h), and h and y move through
-// device-coherent accesses; otherwise h is staged before the first chunks.
+// device-coherent accesses; otherwise the h loads go out first (in the
+// unrolled form all of them, followed by the first chunk's loads before h is
+// written to LDS).
 struct NoWait {
     __device__ void operator()() const {}
 };
@@ -356,15 +393,45 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
             }
         };
 
-        if constexpr (!FUSED) stage_h();
         if constexpr (NCH > 0) {
             uint4 w[3][CH];
             uint32_t v[3][CH];
-            load_w(w[0], v[0], 0);
-            if (NCH > 1) load_w(w[1], v[1], 1);
+            constexpr int I4C = NCH * CH * 64;       // float4 per h row (I4)
+            constexpr int HV = (ST * I4C + kThreads - 1) / kThreads;
             if constexpr (FUSED) {
+                load_w(w[0], v[0], 0);
+                if (NCH > 1) load_w(w[1], v[1], 1);
                 wait_h();
                 stage_h();
+            } else if constexpr (HV <= 2) {
+                // every h load goes out at once, then the first weight chunk;
+                // the LDS stores wait for the h loads only
+                moe::f32x4 hr[HV];                   // (native vectors stay in VGPRs)
+#pragma unroll
+                for (int i = 0; i < HV; ++i) {
+                    // past the pass's last float4 a lane reloads that one (never stored)
+                    const int f = min(tid + i * kThreads, nt * I4C - 1);
+                    const int j = f / I4C, r = f - j * I4C;
+                    hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                load_w(w[0], v[0], 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < HV; ++i) {
+                    const int f = tid + i * kThreads;
+                    if (f < nt * I4C) {
+                        const int j = f / I4C, r = f - j * I4C;
+                        const int sg = r >> 6, rr = r & 63;
+                        reinterpret_cast<moe::f32x4 *>(hl)[j * I4C + sg * 64 + (rr & 7) * 8 + (rr >> 3)] = hr[i];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (NCH > 1) load_w(w[1], v[1], 1);
+            } else {
+                stage_h();
+                load_w(w[0], v[0], 0);
+                if (NCH > 1) load_w(w[1], v[1], 1);
             }
             moe::lds_barrier();
 #pragma unroll
@@ -375,6 +442,7 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
+            if constexpr (!FUSED) stage_h();
             uint4 w0[CH], w1[CH];
             uint32_t v0[CH], v1[CH];
             load_w(w0, v0, 0);
@@ -457,7 +525,7 @@ __device__ __forceinline__ void thin_issue_nv(const FusedArgs &a, const FusedRou
 #pragma unroll
     for (int q = 0; q < (NJ + 1) / 2; ++q) {
         const int d = lane + 64 * q;
-        sd[q] = d < ndw ? __builtin_nontemporal_load(sp + d) : 0u;
+        sd[q] = d < ndw ? moe::load_nt_global<uint32_t>(sp + d) : 0u;
     }
 }
 

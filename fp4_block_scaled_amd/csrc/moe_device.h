@@ -13,6 +13,7 @@ constexpr int kWave = 64;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Sum over each aligned group of 8 lanes; every lane of the group ends with
@@ -38,6 +39,17 @@ __device__ __forceinline__ T *uniform_ptr(T *p)
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return (T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Non-temporal load of a T from global memory, emitted as a global (not a
+// flat) instruction even where the compiler cannot trace p back to a kernel
+// argument (e.g. a pointer made uniform through inline asm).  A flat load
+// also counts against the LDS wait counter, so every wait for an LDS read
+// would then wait for all the weight loads in flight as well.
+template <class T>
+__device__ __forceinline__ T load_nt_global(const void *p)
+{
+    return __builtin_nontemporal_load((const __attribute__((address_space(1))) T *)p);
 }
 
 // Wait until at most N of this wave's vector memory loads are in flight
