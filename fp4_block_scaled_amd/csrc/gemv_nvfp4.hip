@@ -175,6 +175,14 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     const uint8_t *cb0 = (is_up ? a.ucodes : a.gcodes) + row0 * rowb;
     const uint8_t *sb0 = (is_up ? a.uscales : a.gscales) + row0 * rows;
     const uint32_t coff = (uint32_t)grp * rowb + sub * 16, soff = (uint32_t)grp * rows + sub * 2;
+    // Unrolled form: the group scales of the wave's 8 rows (contiguous in
+    // memory) go to LDS with the x rows, in 16-byte loads, each row padded by
+    // 16 bytes so the rows of one read fall in different banks; the K loop
+    // then reads a lane's 2 scale bytes from LDS instead of issuing a 2-byte
+    // load per segment.
+    constexpr bool kScLds = NCH > 0;
+    const int srow = rows + 16;
+    uint8_t *scl = reinterpret_cast<uint8_t *>(xl) + (size_t)a.st * H * 2 + wave * 8 * srow;
 
     for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
         const int nt = min(a.st, ne - s0);
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
 #pragma unroll
             for (int sg = 0; sg < CH; ++sg) {
                 wb[sg] = load16(cbp + (c * CH + sg) * 128 + co);
-                sb[sg] = load2(sbp + (c * CH + sg) * 16 + so);
+                if constexpr (!kScLds) sb[sg] = load2(sbp + (c * CH + sg) * 16 + so);
             }
         };
         float acc[ST];
@@ -196,7 +204,12 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
 #pragma unroll
             for (int sg = 0; sg < CH; ++sg) {
                 const int seg = c * CH + sg;
-                const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)vc[sg], false);
+                uint32_t vs;
+                if constexpr (kScLds)
+                    vs = *reinterpret_cast<const uint16_t *>(scl + grp * srow + seg * 16 + sub * 2);
+                else
+                    vs = vc[sg];
+                const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)vs, false);
                 const uint4 wv = wc[sg];
 #pragma unroll
                 for (int j = 0; j < ST; ++j) {
@@ -219,6 +232,16 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
             constexpr int XV = (ST * H8C + kThreads - 1) / kThreads;
             uint4 w[3][CH];
             uint32_t v[3][CH];
+            // the wave's scale rows: 8 * H/16 bytes, 1 KB per wave-wide load
+            constexpr int SRB = NCH * CH * 16;       // scale bytes per row (H/16)
+            constexpr int SV = (8 * SRB + 1023) / 1024;
+            moe::u32x4 sr[SV];
+#pragma unroll
+            for (int i = 0; i < SV; ++i) {
+                // past the rows' last 16 bytes a lane reloads those (never stored)
+                const int o = min(lane * 16 + i * 1024, 8 * SRB - 16);
+                sr[i] = moe::load_nt_global<moe::u32x4>(sbp + o);
+            }
             if constexpr (XV <= 4) {
                 // x rows to LDS: every x load goes out at once, then the first
                 // weight chunk; the LDS stores wait for the x loads only
@@ -252,6 +275,14 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
                         *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
                 }
                 load_w(w[0], v[0], 0);
+            }
+#pragma unroll
+            for (int i = 0; i < SV; ++i) {
+                const int o = lane * 16 + i * 1024;
+                if (o < 8 * SRB) {
+                    const int r = o / SRB, cc = o - r * SRB;
+                    *reinterpret_cast<moe::u32x4 *>(scl + r * srow + cc) = sr[i];
+                }
             }
             if (NCH > 1) load_w(w[1], v[1], 1);
             moe::lds_barrier();
@@ -340,6 +371,12 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
     const size_t r0 = (size_t)e * H + row0 + wave * 8;
     const uint8_t *cb0 = a.codes + r0 * rowb, *sb0 = a.scales + r0 * rows;
     const uint32_t coff = (uint32_t)grp * rowb + sub * 16, soff = (uint32_t)grp * rows + sub * 2;
+    // Unrolled standalone form: the group scales of the wave's 8 rows go to
+    // LDS after the h rows (as in the gate/up kernel: 16-byte loads, rows
+    // padded by 16 bytes) and the K loop reads them from there.
+    constexpr bool kScLds = NCH > 0 && !FUSED;
+    const int srow = rows + 16;
+    uint8_t *scl = reinterpret_cast<uint8_t *>(hl) + (size_t)a.st * I * 4 + wave * 8 * srow;
 
     for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
         const int nt = min(a.st, ne - s0);
@@ -350,7 +387,7 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
 #pragma unroll
             for (int sg = 0; sg < CH; ++sg) {
                 wb[sg] = load16(cbp + (c * CH + sg) * 128 + co);
-                sb[sg] = load2(sbp + (c * CH + sg) * 16 + so);
+                if constexpr (!kScLds) sb[sg] = load2(sbp + (c * CH + sg) * 16 + so);
             }
         };
         float acc[ST];
@@ -360,7 +397,12 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
 #pragma unroll
             for (int sg = 0; sg < CH; ++sg) {
                 const int seg = c * CH + sg;
-                const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)vc[sg], false);
+                uint32_t vs;
+                if constexpr (kScLds)
+                    vs = *reinterpret_cast<const uint16_t *>(scl + grp * srow + seg * 16 + sub * 2);
+                else
+                    vs = vc[sg];
+                const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)vs, false);
                 const uint4 wv = wc[sg];
 #pragma unroll
                 for (int j = 0; j < ST; ++j) {
@@ -406,6 +448,15 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
             } else if constexpr (HV <= 2) {
                 // every h load goes out at once, then the first weight chunk;
                 // the LDS stores wait for the h loads only
+                constexpr int SRB = NCH * CH * 16;   // scale bytes per row (I/16)
+                constexpr int SV = (8 * SRB + 1023) / 1024;
+                moe::u32x4 sr[SV];
+#pragma unroll
+                for (int i = 0; i < SV; ++i) {
+                    // past the rows' last 16 bytes a lane reloads those (never stored)
+                    const int o = min(lane * 16 + i * 1024, 8 * SRB - 16);
+                    sr[i] = moe::load_nt_global<moe::u32x4>(sbp + o);
+                }
                 moe::f32x4 hr[HV];                   // (native vectors stay in VGPRs)
 #pragma unroll
                 for (int i = 0; i < HV; ++i) {
@@ -426,10 +477,24 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
                         reinterpret_cast<moe::f32x4 *>(hl)[j * I4C + sg * 64 + (rr & 7) * 8 + (rr >> 3)] = hr[i];
                     }
                 }
+#pragma unroll
+                for (int i = 0; i < SV; ++i) {
+                    const int o = lane * 16 + i * 1024;
+                    if (o < 8 * SRB) {
+                        const int r = o / SRB, cc = o - r * SRB;
+                        *reinterpret_cast<moe::u32x4 *>(scl + r * srow + cc) = sr[i];
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 if (NCH > 1) load_w(w[1], v[1], 1);
             } else {
+                // (larger passes: h in a loop; the scales still go to LDS)
                 stage_h();
+                for (int o = lane * 16; o < 8 * rows; o += 1024) {
+                    const int r = o / rows, cc = o - r * rows;
+                    *reinterpret_cast<moe::u32x4 *>(scl + r * srow + cc) =
+                        moe::load_nt_global<moe::u32x4>(sbp + o);
+                }
                 load_w(w[0], v[0], 0);
                 if (NCH > 1) load_w(w[1], v[1], 1);
             }
@@ -672,8 +737,10 @@ constexpr int kGUST = 8, kDNST = 8;
 template <int CH, int NCH, int ST, bool ROUTE>
 void gateup_launch(const GateUpArgs &a, int grid, hipStream_t st)
 {
+    // x rows of a pass, then (unrolled form) the scale rows of the 4 waves
+    const size_t lds = (size_t)a.st * a.H * 2 + (NCH > 0 ? 32 * (size_t)(a.H / 16 + 16) : 0);
     hipLaunchKernelGGL((gemv_gateup_nvfp4_kernel<CH, NCH, ST, ROUTE>), dim3(grid), dim3(kThreads),
-                       (size_t)a.st * a.H * 2, st, a);
+                       lds, st, a);
 }
 
 // Unrolled kernels for 4-segment chunks (hidden a multiple of 1024 up to
@@ -717,8 +784,9 @@ void gateup_dispatch(const GateUpArgs &a, int grid, hipStream_t st)
 template <int CH, int NCH, int ST>
 void down_launch(const DownArgs &a, int grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((gemv_down_nvfp4_kernel<CH, NCH, ST>), dim3(grid), dim3(kThreads),
-                       (size_t)a.st * a.I * 4, st, a);
+    // h rows of a pass, then (unrolled form) the scale rows of the 4 waves
+    const size_t lds = (size_t)a.st * a.I * 4 + (NCH > 0 ? 32 * (size_t)(a.I / 16 + 16) : 0);
+    hipLaunchKernelGGL((gemv_down_nvfp4_kernel<CH, NCH, ST>), dim3(grid), dim3(kThreads), lds, st, a);
 }
 
 // Unrolled kernels for 2-segment chunks (inter a multiple of 512 up to 4096)
