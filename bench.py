@@ -338,17 +338,17 @@ def cpu_baseline(wl, banks, x, sets, budget_s):
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC = {
     "decode_e4m3_m1": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
-        "src": "c2d2d8e62f45df32d610978b517a952c80b4a18ccd74a69d", "fetch_kib": 115067, "write_kib": 65},
+        "src": "addf2292c8a1ffccd610978b517a952c85576205248c54d3", "fetch_kib": 115074, "write_kib": 65},
     "decode_e4m3_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
-        "src": "c2d2d8e62f45df32d610978b517a952c80b4a18ccd74a69d", "fetch_kib": 173068, "write_kib": 1070},
+        "src": "addf2292c8a1ffccd610978b517a952c85576205248c54d3", "fetch_kib": 173074, "write_kib": 1070},
     "nvfp4_m1": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "80a699c1ab8c17d7d610978b517a952c80b4a18ccd74a69d", "fetch_kib": 43377, "write_kib": 49},
+        "src": "82e2e56bcbc03820d610978b517a952c85576205248c54d3", "fetch_kib": 41620, "write_kib": 49},
     "nvfp4_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "80a699c1ab8c17d7d610978b517a952c80b4a18ccd74a69d", "fetch_kib": 64863, "write_kib": 835},
+        "src": "82e2e56bcbc03820d610978b517a952c85576205248c54d3", "fetch_kib": 64885, "write_kib": 835},
     "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h"],
-        "src": "0a5215434968026b46ff9d1401442f7f80b4a18ccd74a69d", "fetch_kib": 4245047, "write_kib": 69876},
+        "src": "0a5215434968026b46ff9d1401442f7f85576205248c54d3", "fetch_kib": 4248660, "write_kib": 69837},
     "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
-        "src": "90d4f2b67c21b99a46ff9d1401442f7f80b4a18ccd74a69d", "fetch_kib": 2096609, "write_kib": 196608},
+        "src": "90d4f2b67c21b99a46ff9d1401442f7f85576205248c54d3", "fetch_kib": 1999770, "write_kib": 196608},
 }
 
 
