@@ -23,7 +23,7 @@
 //                       to E4M3 + scale in the epilogue.
 //   gemm_down_kernel    one block = 128 packed rows x 128 outputs of y.
 // Tiles: 4 waves as 2x2, 64x64 (x2 for gate/up) per wave; A and B move from
-// global memory straight into three swizzled LDS stages (see below).
+// global memory straight into a ring of swizzled LDS stages (see below).
 #include "gemm_common.h"
 
 namespace {
@@ -128,8 +128,8 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t *__restr
 // Block: 256 threads = 4 waves as 2 (rows) x 2 (columns).  Tiles move from
 // global memory straight into LDS (global_load_lds_dwordx4: lane i of one
 // instruction fills bytes 16i..16i+15 of a 1 KB run = 8 rows x 128 bytes),
-// three LDS stages deep, so two K steps of loads are always in flight without
-// holding any VGPRs.  Inside a stage a row's eight 16-byte chunks are stored
+// in a ring of LDS stages (three for gate/up: two K steps in flight; two for
+// down, whose two blocks per CU cover each other's waits), holding no VGPRs.  Inside a stage a row's eight 16-byte chunks are stored
 // XOR-swizzled (swz below), so the lanes that feed one MFMA operand half (16
 // rows, same K chunk) read without bank conflicts.  Each wave
 // loads the activation scales of its own 64 rows into its own 256-byte slot.
@@ -340,10 +340,14 @@ __global__ __launch_bounds__(kGuThreads, 1) void gemm_gateup_kernel(GemmArgs a)
 constexpr int DN_A = 0, DN_B = 128 * 128, DN_S = DN_B + 128 * 128, DN_STAGE = DN_S + 4 * 256;
 constexpr int DN_DMA = 4 + 4 + 1;
 
-constexpr int DN_NST = 3;           // LDS stages of the down GEMM (2 K steps in flight)
-static_assert(DN_NST * DN_STAGE <= 160 * 1024, "down stages exceed LDS");
+// LDS stages of the down GEMM: two (one K step in flight) in 66 KB, so two
+// blocks share a CU.  A down block runs only K/128 = 16 K steps; with one
+// block per CU the ramp of every block's first stages stood exposed, with two
+// one block's ramp runs under the other's MFMAs (1.61 -> 1.11 ms at M=4096).
+constexpr int DN_NST = 2;
+static_assert(2 * DN_NST * DN_STAGE <= 160 * 1024, "two down blocks exceed LDS");
 
-__global__ __launch_bounds__(kThreads, 1) void gemm_down_kernel(GemmArgs a)
+__global__ __launch_bounds__(kThreads, 2) void gemm_down_kernel(GemmArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint8_t sm[DN_NST * DN_STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
