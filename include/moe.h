@@ -136,8 +136,9 @@ typedef struct {
  * ascending slot order.
  *   expert_offsets [E+1]  exclusive prefix sum of per-expert slot counts;
  *                         expert_offsets[E] = number of valid slots
- *   sorted_slot    [S]    packed row -> slot          (first expert_offsets[E])
- *   sorted_token   [S]    packed row -> token
+ *   sorted_slot    [S]    packed row -> slot          (first expert_offsets[E]
+ *   sorted_token   [S]    packed row -> token          rows; the rest of both
+ *                         arrays holds unspecified values)
  *   token_to_perm  [S]    slot -> packed row, -1 for an invalid/unfilled id
  *   active_experts [min(E,S)]  ascending ids of experts with >= 1 slot,
  *                         then -1 up to min(E,S)

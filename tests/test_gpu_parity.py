@@ -60,7 +60,8 @@ def test_route_pack_bit_exact_on_workloads(name, route_set):
 
 
 @pytest.mark.parametrize("case", ["one_expert", "E1", "E2", "k_eq_E", "invalid", "all_invalid",
-                                  "dups", "max_experts", "ragged_chunks", "big"])
+                                  "dups", "max_experts", "ragged_chunks", "big", "split_ragged",
+                                  "split_max_experts"])
 def test_route_pack_bit_exact_adversarial(case):
     rng = np.random.default_rng(17)
     if case == "one_expert":
@@ -91,6 +92,19 @@ def test_route_pack_bit_exact_adversarial(case):
     elif case == "ragged_chunks":
         E = 37
         ids = rng.integers(0, E, (1025, 3)).astype(np.int32)
+    elif case == "split_ragged":
+        # large enough for the split pack (count / place / token launches),
+        # a ragged last group, and invalid ids of every kind
+        E = 100
+        ids = rng.integers(0, E, (2743, 3)).astype(np.int32)
+        flat = ids.ravel()
+        pos = rng.choice(flat.size, 300, replace=False)
+        flat[pos[:100]] = -1
+        flat[pos[100:200]] = E + rng.integers(0, 50, 100)
+        flat[pos[200:]] = -rng.integers(2, 1000, 100)
+    elif case == "split_max_experts":
+        E = B.MOE_MAX_EXPERTS
+        ids = np.stack([rng.choice(E, 8, replace=False) for _ in range(2100)]).astype(np.int32)
     else:
         E = 256
         bias = rng.normal(0, 0.5, E)
