@@ -346,9 +346,9 @@ TRAFFIC = {
     "nvfp4_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
         "src": "82e2e56bcbc03820d610978b517a952c85576205248c54d3", "fetch_kib": 64885, "write_kib": 835},
     "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h"],
-        "src": "0a5215434968026b46ff9d1401442f7f85576205248c54d3", "fetch_kib": 4248660, "write_kib": 69837},
+        "src": "605879b65f3835f546ff9d1401442f7f85576205248c54d3", "fetch_kib": 4247723, "write_kib": 69890},
     "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
-        "src": "90d4f2b67c21b99a46ff9d1401442f7f85576205248c54d3", "fetch_kib": 1999770, "write_kib": 196608},
+        "src": "90d4f2b67c21b99a46ff9d1401442f7f85576205248c54d3", "fetch_kib": 2063581, "write_kib": 196608},
 }
 
 
