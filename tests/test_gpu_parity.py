@@ -231,6 +231,22 @@ def test_layer_parity_many_slots_per_expert_gemv_nvfp4():
     run_and_check(case, ids, w, mode=B.MOE_MODE_GEMV_A16, label="crowded nvfp4")
 
 
+@pytest.mark.parametrize("name", ["decode_e4m3_m1", "nvfp4_m1"])
+def test_layer_parity_full_shape_repeated_expert(name):
+    """One token whose top-k repeats experts, at the full decode shape: the
+    repeated expert holds two or three slots, so the unrolled GEMV kernels
+    (one slot per pass at this hidden size) run several passes over its
+    weights, restaging x, h and the group scales each pass."""
+    wl = workloads.WORKLOADS[name]
+    case = get_case(wl)
+    ids, w, _ = workloads.make_routes(wl, 0)
+    ids[0, 3] = ids[0, 1]
+    ids[0, 6] = ids[0, 1]
+    ids[0, 7] = ids[0, 2]
+    print(f"layer parity repeated experts {name}", flush=True)
+    run_and_check(case, ids, w, label=f"{name} repeated experts")
+
+
 def test_invalid_and_unfilled_ids_contribute_zero():
     wl = workloads.with_shape(workloads.WORKLOADS["tiny_e4m3_m1"], name="e4m3_invalid", M=6)
     case = get_case(wl)
