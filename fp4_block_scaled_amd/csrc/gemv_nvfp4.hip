@@ -445,9 +445,10 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
                 if (NCH > 1) load_w(w[1], v[1], 1);
                 wait_h();
                 stage_h();
-            } else if constexpr (HV <= 2) {
+            } else if constexpr (HV <= 4) {
                 // every h load goes out at once, then the first weight chunk;
-                // the LDS stores wait for the h loads only
+                // the LDS stores wait for the h loads only (up to 4 per thread:
+                // the two-slot passes of a 16-token layer too)
                 constexpr int SRB = NCH * CH * 16;   // scale bytes per row (I/16)
                 constexpr int SV = (8 * SRB + 1023) / 1024;
                 moe::u32x4 sr[SV];

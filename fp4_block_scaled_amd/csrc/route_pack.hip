@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void route_count_kernel(
     const int sh = 6 + lg;                           // run of slot s: s >> sh
     int bad = 0;
     for (int s0 = 0; s0 < S; s0 += kThreads * kGroups) {
-        int idr[kGroups];                            // all loads of a round in flight together
+        int idr[kGroups];                            // all loads of a pass in flight together
 #pragma unroll
         for (int i = 0; i < kGroups; ++i) {
             const int s = s0 + i * kThreads + tid;
