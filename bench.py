@@ -342,9 +342,9 @@ TRAFFIC = {
     "decode_e4m3_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
         "src": "addf2292c8a1ffccd610978b517a952c85576205248c54d3", "fetch_kib": 173074, "write_kib": 1070},
     "nvfp4_m1": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "82e2e56bcbc03820d610978b517a952c85576205248c54d3", "fetch_kib": 41620, "write_kib": 49},
+        "src": "cd6fb700362c8c12d610978b517a952c85576205248c54d3", "fetch_kib": 41620, "write_kib": 49},
     "nvfp4_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "82e2e56bcbc03820d610978b517a952c85576205248c54d3", "fetch_kib": 64885, "write_kib": 835},
+        "src": "cd6fb700362c8c12d610978b517a952c85576205248c54d3", "fetch_kib": 64892, "write_kib": 835},
     "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h"],
         "src": "605879b65f3835f546ff9d1401442f7f85576205248c54d3", "fetch_kib": 4247723, "write_kib": 69890},
     "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
