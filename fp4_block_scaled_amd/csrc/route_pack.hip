@@ -62,7 +62,7 @@ __device__ __forceinline__ uint64_t expert_peers(bool valid, int e, int nbits)
 // Whole 64-slot groups [g0, g1) of run w of R (R runs over S slots).
 __device__ __forceinline__ void wave_run(int S, int R, int w, int &g0, int &g1)
 {
-    const int ngroups = (S + 63) / 64;
+    const int ngroups = (S - 1) / 64 + 1;          // (S >= 1; no overflow near 2^31)
     const int gpw = (ngroups + R - 1) / R;
     g0 = w * gpw;
     g1 = min(ngroups, g0 + gpw);
@@ -71,7 +71,7 @@ __device__ __forceinline__ void wave_run(int S, int R, int w, int &g0, int &g1)
 // Runs of a split pack: 2^lg groups each, so a slot's run is s >> (6 + lg).
 __device__ __forceinline__ void split_run(int S, int lg, int w, int &g0, int &g1)
 {
-    const int ngroups = (S + 63) / 64;
+    const int ngroups = (S - 1) / 64 + 1;
     g0 = w << lg;
     g1 = min(ngroups, g0 + (1 << lg));
 }
@@ -83,7 +83,7 @@ __device__ __forceinline__ void load_ids(const int32_t *ids, int S, int c0, int 
 {
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
-        const int s = (c0 + g) * 64 + lane;
+        const int64_t s = (int64_t)(c0 + g) * 64 + lane;
         idr[g] = (c0 + g < g1 && s < S) ? ids[s] : -1;
     }
 }
@@ -104,7 +104,8 @@ __device__ __forceinline__ void place_run(const int32_t *ids, int S, int k, int 
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
             if (c0 + g >= g1) break;                 // (wave-uniform)
-            const int s = (c0 + g) * 64 + lane;
+            const int64_t s64 = (int64_t)(c0 + g) * 64 + lane;
+            const int s = (int)(s64 < S ? s64 : S);  // a slot index when s64 < S
             const int e = idr[g];
             const bool valid = e >= 0 && e < E;
             const uint64_t peers = expert_peers(valid, e, nbits);
@@ -227,16 +228,17 @@ __global__ __launch_bounds__(kThreads) void route_count_kernel(
 
     const int sh = 6 + lg;                           // run of slot s: s >> sh
     int bad = 0;
-    for (int s0 = 0; s0 < S; s0 += kThreads * kGroups) {
+    for (int64_t s0 = 0; s0 < S; s0 += kThreads * kGroups) {
         int idr[kGroups];                            // all loads of a pass in flight together
 #pragma unroll
         for (int i = 0; i < kGroups; ++i) {
-            const int s = s0 + i * kThreads + tid;
+            const int64_t s = s0 + i * kThreads + tid;
             idr[i] = s < S ? ids[s] : -1;
         }
 #pragma unroll
         for (int i = 0; i < kGroups; ++i) {
-            const int s = s0 + i * kThreads + tid, e = idr[i];
+            const int64_t s = s0 + i * kThreads + tid;
+            const int e = idr[i];
             if (e >= 0 && e < E) atomicAdd(&cnt[(s >> sh) * E + e], 1);
             else if (e != -1) ++bad;
         }
@@ -384,7 +386,7 @@ hipError_t launch_route_pack(const int32_t *ids, int32_t M, int32_t k, int32_t E
     // counters ([R][E] ints in 64 KB) and the stash (sorted_token: R*E <= S)
     // allow, and at most 64 runs.
     if (S >= kSplitMin) {
-        const int ngroups = (S + 63) / 64;
+        const int ngroups = (S - 1) / 64 + 1;
         auto runs = [&](int l) { return (ngroups + (1 << l) - 1) >> l; };
         auto fits = [&](int R) {
             return R <= kMaxRuns && (size_t)R * E * 4 <= kCountLds && (int64_t)R * E <= S;
@@ -398,7 +400,7 @@ hipError_t launch_route_pack(const int32_t *ids, int32_t M, int32_t k, int32_t E
                                r.active, r.num_active, r.status, r.sorted_token);
             hipLaunchKernelGGL(route_place_kernel, dim3(R), dim3(64), sizeof(int32_t) * (size_t)E, st,
                                ids, S, k, E, nbits, lg, r.sorted_token, r.sorted_slot, r.token_to_perm);
-            hipLaunchKernelGGL(route_token_kernel, dim3((unsigned)((S + 255) / 256)), dim3(256), 0, st,
+            hipLaunchKernelGGL(route_token_kernel, dim3((unsigned)(((int64_t)S + 255) / 256)), dim3(256), 0, st,
                                r.sorted_slot, r.offsets, E, k, r.sorted_token);
             return hipGetLastError();
         }
