@@ -355,6 +355,10 @@ TRAFFIC = {
         "src": "605879b65f3835f546ff9d1401442f7f85576205248c54d3", "fetch_kib": 4247723, "write_kib": 69890},
     "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
         "src": "90d4f2b67c21b99a46ff9d1401442f7f85576205248c54d3", "fetch_kib": 2063581, "write_kib": 196608},
+    "verify_e4m3_m8": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
+        "src": "addf2292c8a1ffccd610978b517a952c85576205248c54d3", "fetch_kib": 702115, "write_kib": 514},
+    "nvfp4_m16": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
+        "src": "cd6fb700362c8c12d610978b517a952c85576205248c54d3", "fetch_kib": 495034, "write_kib": 768},
 }
 
 
