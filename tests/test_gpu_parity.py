@@ -61,7 +61,7 @@ def test_route_pack_bit_exact_on_workloads(name, route_set):
 
 @pytest.mark.parametrize("case", ["one_expert", "E1", "E2", "k_eq_E", "invalid", "all_invalid",
                                   "dups", "max_experts", "ragged_chunks", "big", "split_ragged",
-                                  "split_max_experts"])
+                                  "split_max_experts", "split_threshold", "below_split"])
 def test_route_pack_bit_exact_adversarial(case):
     rng = np.random.default_rng(17)
     if case == "one_expert":
@@ -105,6 +105,14 @@ def test_route_pack_bit_exact_adversarial(case):
     elif case == "split_max_experts":
         E = B.MOE_MAX_EXPERTS
         ids = np.stack([rng.choice(E, 8, replace=False) for _ in range(2100)]).astype(np.int32)
+    elif case == "split_threshold":
+        # the smallest split pack: 8192 slots, 16 runs of 512 experts' counters
+        E = B.MOE_MAX_EXPERTS
+        ids = np.stack([rng.choice(E, 8, replace=False) for _ in range(1024)]).astype(np.int32)
+    elif case == "below_split":
+        # one slot short of the split: the one-workgroup pack with a ragged last group
+        E = 77
+        ids = rng.integers(-1, E, (8191, 1)).astype(np.int32)
     else:
         E = 256
         bias = rng.normal(0, 0.5, E)
