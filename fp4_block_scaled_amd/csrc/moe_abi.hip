@@ -358,7 +358,7 @@ static moe_status_t expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, con
         stage_mark(0, s);
         e = launch_quant_act(x_bf16, M, hidden, gs.xq, gs.xs, s);
         if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: activation quantization launch");
-        e = launch_gemm_tiles(r.offsets, E, tmax, gs.tiles, gs.ntiles, s);
+        e = launch_gemm_tiles(r.offsets, E, tmax, gs.tiles, gs.ntiles, s, true);
         if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: tile schedule launch");
         stage_mark(1, s);
         e = launch_gemm_gateup(gs.xq, gs.xs, r.sorted_token, gate->codes, (const float *)gate->scales,
@@ -380,7 +380,7 @@ static moe_status_t expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, con
         GemmA16Scratch gs = carve_gemm_a16(scratch, S, E, inter);
         const int32_t tmax = gemm_max_tiles((int32_t)S, E);
         stage_mark(0, s);
-        e = launch_gemm_tiles(r.offsets, E, tmax, gs.tiles, gs.ntiles, s);
+        e = launch_gemm_tiles(r.offsets, E, tmax, gs.tiles, gs.ntiles, s, false);
         if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: tile schedule launch");
         stage_mark(1, s);
         e = launch_gemm_gateup_nvfp4(x_bf16, r.sorted_token, bg, bu, r.offsets, gs.tiles, gs.ntiles,

@@ -52,6 +52,14 @@ __device__ __forceinline__ T load_nt_global(const void *p)
     return __builtin_nontemporal_load((const __attribute__((address_space(1))) T *)p);
 }
 
+// Ordinary (cached) load of a T from global memory, emitted as a global
+// instruction for the same reason.
+template <class T>
+__device__ __forceinline__ T load_global(const void *p)
+{
+    return *(const __attribute__((address_space(1))) T *)p;
+}
+
 // Wait until at most N of this wave's vector memory loads are in flight
 // (vmcnt(N); expcnt and lgkmcnt not waited).
 template <int N>

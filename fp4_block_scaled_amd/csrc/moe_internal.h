@@ -102,8 +102,10 @@ hipError_t launch_gemv_down_nvfp4(const GemvBankDev &down, const float *h, const
 int gemm_max_tiles(int32_t S, int32_t E);
 hipError_t launch_quant_act(const uint16_t *x, int32_t M, int32_t hidden, uint8_t *xq, float *xs,
                             hipStream_t st);
+// Row tiles per expert: balanced chunks of at most 128 rows (E4M3 tier),
+// or runs of exactly 128 rows but the last (NVFP4 tier).
 hipError_t launch_gemm_tiles(const int32_t *offsets, int32_t E, int32_t tmax, int4 *tiles,
-                             int32_t *ntiles, hipStream_t st);
+                             int32_t *ntiles, hipStream_t st, bool balanced);
 hipError_t launch_gemm_gateup(const uint8_t *xq, const float *xs, const int32_t *sorted_token,
                               const uint8_t *gcodes, const float *gscales, const uint8_t *ucodes,
                               const float *uscales, const int32_t *offsets, const int4 *tiles,

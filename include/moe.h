@@ -159,8 +159,12 @@ typedef struct {
 } moe_route_t;
 
 /* Bytes of device workspace one layer call sequence needs for any M <= max_M
- * (route tables first, then the FFN's scratch).  0 if the sizes break a rule
- * of moe_route_pack / moe_expert_ffn.  Needs no GPU. */
+ * (route tables first, then the FFN's scratch), so a caller sizes and
+ * allocates it once, before any call, without a GPU ("spark_model
+ * glm5next_mlp/forward.rs", fns mlp_ws_bytes / mlp_ws_total_bytes: the MLP
+ * workspace computed from the config and the largest row count, split out of
+ * the constructor so it can be checked with no device).  0 if the sizes
+ * break a rule of moe_route_pack / moe_expert_ffn.  Needs no GPU. */
 size_t moe_workspace_bytes(int32_t max_M, int32_t top_k, int32_t num_experts,
                            int32_t hidden, int32_t inter, int32_t fmt,
                            int32_t mode);
@@ -197,8 +201,14 @@ moe_status_t moe_router_topk(const float *logits, int32_t M, int32_t num_experts
                              int32_t renormalize, int32_t *topk_ids, float *topk_weights,
                              void *stream);
 
-/* The tier moe_expert_ffn runs for `requested` at M tokens (AUTO resolves by
- * M).  Needs no GPU. */
+/* The tier moe_expert_ffn runs for `requested` at M tokens: a non-AUTO
+ * request is returned as is; AUTO gives MOE_MODE_GEMV_A16 for M <=
+ * MOE_GEMV_MAX_M, else MOE_MODE_GEMM_A8 for E4M3 banks and MOE_MODE_GEMM_A16
+ * for NVFP4 banks.  A caller can ask which kernel family a row count takes
+ * before it runs ("spark_model glm5next_mlp/forward.rs", fn gemm: one token
+ * to the GEMV, a few rows to one weight read for all rows, wider shapes to
+ * the tile GEMM; fn forward_moe and its announce_* helpers, which report
+ * which routed-expert arm a row count took).  Needs no GPU. */
 int32_t moe_resolve_mode(int32_t M, int32_t fmt, int32_t requested);
 
 /* Route pack: stable counting sort of the M*top_k slots of topk_ids
@@ -211,7 +221,11 @@ moe_status_t moe_route_pack(const int32_t *topk_ids, int32_t M, int32_t top_k,
                             int32_t num_experts, void *ws, size_t ws_bytes,
                             moe_route_t *route, void *stream);
 
-/* Expert FFN: for every valid slot, in packed order,
+/* Expert FFN ("memra-engine src/dsv4_ep.rs", fn chain: per routed slot the
+ * gate and up projections, the clamped SwiGLU, then the down projection into
+ * an FP32 row; "spark_model glm5next_mlp/forward.rs", fn forward_moe: the
+ * routed sweep over expert-sorted rows).  For every valid slot, in packed
+ * order,
  *   y_packed[row] = Wd[e] (silu(min(Wg[e] x[t], L)) * clamp(Wu[e] x[t], -L, L))
  * x_bf16: bf16 [M][hidden]; y_packed: float [M*top_k][hidden], rows past
  * expert_offsets[E] are left untouched.  `route` (host) must come from
@@ -343,7 +357,12 @@ moe_status_t moe_combine_residual(const float *y_packed, const moe_route_t *rout
 int32_t moe_set_stage_events(void *const *events, int32_t n_events, int32_t fmt,
                              int32_t hidden, int32_t inter, int32_t mode);
 
-/* Message for the last non-OK status returned on this thread. */
+/* Message for the last non-OK status returned on this thread: the call and
+ * the check that failed, or HIP's message for a failed launch.  Every
+ * non-OK status says which step failed and why, as the labelled launch
+ * checks of "memra-engine src/dsv4_ep.rs" do (fn chain: each kernel call
+ * wrapped with its stage name, e.g. "EP w1/w3").  Thread-local; the pointer
+ * stays valid until the next failing call on the same thread. */
 const char *moe_last_error(void);
 
 #ifdef __cplusplus

@@ -191,15 +191,24 @@ def get_case(name_or_wl):
     return _cache[key]
 
 
-@pytest.mark.parametrize("name", ["tiny_e4m3_m1", "decode_e4m3_m1", "verify_e4m3_m8",
-                                  "nvfp4_m1", "nvfp4_m16"])
-def test_layer_parity_gemv_tier_full_workloads(name):
+# Every route set of the tiny, verify and NVFP4 workloads (different expert
+# overlap and duplication patterns per set), the first four of decode M=1.
+GEMV_ROUTE_SETS = ([("tiny_e4m3_m1", r) for r in range(16)] +
+                   [("decode_e4m3_m1", r) for r in range(4)] +
+                   [("verify_e4m3_m8", r) for r in range(16)] +
+                   [("nvfp4_m1", r) for r in range(16)] +
+                   [("nvfp4_m16", r) for r in range(16)])
+
+
+@pytest.mark.parametrize("name,route_set", GEMV_ROUTE_SETS,
+                         ids=[f"{n}-set{r}" for n, r in GEMV_ROUTE_SETS])
+def test_layer_parity_gemv_tier_full_workloads(name, route_set):
     wl = workloads.WORKLOADS[name]
-    print(f"layer parity {name}", flush=True)
+    print(f"layer parity {name} route set {route_set}", flush=True)
     case = get_case(wl)
-    ids, w, info = workloads.make_routes(wl, 0)
-    r = run_and_check(case, ids, w, label=name)
-    print(f"  {name}: max err frac {r[0]:.2e}, rel L2 {r[1]:.2e}, routes {info}", flush=True)
+    ids, w, info = workloads.make_routes(wl, route_set)
+    r = run_and_check(case, ids, w, label=f"{name} set {route_set}")
+    print(f"  {name} set {route_set}: max err frac {r[0]:.2e}, rel L2 {r[1]:.2e}, routes {info}", flush=True)
 
 
 REDUCED = [

@@ -49,17 +49,20 @@ def invariants(got, ids, E):
         assert off[e] <= pos < off[e + 1]
 
 
-def grouped_selected_routes(tokens, experts, k=8):
-    stride = experts // k
-    return np.array([[(j * stride + t) % experts for j in range(k)] for t in range(tokens)], np.int32)
-
-
-def dynamic_grouped_selected_routes(tokens, experts, ranks):
-    owner = {2: [0, 0, 0, 0, 1, 1, 1, 1], 4: [0, 1, 1, 2, 2, 2, 3, 3],
-             8: [0, 1, 2, 3, 4, 5, 6, 7]}[ranks]
+def owner_spread_routes(tokens, experts, slots_per_rank, token_step, slot_step, offset):
+    """Routes of the page's dynamic owner fixture ("memra-engine 0.108.0 --
+    src/bin/ep_step_fp8_gate.rs", benchmark_tests, fn
+    dynamic_grouped_selected_routes), built from its description: the experts
+    split into len(slots_per_rank) equal contiguous ranges, the top-k slots
+    handed to the ranges in order, slots_per_rank[r] of them to range r, and
+    slot j of token t taking the expert at local index
+    (token_step*t + slot_step*j + offset) mod the range size."""
+    ranks = len(slots_per_rank)
     per = experts // ranks
-    return np.array([[owner[j] * per + (t * 11 + j * 7 + 1) % per for j in range(8)]
-                     for t in range(tokens)], np.int32)
+    rank_of_slot = np.repeat(np.arange(ranks), slots_per_rank)
+    t = np.arange(tokens)[:, None]
+    j = np.arange(rank_of_slot.size)[None, :]
+    return (rank_of_slot[None, :] * per + (token_step * t + slot_step * j + offset) % per).astype(np.int32)
 
 
 def _golden():
@@ -73,14 +76,15 @@ def _golden():
 
 def test_page_route_fixtures_and_their_packs():
     g = _golden()
-    r = grouped_selected_routes(2, 288)
-    assert list(r[0]) == g["grouped_2_288_token0"]
-    assert list(r[1]) == g["grouped_2_288_token1"]
+    # the page prints both rows of its two-token fixture: they are the input
+    r = np.array([g["grouped_2_288_token0"], g["grouped_2_288_token1"]], np.int32)
     got = oracle.route_pack(r, 288)
     check_same(got, brute_pack(r, 288))
     # expert j*36 holds slot j (token 0) and expert j*36+1 holds slot 8+j
     assert list(got["active_experts"]) == sorted(g["grouped_2_288_token0"] + g["grouped_2_288_token1"])
-    d = dynamic_grouped_selected_routes(3, 288, 4)
+    # four ranks of 72 experts; slots 0 | 1-2 | 3-5 | 6-7 per rank
+    d = owner_spread_routes(3, 288, [1, 2, 3, 2], token_step=11, slot_step=7, offset=1)
+    assert all(len(set(row)) == 8 for row in d.tolist())     # no duplicate route in a token
     counts = np.bincount(d.ravel() // 72, minlength=4)
     assert list(counts) == g["dynamic_3_288_4_owner_counts"]
     got = oracle.route_pack(d, 288)
