@@ -35,12 +35,14 @@ MOE_ROUTER_SOFTMAX = 0
 MOE_ROUTER_SIGMOID = 1
 
 MOE_GEMV_MAX_M = 16
+MOE_STATIC_SCRATCH_BYTES = 8 << 20
 MOE_MAX_EXPERTS = 512
 MOE_MAX_DIM = 16384
 MOE_FUSED_MAX_SLOTS = 256
 
 EXPORTS = ("moe_workspace_bytes", "moe_resolve_mode", "moe_router_topk", "moe_route_pack",
-           "moe_expert_ffn", "moe_layer", "moe_layer_fused", "moe_combine", "moe_shared_workspace_bytes",
+           "moe_expert_ffn", "moe_layer", "moe_layer_static", "moe_layer_fused", "moe_combine",
+           "moe_shared_workspace_bytes",
            "moe_shared_expert", "moe_combine_residual", "moe_set_stage_events", "moe_last_error")
 
 
@@ -87,6 +89,10 @@ def _load():
     L.moe_layer.argtypes = [C.POINTER(moe_bank_t)] * 3 + [P, P, P, i32, i32, i32, i32, C.c_float,
                                                          i32, P, P, P, sz, C.POINTER(moe_route_t), P]
     L.moe_layer.restype = i32
+    L.moe_layer_static.argtypes = [C.POINTER(moe_bank_t)] * 3 + [P, P, P, i32, i32, i32, i32,
+                                                                C.c_float, i32, P, P,
+                                                                C.POINTER(moe_route_t), P]
+    L.moe_layer_static.restype = i32
     L.moe_combine.argtypes = [P, C.POINTER(moe_route_t), P, i32, P, P]
     L.moe_combine.restype = i32
     L.moe_combine_residual.argtypes = [P, C.POINTER(moe_route_t), P, P, P, i32, P, P]
@@ -183,6 +189,16 @@ def moe_layer(gate: Bank, up: Bank, down: Bank, x_bf16, topk_ids, topk_weights, 
                          _ptr(topk_ids), _ptr(topk_weights), M, top_k, hidden, inter, float(limit),
                          mode, _ptr(y_packed), _ptr(out), _ptr(ws), nbytes, C.byref(route),
                          _stream(stream)))
+    return route
+
+
+def moe_layer_static(gate: Bank, up: Bank, down: Bank, x_bf16, topk_ids, topk_weights, M, top_k,
+                     hidden, inter, limit, mode, y_packed, out, stream=None) -> moe_route_t:
+    route = moe_route_t()
+    _check(lib.moe_layer_static(C.byref(gate.c), C.byref(up.c), C.byref(down.c), _ptr(x_bf16),
+                                _ptr(topk_ids), _ptr(topk_weights), M, top_k, hidden, inter,
+                                float(limit), mode, _ptr(y_packed), _ptr(out), C.byref(route),
+                                _stream(stream)))
     return route
 
 

@@ -9,10 +9,17 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
+
+// The workspace of moe_layer_static: one array per GPU the library runs on,
+// held until the process ends.  Host code never uses its name as an address
+// (on the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -456,6 +463,57 @@ moe_status_t moe_layer(const moe_bank_t *gate, const moe_bank_t *up, const moe_b
     }
     if (st != MOE_OK) return st;
     return moe_combine(y_packed, route, topk_weights, hidden, out, stream);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+static moe_status_t static_scratch(const char *fn, void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_static: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: device %d past the %d the static scratch serves", fn,
+                    dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "moe_layer_static: hipGetSymbolAddress(scratch)");
+        if (!p || ((uintptr_t)p & 255) != 0)
+            return fail(MOE_ERR_HIP, "%s: static scratch at %p is not 256-byte aligned", fn, p);
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_static(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
+                              const uint16_t *x_bf16, const int32_t *topk_ids,
+                              const float *topk_weights, int32_t M, int32_t top_k, int32_t hidden,
+                              int32_t inter, float limit, int32_t mode, float *y_packed, float *out,
+                              moe_route_t *route, void *stream)
+{
+    static const char *fn = "moe_layer_static";
+    if (!gate || !up || !down || !route) return fail(MOE_ERR_ARG, "%s: null pointer", fn);
+    if (!valid_mode(mode) || mode == MOE_MODE_FUSED)
+        return fail(MOE_ERR_ARG, "%s: unknown mode %d", fn, mode);
+    const int32_t fmt = gate->fmt, E = gate->num_experts;
+    const size_t need = moe_workspace_bytes(M, top_k, E, hidden, inter, fmt, resolve(M, fmt, mode));
+    if (need > MOE_STATIC_SCRATCH_BYTES)
+        return fail(MOE_ERR_WORKSPACE,
+                    "%s: the layer needs %zu bytes of scratch, more than the static %u; "
+                    "call moe_layer with a workspace of your own", fn, need,
+                    (unsigned)MOE_STATIC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    moe_status_t st = static_scratch(fn, &ws);
+    if (st != MOE_OK) return st;
+    // moe_layer checks everything else (a zero `need` included) before any launch
+    return moe_layer(gate, up, down, x_bf16, topk_ids, topk_weights, M, top_k, hidden, inter,
+                     limit, mode, y_packed, out, ws, MOE_STATIC_SCRATCH_BYTES, route, stream);
 }
 
 moe_status_t moe_layer_fused(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,

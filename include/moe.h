@@ -272,6 +272,33 @@ moe_status_t moe_layer(const moe_bank_t *gate, const moe_bank_t *up, const moe_b
                        int32_t mode, float *y_packed, float *out, void *ws, size_t ws_bytes,
                        moe_route_t *route, void *stream);
 
+/* Bytes of the library's static scratch for moe_layer_static, per GPU. */
+#define MOE_STATIC_SCRATCH_BYTES (8u << 20)
+
+/* moe_layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call, kernels and outputs (route tables in *route, y_packed, out) as
+ * moe_layer, bit for bit, but the workspace is the library's own static
+ * device array of MOE_STATIC_SCRATCH_BYTES on the current device
+ * (hipGetDevice; `stream` must belong to it) instead of a caller buffer.
+ * The caller still passes inputs and outputs.  *route points into that
+ * array and stays valid until the next moe_layer_static call on the same
+ * GPU.  Nothing in the array needs clearing: every call writes the route
+ * tables and all the scratch it then reads.  The array is shared by every
+ * call on one GPU and keeps the last call's contents, so calls that overlap
+ * on one GPU (other streams, other threads) race; order them on one stream.
+ * Rules: those of moe_layer; a layer whose workspace
+ * (moe_workspace_bytes(M, top_k, E, hidden, inter, fmt, mode)) exceeds
+ * MOE_STATIC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE and launches nothing
+ * (at decode shapes it needs about 1 MB at M = 16).  Allocates nothing and
+ * calls no allocating routine; the array's device address is looked up once
+ * per device (hipGetSymbolAddress) on the first call there. */
+moe_status_t moe_layer_static(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
+                              const uint16_t *x_bf16, const int32_t *topk_ids,
+                              const float *topk_weights, int32_t M, int32_t top_k, int32_t hidden,
+                              int32_t inter, float limit, int32_t mode, float *y_packed, float *out,
+                              moe_route_t *route, void *stream);
+
 /* Fused decode layer: moe_route_pack, moe_expert_ffn on the GEMV tier and
  * moe_combine as ONE kernel launch of resident blocks ("spark_model
  * glm5next_mlp/forward.rs", doc of forward_moe: the per-row MoE path without
