@@ -24,13 +24,19 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
+# Per-source extra flags.  The grouped GEMMs keep MFMA results in VGPRs: the
+# promotion FMAs read every product, and results left in AGPRs cost an
+# accvgpr read each.
+EXTRA = {"gemm_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass warns that it does not know the packed-fp32 feature
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l

@@ -13,12 +13,13 @@
 //                       (scale = amax/448, code = RNE(x/scale) saturated).
 //   gemm_tiles_kernel   per-expert row chunks over the expert-sorted rows,
 //                       built on the device from expert_offsets.
-//   gemm_gateup_kernel  one block = one chunk of <= 128 rows of one expert x
-//                       128 h columns: the gate AND the up projection of
-//                       those columns, the clamped SwiGLU, and the E4M3
-//                       quantization of the 128-wide h row segment (exactly
-//                       one 1x128 group) in the epilogue.
-//   gemm_down_kernel    one block = one chunk x 128 outputs of y.
+//   gemm_gateup8_kernel one block (8 waves) = one chunk of <= 128 rows of
+//                       one expert x 128 h columns: the gate AND the up
+//                       projection of those columns, the clamped SwiGLU, and
+//                       the E4M3 quantization of the 128-wide h row segment
+//                       (exactly one 1x128 group) in the epilogue.
+//   gemm_down_kernel    persistent: a block per CU runs a fixed list of
+//                       (chunk, 128 outputs of y) items as one pipeline.
 //
 // Matrix-core precision.  gfx950's FP8 MFMA sums its products in groups of
 // eight, each group in a fixed-point window about 13 bits below the group's
@@ -33,18 +34,22 @@
 // down keeps the FP8 MFMA (one v_mfma_f32_16x16x128_f8f6f4 per 128-wide K
 // block), whose error stays far inside the output tolerance.
 //
-// Data movement.  Weights are read once per chunk straight from global
-// memory into VGPRs, in exactly the lane layout of the MFMA operand (lane l:
-// row l % 16, 32 bytes of K), several K steps ahead; they never touch LDS.
-// The activation rows of the chunk, shared by every wave, go to LDS (XOR
-// swizzled, two stages) through VGPRs.  All loads are ordinary compiler-
-// visible loads, so the compiler's waits are exact.
+// Data movement.  Gate/up: weights are read once per chunk straight from
+// global memory into VGPRs, in exactly the lane layout of the MFMA operand
+// (lane l: row l % 16, 32 bytes of K), several K steps ahead; they never
+// touch LDS.  The activation rows of the chunk, shared by every wave, go to
+// LDS (XOR swizzled, two stages) through VGPRs.  All its loads are ordinary
+// compiler-visible loads, so the compiler's waits are exact.  Down: both
+// operands go from global memory straight into LDS stages (DMA), with
+// explicit waits.
 //
 // K order inside a 128-wide block: a lane's 32 bytes are K offsets
 // 16q..16q+15 and 64+16q..64+16q+15 (q = lane / 16), so each half is one
 // 16-byte load of a row; A and B use the same order, and a dot product over
 // the block does not depend on the order of its terms.
 #include "gemm_common.h"
+
+#include <algorithm>
 
 namespace {
 
@@ -192,23 +197,17 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 // ---------------------------------------------------------------------------
 // activation rows of a chunk in LDS
 // ---------------------------------------------------------------------------
-// A chunk's activation rows for one K step of 128 move global -> VGPRs ->
-// LDS.  RB = bytes of one row's K step: 256 for gate/up (bf16 values of the
-// x codes), 128 for down (E4M3 h codes).  A row is RB/16 16-byte chunks;
-// thread t moves chunk t % C of rows G*j + t / C (C = RB/16, G = 256/C row
-// groups per pass), j = 0..NJ-1, and thread t the activation scale of row
-// t % RMAX.  Rows past the chunk's read its first row: their products land
-// in output rows that are never stored.
+// A stage holds a chunk's activation rows for one K step of 128 as bf16
+// values (256 bytes a row: 16 chunks of 16 bytes, XOR swizzled), then the
+// two promotion factors of each row.  Rows past the chunk's hold its first
+// row: their products land in output rows that are never stored.
 template <int RB>
 struct AStage {
     static constexpr int C = RB / 16;                 // 16-byte chunks per row
-    static constexpr int G = kThreads / C;            // rows per pass
-    static constexpr int S_OFF = RMAX * RB;           // scales after the rows
-    static constexpr int BYTES = S_OFF + RMAX * 4;
+    static constexpr int S_OFF = RMAX * RB;           // factors after the rows
     // physical chunk of logical chunk c in row r: an XOR with the row's low
     // bits, so the 16 rows an operand read touches at one logical chunk land
-    // on distinct chunks (distinct banks), and so do the chunks of one row
-    // written by consecutive threads
+    // on distinct chunks (distinct banks)
     static __device__ __forceinline__ int swz(int r, int c)
     {
         if constexpr (C == 16) return c ^ (r & 15);
@@ -216,81 +215,9 @@ struct AStage {
     }
 };
 
-template <int RB, int NJ>
-struct ARegs {
-    u32x4 v[NJ];
-    float s;
-};
-
-// Per-thread sources: byte offsets at K step 0 of its row chunks and of its
-// scale.
-template <int NJ>
-struct ASrc {
-    uint32_t off[NJ];
-    uint32_t soff;
-};
-
-template <int RB, int NJ>
-__device__ __forceinline__ ARegs<RB, NJ> load_a(const uint8_t *a, const float *as,
-                                                const ASrc<NJ> &src, int kb)
-{
-    ARegs<RB, NJ> r;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-        r.v[j] = moe::load_global<u32x4>(a + (src.off[j] + (uint32_t)kb * RB));
-    r.s = moe::load_global<float>(as + (src.soff + (uint32_t)kb));
-    return r;
-}
-
-// Byte offset in a stage where thread t stores its chunk of row group 0; row
-// group j is G*j rows (G*j*RB bytes) further, and the swizzle depends only on
-// the row's low bits, which j does not change.
-template <int RB>
-__device__ __forceinline__ uint32_t a_store_base(int tid)
-{
-    using L = AStage<RB>;
-    const int row = tid / L::C;
-    return row * RB + L::swz(row, tid % L::C) * 16;
-}
-
-template <int RB, int NJ>
-__device__ __forceinline__ void store_a(uint8_t *st, const ARegs<RB, NJ> &r, int tid, uint32_t sbase)
-{
-    using L = AStage<RB>;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4 *>(st + sbase + L::G * RB * j) = r.v[j];
-    // threads t and t + RMAX hold the same row's scale: both store it
-    reinterpret_cast<float *>(st + L::S_OFF)[tid & (RMAX - 1)] = r.s;
-}
-
-// Gate/up staging: thread t loaded 16 E4M3 codes (chunk t % 8) of rows 32j +
-// t / 8 and stores them as 32 bytes of bf16 values (bf16 chunks 2(t % 8) and
-// 2(t % 8) + 1 of the 256-byte bf16 row).  Each code is converted once per
-// block.
-template <int NJ>
-__device__ __forceinline__ void store_a_bf16(uint8_t *st, const ARegs<128, NJ> &r, int tid)
-{
-    using L = AStage<256>;
-    const int r0 = tid >> 3, c8 = tid & 7;
-    const uint32_t lo = r0 * 256 + L::swz(r0, 2 * c8) * 16;
-    const uint32_t hi = r0 * 256 + L::swz(r0, 2 * c8 + 1) * 16;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const u32x4 v = r.v[j];
-        *reinterpret_cast<bf16x8 *>(st + lo + 32 * 256 * j) = cvt8(v[0], v[1]);
-        *reinterpret_cast<bf16x8 *>(st + hi + 32 * 256 * j) = cvt8(v[2], v[3]);
-    }
-    reinterpret_cast<float *>(st + L::S_OFF)[tid & (RMAX - 1)] = r.s;
-}
-
 // ---------------------------------------------------------------------------
 // gate + up (+ SwiGLU + h quantization), bf16 MFMA
 // ---------------------------------------------------------------------------
-// Block: 4 waves, one per SIMD; wave w = every row of the chunk x h columns
-// n0 + 32w .. +31 of gate and of up (four 16-column operand tiles: gate
-// 0-15, gate 16-31, up 0-15, up 16-31), so gate and up of one h element sit
-// in the same lane and the SwiGLU needs no exchange.  One activation operand
-// (read from LDS) feeds the four tiles.
 struct GuArgs {
     const uint8_t *xq;         // x codes [M][K]
     const float *xs;           // x scales [M][K/128]
@@ -306,13 +233,9 @@ struct GuArgs {
     float limit;
 };
 
-constexpr int GU_D = 4;       // K steps of weights in flight per wave (2 or 4)
 constexpr int GU_RB = 256;    // activation bytes per row and K step (bf16)
 using GuStage = AStage<GU_RB>;
-
-struct GuB {
-    u32x4 v[8];               // [operand tile c][half]: weight rows' 32 bytes of K
-};
+constexpr int GU_STAGE = GuStage::S_OFF + 2 * RMAX * 4;   // rows, gate factors, up factors
 
 // K order inside a step (the same for both operands of every MFMA): MFMA k
 // of lane group q takes K 16q + 8k .. +7 for k = 0, 1 and 64 + 16q + 8(k-2)
@@ -320,233 +243,287 @@ struct GuB {
 // activation row and bytes 16q.., 64+16q.. of the weight row.
 __device__ __forceinline__ int gu_chunk(int q, int k) { return (k < 2 ? 0 : 8) + 2 * q + (k & 1); }
 
-// Chunk body for NRS 16-row operand tiles (rows <= 16 * NRS).
-template <int NRS>
-__device__ __forceinline__ void gateup_chunk(const GuArgs &a, int e, int p0, int rows, int nb,
-                                             uint8_t *sm)
+// Block: 8 waves, two per SIMD, so one wave's weight conversions and
+// promotions issue while the other's MFMAs run.  Wave w = every row of the
+// chunk x h columns n0 + 16w .. +15 of gate and of up (two 16-column operand
+// tiles), so gate and up of one h element sit in the same lane and the
+// SwiGLU needs no exchange.  Every wave reads the chunk's whole activation
+// tile from LDS; the weights stream from global memory straight into VGPRs in
+// the MFMA operand layout, G8_D K steps ahead, and are converted to bf16 in
+// registers once per wave.  The activation codes of step kb+1 move global ->
+// VGPRs -> LDS (converted to bf16 once per block) while step kb multiplies;
+// they are loaded two steps ahead.
+constexpr int G8_THREADS = 512;
+constexpr int G8_D = 2;       // K steps of weights in flight per wave
+
+struct G8B {
+    u32x4 v[4];               // [tile: gate, up][half]
+};
+
+struct G8A {
+    u32x4 v[2];               // 16 codes of rows t/8 and t/8 + 64
+    float s;                  // activation scale of row t % 128
+};
+
+template <int NJ>
+__device__ __forceinline__ G8A g8_load_a(const uint8_t *xq, const float *xs, const uint32_t (&off)[2],
+                                         uint32_t soff, int kb)
 {
-    constexpr int NJ = (NRS + 1) / 2;         // 32-row groups of A codes moved per step
+    G8A r;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) r.v[j] = moe::load_global<u32x4>(xq + (off[j] + (uint32_t)kb * BK));
+    r.s = moe::load_global<float>(xs + (soff + (uint32_t)kb));
+    return r;
+}
+
+// thread t: bf16 chunks 2(t % 8), 2(t % 8) + 1 of rows t / 8 (+ 64), and the
+// promotion factor t % 256 (gate factors of the 128 rows, then up factors)
+template <int NJ>
+__device__ __forceinline__ void g8_store_a(uint8_t *st, const G8A &r, int tid, float swg, float swu)
+{
+    using L = AStage<256>;
+    const int r0 = (tid >> 3) & 63, c8 = tid & 7;
+    const uint32_t lo = r0 * 256 + L::swz(r0, 2 * c8) * 16;
+    const uint32_t hi = r0 * 256 + L::swz(r0, 2 * c8 + 1) * 16;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const u32x4 v = r.v[j];
+        *reinterpret_cast<bf16x8 *>(st + lo + 64 * 256 * j) = cvt8(v[0], v[1]);
+        *reinterpret_cast<bf16x8 *>(st + hi + 64 * 256 * j) = cvt8(v[2], v[3]);
+    }
+    // threads t and t + 256 hold the same factor: both store it
+    reinterpret_cast<float *>(st + L::S_OFF)[tid & 255] = r.s * ((tid & 128) ? swu : swg);
+}
+
+template <int NRS>
+__device__ __forceinline__ void gateup8_chunk(const GuArgs &a, int e, int p0, int rows, int nb,
+                                              uint8_t *sm)
+{
+    constexpr int NJ = NRS <= 4 ? 1 : 2;     // 64-row groups of A codes moved per step
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int q = lane >> 4, r16 = lane & 15;
     const int K = a.K, N = a.N, KB = K / BK;
     const int n0 = nb * 128;
 
-    // activation sources (gathered token rows, 16 codes per thread and row group)
-    ASrc<NJ> src;
+    uint32_t off[2] = {0u, 0u}, soff;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const int row = 32 * j + (tid >> 3);
-        src.off[j] = (uint32_t)a.sorted_token[p0 + (row < rows ? row : 0)] * (uint32_t)K + (tid & 7) * 16;
+        const int row = 64 * j + ((tid >> 3) & 63);
+        off[j] = (uint32_t)a.sorted_token[p0 + (row < rows ? row : 0)] * (uint32_t)K + (tid & 7) * 16;
     }
     {
         const int row = tid & (RMAX - 1);
-        src.soff = (uint32_t)a.sorted_token[p0 + (row < rows ? row : 0)] * KB;
+        soff = (uint32_t)a.sorted_token[p0 + (row < rows ? row : 0)] * KB;
     }
     uint32_t aoff[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) aoff[k] = r16 * GU_RB + GuStage::swz(r16, gu_chunk(q, k)) * 16;
-    const uint8_t *xa = a.xq;
 
-    // weight rows of this wave: gate n0+32w+r16 (+16), up likewise; lane
-    // offset within a 16-row operand tile: row r16, bytes 16q
-    const uint8_t *gbase = moe::uniform_ptr(a.w0 + ((size_t)e * N + n0 + 32 * wave) * K);
-    const uint8_t *ubase = moe::uniform_ptr(a.w1 + ((size_t)e * N + n0 + 32 * wave) * K);
+    const uint8_t *gbase = moe::uniform_ptr(a.w0 + ((size_t)e * N + n0 + 16 * wave) * K);
+    const uint8_t *ubase = moe::uniform_ptr(a.w1 + ((size_t)e * N + n0 + 16 * wave) * K);
     const uint32_t boff = (uint32_t)r16 * K + 16 * q;
-    const uint32_t boff16 = boff + 16u * K;
     auto load_b = [&](int kb) {
-        GuB b;
+        G8B b;
         const uint32_t k0 = (uint32_t)kb * BK;
         b.v[0] = moe::load_global<u32x4>(gbase + (boff + k0));
         b.v[1] = moe::load_global<u32x4>(gbase + (boff + k0 + 64));
-        b.v[2] = moe::load_global<u32x4>(gbase + (boff16 + k0));
-        b.v[3] = moe::load_global<u32x4>(gbase + (boff16 + k0 + 64));
-        b.v[4] = moe::load_global<u32x4>(ubase + (boff + k0));
-        b.v[5] = moe::load_global<u32x4>(ubase + (boff + k0 + 64));
-        b.v[6] = moe::load_global<u32x4>(ubase + (boff16 + k0));
-        b.v[7] = moe::load_global<u32x4>(ubase + (boff16 + k0 + 64));
+        b.v[2] = moe::load_global<u32x4>(ubase + (boff + k0));
+        b.v[3] = moe::load_global<u32x4>(ubase + (boff + k0 + 64));
         return b;
     };
 
-    // weight block scales of this column block, K block j in lane j % 64 of
-    // register j / 64 (K <= 16384); a uniform readlane picks one per K step
     const float *sg = a.ws0 + ((size_t)e * a.ntn + nb) * KB;
     const float *su = a.ws1 + ((size_t)e * a.ntn + nb) * KB;
     const float g_lo = lane < KB ? sg[lane] : 0.0f, g_hi = lane + 64 < KB ? sg[lane + 64] : 0.0f;
     const float u_lo = lane < KB ? su[lane] : 0.0f, u_hi = lane + 64 < KB ? su[lane + 64] : 0.0f;
 
-    f32x4 acc[NRS][4];
+    f32x4 acc[NRS][2];
 #pragma unroll
     for (int i = 0; i < NRS; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Step kb: store A(kb+1) into the other stage, load A(kb+3), convert the
-    // weights of kb, load those of kb+4, multiply, barrier.  Every step runs
-    // unconditionally: loads past the last K step re-read it (valid memory),
-    // and a step past the end adds nothing (its weight block scale, a lane
-    // past KB, is 0).  The prologue issues the loads of steps -4..-1 in the
-    // same order, so the waits the compiler places are those of the steady
-    // state.
     const int klast = KB - 1;
-    GuB b[GU_D];
-    ARegs<128, NJ> ar[2];
-    // steps -4..-1 of the pattern: A loads of steps 0..2, weight loads of
-    // steps 0..D-1 (each after the A load issued in the same step)
-    if constexpr (GU_D == 4) b[0] = load_b(0);
-    ar[0] = load_a<128, NJ>(xa, a.xs, src, 0);
-    if constexpr (GU_D == 4) b[1] = load_b(min(1, klast));
-    ar[1] = load_a<128, NJ>(xa, a.xs, src, min(1, klast));
-    b[GU_D - 2] = load_b(min(GU_D - 2, klast));
-    store_a_bf16<NJ>(sm, ar[0], tid);
-    ar[0] = load_a<128, NJ>(xa, a.xs, src, min(2, klast));
-    b[GU_D - 1] = load_b(min(GU_D - 1, klast));
+    G8B b[G8_D];
+    G8A ar[2];
+    if constexpr (G8_D == 4) b[0] = load_b(0);
+    ar[0] = g8_load_a<NJ>(a.xq, a.xs, off, soff, 0);
+    if constexpr (G8_D == 4) b[1] = load_b(min(1, klast));
+    ar[1] = g8_load_a<NJ>(a.xq, a.xs, off, soff, min(1, klast));
+    b[G8_D - 2] = load_b(min(G8_D - 2, klast));
+    g8_store_a<NJ>(sm, ar[0], tid, lane_f(g_lo, 0), lane_f(u_lo, 0));
+    ar[0] = g8_load_a<NJ>(a.xq, a.xs, off, soff, min(2, klast));
+    b[G8_D - 1] = load_b(min(G8_D - 1, klast));
     moe::lds_barrier();
 
-    auto step = [&](int kb, GuB &bk, ARegs<128, NJ> &an, uint8_t *cur, uint8_t *nxt) {
-        __builtin_amdgcn_sched_barrier(0);
-        // A of step kb+1 (loaded two steps ago) into the other stage, whose
-        // last reader (step kb-1) every wave has passed
-        store_a_bf16<NJ>(nxt, an, tid);
-        an = load_a<128, NJ>(xa, a.xs, src, min(kb + 3, klast));
-        // this step's weights as bf16 operands, then the next load into the registers
-        bf16x8 bw[4][4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const u32x4 &v = bk.v[2 * c + t];
-                bw[c][2 * t] = cvt8(v[0], v[1]);
-                bw[c][2 * t + 1] = cvt8(v[2], v[3]);
-            }
-        bk = load_b(min(kb + GU_D, klast));
-        const float swg = lane_f(kb < 64 ? g_lo : g_hi, kb & 63);
-        const float swu = lane_f(kb < 64 ? u_lo : u_hi, kb & 63);
-        const float *ss = reinterpret_cast<const float *>(cur + GuStage::S_OFF);
-        // operand tile rs: its MFMAs, the promotion of tile rs-1 (independent
-        // VALU work beside them), and the LDS reads of tile rs+1; then a
-        // scheduling fence, so no tile's reads are hoisted further
-        bf16x8 av[4], an4[4];
-        f32x4 sx, snx, t[4], tp[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) av[k] = *reinterpret_cast<const bf16x8 *>(cur + aoff[k]);
-        sx = *reinterpret_cast<const f32x4 *>(ss + 4 * q);
-        auto promote = [&](int r, const f32x4 (&tt)[4], const f32x4 &sxr) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float fg = sxr[i] * swg, fu = sxr[i] * swu;
-                acc[r][0][i] = fmaf(tt[0][i], fg, acc[r][0][i]);
-                acc[r][1][i] = fmaf(tt[1][i], fg, acc[r][1][i]);
-                acc[r][2][i] = fmaf(tt[2][i], fu, acc[r][2][i]);
-                acc[r][3][i] = fmaf(tt[3][i], fu, acc[r][3][i]);
-            }
-        };
-        f32x4 sp;
-#pragma unroll
-        for (int rs = 0; rs < NRS; ++rs) {
-            if (rs + 1 < NRS) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    an4[k] = *reinterpret_cast<const bf16x8 *>(cur + aoff[k] + 16 * GU_RB * (rs + 1));
-                snx = *reinterpret_cast<const f32x4 *>(ss + (rs + 1) * 16 + 4 * q);
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) t[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) t[c] = mfma_bf16(av[k], bw[c][k], t[c]);
-            if (rs > 0) promote(rs - 1, tp, sp);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) tp[c] = t[c];
-            sp = sx;
-            if (rs + 1 < NRS) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) av[k] = an4[k];
-                sx = snx;
-            }
-            __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](int kb, G8B &bk, G8A &an, uint8_t *cur, uint8_t *nxt) {
+        {
+            const int kn = kb + 1;
+            g8_store_a<NJ>(nxt, an, tid, lane_f(kn < 64 ? g_lo : g_hi, kn & 63),
+                           lane_f(kn < 64 ? u_lo : u_hi, kn & 63));
         }
-        promote(NRS - 1, tp, sp);
-        moe::lds_barrier();
+        an = g8_load_a<NJ>(a.xq, a.xs, off, soff, min(kb + 3, klast));
+        // this step's weights as bf16 operands; their registers take the
+        // load of step kb + G8_D at once
+        bf16x8 bw[2][4];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const u32x4 &v = bk.v[2 * c + (k >> 1)];
+                bw[c][k] = cvt8(v[2 * (k & 1)], v[2 * (k & 1) + 1]);
+            }
+        bk = load_b(min(kb + G8_D, klast));
+        // Row tiles in pairs, K-outer inside a pair: the 2 x 2 block sums of a
+        // pair are independent MFMA chains, four deep.  Software pipeline,
+        // fenced so the scheduler keeps it: the activation operands of the
+        // next K slice (or of the next pair's first) are read while this
+        // slice's MFMAs run, and a pair is promoted beside the next pair's
+        // first MFMAs.
+        const float *ss = reinterpret_cast<const float *>(cur + GuStage::S_OFF);
+        auto a_op = [&](int k, int rs) {
+            return *reinterpret_cast<const bf16x8 *>(cur + aoff[k] + 16 * GU_RB * rs);
+        };
+        f32x4 tp[2][2], fgp[2], fup[2];
+        auto promote = [&](int rs0) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[rs0 + r][0][i] = fmaf(tp[r][0][i], fgp[r][i], acc[rs0 + r][0][i]);
+                    acc[rs0 + r][1][i] = fmaf(tp[r][1][i], fup[r][i], acc[rs0 + r][1][i]);
+                }
+        };
+        bf16x8 acur[2], anxt[2];
+        acur[0] = a_op(0, 0);
+        acur[1] = a_op(0, 1);
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g0 = 0; g0 < NRS; g0 += 2) {
+            f32x4 t[2][2], fg[2], fu[2];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool more = k < 3 || g0 + 2 < NRS;
+                if (more) {
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) anxt[r] = k < 3 ? a_op(k + 1, g0 + r) : a_op(0, g0 + 2 + r);
+                }
+                if (k == 0) {
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        fg[r] = *reinterpret_cast<const f32x4 *>(ss + (g0 + r) * 16 + 4 * q);
+                        fu[r] = *reinterpret_cast<const f32x4 *>(ss + RMAX + (g0 + r) * 16 + 4 * q);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const f32x4 zg = k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : t[r][0];
+                    const f32x4 zu = k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : t[r][1];
+                    t[r][0] = mfma_bf16(acur[r], bw[0][k], zg);
+                    t[r][1] = mfma_bf16(acur[r], bw[1][k], zu);
+                }
+                if (k == 0 && g0 > 0) promote(g0 - 2);
+                if (more) {
+                    acur[0] = anxt[0];
+                    acur[1] = anxt[1];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                tp[r][0] = t[r][0];
+                tp[r][1] = t[r][1];
+                fgp[r] = fg[r];
+                fup[r] = fu[r];
+            }
+        }
+        promote(NRS - 2);
+        moe::lds_barrier();
     };
 
-    uint8_t *s0 = sm, *s1 = sm + GuStage::BYTES;
-    static_assert(GU_D == 2 || GU_D == 4, "the K loop is unrolled by 4");
+    uint8_t *s0 = sm, *s1 = sm + GU_STAGE;
+    static_assert(G8_D == 2 || G8_D == 4, "the K loop is unrolled by 4");
 #pragma unroll 1
     for (int kb0 = 0; kb0 < KB; kb0 += 4) {
         step(kb0, b[0], ar[1], s0, s1);
-        step(kb0 + 1, b[1 % GU_D], ar[0], s1, s0);
-        step(kb0 + 2, b[2 % GU_D], ar[1], s0, s1);
-        step(kb0 + 3, b[3 % GU_D], ar[0], s1, s0);
+        step(kb0 + 1, b[1 % G8_D], ar[0], s1, s0);
+        step(kb0 + 2, b[2 % G8_D], ar[1], s0, s1);
+        step(kb0 + 3, b[3 % G8_D], ar[0], s1, s0);
     }
 
-    // epilogue: h = SwiGLU(g, u) in place of the gate sums; per-row amax of
-    // the wave's 32 columns, then over the 4 waves through LDS
-    float *rmax = reinterpret_cast<float *>(sm);          // [4 waves][RMAX]
+    // epilogue: h = SwiGLU(g, u); per-row amax of the wave's 16 columns, then
+    // over the 8 waves through LDS
+    float *rmax = reinterpret_cast<float *>(sm);          // [8 waves][RMAX]
 #pragma unroll
     for (int rs = 0; rs < NRS; ++rs) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc[rs][0][i] = swiglu_clamp(acc[rs][0][i], acc[rs][2][i], a.limit);
-            acc[rs][1][i] = swiglu_clamp(acc[rs][1][i], acc[rs][3][i], a.limit);
-            float m = fmaxf(fabsf(acc[rs][0][i]), fabsf(acc[rs][1][i]));
+            acc[rs][0][i] = swiglu_clamp(acc[rs][0][i], acc[rs][1][i], a.limit);
+            float m = fabsf(acc[rs][0][i]);
 #pragma unroll
             for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
             if (r16 == 0) rmax[wave * RMAX + rs * 16 + 4 * q + i] = m;
         }
     }
     __syncthreads();
-    uint8_t *ct = sm + 4 * RMAX * 4;                      // codes tile [RMAX][144]
+    uint8_t *ct = sm + 8 * RMAX * 4;                      // codes tile [RMAX][144]
 #pragma unroll
     for (int rs = 0; rs < NRS; ++rs) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rs * 16 + 4 * q + i;
-            const float amax = fmaxf(fmaxf(rmax[r], rmax[RMAX + r]),
-                                     fmaxf(rmax[2 * RMAX + r], rmax[3 * RMAX + r]));
+            float amax = rmax[r];
+#pragma unroll
+            for (int w = 1; w < 8; ++w) amax = fmaxf(amax, rmax[w * RMAX + r]);
             const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;
-            const uint32_t c2 = e4m3_pair(acc[rs][0][i] / scale, acc[rs][1][i] / scale);
-            ct[r * 144 + 32 * wave + r16] = (uint8_t)(c2 & 0xFFu);
-            ct[r * 144 + 32 * wave + 16 + r16] = (uint8_t)(c2 >> 8);
+            ct[r * 144 + 16 * wave + r16] = (uint8_t)(e4m3_pair(acc[rs][0][i] / scale, 0.0f) & 0xFFu);
             if (wave == 0 && r16 == 0 && r < rows) a.hs[(size_t)(p0 + r) * a.ntn + nb] = scale;
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < (NRS + 1) / 2; ++j) {
-        const int r = 32 * j + (tid >> 3), part = tid & 7;
+    for (int j = 0; j < (NRS + 3) / 4; ++j) {
+        const int r = 64 * j + (tid >> 3), part = tid & 7;
         if (r < rows)
             *reinterpret_cast<uint4 *>(a.hq + (size_t)(p0 + r) * N + n0 + part * 16) =
                 *reinterpret_cast<const uint4 *>(ct + r * 144 + part * 16);
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void gemm_gateup_kernel(GuArgs a)
+__global__ __launch_bounds__(G8_THREADS, 1) void gemm_gateup8_kernel(GuArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sm[2 * GuStage::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sm[2 * GU_STAGE];
     int4 tile;
     int nb;
     if (!gemm_item(a, tile, nb)) return;
     const int e = tile.x, p0 = tile.y;
     const int rows = moe::uniform(chunk_rows(a.offsets, e, p0, tile.w));
     if (rows <= 0) return;
-    // rows rounded up to a multiple of 32
     switch ((rows + 31) >> 5) {
-    case 1: gateup_chunk<2>(a, e, p0, rows, nb, sm); break;
-    case 2: gateup_chunk<4>(a, e, p0, rows, nb, sm); break;
-    case 3: gateup_chunk<6>(a, e, p0, rows, nb, sm); break;
-    default: gateup_chunk<8>(a, e, p0, rows, nb, sm); break;
+    case 1: gateup8_chunk<2>(a, e, p0, rows, nb, sm); break;
+    case 2: gateup8_chunk<4>(a, e, p0, rows, nb, sm); break;
+    case 3: gateup8_chunk<6>(a, e, p0, rows, nb, sm); break;
+    default: gateup8_chunk<8>(a, e, p0, rows, nb, sm); break;
     }
 }
 
 // ---------------------------------------------------------------------------
-// down, FP8 MFMA
+// down, FP8 MFMA, persistent
 // ---------------------------------------------------------------------------
-// Block: 4 waves; wave w = every row of the chunk x outputs n0 + 32w .. +31
-// (two 16-column operand tiles).  Two blocks share a CU: a down block runs
-// only K/128 = 16 K steps, and one block's ramp runs under another's stream.
+// The W = chunks x (N/128) items (one chunk of <= 128 rows x 128 outputs of
+// y each) split into 8 contiguous runs in the order of gemm_item, one per XCD
+// (block b runs on XCD b % 8), and the blocks of an XCD deal its run out
+// round-robin: the items in flight on an XCD at any time are neighbours (the
+// chunks of one expert on one weight block, then the next column block), so
+// they share weight blocks and h rows in that XCD's L2.  A block runs its
+// items as one continuous K-step pipeline: every step's operands (128 h rows,
+// 128 weight rows, the h scales and the weight block scale) go from global
+// memory straight into a ring of LDS stages (DMA), and the loads of the next
+// item's first steps are in flight while the current item finishes and
+// stores its y block, so no item pays the ramp of its first loads.  Only the
+// descriptors are read before the pipeline starts: each block decodes its
+// items into LDS once.  Waves as 2 x 2, 64 x 64 outputs each.
 struct DnArgs {
     const uint8_t *hq;         // h codes [S][K] (packed rows)
     const float *hs;           // h scales [S][K/128]
@@ -559,146 +536,173 @@ struct DnArgs {
     int32_t K, N, ntn;
 };
 
-constexpr int DN_D = 4;
-constexpr int DN_RB = 128;    // activation bytes per row and K step (E4M3)
-using DnStage = AStage<DN_RB>;
+constexpr int DN_NST = 2;                 // LDS stages (DN_NST - 1 K steps in flight)
+constexpr int DN_BPC = 2;                 // blocks per CU
+constexpr int DN_MAXI = 256;              // items per block (the host sizes the grid for it)
+constexpr int DN_A = 0, DN_B = 128 * 128, DN_S = DN_B + 128 * 128, DN_W = DN_S + 4 * 256;
+constexpr int DN_STAGE = DN_W + 4 * 256;
+constexpr int DN_PER = 4 + 4 + 1 + 1;     // DMA instructions per stage and wave
+static_assert(DN_BPC * (DN_NST * DN_STAGE + DN_MAXI * 16) <= 160 * 1024, "down stages exceed LDS");
+static_assert((DN_NST - 2) * DN_PER < 64, "vmcnt is 6 bits");
 
-struct DnB {
-    u32x4 v[4];               // [operand tile c][half]
-};
-
-template <int NRS>
-__device__ __forceinline__ void down_chunk(const DnArgs &a, int e, int p0, int rows, int nb,
-                                           uint8_t *sm)
+// A 16 x 128 FP8 operand from a swizzled 128-byte-row tile: lane l takes
+// row l % 16, bytes 32 (l / 16) .. +31.
+__device__ __forceinline__ i32x8 lds_op(const uint8_t *tile, int row, int lane)
 {
-    constexpr int NJ = (NRS + 1) / 2;         // 32-row groups of A moved per step
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = moe::uniform(tid >> 6);
-    const int q = lane >> 4, r16 = lane & 15;
-    const int K = a.K, N = a.N, KB = K / BK;
-    const int n0 = nb * 128;
-
-    ASrc<NJ> src;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int row = DnStage::G * j + tid / DnStage::C;
-        src.off[j] = (uint32_t)(p0 + (row < rows ? row : 0)) * K + (tid % DnStage::C) * 16;
-    }
-    {
-        const int row = tid & (RMAX - 1);
-        src.soff = (uint32_t)(p0 + (row < rows ? row : 0)) * KB;
-    }
-    const uint32_t sbase = a_store_base<DN_RB>(tid);
-    // A operand halves of lane (row r16): logical chunks q and 4+q (K 16q..
-    // and 64+16q..), the weight rows' byte order
-    const uint32_t ao0 = r16 * DN_RB + DnStage::swz(r16, q) * 16;
-    const uint32_t ao1 = r16 * DN_RB + DnStage::swz(r16, 4 + q) * 16;
-
-    const uint8_t *wbase = moe::uniform_ptr(a.w0 + ((size_t)e * N + n0 + 32 * wave) * K);
-    const uint32_t boff = (uint32_t)r16 * K + 16 * q;
-    const uint32_t boff16 = boff + 16u * K;
-    auto load_b = [&](int kb) {
-        DnB b;
-        const uint32_t k0 = (uint32_t)kb * BK;
-        b.v[0] = moe::load_nt_global<u32x4>(wbase + (boff + k0));
-        b.v[1] = moe::load_nt_global<u32x4>(wbase + (boff + k0 + 64));
-        b.v[2] = moe::load_nt_global<u32x4>(wbase + (boff16 + k0));
-        b.v[3] = moe::load_nt_global<u32x4>(wbase + (boff16 + k0 + 64));
-        return b;
-    };
-    const float *sw0 = a.ws0 + ((size_t)e * a.ntn + nb) * KB;
-    const float w_lo = lane < KB ? sw0[lane] : 0.0f, w_hi = lane + 64 < KB ? sw0[lane + 64] : 0.0f;
-
-    f32x4 acc[NRS][2];
-#pragma unroll
-    for (int i = 0; i < NRS; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // the K loop of the gate/up kernel, with FP8 operands taken as they are
-    const int klast = KB - 1;
-    DnB b[DN_D];
-    ARegs<DN_RB, NJ> ar[2];
-    b[0] = load_b(0);
-    ar[0] = load_a<DN_RB, NJ>(a.hq, a.hs, src, 0);
-    b[1] = load_b(min(1, klast));
-    ar[1] = load_a<DN_RB, NJ>(a.hq, a.hs, src, min(1, klast));
-    b[2] = load_b(min(2, klast));
-    store_a<DN_RB, NJ>(sm, ar[0], tid, sbase);
-    ar[0] = load_a<DN_RB, NJ>(a.hq, a.hs, src, min(2, klast));
-    b[3] = load_b(min(3, klast));
-    moe::lds_barrier();
-
-    auto step = [&](int kb, DnB &bk, ARegs<DN_RB, NJ> &an, uint8_t *cur, uint8_t *nxt) {
-        __builtin_amdgcn_sched_barrier(0);
-        store_a<DN_RB, NJ>(nxt, an, tid, sbase);
-        an = load_a<DN_RB, NJ>(a.hq, a.hs, src, min(kb + 3, klast));
-        i32x8 bv[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-            bv[c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(bk.v[2 * c], bk.v[2 * c + 1],
-                                                                      0, 1, 2, 3, 4, 5, 6, 7));
-        bk = load_b(min(kb + DN_D, klast));
-        const float sw = lane_f(kb < 64 ? w_lo : w_hi, kb & 63);
-        const float *ss = reinterpret_cast<const float *>(cur + DnStage::S_OFF);
-#pragma unroll
-        for (int rs = 0; rs < NRS; ++rs) {
-            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(cur + ao0 + 16 * DN_RB * rs);
-            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(cur + ao1 + 16 * DN_RB * rs);
-            const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-            const f32x4 sx = *reinterpret_cast<const f32x4 *>(ss + rs * 16 + 4 * q);
-            const f32x4 t0 = mfma_fp8(av, bv[0]);
-            const f32x4 t1 = mfma_fp8(av, bv[1]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float f = sx[i] * sw;
-                acc[rs][0][i] = fmaf(t0[i], f, acc[rs][0][i]);
-                acc[rs][1][i] = fmaf(t1[i], f, acc[rs][1][i]);
-            }
-        }
-        moe::lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    uint8_t *s0 = sm, *s1 = sm + DnStage::BYTES;
-    static_assert(DN_D == 4, "the K loop is unrolled by the weight registers' rotation");
-#pragma unroll 1
-    for (int kb0 = 0; kb0 < KB; kb0 += 4) {
-        step(kb0, b[0], ar[1], s0, s1);
-        step(kb0 + 1, b[1], ar[0], s1, s0);
-        step(kb0 + 2, b[2], ar[1], s0, s1);
-        step(kb0 + 3, b[3], ar[0], s1, s0);
-    }
-
-#pragma unroll
-    for (int rs = 0; rs < NRS; ++rs) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rs * 16 + 4 * q + i;
-            if (r < rows) {
-                float *yr = a.y + (size_t)(p0 + r) * N + n0 + 32 * wave + r16;
-                yr[0] = acc[rs][0][i];
-                yr[16] = acc[rs][1][i];
-            }
-        }
-    }
+    const int c = (lane >> 4) * 2;
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(tile + (row * 128 + swz(row, c) * 16));
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(tile + (row * 128 + swz(row, c + 1) * 16));
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__global__ __launch_bounds__(kThreads, 2) void gemm_down_kernel(DnArgs a)
+__global__ __launch_bounds__(kThreads, DN_BPC) void gemm_down_kernel(DnArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sm[2 * DnStage::BYTES];
-    int4 tile;
-    int nb;
-    if (!gemm_item(a, tile, nb)) return;
-    const int e = tile.x, p0 = tile.y;
-    const int rows = moe::uniform(chunk_rows(a.offsets, e, p0, tile.w));
-    if (rows <= 0) return;
-    switch ((rows + 31) >> 5) {
-    case 1: down_chunk<2>(a, e, p0, rows, nb, sm); break;
-    case 2: down_chunk<4>(a, e, p0, rows, nb, sm); break;
-    case 3: down_chunk<6>(a, e, p0, rows, nb, sm); break;
-    default: down_chunk<8>(a, e, p0, rows, nb, sm); break;
+    __shared__ __attribute__((aligned(16))) uint8_t sm[DN_NST * DN_STAGE];
+    __shared__ int4 s_item[DN_MAXI];       // (expert, first row, rows, column block)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = moe::uniform(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int K = a.K, N = a.N, KB = K / BK;
+
+    // this block's items: L = begin + bi + t * nbx, t < T
+    const int W = moe::uniform(*a.ntiles) * a.ntn;
+    const int x = blockIdx.x & 7, bi = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+    const int q = W >> 3, rr = W & 7;
+    const int begin = x * q + min(x, rr), len = q + (x < rr ? 1 : 0);
+    const int T = bi < len ? min((len - bi + nbx - 1) / nbx, DN_MAXI) : 0;
+    if (T == 0) return;
+    if (tid < T) {
+        const int L = begin + bi + tid * nbx;
+        const int4 head = a.tiles[L / a.ntn];
+        const int local = L - head.z * a.ntn;
+        const int4 tl = a.tiles[head.z + local % head.w];
+        const int lo = a.offsets[tl.x], hi = a.offsets[tl.x + 1];
+        const int cs = (hi - lo + head.w - 1) / head.w;
+        const int rows = min(cs, hi - tl.y);
+        // a chunk with no rows loads the expert's first row and stores nothing
+        s_item[tid] = make_int4(tl.x, rows > 0 ? tl.y : lo, rows, local / head.w);
     }
+    __syncthreads();
+
+    // issue side: per-thread sources of the item being loaded
+    uint32_t aoff[4], boff[4], soff = 0;
+    const uint8_t *wbase = nullptr;
+    const float *wsb = nullptr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = (wave * 4 + j) * 8 + (lane >> 3);
+        boff[j] = (uint32_t)r * K + swz(r, lane & 7) * 16;
+        aoff[j] = 0;
+    }
+    auto set_issue = [&](int t) {
+        const int4 d = s_item[t];
+        const int e = moe::uniform(d.x), p0 = moe::uniform(d.y), rows = moe::uniform(d.z);
+        const int nb = moe::uniform(d.w);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = (wave * 4 + j) * 8 + (lane >> 3);
+            aoff[j] = (uint32_t)(p0 + (r < rows ? r : 0)) * K + swz(r, lane & 7) * 16;
+        }
+        const int srow = wm * 64 + lane;
+        soff = (uint32_t)(p0 + (srow < rows ? srow : 0)) * KB * 4;
+        wbase = moe::uniform_ptr(a.w0 + ((size_t)e * N + (size_t)nb * 128) * K);
+        wsb = moe::uniform_ptr(a.ws0 + ((size_t)e * a.ntn + nb) * KB);
+    };
+    auto issue = [&](int kb, uint8_t *st) {
+        const uint8_t *ab = a.hq + (size_t)kb * BK, *bb = wbase + (size_t)kb * BK;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(ab, aoff[j], lds_addr(st + DN_A + (wave * 4 + j) * 1024));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(bb, boff[j], lds_addr(st + DN_B + (wave * 4 + j) * 1024));
+        dma4(a.hs + kb, soff, lds_addr(st + DN_S + wave * 256));
+        dma4(wsb + kb, 0u, lds_addr(st + DN_W + wave * 256));     // one float, every lane
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const uint8_t *st) {
+        const float sw = *reinterpret_cast<const float *>(st + DN_W + wave * 256);
+        const float *sa = reinterpret_cast<const float *>(st + DN_S) + wave * 64;
+        i32x8 av[4];
+        f32x4 fa[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            av[mt] = lds_op(st + DN_A, wm * 64 + mt * 16 + (lane & 15), lane);
+            fa[mt] = *reinterpret_cast<const f32x4 *>(sa + mt * 16 + (lane >> 4) * 4) * sw;
+        }
+        f32x4 p[4][4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const i32x8 bv = lds_op(st + DN_B, wn * 64 + nt * 16 + (lane & 15), lane);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) p[mt][nt] = mfma_fp8(av[mt], bv);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(p[mt][nt][i], fa[mt][i], acc[mt][nt][i]);
+    };
+    auto store_y = [&](int t) {
+        const int4 d = s_item[t];
+        const int p0 = moe::uniform(d.y), rows = moe::uniform(d.z), nb = moe::uniform(d.w);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wm * 64 + mt * 16 + (lane >> 4) * 4 + i;
+                if (r < rows) {
+                    float *yr = a.y + (size_t)(p0 + r) * N + nb * 128 + wn * 64 + (lane & 15);
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) yr[nt * 16] = acc[mt][nt][i];
+                }
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) acc[mt][nt][i] = 0.0f;
+            }
+    };
+
+    // the block's T x KB steps as one ring of DN_NST stages
+    const int G = T * KB;
+    int it = 0, ikb = 0;                 // next step to load: item it, K step ikb
+    set_issue(0);
+    auto advance = [&]() {
+        if (++ikb == KB) {
+            ikb = 0;
+            if (++it < T) set_issue(it);
+        }
+    };
+    MOE_WAIT_VM(0);
+#pragma unroll
+    for (int j = 0; j < DN_NST - 1; ++j)
+        if (j < G) {
+            issue(ikb, sm + j * DN_STAGE);
+            advance();
+        }
+    int cs = 0, is = DN_NST - 1, ckb = 0, ct = 0;
+    for (int g = 0; g < G; ++g) {
+        wait_stages<DN_PER, DN_NST - 2>(G - 1 - g);
+        MOE_WAIT_LGKM0();
+        MOE_BARRIER();
+        if (g + DN_NST - 1 < G) {
+            issue(ikb, sm + is * DN_STAGE);
+            advance();
+        }
+        // y of the item finished last step, stored under the loads in flight
+        if (ckb == 0 && g > 0) store_y(ct - 1);
+        compute(sm + cs * DN_STAGE);
+        cs = cs + 1 == DN_NST ? 0 : cs + 1;
+        is = is + 1 == DN_NST ? 0 : is + 1;
+        if (++ckb == KB) {
+            ckb = 0;
+            ++ct;
+        }
+    }
+    store_y(T - 1);
 }
 
 }  // namespace
@@ -734,7 +738,7 @@ hipError_t launch_gemm_gateup(const uint8_t *xq, const float *xs, const int32_t 
     a.w0 = gcodes; a.w1 = ucodes; a.ws0 = gscales; a.ws1 = uscales;
     a.offsets = offsets; a.tiles = tiles; a.ntiles = ntiles;
     a.hq = hq; a.hs = hs; a.K = hidden; a.N = inter; a.ntn = inter / 128; a.limit = limit;
-    hipLaunchKernelGGL(gemm_gateup_kernel, dim3((unsigned)(tmax * a.ntn)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(gemm_gateup8_kernel, dim3((unsigned)(tmax * a.ntn)), dim3(G8_THREADS), 0, st, a);
     return hipGetLastError();
 }
 
@@ -747,6 +751,17 @@ hipError_t launch_gemm_down(const uint8_t *hq, const float *hs, const uint8_t *d
     a.hq = hq; a.hs = hs; a.w0 = dcodes; a.ws0 = dscales;
     a.offsets = offsets; a.tiles = tiles; a.ntiles = ntiles;
     a.y = y; a.K = inter; a.N = hidden; a.ntn = hidden / 128;
-    hipLaunchKernelGGL(gemm_down_kernel, dim3((unsigned)(tmax * a.ntn)), dim3(kThreads), 0, st, a);
+    // DN_BPC blocks per CU, more where a block would hold over DN_MAXI items
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t wmax = (int64_t)tmax * a.ntn;
+    const int64_t per_xcd = (wmax + 7) / 8;
+    const int64_t nbx = std::max<int64_t>((DN_BPC * cus + 7) / 8, (per_xcd + DN_MAXI - 1) / DN_MAXI);
+    hipLaunchKernelGGL(gemm_down_kernel, dim3((unsigned)(8 * nbx)), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
