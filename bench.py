@@ -39,6 +39,8 @@ def parse():
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-also-seconds", type=float, default=6.0,
+                    help="CPU budget of the oracle beside each 'also' workload (at least one layer)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the one-launch fused layer rows")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -298,14 +300,19 @@ def measure(wl, banks, steps, warmup, route_sets, hip, want_stages=True, fused=F
                 flops=flops, mode=mode, layer=layer, x=x, sets=sets)
 
 
-def cpu_baseline(wl, banks, x, sets, budget_s):
-    """The oracle, as it stands, on whole layers of the same workload."""
+def cpu_baseline(wl, banks, x, sets, budget_s, stride=1, act_fp8=False):
+    """The oracle, as it stands, on whole layers of the same workload; with
+    stride > 1 on the deterministic subset of tokens t = 0, stride, 2*stride,
+    ... of each layer (its routes, weights and x rows as they are), the time
+    scaled by stride to a whole layer.  act_fp8: the oracle of the FP8 GEMM
+    tier (x and h quantized per 1x128 group)."""
     import numpy as np
 
     import oracle  # CPU baseline leg only
     import torch
     E = wl.experts
-    xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    xb = x.view(torch.int16).cpu().numpy().view(np.uint16)[::stride]
+    sets = [(ids[::stride], w[::stride], extra) for ids, w, extra in sets]
     # the route sets' selected experts, copied to the host once (outside the
     # timing), as many sets as fit about 2 GB of host memory (at least one)
     host, held = [], 0
@@ -325,13 +332,18 @@ def cpu_baseline(wl, banks, x, sets, budget_s):
     while sum(times) < budget_s and len(times) < 100000:
         hb, remap, w = host[len(times) % len(host)]
         t0 = time.perf_counter()
-        oracle.moe_layer(*hb, xb, remap, w, wl.limit, False)
+        oracle.moe_layer(*hb, xb, remap, w, wl.limit, act_fp8)
         times.append(time.perf_counter() - t0)
     n = len(times)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=float(np.mean(times) * 1e6), unit="us/layer", cores=threads, kind="oracle",
-                sample=f"{n} whole layers of {wl.name} ({sum(times):.1f} s), cycling over route sets "
-                       f"0..{len(host) - 1}, FP64, selected experts copied to host before timing")
+    what = (f"{n} whole layers of {wl.name}" if stride == 1 else
+            f"{n} layers of {wl.name} on the 1/{stride} token subset t % {stride} == 0 "
+            f"({len(xb)} of {wl.M} tokens), time x {stride} per whole layer")
+    return dict(value=float(np.mean(times) * stride * 1e6), unit="us/layer", cores=threads,
+                kind="oracle",
+                sample=f"{what} ({sum(times):.1f} s), cycling over route sets 0..{len(host) - 1}, "
+                       f"FP64{', x and h quantized per 1x128 as the FP8 GEMM tier' if act_fp8 else ''}, "
+                       f"selected experts copied to host before timing")
 
 
 # HBM bytes per launch of the roofline kernel, from two rocprofv3 --pmc passes
@@ -352,7 +364,7 @@ TRAFFIC = {
     "nvfp4_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
         "src": "cd6fb700362c8c12d610978b517a952c85576205248c54d3", "fetch_kib": 64892, "write_kib": 835},
     "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h"],
-        "src": "605879b65f3835f546ff9d1401442f7f85576205248c54d3", "fetch_kib": 4247723, "write_kib": 69890},
+        "src": "e7bd3c69fc01c3df46ff9d1401442f7fe0174e2455c8b818", "fetch_kib": 4022574, "write_kib": 68917},
     "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
         "src": "90d4f2b67c21b99a46ff9d1401442f7f85576205248c54d3", "fetch_kib": 2063581, "write_kib": 196608},
     "verify_e4m3_m8": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
@@ -388,11 +400,13 @@ def roofline(r):
                 "traffic": measured_traffic(r["name"] + "/fused"),
                 "alg_bytes_per_launch": round(r["alg_layer_bytes"]), "avg_launch_us": round(us, 3)}
     if r["mode"] == 2:
+        # the E4M3 tier's gate/up contracts on the bf16 MFMA (E4M3 codes are
+        # bf16 values exactly): its peak is the bf16 one
         us = r["stages"]["gateup_gemm"]
         flop = r["flops"] * 2.0 / 3.0
         tf = flop / (us * 1e-6) / 1e12
         return {"kernel": "gemm_gateup", "bound": "mfma", "achieved": round(tf, 1),
-                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(r["name"]), "alg_flop_per_launch": round(flop),
                 "avg_launch_us": round(us, 3)}
     if r["mode"] == 4:
@@ -659,14 +673,22 @@ def main():
             also[name]["router"] = router_rows(w2, b2, max(20, args.steps // 2), args.route_sets,
                                                hip)
         if r2["mode"] == 2:
-            also[name].update({"tier": "fp8_mfma_grouped_gemm", "alg_TFLOPs": round(tf, 1),
-                               "mfma_frac_fp8": round(tf / FP8_PEAK_TFLOPS, 4)})
+            also[name].update({"tier": "grouped_gemm_bf16_gateup_fp8_down", "alg_TFLOPs": round(tf, 1),
+                               "mfma_frac_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
             line["prefill_tokens_per_s"] = also[name]["tokens_per_s"]
         elif r2["mode"] == 4:
             also[name].update({"tier": "bf16_mfma_grouped_gemm_w4a16", "alg_TFLOPs": round(tf, 1),
                                "mfma_frac_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
             line["nvfp4_prefill_tokens_per_s"] = also[name]["tokens_per_s"]
         print(f"# {name}: {r2['us_layer']:.2f} us/layer", file=sys.stderr, flush=True)
+        if not args.no_cpu_baseline:
+            # the oracle beside this config: whole layers at decode sizes, a
+            # 1/8 token subset of the prefill layers
+            cb = cpu_baseline(w2, b2, r2["x"], r2["sets"], args.cpu_also_seconds,
+                              stride=8 if w2.M > 16 else 1, act_fp8=r2["mode"] == 2)
+            also[name]["cpu_baseline"] = cb
+            print(f"# {name}: oracle {cb['value']:.0f} us/layer on {cb['cores']} threads",
+                  file=sys.stderr, flush=True)
         if not same:
             del b2
         del r2
