@@ -24,6 +24,8 @@
 #include "moe_internal.h"
 #include "fused_common.h"
 
+#include <type_traits>
+
 namespace {
 
 using moe::bf16x2;
@@ -113,13 +115,20 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 // keeps the block scales of all K segments in two registers (lane l:
 // segments l and l + 64).
 //
+// XW (unrolled form, more slots than whole x rows fit): the x rows of the
+// pass go to LDS one K chunk at a time into two buffers ([2][ST][CH * 16]
+// uint4): chunk c+1's rows are loaded into VGPRs while chunk c is
+// multiplied, stored after it, and a barrier ends the chunk.  Every slot of
+// the expert (up to ST) is then served by one weight pass.
+//
 // gateup_e4m3_item does one (expert e, 16-row tile) item for the ne slots of
 // e, whose packed rows start at p0 and whose tokens are tok[0..ne); xl is
 // the LDS x tile ([a.st][H / 8] uint4), ush the LDS up-sum exchange.
-template <int CH, int NCH, int ST, bool FUSED = false>
+template <int CH, int NCH, int ST, bool FUSED = false, bool XW = false>
 __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int tile, int p0, int ne,
                                                  const int32_t *tok, uint4 *xl, float (*ush)[16])
 {
+    static_assert(!XW || (NCH > 0 && !FUSED), "chunked x staging is an unrolled, standalone form");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
     const int grp = lane >> 3, sub = lane & 7;
@@ -150,6 +159,9 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
         float acc[ST];
 #pragma unroll
         for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
+        // x tile as mul_chunk reads it: base, row stride (uint4), first segment
+        const uint4 *xcur = xl;
+        int xstr = H8, xseg0 = 0;
 
         auto mul_chunk = [&](const uint4 (&wc)[CH], int c) {
 #pragma unroll
@@ -168,8 +180,8 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
 #pragma unroll
                 for (int j = 0; j < ST; ++j) {
                     if (j < nt) {
-                        const uint4 xa = xl[j * H8 + seg * 16 + sub * 2];
-                        const uint4 xb = xl[j * H8 + seg * 16 + sub * 2 + 1];
+                        const uint4 xa = xcur[j * xstr + (seg - xseg0) * 16 + sub * 2];
+                        const uint4 xb = xcur[j * xstr + (seg - xseg0) * 16 + sub * 2 + 1];
                         float d = dot2(wb[0], xa.x, 0.0f);
                         d = dot2(wb[1], xa.y, d);
                         d = dot2(wb[2], xa.z, d);
@@ -185,7 +197,53 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
             }
         };
 
-        if constexpr (NCH > 0) {
+        if constexpr (XW) {
+            constexpr int XC = CH * 16;              // uint4 of one slot's x per chunk
+            constexpr int XB = ST * XC;              // uint4 per buffer
+            constexpr int XR = (XB + kThreads - 1) / kThreads;
+            moe::u32x4 xr[XR];                       // (native vectors stay in VGPRs)
+            auto load_x = [&](int c) {
+#pragma unroll
+                for (int i = 0; i < XR; ++i) {
+                    // past the pass's last uint4 a lane reloads that one (never stored)
+                    const int f = min(tid + i * kThreads, nt * XC - 1);
+                    const int j = f / XC, r = f - j * XC;
+                    xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H +
+                                                                  (size_t)(c * XC + r) * 8);
+                }
+            };
+            auto store_x = [&](int c) {
+                moe::u32x4 *buf = reinterpret_cast<moe::u32x4 *>(xl) + (c & 1) * XB;
+#pragma unroll
+                for (int i = 0; i < XR; ++i) {
+                    const int f = tid + i * kThreads;
+                    if (f < nt * XC) buf[f] = xr[i];
+                }
+            };
+            uint4 w[3][CH];
+            xstr = XC;
+            load_x(0);
+            load_w(w[0], 0);
+            if (NCH > 1) load_w(w[1], 1);
+            store_x(0);
+            moe::lds_barrier();
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                // x of chunk c+1 before the weights of c+2, so the wait for the x
+                // leaves those weight loads in flight
+                if (c + 1 < NCH) load_x(c + 1);
+                if (c + 2 < NCH) load_w(w[(c + 2) % 3], c + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                xcur = xl + (c & 1) * XB;
+                xseg0 = c * CH;
+                mul_chunk(w[c % 3], c);
+                __builtin_amdgcn_sched_barrier(0);
+                if (c + 1 < NCH) {
+                    store_x(c + 1);
+                    moe::lds_barrier();
+                }
+            }
+        } else if constexpr (NCH > 0) {
             constexpr int H8C = NCH * CH * 16;       // uint4 per x row (H8)
             constexpr int XV = (ST * H8C + kThreads - 1) / kThreads;
             uint4 w[3][CH];
@@ -282,7 +340,7 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
 // pack launched before: every block works out its own expert; block 0 also
 // builds the whole route and writes the tables for the down and combine
 // launches that follow.
-template <int CH, int NCH, int ST, bool ROUTE>
+template <int CH, int NCH, int ST, bool ROUTE, bool XW = false>
 __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArgs a)
 {
     extern __shared__ uint4 xl[];                    // [a.st][H / 8] bf16 x rows, K order
@@ -299,8 +357,8 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
             tokl[__popcll(lr.mask & ((1ull << threadIdx.x) - 1))] = (int)threadIdx.x / a.k;
         moe::lds_barrier();
         if (lr.e >= 0)
-            gateup_e4m3_item<CH, NCH, ST>(a, moe::uniform(lr.e), tile, moe::uniform(lr.p0),
-                                          moe::uniform(lr.ne), tokl, xl, ush);
+            gateup_e4m3_item<CH, NCH, ST, false, XW>(a, moe::uniform(lr.e), tile, moe::uniform(lr.p0),
+                                                     moe::uniform(lr.ne), tokl, xl, ush);
         if (blockIdx.x == 0) {
             __shared__ FusedRoute R;
             const int id_in = (int)threadIdx.x < a.M * a.k ? a.ids[threadIdx.x] : -1;
@@ -313,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
         if (e < 0) return;
         const int p0 = moe::uniform(a.offsets[e]);
         const int ne = moe::uniform(a.offsets[e + 1]) - p0;
-        gateup_e4m3_item<CH, NCH, ST>(a, e, tile, p0, ne, a.sorted_token + p0, xl, ush);
+        gateup_e4m3_item<CH, NCH, ST, false, XW>(a, e, tile, p0, ne, a.sorted_token + p0, xl, ush);
     }
 }
 
@@ -784,9 +842,24 @@ bool gateup_launch_unrolled(const GateUpArgs &a, int nch, int grid, hipStream_t 
     }
 }
 
+// More slots than whole x rows fit (the pages' verify shape, hidden 7168 =
+// 14 chunks of 512): one pass of up to MOE_E4M3_GU_ST slots, x staged per
+// chunk (XW).  False for other shapes.
+template <bool ROUTE>
+bool gateup_launch_xw(const GateUpArgs &a, int grid, hipStream_t st)
+{
+    if (a.H != 7168) return false;
+    const size_t lds = 2 * (size_t)MOE_E4M3_GU_ST * 4 * 16 * sizeof(uint4);
+    hipLaunchKernelGGL((gemv_gateup_e4m3_kernel<4, 14, MOE_E4M3_GU_ST, ROUTE, true>), dim3(grid),
+                       dim3(kThreads), lds, st, a);
+    return true;
+}
+
 template <bool ROUTE>
 void gateup_dispatch(const GateUpArgs &a, int grid, hipStream_t st)
 {
+    if (a.st > gemv_gateup_pass_slots(a.st, a.H, MOE_E4M3_GU_ST) && gateup_launch_xw<ROUTE>(a, grid, st))
+        return;
     const int ch = gemv_chunk_segs(kFmtE4M3, a.H), nch = a.H / 128 / ch;
     bool done = false;
     if (ch == 8) {
@@ -840,7 +913,11 @@ hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &u
                                    hipStream_t st, const int32_t *route_ids, int32_t top_k)
 {
     GateUpArgs a{};
+    // whole x rows of as many slots as fit the tile; the chunk-staged form
+    // takes every slot of an expert (up to the cap) where it is built
     a.st = gemv_gateup_pass_slots(M, hidden, MOE_E4M3_GU_ST);
+    if (a.st < (M < MOE_E4M3_GU_ST ? M : MOE_E4M3_GU_ST) && hidden == 7168)
+        a.st = M < MOE_E4M3_GU_ST ? M : MOE_E4M3_GU_ST;
     a.gcodes = gate.codes; a.ucodes = up.codes;
     a.gscales = (const float *)gate.scales; a.uscales = (const float *)up.scales;
     a.x = x; a.offsets = r.offsets; a.sorted_token = r.sorted_token; a.active = r.active;
