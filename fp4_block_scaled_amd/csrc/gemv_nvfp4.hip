@@ -128,9 +128,15 @@ __device__ __forceinline__ void route_tables_block0(const Args &a, Route &R)
     fused_route_tables(a, R);
 }
 
-template <int CH, int NCH, int ST, bool ROUTE>
+// XW (unrolled form, more slots than whole x rows fit): the x rows of the
+// pass go to LDS one K chunk at a time into two buffers ([2][ST][CH * 32]
+// uint4, permuted per segment as above), chunk c+1's loaded into VGPRs while
+// chunk c is multiplied, so one weight pass serves every slot of the expert
+// (up to ST); the scale rows follow the two buffers.
+template <int CH, int NCH, int ST, bool ROUTE, bool XW = false>
 __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpArgs a)
 {
+    static_assert(!XW || NCH > 0, "chunked x staging is an unrolled form");
     extern __shared__ uint4 xl[];                    // [a.st][H / 8], permuted per segment
     __shared__ float ush[ST][16];
     __shared__ typename std::conditional<ROUTE, FusedRoute, NoRoute>::type R;
@@ -182,7 +188,10 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     // load per segment.
     constexpr bool kScLds = NCH > 0;
     const int srow = rows + 16;
-    uint8_t *scl = reinterpret_cast<uint8_t *>(xl) + (size_t)a.st * H * 2 + wave * 8 * srow;
+    constexpr int XC = CH * 32;                      // XW: uint4 of one slot's x per chunk
+    constexpr int XB = ST * XC;                      // XW: uint4 per buffer
+    const size_t xbytes = XW ? 2 * (size_t)XB * 16 : (size_t)a.st * H * 2;
+    uint8_t *scl = reinterpret_cast<uint8_t *>(xl) + xbytes + wave * 8 * srow;
 
     for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
         const int nt = min(a.st, ne - s0);
@@ -200,6 +209,9 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
         float acc[ST];
 #pragma unroll
         for (int j = 0; j < ST; ++j) acc[j] = 0.0f;
+        // x tile as mul_chunk reads it: base, row stride (uint4), first segment
+        const uint4 *xcur = xl;
+        int xstr = H8, xseg0 = 0;
         auto mul_chunk = [&](const uint4 (&wc)[CH], const uint32_t (&vc)[CH], int c) {
 #pragma unroll
             for (int sg = 0; sg < CH; ++sg) {
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
 #pragma unroll
                 for (int j = 0; j < ST; ++j) {
                     if (j < nt) {
-                        const uint4 *xv = &xl[j * H8 + seg * 32 + sub];
+                        const uint4 *xv = &xcur[j * xstr + (seg - xseg0) * 32 + sub];
                         float d0 = dot8_fp4_bf16(wv.x, xv[0], 0.0f);
                         d0 = dot8_fp4_bf16(wv.y, xv[8], d0);
                         float d1 = dot8_fp4_bf16(wv.z, xv[16], 0.0f);
@@ -242,7 +254,27 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
                 const int o = min(lane * 16 + i * 1024, 8 * SRB - 16);
                 sr[i] = moe::load_nt_global<moe::u32x4>(sbp + o);
             }
-            if constexpr (XV <= 4) {
+            if constexpr (XW) {
+                // the first chunk's x rows (the rest go chunk by chunk below)
+                xstr = XC;
+                moe::u32x4 xr[(XB + kThreads - 1) / kThreads];
+#pragma unroll
+                for (int i = 0; i < (XB + kThreads - 1) / kThreads; ++i) {
+                    const int f = min(tid + i * kThreads, nt * XC - 1);
+                    const int j = f / XC, r = f - j * XC;
+                    xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H + (size_t)r * 8);
+                }
+                load_w(w[0], v[0], 0);
+#pragma unroll
+                for (int i = 0; i < (XB + kThreads - 1) / kThreads; ++i) {
+                    const int f = tid + i * kThreads;
+                    if (f < nt * XC) {
+                        const int j = f / XC, r = f - j * XC;
+                        const int sg = r >> 5, rr = r & 31;
+                        reinterpret_cast<moe::u32x4 *>(xl)[j * XC + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = xr[i];
+                    }
+                }
+            } else if constexpr (XV <= 4) {
                 // x rows to LDS: every x load goes out at once, then the first
                 // weight chunk; the LDS stores wait for the x loads only
                 moe::u32x4 xr[XV];                   // (native vectors stay in VGPRs)
@@ -286,12 +318,50 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
             }
             if (NCH > 1) load_w(w[1], v[1], 1);
             moe::lds_barrier();
+            if constexpr (XW) {
+                constexpr int XR = (XB + kThreads - 1) / kThreads;
+                moe::u32x4 xr[XR];
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                if (c + 2 < NCH) load_w(w[(c + 2) % 3], v[(c + 2) % 3], c + 2);
-                __builtin_amdgcn_sched_barrier(0);
-                mul_chunk(w[c % 3], v[c % 3], c);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int c = 0; c < NCH; ++c) {
+                    // x of chunk c+1 before the weights of c+2, so the wait for the
+                    // x leaves those weight loads in flight
+                    if (c + 1 < NCH) {
+#pragma unroll
+                        for (int i = 0; i < XR; ++i) {
+                            const int f = min(tid + i * kThreads, nt * XC - 1);
+                            const int j = f / XC, r = f - j * XC;
+                            xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H +
+                                                                          (size_t)((c + 1) * XC + r) * 8);
+                        }
+                    }
+                    if (c + 2 < NCH) load_w(w[(c + 2) % 3], v[(c + 2) % 3], c + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    xcur = xl + (c & 1) * XB;
+                    xseg0 = c * CH;
+                    mul_chunk(w[c % 3], v[c % 3], c);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (c + 1 < NCH) {
+                        moe::u32x4 *buf = reinterpret_cast<moe::u32x4 *>(xl) + ((c + 1) & 1) * XB;
+#pragma unroll
+                        for (int i = 0; i < XR; ++i) {
+                            const int f = tid + i * kThreads;
+                            if (f < nt * XC) {
+                                const int j = f / XC, r = f - j * XC;
+                                const int sg = r >> 5, rr = r & 31;
+                                buf[j * XC + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = xr[i];
+                            }
+                        }
+                        moe::lds_barrier();
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    if (c + 2 < NCH) load_w(w[(c + 2) % 3], v[(c + 2) % 3], c + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mul_chunk(w[c % 3], v[c % 3], c);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         } else {
             for (int f = tid; f < nt * H8; f += kThreads) {
@@ -762,9 +832,25 @@ bool gateup_launch_unrolled(const GateUpArgs &a, int nch, int grid, hipStream_t 
     }
 }
 
+// More slots than whole x rows fit (the pages' NVFP4 shape, hidden 6144 = 6
+// chunks of 1024): one pass of up to kGUXW slots, x staged per chunk (XW).
+// False for other shapes.
+constexpr int kGUXW = 6;
+template <bool ROUTE>
+bool gateup_launch_xw(const GateUpArgs &a, int grid, hipStream_t st)
+{
+    if (a.H != 6144) return false;
+    const size_t lds = 2 * (size_t)kGUXW * 4 * 32 * sizeof(uint4) + 32 * (size_t)(a.H / 16 + 16);
+    hipLaunchKernelGGL((gemv_gateup_nvfp4_kernel<4, 6, kGUXW, ROUTE, true>), dim3(grid), dim3(kThreads),
+                       lds, st, a);
+    return true;
+}
+
 template <bool ROUTE>
 void gateup_dispatch(const GateUpArgs &a, int grid, hipStream_t st)
 {
+    if (a.st > gemv_gateup_pass_slots(a.st, a.H, kGUST) && a.st <= kGUXW && gateup_launch_xw<ROUTE>(a, grid, st))
+        return;
     const int ch = gemv_chunk_segs(kFmtNVFP4, a.H), nch = a.H / kSegK / ch;
     bool done = false;
     if (ch == 4) {
@@ -816,7 +902,10 @@ hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &
                                     hipStream_t st, const int32_t *route_ids, int32_t top_k)
 {
     GateUpArgs a{};
+    // whole x rows of as many slots as fit the tile; the chunk-staged form
+    // takes up to kGUXW slots of an expert in one pass where it is built
     a.st = gemv_gateup_pass_slots(M, hidden, kGUST);
+    if (a.st < (M < kGUXW ? M : kGUXW) && hidden == 6144) a.st = M < kGUXW ? M : kGUXW;
     a.gcodes = gate.codes; a.ucodes = up.codes;
     a.gscales = (const uint8_t *)gate.scales; a.uscales = (const uint8_t *)up.scales;
     a.gscale2 = gate.scale2; a.uscale2 = up.scale2;
