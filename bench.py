@@ -370,7 +370,7 @@ TRAFFIC = {
     "verify_e4m3_m8": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
         "src": "c64d246dd8540965d610978b517a952ce0174e2455c8b818", "fetch_kib": 646010, "write_kib": 514},
     "nvfp4_m16": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "cd6fb700362c8c12d610978b517a952ce0174e2455c8b818", "fetch_kib": 487615, "write_kib": 768},
+        "src": "21e41ef7cc964132d610978b517a952ce0174e2455c8b818", "fetch_kib": 444745, "write_kib": 768},
 }
 
 

@@ -62,6 +62,17 @@ struct DownArgs {
     int32_t H, I, ntiles, st;           // st: slots per weight pass (<= ST)
 };
 
+// Down projection and combine of one token (gemv_down1_e4m3_kernel).
+struct Down1Args {
+    const uint8_t *codes;
+    const float *scales;
+    const float *h;                     // [S][I]
+    const int32_t *ids, *t2p;           // [k]: the token's expert ids and packed rows (-1: none)
+    const float *w;                     // [k]: its top-k weights
+    float *y, *out;                     // y [S][H] packed rows, out [H]
+    int32_t H, k;
+};
+
 // Weights are streamed once per call: non-temporal loads keep them from
 // displacing the activations and partial sums in the caches.
 __device__ __forceinline__ uint4 load16(const uint8_t *p)
@@ -578,6 +589,140 @@ __global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kern
 }
 
 // ---------------------------------------------------------------------------
+// down + combine of one token
+// ---------------------------------------------------------------------------
+// With one token the layer's k <= 8 slots all feed the same output row, so
+// the down projection and the combine run in one launch without any hand-off
+// between blocks: a block owns 8*RG output rows for EVERY slot.  Wave j
+// streams those rows of slot j's expert (8 lanes per row as in the down
+// item, the same products in the same order: y is bit-identical) against
+// slot j's h row, which it stages in an LDS region of its own; the block then
+// sums the slots' rows of its tile in slot order, each product rounded before
+// its add (the combine's arithmetic), and writes the output rows.
+template <int CH, int NCH, int RG>
+__global__ __launch_bounds__(512, RG <= 2 ? 4 : 2) void gemv_down1_e4m3_kernel(Down1Args a)
+{
+    extern __shared__ float4 hl[];                   // [8][I/4] h rows, [8][8*RG] row sums, slot table
+    constexpr int ROWS = 8 * RG;
+    constexpr int I4 = NCH * CH * 32, I = I4 * 4;    // float4 per h row, K
+    constexpr int NSEG = I / 128, HV = I4 / 64;      // 128-wide segments; h float4 per lane
+    static_assert(I4 % 64 == 0 && NSEG <= 128, "K must be a multiple of 256 up to 16384");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int j = moe::uniform(tid >> 6);            // this wave's slot
+    const int grp = lane >> 3, sub = lane & 7;
+    const int H = a.H, row0 = blockIdx.x * ROWS;
+    float *sums = reinterpret_cast<float *>(hl + 8 * I4);
+    // the combine's slot table (packed row, weight) goes out first; its
+    // lanes store it in LDS once their rows are done
+    const int pc = tid < a.k ? a.t2p[tid] : -1;
+    const float wc = tid < a.k ? a.w[tid] : 0.0f;
+    const int p = j < a.k ? moe::uniform(a.t2p[j]) : -1;   // packed row; -1: no slot
+    const int e = j < a.k ? moe::uniform(a.ids[j]) : 0;     // (loaded beside p, not after it)
+    const bool live = p >= 0;
+    moe::f32x4 *hw = reinterpret_cast<moe::f32x4 *>(hl + j * I4);
+    const uint8_t *wb = moe::uniform_ptr(a.codes + ((size_t)e * H + row0) * I);
+    uint32_t lo = (uint32_t)grp * I + sub * 16;
+    asm volatile("" : "+s"(wb), "+v"(lo));
+    auto load_w = [&](uint4 (&wc)[RG][CH], int c) {
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int sg = 0; sg < CH; ++sg)
+                wc[g][sg] = load16(wb + g * 8 * I + (c * CH + sg) * 128 + lo);
+    };
+    if (live) {
+        // h row loads, then the first weight chunk, then the h stores
+        uint4 w[3][RG][CH];
+        moe::f32x4 hr[HV];
+#pragma unroll
+        for (int i = 0; i < HV; ++i)
+            hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)p * I + (lane + i * 64) * 4);
+        const float *scb = a.scales + ((size_t)e * (H >> 7) + (row0 >> 7)) * NSEG;
+        const float sc_lo = lane < NSEG ? scb[lane] : 0.0f;
+        const float sc_hi = lane + 64 < NSEG ? scb[lane + 64] : 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(w[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < HV; ++i) {
+            const int r = lane + i * 64, sg = r >> 5, rr = r & 31;
+            hw[sg * 32 + (rr & 3) * 8 + (rr >> 2)] = hr[i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (NCH > 1) load_w(w[1], 1);
+        // the h region is this wave's own: a wave-level barrier orders its
+        // LDS stores before the reads of the other lanes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float acc[RG];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) acc[g] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (c + 2 < NCH) load_w(w[(c + 2) % 3], c + 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sg = 0; sg < CH; ++sg) {
+                const int seg = c * CH + sg;
+                const float s = seg < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, sc_lo), seg))
+                                         : __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, sc_hi), seg - 64));
+                float d[RG];
+#pragma unroll
+                for (int g = 0; g < RG; ++g) d[g] = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const moe::f32x4 hv = hw[seg * 32 + q * 8 + sub];
+#pragma unroll
+                    for (int g = 0; g < RG; ++g) {
+                        const uint4 wv = w[c % 3][g][sg];
+                        const uint32_t dw = q == 0 ? wv.x : q == 1 ? wv.y : q == 2 ? wv.z : wv.w;
+                        const f32x2 w01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw, false);
+                        const f32x2 w23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw, true);
+                        d[g] = fmaf(w01.x, hv.x, d[g]);
+                        d[g] = fmaf(w01.y, hv.y, d[g]);
+                        d[g] = fmaf(w23.x, hv.z, d[g]);
+                        d[g] = fmaf(w23.y, hv.w, d[g]);
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    acc[g] = fmaf(d[g], s, acc[g]);
+                    // (pins the row groups' sums here: left alone, the
+                    // compiler sinks the later groups' products to the end of
+                    // the loop and keeps every h value live until then)
+                    asm volatile("" : "+v"(acc[g]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const float v = moe::sum8_lanes(acc[g]);
+            if (sub == 0) {
+                a.y[(size_t)p * H + row0 + g * 8 + grp] = v;
+                sums[j * ROWS + g * 8 + grp] = v;
+            }
+        }
+    }
+    int *cp = reinterpret_cast<int *>(sums + 8 * ROWS);
+    float *cw = reinterpret_cast<float *>(cp + 8);
+    if (tid < 8) {
+        cp[tid] = pc;
+        cw[tid] = wc;
+    }
+    moe::lds_barrier();
+    if (tid < ROWS) {
+        float o = 0.0f;
+        for (int jj = 0; jj < a.k; ++jj)
+            if (cp[jj] >= 0) o = __fadd_rn(o, __fmul_rn(cw[jj], sums[jj * ROWS + tid]));
+        a.out[row0 + tid] = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fused decode layer: route pack, gate/up + SwiGLU, down and combine in one launch
 // ---------------------------------------------------------------------------
 // The route, flags, waits and launch are in fused_common.h; the items below
@@ -905,6 +1050,14 @@ bool down_launch_unrolled(const DownArgs &a, int nch, int grid, hipStream_t st)
     }
 }
 
+template <int CH, int NCH, int RG>
+void down1_launch(const Down1Args &a, hipStream_t st)
+{
+    constexpr int I = NCH * CH * 128;
+    hipLaunchKernelGGL((gemv_down1_e4m3_kernel<CH, NCH, RG>), dim3(a.H / (8 * RG)), dim3(512),
+                       (size_t)8 * I * 4 + 8 * 8 * RG * 4 + 64, st, a);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
@@ -959,6 +1112,25 @@ hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const 
         case 2: down_launch<2, 0, MOE_E4M3_DN_ST>(a, grid, st); break;
         default: down_launch<1, 0, MOE_E4M3_DN_ST>(a, grid, st); break;
         }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_down1_e4m3(const GemvBankDev &down, const float *h, const int32_t *ids,
+                                  const int32_t *t2p, const float *w, int32_t k, int32_t hidden,
+                                  int32_t inter, float *y, float *out, hipStream_t st)
+{
+    if (!gemv_down1_fits(kFmtE4M3, 1, k, hidden, inter)) return hipErrorInvalidValue;
+    Down1Args a;
+    a.codes = down.codes; a.scales = (const float *)down.scales; a.h = h;
+    a.ids = ids; a.t2p = t2p; a.w = w; a.y = y; a.out = out;
+    a.H = hidden; a.k = k;
+    switch (inter / 512) {
+    case 1: down1_launch<4, 1, 2>(a, st); break;
+    case 2: down1_launch<4, 2, 2>(a, st); break;
+    case 3: down1_launch<4, 3, 2>(a, st); break;
+    case 4: down1_launch<4, 4, 2>(a, st); break;
+    default: down1_launch<4, 5, 2>(a, st); break;
     }
     return hipGetLastError();
 }

@@ -50,6 +50,17 @@ struct DownArgs {
     int32_t H, I, ntiles, st;           // st: slots per weight pass (<= ST)
 };
 
+// Down projection and combine of one token (gemv_down1_nvfp4_kernel).
+struct Down1Args {
+    const uint8_t *codes, *scales;
+    const float *scale2;
+    const float *h;                     // [S][I]
+    const int32_t *ids, *t2p;           // [k]: the token's expert ids and packed rows (-1: none)
+    const float *w;                     // [k]: its top-k weights
+    float *y, *out;                     // y [S][H] packed rows, out [H]
+    int32_t H, k;
+};
+
 // Codes and group scales are streamed once per call (non-temporal loads).
 __device__ __forceinline__ uint4 load16(const uint8_t *p)
 {
@@ -628,6 +639,156 @@ __global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// down + combine of one token
+// ---------------------------------------------------------------------------
+// As the E4M3 kernel of the same name: a block owns 8*RG output rows for
+// every one of the token's k <= 8 slots, wave j streams those rows of slot
+// j's expert (codes from HBM; its h row and its rows' group scales staged in
+// an LDS region of its own) with the down item's products in the down item's
+// order, and the block adds the slots' rows in slot order.
+template <int CH, int NCH, int RG>
+__global__ __launch_bounds__(512, 4) void gemv_down1_nvfp4_kernel(Down1Args a)
+{
+    extern __shared__ float4 hl[];                   // per wave: h row, scale rows; row sums, slot table
+    constexpr int ROWS = 8 * RG;
+    constexpr int I4 = NCH * CH * 64, I = I4 * 4;    // float4 per h row, K
+    constexpr int HV = I4 / 64;                      // h float4 per lane
+    constexpr int RB = I / 2, SB = I / 16;           // code and scale bytes per row
+    constexpr int SROW = SB + 16;                    // LDS scale row (padded)
+    constexpr int SV = (ROWS * SB + 1023) / 1024;    // 16-byte scale loads per lane
+    constexpr int WL = I * 4 + ROWS * SROW;          // LDS bytes per wave
+    static_assert(WL % 16 == 0, "wave regions stay 16-byte aligned");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int j = moe::uniform(tid >> 6);            // this wave's slot
+    const int grp = lane >> 3, sub = lane & 7;
+    const int H = a.H, row0 = blockIdx.x * ROWS;
+    uint8_t *wl = reinterpret_cast<uint8_t *>(hl) + j * WL;
+    moe::f32x4 *hw = reinterpret_cast<moe::f32x4 *>(wl);
+    uint8_t *scl = wl + I * 4;
+    float *sums = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(hl) + 8 * WL);
+    // the combine's slot table (packed row, weight) goes out first; its
+    // lanes store it in LDS once their rows are done
+    const int pc = tid < a.k ? a.t2p[tid] : -1;
+    const float wc = tid < a.k ? a.w[tid] : 0.0f;
+    const int p = j < a.k ? moe::uniform(a.t2p[j]) : -1;   // packed row; -1: no slot
+    const int e = j < a.k ? moe::uniform(a.ids[j]) : 0;     // (loaded beside p, not after it)
+    if (p >= 0) {
+        const size_t r0 = (size_t)e * H + row0;
+        const uint8_t *cb = moe::uniform_ptr(a.codes + r0 * RB);
+        const uint8_t *sb = moe::uniform_ptr(a.scales + r0 * SB);
+        uint32_t co = (uint32_t)grp * RB + sub * 16;
+        asm volatile("" : "+s"(cb), "+v"(co));
+        auto load_w = [&](uint4 (&wc)[RG][CH], int c) {
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+#pragma unroll
+                for (int sg = 0; sg < CH; ++sg)
+                    wc[g][sg] = load16(cb + g * 8 * RB + (c * CH + sg) * 128 + co);
+        };
+        // scale rows and h row loads, then the first weight chunk, then the
+        // LDS stores
+        uint4 w[3][RG][CH];
+        moe::u32x4 sr[SV];
+#pragma unroll
+        for (int i = 0; i < SV; ++i) {
+            // past the rows' last 16 bytes a lane reloads those (never stored)
+            const int o = min(lane * 16 + i * 1024, ROWS * SB - 16);
+            sr[i] = moe::load_nt_global<moe::u32x4>(sb + o);
+        }
+        moe::f32x4 hr[HV];
+#pragma unroll
+        for (int i = 0; i < HV; ++i)
+            hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)p * I + (lane + i * 64) * 4);
+        const float s2 = a.scale2[e];
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(w[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < HV; ++i) {
+            const int r = lane + i * 64, sg = r >> 6, rr = r & 63;
+            hw[sg * 64 + (rr & 7) * 8 + (rr >> 3)] = hr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < SV; ++i) {
+            const int o = lane * 16 + i * 1024;
+            if (o < ROWS * SB) {
+                const int r = o / SB, cc = o - r * SB;
+                *reinterpret_cast<moe::u32x4 *>(scl + r * SROW + cc) = sr[i];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (NCH > 1) load_w(w[1], 1);
+        // the LDS region is this wave's own: a wave-level barrier orders its
+        // stores before the reads of the other lanes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float acc[RG];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) acc[g] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (c + 2 < NCH) load_w(w[(c + 2) % 3], c + 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sg = 0; sg < CH; ++sg) {
+                const int seg = c * CH + sg;
+                const float4 *hv = reinterpret_cast<const float4 *>(hw) + seg * 64 + sub;
+                // each pair of h float4 serves every row group
+                float d0[RG], d1[RG];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 ha = hv[q * 16], hb = hv[q * 16 + 8];
+#pragma unroll
+                    for (int g = 0; g < RG; ++g) {
+                        const uint4 wv = w[c % 3][g][sg];
+                        const uint32_t dw = q == 0 ? wv.x : q == 1 ? wv.y : q == 2 ? wv.z : wv.w;
+                        if (q == 0) d0[g] = dot8_fp4_f32(dw, ha, hb, 0.0f);
+                        else if (q == 1) d0[g] = dot8_fp4_f32(dw, ha, hb, d0[g]);
+                        else if (q == 2) d1[g] = dot8_fp4_f32(dw, ha, hb, 0.0f);
+                        else d1[g] = dot8_fp4_f32(dw, ha, hb, d1[g]);
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    const uint32_t vs =
+                        *reinterpret_cast<const uint16_t *>(scl + (g * 8 + grp) * SROW + seg * 16 + sub * 2);
+                    const f32x2 sc = __builtin_amdgcn_cvt_pk_f32_fp8((int)vs, false);
+                    acc[g] = fmaf(d0[g], sc.x, acc[g]);
+                    acc[g] = fmaf(d1[g], sc.y, acc[g]);
+                    // (pins each row group's sum here, so the compiler does
+                    // not sink the later groups' products to the end of the
+                    // loop and keep every h value live until then)
+                    asm volatile("" : "+v"(acc[g]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const float v = moe::sum8_lanes(acc[g]) * s2;
+            if (sub == 0) {
+                a.y[(size_t)p * H + row0 + g * 8 + grp] = v;
+                sums[j * ROWS + g * 8 + grp] = v;
+            }
+        }
+    }
+    int *cp = reinterpret_cast<int *>(sums + 8 * ROWS);
+    float *cw = reinterpret_cast<float *>(cp + 8);
+    if (tid < 8) {
+        cp[tid] = pc;
+        cw[tid] = wc;
+    }
+    moe::lds_barrier();
+    if (tid < ROWS) {
+        float o = 0.0f;
+        for (int jj = 0; jj < a.k; ++jj)
+            if (cp[jj] >= 0) o = __fadd_rn(o, __fmul_rn(cw[jj], sums[jj * ROWS + tid]));
+        a.out[row0 + tid] = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fused decode layer for one token (M == 1), NVFP4 banks
 // ---------------------------------------------------------------------------
 // The one-launch layer of fused_common.h with gate/up items of 2 h rows: wave
@@ -894,6 +1055,15 @@ bool down_launch_unrolled(const DownArgs &a, int nch, int grid, hipStream_t st)
     }
 }
 
+template <int CH, int NCH, int RG>
+void down1_launch(const Down1Args &a, hipStream_t st)
+{
+    constexpr int I = NCH * CH * 256, ROWS = 8 * RG;
+    constexpr size_t lds = 8 * ((size_t)I * 4 + ROWS * (I / 16 + 16)) + 8 * ROWS * 4 + 64;
+    hipLaunchKernelGGL((gemv_down1_nvfp4_kernel<CH, NCH, RG>), dim3(a.H / ROWS), dim3(512), lds, st,
+                       a);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
@@ -944,6 +1114,24 @@ hipError_t launch_gemv_down_nvfp4(const GemvBankDev &down, const float *h, const
     if (!done) {
         if (ch == 2) down_launch<2, 0, kDNST>(a, grid, st);
         else down_launch<1, 0, kDNST>(a, grid, st);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_down1_nvfp4(const GemvBankDev &down, const float *h, const int32_t *ids,
+                                   const int32_t *t2p, const float *w, int32_t k, int32_t hidden,
+                                   int32_t inter, float *y, float *out, hipStream_t st)
+{
+    if (!gemv_down1_fits(kFmtNVFP4, 1, k, hidden, inter)) return hipErrorInvalidValue;
+    Down1Args a;
+    a.codes = down.codes; a.scales = (const uint8_t *)down.scales; a.scale2 = down.scale2;
+    a.h = h; a.ids = ids; a.t2p = t2p; a.w = w; a.y = y; a.out = out;
+    a.H = hidden; a.k = k;
+    switch (inter / 512) {
+    case 1: down1_launch<2, 1, 2>(a, st); break;
+    case 2: down1_launch<2, 2, 2>(a, st); break;
+    case 3: down1_launch<2, 3, 2>(a, st); break;
+    default: down1_launch<2, 4, 2>(a, st); break;
     }
     return hipGetLastError();
 }

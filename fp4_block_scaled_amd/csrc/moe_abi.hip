@@ -303,12 +303,18 @@ static moe_status_t check_bank(const char *fn, const moe_bank_t *b, const char *
 
 // The expert FFN of moe_expert_ffn.  With route_ids, the route tables of
 // `route` (carved, not yet filled) are built by the gate/up launch itself
-// from the ids: only for the GEMV tier and S <= 64.
+// from the ids: only for the GEMV tier and S <= 64.  With comb_out as well
+// (moe_layer), one token whose shape gemv_down1_fits accepts gets the down
+// projection and the combine in one launch (out = comb_out, weights comb_w),
+// and *combined says so; otherwise the caller runs the combine.
 static moe_status_t expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, const moe_bank_t *down,
                                const uint16_t *x_bf16, const moe_route_t *route, int32_t hidden,
                                int32_t inter, float limit, int32_t mode, float *y_packed, void *ws,
-                               size_t ws_bytes, void *stream, const int32_t *route_ids)
+                               size_t ws_bytes, void *stream, const int32_t *route_ids,
+                               const float *comb_w = nullptr, float *comb_out = nullptr,
+                               bool *combined = nullptr)
 {
+    if (combined) *combined = false;
     if (!gate || !up || !down || !x_bf16 || !route || !y_packed || !ws)
         return fail(MOE_ERR_ARG, "moe_expert_ffn: null pointer");
     const int32_t fmt = gate->fmt;
@@ -410,6 +416,19 @@ static moe_status_t expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, con
                                      route_ids, k);
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: gate/up GEMV launch");
     stage_mark(1, s);
+    const int kfmt = fmt == MOE_W_E4M3_B128 ? kFmtE4M3 : kFmtNVFP4;
+    if (route_ids && comb_w && comb_out && gemv_down1_fits(kfmt, M, k, hidden, inter)) {
+        if (fmt == MOE_W_E4M3_B128)
+            e = launch_gemv_down1_e4m3(bd, h, route_ids, r.token_to_perm, comb_w, k, hidden, inter,
+                                       y_packed, comb_out, s);
+        else
+            e = launch_gemv_down1_nvfp4(bd, h, route_ids, r.token_to_perm, comb_w, k, hidden, inter,
+                                        y_packed, comb_out, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_layer: down + combine GEMV launch");
+        *combined = true;
+        stage_mark(2, s);
+        return MOE_OK;
+    }
     if (fmt == MOE_W_E4M3_B128)
         e = launch_gemv_down_e4m3(bd, h, r, M, (int32_t)S, E, hidden, inter, y_packed, s);
     else
@@ -453,8 +472,11 @@ moe_status_t moe_layer(const moe_bank_t *gate, const moe_bank_t *up, const moe_b
                         moe::route_region_bytes(S, E));
         if (((uintptr_t)ws & 255) != 0) return fail(MOE_ERR_ARG, "%s: ws not 256-byte aligned", fn);
         carve_route(ws, M, top_k, E, route);
+        bool combined = false;
         st = expert_ffn(gate, up, down, x_bf16, route, hidden, inter, limit, mode, y_packed, ws,
-                        ws_bytes, stream, topk_ids);
+                        ws_bytes, stream, topk_ids, topk_weights, aligned16(out) ? out : nullptr,
+                        &combined);
+        if (st != MOE_OK || combined) return st;
     } else {
         st = moe_route_pack(topk_ids, M, top_k, E, ws, ws_bytes, route, stream);
         if (st == MOE_OK)

@@ -186,3 +186,20 @@ inline int gemv_down_chunk_segs(int fmt, int inter)
 {
     return gemv_pick_segs(inter / gemv_seg_k(fmt), fmt == kFmtNVFP4 ? 2 : 4);
 }
+
+// Down projection and combine of one token in one launch (M == 1): y rows as
+// launch_gemv_down_*, and out[hidden] = the slots' y rows weighted by w and
+// added in slot order (the combine's arithmetic).  t2p [k]: the packed row
+// of each slot, -1 for none; ids [k]: the slots' experts.  For the shapes
+// gemv_down1_fits accepts (else hipErrorInvalidValue).
+inline bool gemv_down1_fits(int fmt, int M, int k, int hidden, int inter)
+{
+    if (M != 1 || k < 1 || k > 8 || hidden % 16 != 0 || inter % 512 != 0) return false;
+    return fmt == kFmtNVFP4 ? inter <= 2048 : inter <= 2560;
+}
+hipError_t launch_gemv_down1_e4m3(const GemvBankDev &down, const float *h, const int32_t *ids,
+                                  const int32_t *t2p, const float *w, int32_t k, int32_t hidden,
+                                  int32_t inter, float *y, float *out, hipStream_t st);
+hipError_t launch_gemv_down1_nvfp4(const GemvBankDev &down, const float *h, const int32_t *ids,
+                                   const int32_t *t2p, const float *w, int32_t k, int32_t hidden,
+                                   int32_t inter, float *y, float *out, hipStream_t st);

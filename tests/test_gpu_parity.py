@@ -218,6 +218,13 @@ REDUCED = [
     ("e4m3_h256_i2304", "tiny_e4m3_m1", dict(hidden=256, inter=2304, experts=4, top_k=2), [1, 5]),
     ("nvfp4_h2304_i512", "nvfp4_m1", dict(hidden=2304, inter=512, experts=8, top_k=3), [1, 16]),
     ("nvfp4_h256_i2560", "nvfp4_m1", dict(hidden=256, inter=2560, experts=4, top_k=2), [2]),
+    # one token: the down launch also does the combine, one K unrolling per
+    # inter of 512..2560 (E4M3) or 512..2048 (NVFP4)
+    ("e4m3_h384_i512", "tiny_e4m3_m1", dict(hidden=384, inter=512, experts=8, top_k=3), [1, 3]),
+    ("e4m3_h1024_i1536", "tiny_e4m3_m1", dict(hidden=1024, inter=1536, experts=12, top_k=8), [1]),
+    ("e4m3_h768_i2560", "tiny_e4m3_m1", dict(hidden=768, inter=2560, experts=4, top_k=2), [1]),
+    ("nvfp4_h512_i1024", "nvfp4_m1", dict(hidden=512, inter=1024, experts=6, top_k=5), [1, 2]),
+    ("nvfp4_h1024_i2048", "nvfp4_m1", dict(hidden=1024, inter=2048, experts=10, top_k=8), [1]),
 ]
 
 
@@ -315,6 +322,8 @@ def test_grouping_rows_never_changes_a_row():
     ("tiny_e4m3_m1", 20, B.MOE_MODE_AUTO, "some"), ("tiny_e4m3_m1", 6, B.MOE_MODE_AUTO, "all"),
     ("tiny_e4m3_m1", 5, B.MOE_MODE_AUTO, "token"), ("nvfp4_m16", 8, B.MOE_MODE_AUTO, "some"),
     ("nvfp4_m16", 16, B.MOE_MODE_AUTO, "some"),
+    ("decode_e4m3_m1", 1, B.MOE_MODE_AUTO, "slots"), ("nvfp4_m1", 1, B.MOE_MODE_AUTO, "slots"),
+    ("decode_e4m3_m1", 1, B.MOE_MODE_AUTO, "all"), ("nvfp4_m1", 1, B.MOE_MODE_AUTO, "all"),
 ])
 def test_single_call_layer_matches_three_calls(name, M, mode, invalid):
     """moe_layer (route pack inside the gate/up launch for small routes)
@@ -331,6 +340,9 @@ def test_single_call_layer_matches_three_calls(name, M, mode, invalid):
         ids[0, 0] = wl.experts
     elif invalid == "token":
         ids[2, :] = -1
+    elif invalid == "slots":
+        ids[0, 2] = -1
+        ids[0, -1] = wl.experts + 3
     elif M > 1:
         ids[1, 0] = -1
         ids[M - 1, -1] = wl.experts + 3
