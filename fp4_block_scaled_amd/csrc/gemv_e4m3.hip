@@ -86,6 +86,17 @@ __device__ __forceinline__ uint4 load16(const uint8_t *p)
 #endif
 }
 
+// The down kernels keep an FP32 h row in LDS permuted per 128-wide segment,
+// so that the 8 lanes of a weight row read 128 contiguous bytes: LDS float4
+// q*8 + sub of a segment holds the source float4 sub*4 + q (K values
+// sub*16 + q*4 .. +3).  Staging walks the LDS positions in order (each
+// 64-lane store is one contiguous 1 KB, free of bank conflicts) and loads the
+// source float4 of each position.
+__device__ __forceinline__ int h_src(int pos)
+{
+    return (pos & ~31) | ((pos & 7) << 2) | ((pos >> 3) & 3);
+}
+
 // 4 code bytes -> two bf16 pairs (bytes 0,1 and 2,3).  E4M3 values are exact
 // in bf16 (3 mantissa bits, exponent range inside bf16's).
 __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t d, bf16x2 &lo, bf16x2 &hi)
@@ -480,8 +491,7 @@ __device__ __forceinline__ void down_e4m3_item(const DownArgs &a, int e, int til
 
         auto stage_h = [&]() {
             for (int f = tid; f < nt * I4; f += kThreads) {
-                const int j = f / I4, r = f - j * I4; // r: source float4 (4 K values)
-                const int sg = r >> 5, rr = r & 31;
+                const int j = f / I4, r = h_src(f - j * I4);   // r: source float4 (4 K values)
                 const float *hp = a.h + (size_t)(p0 + s0 + j) * I + r * 4;
                 float4 hv;
                 if constexpr (FUSED) {
@@ -490,7 +500,7 @@ __device__ __forceinline__ void down_e4m3_item(const DownArgs &a, int e, int til
                 } else {
                     hv = *reinterpret_cast<const float4 *>(hp);
                 }
-                hl[j * I4 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = hv;
+                hl[f] = hv;
             }
         };
         if constexpr (NCH > 0) {
@@ -510,7 +520,7 @@ __device__ __forceinline__ void down_e4m3_item(const DownArgs &a, int e, int til
                 for (int i = 0; i < HV; ++i) {
                     // past the pass's last float4 a lane reloads that one (never stored)
                     const int f = min(tid + i * kThreads, nt * I4C - 1);
-                    const int j = f / I4C, r = f - j * I4C;
+                    const int j = f / I4C, r = h_src(f - j * I4C);
                     hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -519,11 +529,7 @@ __device__ __forceinline__ void down_e4m3_item(const DownArgs &a, int e, int til
 #pragma unroll
                 for (int i = 0; i < HV; ++i) {
                     const int f = tid + i * kThreads;
-                    if (f < nt * I4C) {
-                        const int j = f / I4C, r = f - j * I4C;
-                        const int sg = r >> 5, rr = r & 31;
-                        reinterpret_cast<moe::f32x4 *>(hl)[j * I4C + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = hr[i];
-                    }
+                    if (f < nt * I4C) reinterpret_cast<moe::f32x4 *>(hl)[f] = hr[i];
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (NCH > 1) load_w(w[1], 1);
@@ -636,7 +642,7 @@ __global__ __launch_bounds__(512, RG <= 2 ? 4 : 2) void gemv_down1_e4m3_kernel(D
         moe::f32x4 hr[HV];
 #pragma unroll
         for (int i = 0; i < HV; ++i)
-            hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)p * I + (lane + i * 64) * 4);
+            hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)p * I + h_src(lane + i * 64) * 4);
         const float *scb = a.scales + ((size_t)e * (H >> 7) + (row0 >> 7)) * NSEG;
         const float sc_lo = lane < NSEG ? scb[lane] : 0.0f;
         const float sc_hi = lane + 64 < NSEG ? scb[lane + 64] : 0.0f;
@@ -644,10 +650,7 @@ __global__ __launch_bounds__(512, RG <= 2 ? 4 : 2) void gemv_down1_e4m3_kernel(D
         load_w(w[0], 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < HV; ++i) {
-            const int r = lane + i * 64, sg = r >> 5, rr = r & 31;
-            hw[sg * 32 + (rr & 3) * 8 + (rr >> 2)] = hr[i];
-        }
+        for (int i = 0; i < HV; ++i) hw[lane + i * 64] = hr[i];
         __builtin_amdgcn_sched_barrier(0);
         if (NCH > 1) load_w(w[1], 1);
         // the h region is this wave's own: a wave-level barrier orders its

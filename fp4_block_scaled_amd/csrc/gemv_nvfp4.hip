@@ -69,6 +69,21 @@ __device__ __forceinline__ uint4 load16(const uint8_t *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Activation rows sit in LDS permuted per 256-wide segment so that the 8
+// lanes of a weight row read 128 contiguous bytes: bf16 x keeps uint4 q*8 +
+// sub of a segment for the source uint4 sub*4 + q, FP32 h keeps float4 q*8 +
+// sub for the source float4 sub*8 + q.  Staging walks the LDS positions in
+// order (each 64-lane store is one contiguous 1 KB, free of bank conflicts)
+// and loads the source element of each position.
+__device__ __forceinline__ int x_src(int pos)
+{
+    return (pos & ~31) | ((pos & 7) << 2) | ((pos >> 3) & 3);
+}
+__device__ __forceinline__ int h_src(int pos)
+{
+    return (pos & ~63) | ((pos & 7) << 3) | ((pos >> 3) & 7);
+}
+
 __device__ __forceinline__ uint32_t load2(const uint8_t *p)
 {
     return moe::load_nt_global<uint16_t>(p);
@@ -272,18 +287,14 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
 #pragma unroll
                 for (int i = 0; i < (XB + kThreads - 1) / kThreads; ++i) {
                     const int f = min(tid + i * kThreads, nt * XC - 1);
-                    const int j = f / XC, r = f - j * XC;
+                    const int j = f / XC, r = x_src(f - j * XC);
                     xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H + (size_t)r * 8);
                 }
                 load_w(w[0], v[0], 0);
 #pragma unroll
                 for (int i = 0; i < (XB + kThreads - 1) / kThreads; ++i) {
                     const int f = tid + i * kThreads;
-                    if (f < nt * XC) {
-                        const int j = f / XC, r = f - j * XC;
-                        const int sg = r >> 5, rr = r & 31;
-                        reinterpret_cast<moe::u32x4 *>(xl)[j * XC + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = xr[i];
-                    }
+                    if (f < nt * XC) reinterpret_cast<moe::u32x4 *>(xl)[f] = xr[i];
                 }
             } else if constexpr (XV <= 4) {
                 // x rows to LDS: every x load goes out at once, then the first
@@ -293,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
                 for (int i = 0; i < XV; ++i) {
                     // past the pass's last uint4 a lane reloads that one (never stored)
                     const int f = min(tid + i * kThreads, nt * H8C - 1);
-                    const int j = f / H8C, r = f - j * H8C;
+                    const int j = f / H8C, r = x_src(f - j * H8C);
                     xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -302,20 +313,14 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
 #pragma unroll
                 for (int i = 0; i < XV; ++i) {
                     const int f = tid + i * kThreads;
-                    if (f < nt * H8C) {
-                        const int j = f / H8C, r = f - j * H8C;
-                        const int sg = r >> 5, rr = r & 31;
-                        reinterpret_cast<moe::u32x4 *>(xl)[j * H8C + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = xr[i];
-                    }
+                    if (f < nt * H8C) reinterpret_cast<moe::u32x4 *>(xl)[f] = xr[i];
                 }
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 // larger passes: x rows to LDS in a loop, then the first chunk
                 for (int f = tid; f < nt * H8; f += kThreads) {
-                    const int j = f / H8, r = f - j * H8;
-                    const int sg = r >> 5, rr = r & 31;
-                    xl[j * H8 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] =
-                        *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
+                    const int j = f / H8, r = x_src(f - j * H8);
+                    xl[f] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
                 }
                 load_w(w[0], v[0], 0);
             }
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
 #pragma unroll
                         for (int i = 0; i < XR; ++i) {
                             const int f = min(tid + i * kThreads, nt * XC - 1);
-                            const int j = f / XC, r = f - j * XC;
+                            const int j = f / XC, r = x_src(f - j * XC);
                             xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H +
                                                                           (size_t)((c + 1) * XC + r) * 8);
                         }
@@ -356,11 +361,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
 #pragma unroll
                         for (int i = 0; i < XR; ++i) {
                             const int f = tid + i * kThreads;
-                            if (f < nt * XC) {
-                                const int j = f / XC, r = f - j * XC;
-                                const int sg = r >> 5, rr = r & 31;
-                                buf[j * XC + sg * 32 + (rr & 3) * 8 + (rr >> 2)] = xr[i];
-                            }
+                            if (f < nt * XC) buf[f] = xr[i];
                         }
                         moe::lds_barrier();
                     }
@@ -376,10 +377,8 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
             }
         } else {
             for (int f = tid; f < nt * H8; f += kThreads) {
-                const int j = f / H8, r = f - j * H8; // r: source uint4 (8 K values)
-                const int sg = r >> 5, rr = r & 31;
-                xl[j * H8 + sg * 32 + (rr & 3) * 8 + (rr >> 2)] =
-                    *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
+                const int j = f / H8, r = x_src(f - j * H8); // r: source uint4 (8 K values)
+                xl[f] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tok[s0 + j] * H + r * 8);
             }
             uint4 w0[CH], w1[CH];
             uint32_t v0[CH], v1[CH];
@@ -502,8 +501,7 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
         };
         auto stage_h = [&]() {
             for (int f = tid; f < nt * I4; f += kThreads) {
-                const int j = f / I4, r = f - j * I4; // r: source float4 (4 K values)
-                const int sg = r >> 6, rr = r & 63;
+                const int j = f / I4, r = h_src(f - j * I4);   // r: source float4 (4 K values)
                 const float *hp = a.h + (size_t)(p0 + s0 + j) * I + r * 4;
                 float4 hv;
                 if constexpr (FUSED) {
@@ -512,7 +510,7 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
                 } else {
                     hv = *reinterpret_cast<const float4 *>(hp);
                 }
-                hl[j * I4 + sg * 64 + (rr & 7) * 8 + (rr >> 3)] = hv;
+                hl[f] = hv;
             }
         };
 
@@ -544,7 +542,7 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
                 for (int i = 0; i < HV; ++i) {
                     // past the pass's last float4 a lane reloads that one (never stored)
                     const int f = min(tid + i * kThreads, nt * I4C - 1);
-                    const int j = f / I4C, r = f - j * I4C;
+                    const int j = f / I4C, r = h_src(f - j * I4C);
                     hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -553,11 +551,7 @@ __device__ __forceinline__ void down_nvfp4_item(const DownArgs &a, int e, int ti
 #pragma unroll
                 for (int i = 0; i < HV; ++i) {
                     const int f = tid + i * kThreads;
-                    if (f < nt * I4C) {
-                        const int j = f / I4C, r = f - j * I4C;
-                        const int sg = r >> 6, rr = r & 63;
-                        reinterpret_cast<moe::f32x4 *>(hl)[j * I4C + sg * 64 + (rr & 7) * 8 + (rr >> 3)] = hr[i];
-                    }
+                    if (f < nt * I4C) reinterpret_cast<moe::f32x4 *>(hl)[f] = hr[i];
                 }
 #pragma unroll
                 for (int i = 0; i < SV; ++i) {
@@ -698,16 +692,13 @@ __global__ __launch_bounds__(512, 4) void gemv_down1_nvfp4_kernel(Down1Args a)
         moe::f32x4 hr[HV];
 #pragma unroll
         for (int i = 0; i < HV; ++i)
-            hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)p * I + (lane + i * 64) * 4);
+            hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)p * I + h_src(lane + i * 64) * 4);
         const float s2 = a.scale2[e];
         __builtin_amdgcn_sched_barrier(0);
         load_w(w[0], 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < HV; ++i) {
-            const int r = lane + i * 64, sg = r >> 6, rr = r & 63;
-            hw[sg * 64 + (rr & 7) * 8 + (rr >> 3)] = hr[i];
-        }
+        for (int i = 0; i < HV; ++i) hw[lane + i * 64] = hr[i];
 #pragma unroll
         for (int i = 0; i < SV; ++i) {
             const int o = lane * 16 + i * 1024;
