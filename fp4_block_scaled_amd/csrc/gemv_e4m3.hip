@@ -595,6 +595,139 @@ __global__ __launch_bounds__(kThreads, ST == 1 ? 7 : 4) void gemv_down_e4m3_kern
 }
 
 // ---------------------------------------------------------------------------
+// down, several slots a pass
+// ---------------------------------------------------------------------------
+// With more slots per pass every weight value meets more h values, and the LDS
+// reads of h (one float4 per slot for every 4 weights) become the limit.  So
+// each wave here takes RG row groups 32 rows apart (a block: 32*RG output rows)
+// and every h value it reads from LDS serves all of them: with RG = 2, four
+// slots a pass cost the LDS reads per weight byte of two.  The products of a
+// slot are those of the down item, in the same order (y is bit-identical).
+// Unrolled only: K = NCH chunks of CH segments, the next two chunks in flight.
+template <int CH, int NCH, int ST, int RG>
+__global__ __launch_bounds__(kThreads, 4) void gemv_down_rg_e4m3_kernel(DownArgs a)
+{
+    extern __shared__ float4 hl[];                   // [a.st][I / 4], permuted per segment
+    constexpr int I4 = NCH * CH * 32, I = I4 * 4;    // float4 per h row, K
+    constexpr int NSEG = I / 128, HV = (ST * I4 + kThreads - 1) / kThreads;
+    static_assert(NSEG <= 128, "K at most 16384");
+    const int tile = blockIdx.x % a.ntiles;
+    const int ai = blockIdx.x / a.ntiles;
+    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
+    if (e < 0) return;
+    const int p0 = moe::uniform(a.offsets[e]);
+    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = moe::uniform(tid >> 6);
+    const int grp = lane >> 3, sub = lane & 7;
+    const int H = a.H, row0 = tile * 32 * RG;
+    const float *scb = a.scales + ((size_t)e * (H >> 7) + (row0 >> 7)) * NSEG;
+    const float sc_lo = lane < NSEG ? scb[lane] : 0.0f;
+    const float sc_hi = lane + 64 < NSEG ? scb[lane + 64] : 0.0f;
+
+    for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
+        const int nt = min(a.st, ne - s0);
+        const uint8_t *wb = moe::uniform_ptr(a.codes + ((size_t)e * H + row0 + wave * 8) * I);
+        uint32_t lo = (uint32_t)grp * I + sub * 16;
+        asm volatile("" : "+s"(wb), "+v"(lo));      // keep per-chunk addresses inside the pass
+        auto load_w = [&](uint4 (&wc)[RG][CH], int c) {
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+#pragma unroll
+                for (int sg = 0; sg < CH; ++sg)
+                    wc[g][sg] = load16(wb + g * 32 * I + (c * CH + sg) * 128 + lo);
+        };
+        // every h load of the pass goes out, then the first weight chunk;
+        // the LDS stores wait for the h loads only
+        uint4 w[3][RG][CH];
+        moe::f32x4 hr[HV];
+#pragma unroll
+        for (int i = 0; i < HV; ++i) {
+            // past the pass's last float4 a lane reloads that one (never stored)
+            const int f = min(tid + i * kThreads, nt * I4 - 1);
+            const int j = f / I4, r = h_src(f - j * I4);
+            hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(w[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < HV; ++i) {
+            const int f = tid + i * kThreads;
+            if (f < nt * I4) reinterpret_cast<moe::f32x4 *>(hl)[f] = hr[i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (NCH > 1) load_w(w[1], 1);
+        moe::lds_barrier();
+        float acc[ST][RG];
+#pragma unroll
+        for (int j = 0; j < ST; ++j)
+#pragma unroll
+            for (int g = 0; g < RG; ++g) acc[j][g] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (c + 2 < NCH) load_w(w[(c + 2) % 3], c + 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sg = 0; sg < CH; ++sg) {
+                const int seg = c * CH + sg;
+                const float s = seg < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, sc_lo), seg))
+                                         : __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, sc_hi), seg - 64));
+                float d[ST][RG];
+#pragma unroll
+                for (int j = 0; j < ST; ++j)
+#pragma unroll
+                    for (int g = 0; g < RG; ++g) d[j][g] = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f32x2 w01[RG], w23[RG];
+#pragma unroll
+                    for (int g = 0; g < RG; ++g) {
+                        const uint4 wv = w[c % 3][g][sg];
+                        const uint32_t dw = q == 0 ? wv.x : q == 1 ? wv.y : q == 2 ? wv.z : wv.w;
+                        w01[g] = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw, false);
+                        w23[g] = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw, true);
+                    }
+#pragma unroll
+                    for (int j = 0; j < ST; ++j) {
+                        if (j < nt) {
+                            const float4 hv = hl[j * I4 + seg * 32 + q * 8 + sub];
+#pragma unroll
+                            for (int g = 0; g < RG; ++g) {
+                                d[j][g] = fmaf(w01[g].x, hv.x, d[j][g]);
+                                d[j][g] = fmaf(w01[g].y, hv.y, d[j][g]);
+                                d[j][g] = fmaf(w23[g].x, hv.z, d[j][g]);
+                                d[j][g] = fmaf(w23[g].y, hv.w, d[j][g]);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < ST; ++j)
+                    if (j < nt)
+#pragma unroll
+                        for (int g = 0; g < RG; ++g) {
+                            acc[j][g] = fmaf(d[j][g], s, acc[j][g]);
+                            asm volatile("" : "+v"(acc[j][g]));   // (keeps the sums per segment)
+                        }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < ST; ++j)
+            if (j < nt)
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    const float v = moe::sum8_lanes(acc[j][g]);
+                    if (sub == 0) a.y[(size_t)(p0 + s0 + j) * H + row0 + g * 32 + wave * 8 + grp] = v;
+                }
+        moe::lds_barrier();                           // h is reused by the next pass
+    }
+}
+
+// ---------------------------------------------------------------------------
 // down + combine of one token
 // ---------------------------------------------------------------------------
 // With one token the layer's k <= 8 slots all feed the same output row, so
@@ -1053,6 +1186,13 @@ bool down_launch_unrolled(const DownArgs &a, int nch, int grid, hipStream_t st)
     }
 }
 
+template <int NCH>
+void down_rg_launch(const DownArgs &a, int grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((gemv_down_rg_e4m3_kernel<2, NCH, 4, 2>), dim3(grid), dim3(kThreads),
+                       (size_t)a.st * a.I * 4, st, a);
+}
+
 template <int CH, int NCH, int RG>
 void down1_launch(const Down1Args &a, hipStream_t st)
 {
@@ -1099,6 +1239,25 @@ hipError_t launch_gemv_down_e4m3(const GemvBankDev &down, const float *h, const 
     a.codes = down.codes; a.scales = (const float *)down.scales; a.h = h;
     a.offsets = r.offsets; a.active = r.active; a.y = y;
     a.H = hidden; a.I = inter;
+    if (M >= 3 && a.st < 4 && inter % 256 == 0 && inter <= 2560 && hidden % 64 == 0) {
+        // four slots a pass, two row groups per wave (64-row tiles)
+        a.st = M < 4 ? M : 4;
+        a.ntiles = hidden / 64;
+        const int grid = (S < E ? S : E) * a.ntiles;
+        switch (inter / 256) {
+        case 1: down_rg_launch<1>(a, grid, st); break;
+        case 2: down_rg_launch<2>(a, grid, st); break;
+        case 3: down_rg_launch<3>(a, grid, st); break;
+        case 4: down_rg_launch<4>(a, grid, st); break;
+        case 5: down_rg_launch<5>(a, grid, st); break;
+        case 6: down_rg_launch<6>(a, grid, st); break;
+        case 7: down_rg_launch<7>(a, grid, st); break;
+        case 8: down_rg_launch<8>(a, grid, st); break;
+        case 9: down_rg_launch<9>(a, grid, st); break;
+        default: down_rg_launch<10>(a, grid, st); break;
+        }
+        return hipGetLastError();
+    }
     a.ntiles = hidden / 32;
     const int grid = (S < E ? S : E) * a.ntiles;
     const int ch = gemv_down_chunk_segs(kFmtE4M3, inter), nch = inter / 128 / ch;

@@ -633,6 +633,151 @@ __global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// down, several slots a pass
+// ---------------------------------------------------------------------------
+// As the E4M3 kernel of the same name: each wave takes RG row groups 32 rows
+// apart (a block: 32*RG output rows), so every h value it reads from LDS
+// serves all of them and four slots a pass cost the LDS reads per weight byte
+// of two.  The group scales of the wave's rows go to LDS with the h rows.  The
+// products of a slot are the down item's, in the same order.
+template <int CH, int NCH, int ST, int RG>
+__global__ __launch_bounds__(kThreads, 3) void gemv_down_rg_nvfp4_kernel(DownArgs a)
+{
+    extern __shared__ float4 hl[];                   // [a.st][I / 4] h rows, then the scale rows
+    constexpr int I4 = NCH * CH * 64, I = I4 * 4;    // float4 per h row, K
+    constexpr int HV = (ST * I4 + kThreads - 1) / kThreads;
+    constexpr int RB = I / 2, SB = I / 16;           // code and scale bytes per row
+    constexpr int SROW = SB + 16;                    // LDS scale row (padded)
+    constexpr int SV = (8 * SB + 1023) / 1024;       // 16-byte scale loads per lane and row group
+    const int tile = blockIdx.x % a.ntiles;
+    const int ai = blockIdx.x / a.ntiles;
+    const int e = moe::uniform(a.active[ai]);       // -1 past the active experts
+    if (e < 0) return;
+    const int p0 = moe::uniform(a.offsets[e]);
+    const int ne = moe::uniform(a.offsets[e + 1]) - p0;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = moe::uniform(tid >> 6);
+    const int grp = lane >> 3, sub = lane & 7;
+    const int H = a.H, row0 = tile * 32 * RG;
+    const float s2 = a.scale2[e];
+    uint8_t *scl = reinterpret_cast<uint8_t *>(hl) + (size_t)a.st * I * 4 + wave * 8 * RG * SROW;
+
+    for (int s0 = 0; s0 < ne; s0 += a.st) {          // passes over the weights
+        const int nt = min(a.st, ne - s0);
+        const size_t r0 = (size_t)e * H + row0 + wave * 8;
+        const uint8_t *cb = moe::uniform_ptr(a.codes + r0 * RB);
+        const uint8_t *sb = moe::uniform_ptr(a.scales + r0 * SB);
+        uint32_t co = (uint32_t)grp * RB + sub * 16;
+        asm volatile("" : "+s"(cb), "+s"(sb), "+v"(co));
+        auto load_w = [&](uint4 (&wc)[RG][CH], int c) {
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+#pragma unroll
+                for (int sg = 0; sg < CH; ++sg)
+                    wc[g][sg] = load16(cb + g * 32 * RB + (c * CH + sg) * 128 + co);
+        };
+        // scale rows and every h load of the pass, then the first weight
+        // chunk, then the LDS stores
+        uint4 w[3][RG][CH];
+        moe::u32x4 sr[RG][SV];
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int i = 0; i < SV; ++i) {
+                // past the rows' last 16 bytes a lane reloads those (never stored)
+                const int o = min(lane * 16 + i * 1024, 8 * SB - 16);
+                sr[g][i] = moe::load_nt_global<moe::u32x4>(sb + g * 32 * SB + o);
+            }
+        moe::f32x4 hr[HV];
+#pragma unroll
+        for (int i = 0; i < HV; ++i) {
+            // past the pass's last float4 a lane reloads that one (never stored)
+            const int f = min(tid + i * kThreads, nt * I4 - 1);
+            const int j = f / I4, r = h_src(f - j * I4);
+            hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)(p0 + s0 + j) * I + r * 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(w[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < HV; ++i) {
+            const int f = tid + i * kThreads;
+            if (f < nt * I4) reinterpret_cast<moe::f32x4 *>(hl)[f] = hr[i];
+        }
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int i = 0; i < SV; ++i) {
+                const int o = lane * 16 + i * 1024;
+                if (o < 8 * SB) {
+                    const int r = o / SB, cc = o - r * SB;
+                    *reinterpret_cast<moe::u32x4 *>(scl + (g * 8 + r) * SROW + cc) = sr[g][i];
+                }
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        if (NCH > 1) load_w(w[1], 1);
+        moe::lds_barrier();
+        float acc[ST][RG];
+#pragma unroll
+        for (int j = 0; j < ST; ++j)
+#pragma unroll
+            for (int g = 0; g < RG; ++g) acc[j][g] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (c + 2 < NCH) load_w(w[(c + 2) % 3], c + 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sg = 0; sg < CH; ++sg) {
+                const int seg = c * CH + sg;
+                f32x2 sc[RG];
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    const uint32_t vs =
+                        *reinterpret_cast<const uint16_t *>(scl + (g * 8 + grp) * SROW + seg * 16 + sub * 2);
+                    sc[g] = __builtin_amdgcn_cvt_pk_f32_fp8((int)vs, false);
+                }
+#pragma unroll
+                for (int j = 0; j < ST; ++j) {
+                    if (j < nt) {
+                        const float4 *hv = &hl[j * I4 + seg * 64 + sub];
+                        float d0[RG], d1[RG];
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq) {
+                            const float4 ha = hv[qq * 16], hb = hv[qq * 16 + 8];
+#pragma unroll
+                            for (int g = 0; g < RG; ++g) {
+                                const uint4 wv = w[c % 3][g][sg];
+                                const uint32_t dw = qq == 0 ? wv.x : qq == 1 ? wv.y : qq == 2 ? wv.z : wv.w;
+                                if (qq == 0) d0[g] = dot8_fp4_f32(dw, ha, hb, 0.0f);
+                                else if (qq == 1) d0[g] = dot8_fp4_f32(dw, ha, hb, d0[g]);
+                                else if (qq == 2) d1[g] = dot8_fp4_f32(dw, ha, hb, 0.0f);
+                                else d1[g] = dot8_fp4_f32(dw, ha, hb, d1[g]);
+                            }
+                        }
+#pragma unroll
+                        for (int g = 0; g < RG; ++g) {
+                            acc[j][g] = fmaf(d0[g], sc[g].x, acc[j][g]);
+                            acc[j][g] = fmaf(d1[g], sc[g].y, acc[j][g]);
+                            asm volatile("" : "+v"(acc[j][g]));   // (keeps the sums per segment)
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < ST; ++j)
+            if (j < nt)
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    const float v = moe::sum8_lanes(acc[j][g]) * s2;
+                    if (sub == 0) a.y[(size_t)(p0 + s0 + j) * H + row0 + g * 32 + wave * 8 + grp] = v;
+                }
+        moe::lds_barrier();                           // h and the scales are reused by the next pass
+    }
+}
+
+// ---------------------------------------------------------------------------
 // down + combine of one token
 // ---------------------------------------------------------------------------
 // As the E4M3 kernel of the same name: a block owns 8*RG output rows for
@@ -1046,6 +1191,15 @@ bool down_launch_unrolled(const DownArgs &a, int nch, int grid, hipStream_t st)
     }
 }
 
+template <int NCH>
+void down_rg_launch(const DownArgs &a, int grid, hipStream_t st)
+{
+    constexpr int RG = 2;
+    const size_t lds = (size_t)a.st * a.I * 4 + 4 * 8 * RG * (size_t)(a.I / 16 + 16);
+    hipLaunchKernelGGL((gemv_down_rg_nvfp4_kernel<2, NCH, 4, RG>), dim3(grid), dim3(kThreads), lds,
+                       st, a);
+}
+
 template <int CH, int NCH, int RG>
 void down1_launch(const Down1Args &a, hipStream_t st)
 {
@@ -1093,6 +1247,23 @@ hipError_t launch_gemv_down_nvfp4(const GemvBankDev &down, const float *h, const
     a.codes = down.codes; a.scales = (const uint8_t *)down.scales; a.scale2 = down.scale2;
     a.h = h; a.offsets = r.offsets; a.active = r.active; a.y = y;
     a.H = hidden; a.I = inter;
+    if (M >= 3 && a.st < 4 && inter % 512 == 0 && inter <= 4096 && hidden % 64 == 0) {
+        // four slots a pass, two row groups per wave (64-row tiles)
+        a.st = M < 4 ? M : 4;
+        a.ntiles = hidden / 64;
+        const int grid = (S < E ? S : E) * a.ntiles;
+        switch (inter / 512) {
+        case 1: down_rg_launch<1>(a, grid, st); break;
+        case 2: down_rg_launch<2>(a, grid, st); break;
+        case 3: down_rg_launch<3>(a, grid, st); break;
+        case 4: down_rg_launch<4>(a, grid, st); break;
+        case 5: down_rg_launch<5>(a, grid, st); break;
+        case 6: down_rg_launch<6>(a, grid, st); break;
+        case 7: down_rg_launch<7>(a, grid, st); break;
+        default: down_rg_launch<8>(a, grid, st); break;
+        }
+        return hipGetLastError();
+    }
     a.ntiles = hidden / 32;
     const int grid = (S < E ? S : E) * a.ntiles;
     const int ch = gemv_down_chunk_segs(kFmtNVFP4, inter), nch = inter / kSegK / ch;

@@ -225,6 +225,9 @@ REDUCED = [
     ("e4m3_h768_i2560", "tiny_e4m3_m1", dict(hidden=768, inter=2560, experts=4, top_k=2), [1]),
     ("nvfp4_h512_i1024", "nvfp4_m1", dict(hidden=512, inter=1024, experts=6, top_k=5), [1, 2]),
     ("nvfp4_h1024_i2048", "nvfp4_m1", dict(hidden=1024, inter=2048, experts=10, top_k=8), [1]),
+    # several tokens: the down GEMVs' four-slot passes over two row groups per wave
+    ("nvfp4_h512_i2048", "nvfp4_m1", dict(hidden=512, inter=2048, experts=6, top_k=4), [3, 5]),
+    ("e4m3_h640_i1280", "tiny_e4m3_m1", dict(hidden=640, inter=1280, experts=5, top_k=3), [4, 6]),
 ]
 
 
