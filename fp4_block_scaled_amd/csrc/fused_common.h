@@ -104,7 +104,7 @@ struct FusedWait {
 // LDS-only, so global loads the caller has in flight stay in flight.
 static_assert(kFusedMaxSlots == kFusedThreads, "one slot per thread");
 template <class Args>
-__device__ void fused_route(const Args &a, FusedRoute &R, int id_in)
+__device__ __forceinline__ void fused_route(const Args &a, FusedRoute &R, int id_in)
 {
     const int tid = threadIdx.x, S = a.M * a.k, E = a.E;
     if (tid == 0) { R.na = 0; R.nvalid = 0; R.ninvalid = 0; R.flag = 0; }
@@ -136,18 +136,69 @@ __device__ void fused_route(const Args &a, FusedRoute &R, int id_in)
     moe::lds_barrier();
 }
 
-// The active expert of index ai of a route of S <= 64 slots, worked out by
-// each wave on its own from the ids (lane s holds slot s; no LDS, no
-// barrier), for a launch whose blocks each need only their own expert: e
+// The active expert of index ai of a route of S <= 128 slots, worked out by
+// each wave on its own from the ids (lane s holds slots s and s + 64; no LDS,
+// no barrier), for a launch whose blocks each need only their own expert: e
 // (-1 when ai is past the active experts), its first packed row p0 (the
-// valid slots of smaller experts), its slot count ne and the mask of its
-// slots (bit s: slot s chose it), in slot order -- the stable pack.
+// valid slots of smaller experts), its slot count ne and the masks of its
+// slots (bit s of mask[h]: slot 64 h + s chose it), in slot order -- the
+// stable pack.  Key comparisons come from one ballot per key bit and half,
+// most significant bit first: for each of a lane's two keys, the lanes of
+// each half holding a smaller key (lt) and an equal one (eq).
 struct LightRoute {
     int e, p0, ne;
-    uint64_t mask;
+    uint64_t mask[2];
 };
 
-__device__ __forceinline__ LightRoute light_route(const int32_t *ids, int S, int E, int ai)
+__device__ __forceinline__ LightRoute light_route_wide(const int32_t *ids, int S, int E, int ai)
+{
+    const int lane = threadIdx.x & 63;
+    const int id0 = lane < S ? ids[lane] : -1;
+    const int id1 = lane + 64 < S ? ids[lane + 64] : -1;
+    // key: the expert, E for an invalid or missing slot (after every expert)
+    const int k0 = id0 >= 0 && id0 < E ? id0 : E;
+    const int k1 = id1 >= 0 && id1 < E ? id1 : E;
+    uint64_t lt00 = 0, eq00 = ~0ull, lt01 = 0, eq01 = ~0ull;   // key k0 against halves 0, 1
+    uint64_t lt10 = 0, eq10 = ~0ull, lt11 = 0, eq11 = ~0ull;   // key k1 against halves 0, 1
+    for (int b = 9; b >= 0; --b) {                   // keys <= E <= 512
+        const uint64_t b0 = __ballot((k0 >> b) & 1), b1 = __ballot((k1 >> b) & 1);
+        if ((k0 >> b) & 1) {
+            lt00 |= eq00 & ~b0; eq00 &= b0;
+            lt01 |= eq01 & ~b1; eq01 &= b1;
+        } else {
+            eq00 &= ~b0; eq01 &= ~b1;
+        }
+        if ((k1 >> b) & 1) {
+            lt10 |= eq10 & ~b0; eq10 &= b0;
+            lt11 |= eq11 & ~b1; eq11 &= b1;
+        } else {
+            eq10 &= ~b0; eq11 &= ~b1;
+        }
+    }
+    const uint64_t below = (1ull << lane) - 1;
+    // the first slot of its expert: no earlier slot holds the same key
+    const bool first0 = k0 < E && (eq00 & below) == 0;
+    const bool first1 = k1 < E && eq10 == 0 && (eq11 & below) == 0;
+    const uint64_t fm0 = __ballot(first0), fm1 = __ballot(first1);
+    // distinct valid experts below the key
+    const int rank0 = __popcll(lt00 & fm0) + __popcll(lt01 & fm1);
+    const int rank1 = __popcll(lt10 & fm0) + __popcll(lt11 & fm1);
+    const uint64_t sel0 = __ballot(first0 && rank0 == ai), sel1 = __ballot(first1 && rank1 == ai);
+    LightRoute r{-1, 0, 0, {0, 0}};
+    if (sel0 == 0 && sel1 == 0) return r;
+    r.e = sel0 ? __builtin_amdgcn_readlane(k0, __ffsll((unsigned long long)sel0) - 1)
+               : __builtin_amdgcn_readlane(k1, __ffsll((unsigned long long)sel1) - 1);
+    r.p0 = __popcll(__ballot(k0 < r.e)) + __popcll(__ballot(k1 < r.e));
+    r.mask[0] = __ballot(k0 == r.e);
+    r.mask[1] = __ballot(k1 == r.e);
+    r.ne = __popcll(r.mask[0]) + __popcll(r.mask[1]);
+    return r;
+}
+
+// The same for S <= 16 slots (one token's top-k): lane s holds slot s, and
+// the duplicates before it and the distinct experts below it are counted over
+// the S slots one by one, which is shorter here than the 20 ballots above.
+__device__ __forceinline__ LightRoute light_route_narrow(const int32_t *ids, int S, int E, int ai)
 {
     const int lane = threadIdx.x & 63;
     const int id = lane < S ? ids[lane] : -1;
@@ -165,19 +216,36 @@ __device__ __forceinline__ LightRoute light_route(const int32_t *ids, int S, int
         rank += (int)((fm >> j) & 1) & (kj < key);
     }
     const uint64_t sel = __ballot(first && rank == ai);
-    LightRoute r{-1, 0, 0, 0};
+    LightRoute r{-1, 0, 0, {0, 0}};
     if (sel == 0) return r;
     r.e = __builtin_amdgcn_readlane(key, __ffsll((unsigned long long)sel) - 1);
     r.p0 = __popcll(__ballot(key < r.e));
-    r.mask = __ballot(key == r.e);
-    r.ne = __popcll(r.mask);
+    r.mask[0] = __ballot(key == r.e);
+    r.ne = __popcll(r.mask[0]);
     return r;
+}
+
+__device__ __forceinline__ LightRoute light_route(const int32_t *ids, int S, int E, int ai)
+{
+    return S <= 16 ? light_route_narrow(ids, S, E, ai) : light_route_wide(ids, S, E, ai);
+}
+
+// Token of each slot of lr's expert, in slot order, into tok[0..ne): thread
+// t < 128 looks at slot t.
+__device__ __forceinline__ void light_route_tokens(const LightRoute &lr, int k, int32_t *tok)
+{
+    const int t = threadIdx.x;
+    if (lr.e < 0 || t >= 128) return;
+    const int s = t & 63;
+    const uint64_t m = t < 64 ? lr.mask[0] : lr.mask[1];   // (a select: no indexed private array)
+    if ((m >> s) & 1)
+        tok[(t < 64 ? 0 : __popcll(lr.mask[0])) + __popcll(m & ((1ull << s) - 1))] = t / k;
 }
 
 // Block 0 writes the other route tables, as route_pack writes them.  Nothing
 // in the launch reads them, so this runs at the end, off the critical path.
 template <class Args>
-__device__ void fused_route_tables(const Args &a, const FusedRoute &R)
+__device__ __forceinline__ void fused_route_tables(const Args &a, const FusedRoute &R)
 {
     if (blockIdx.x != 0) return;
     const int tid = threadIdx.x, S = a.M * a.k, E = a.E;

@@ -357,7 +357,7 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
     }
 }
 
-// ROUTE: the route of the S <= 64 slots comes from the ids inside the launch
+// ROUTE: the route of the S <= 128 slots comes from the ids inside the launch
 // (the same stable pack as route_pack) instead of from the tables of a route
 // pack launched before: every block works out its own expert; block 0 also
 // builds the whole route and writes the tables for the down and combine
@@ -373,10 +373,9 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
         // every wave finds this block's expert from the ids on its own; the
         // tokens of its slots go to LDS; block 0 builds and writes the whole
         // route tables after its item, off the critical path
-        __shared__ int32_t tokl[64];
+        __shared__ int32_t tokl[128];
         const LightRoute lr = light_route(a.ids, a.M * a.k, a.E, ai);
-        if (lr.e >= 0 && threadIdx.x < 64 && ((lr.mask >> threadIdx.x) & 1))
-            tokl[__popcll(lr.mask & ((1ull << threadIdx.x) - 1))] = (int)threadIdx.x / a.k;
+        light_route_tokens(lr, a.k, tokl);
         moe::lds_barrier();
         if (lr.e >= 0)
             gateup_e4m3_item<CH, NCH, ST, false, XW>(a, moe::uniform(lr.e), tile, moe::uniform(lr.p0),
@@ -1222,7 +1221,7 @@ hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &u
     a.ids = route_ids; a.M = M; a.k = top_k; a.E = E; a.r = r;
     const int grid = (S < E ? S : E) * a.ntiles;
     if (route_ids) {
-        if (S > 64) return hipErrorInvalidValue;
+        if (S > 128) return hipErrorInvalidValue;
         gateup_dispatch<true>(a, grid, st);
     } else {
         gateup_dispatch<false>(a, grid, st);

@@ -137,7 +137,7 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
 // compiler waits for exactly the chunk it multiplies); NCH == 0 is the
 // generic looped form with one chunk in flight.  The up sums reach the gate
 // waves through LDS; they apply scale_2, the clamped SwiGLU, and write h.
-// ROUTE: the route of the S <= 64 slots comes from the ids inside the launch
+// ROUTE: the route of the S <= 128 slots comes from the ids inside the launch
 // (the same stable pack as route_pack) instead of from the tables of a route
 // pack launched before: every block works out its own expert; block 0 also
 // builds the whole route and writes the tables for the down and combine
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     extern __shared__ uint4 xl[];                    // [a.st][H / 8], permuted per segment
     __shared__ float ush[ST][16];
     __shared__ typename std::conditional<ROUTE, FusedRoute, NoRoute>::type R;
-    __shared__ int32_t tokl[ROUTE ? 64 : 1];
+    __shared__ int32_t tokl[ROUTE ? 128 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
@@ -177,8 +177,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     const int32_t *tok;
     if constexpr (ROUTE) {
         const LightRoute lr = light_route(a.ids, a.M * a.k, a.E, ai);
-        if (lr.e >= 0 && tid < 64 && ((lr.mask >> tid) & 1))
-            tokl[__popcll(lr.mask & ((1ull << tid) - 1))] = tid / a.k;
+        light_route_tokens(lr, a.k, tokl);
         moe::lds_barrier();
         if (lr.e < 0) {
             route_tables_block0(a, R);
@@ -1230,7 +1229,7 @@ hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &
     a.ids = route_ids; a.M = M; a.k = top_k; a.E = E; a.r = r;
     const int grid = (S < E ? S : E) * a.ntiles;
     if (route_ids) {
-        if (S > 64) return hipErrorInvalidValue;
+        if (S > 128) return hipErrorInvalidValue;
         gateup_dispatch<true>(a, grid, st);
     } else {
         gateup_dispatch<false>(a, grid, st);

@@ -303,7 +303,7 @@ static moe_status_t check_bank(const char *fn, const moe_bank_t *b, const char *
 
 // The expert FFN of moe_expert_ffn.  With route_ids, the route tables of
 // `route` (carved, not yet filled) are built by the gate/up launch itself
-// from the ids: only for the GEMV tier and S <= 64.  With comb_out as well
+// from the ids: only for the GEMV tier and S <= 128 (E4M3) or 64 (NVFP4).  With comb_out as well
 // (moe_layer), one token whose shape gemv_down1_fits accepts gets the down
 // projection and the combine in one launch (out = comb_out, weights comb_w),
 // and *combined says so; otherwise the caller runs the combine.
@@ -465,7 +465,9 @@ moe_status_t moe_layer(const moe_bank_t *gate, const moe_bank_t *up, const moe_b
         return fail(MOE_ERR_ARG, "%s: unknown mode %d", fn, mode);
     const int64_t S = (int64_t)M * top_k;
     moe_status_t st;
-    if (S <= 64 && resolve(M, fmt, mode) == MOE_MODE_GEMV_A16) {
+    // (E4M3 up to 128 slots; the NVFP4 gate/up kernel with the route built in
+    // ran slower at 128 slots than route_pack and the plain kernel together)
+    if (S <= (fmt == MOE_W_E4M3_B128 ? 128 : 64) && resolve(M, fmt, mode) == MOE_MODE_GEMV_A16) {
         // the route pack runs inside the gate/up launch
         if (ws_bytes < moe::route_region_bytes(S, E))
             return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes,

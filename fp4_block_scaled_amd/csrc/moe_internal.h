@@ -54,7 +54,7 @@ struct GemvBankDev {
 // slot tile of a pass.  Experts holding more slots are swept in several
 // passes.  Gate/up covers the whole of K per block and writes h =
 // SwiGLU(gate x, up x) ([S][inter] floats) directly.
-// With route_ids (S <= 64 slots of top_k each), the route is built inside
+// With route_ids (S <= 128 slots of top_k each), the route is built inside
 // the launch from the ids and block 0 writes the tables of r; otherwise the
 // tables of r come from route_pack.
 hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,

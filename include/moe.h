@@ -258,14 +258,15 @@ moe_status_t moe_combine(const float *y_packed, const moe_route_t *route,
 /* The whole layer in one call: the route pack, the expert FFN of tier `mode`
  * and the combine, with the outputs (route tables in *route, y_packed, out)
  * of moe_route_pack + moe_expert_ffn + moe_combine, bit for bit.  For the
- * GEMV tier (either format) and M*top_k <= 64 slots the route pack runs
+ * GEMV tier and M*top_k <= 128 slots (E4M3; 64 for NVFP4) the route pack runs
  * inside the gate/up launch (every block builds the route of the slots from
  * the ids in LDS; block 0 writes the tables for the down and combine
  * launches), so the layer is three launches; with one token (M == 1,
  * top_k <= 8, inter a multiple of 512 up to 2560 for E4M3 or 2048 for
  * NVFP4, out 16-byte aligned) the down launch also does the combine (each
  * block owns some output rows for every slot and adds them in slot order),
- * two launches; otherwise the three calls' launches run in sequence.  No host state: capturable in a HIP graph.
+ * two launches; otherwise the three calls' launches run in sequence.  No
+ * host state: capturable in a HIP graph.
  * Rules and workspace: those of the three calls (ws_bytes >=
  * moe_workspace_bytes(M, top_k, E, hidden, inter, fmt, mode)); a failed
  * check launches nothing of the failing call. */

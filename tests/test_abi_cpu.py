@@ -356,6 +356,8 @@ def test_single_call_layer_error_contract_on_host():
     assert layer(hidden=200) == B.MOE_ERR_SHAPE                # the FFN's checks apply
     assert layer(limit=0.0) == B.MOE_ERR_ARG
     assert layer(gate=_bank(B, E=8)) == B.MOE_ERR_SHAPE
-    # NVFP4 banks or more than 64 slots take the three calls' path: the route
-    # pack's and FFN's own checks still apply
+    # up to 128 slots the route is built in the gate/up launch (its route
+    # region is checked first); more take the three calls' path, where the
+    # route pack's and FFN's own checks still apply
     assert layer(M=20, k=4, mode=B.MOE_MODE_GEMV_A16, nbytes=600) == B.MOE_ERR_WORKSPACE
+    assert layer(M=40, k=4, mode=B.MOE_MODE_GEMV_A16, nbytes=600) == B.MOE_ERR_WORKSPACE
