@@ -224,15 +224,19 @@ __device__ __forceinline__ void gateup_e4m3_item(const GateUpArgs &a, int e, int
             constexpr int XB = ST * XC;              // uint4 per buffer
             constexpr int XR = (XB + kThreads - 1) / kThreads;
             moe::u32x4 xr[XR];                       // (native vectors stay in VGPRs)
+            // each load's source in chunk 0, looked up once per pass (the
+            // chunks of a load differ by XC uint4): no token read per chunk
+            const moe::u32x4 *xsrc[XR];
+#pragma unroll
+            for (int i = 0; i < XR; ++i) {
+                // past the pass's last uint4 a lane reloads that one (never stored)
+                const int f = min(tid + i * kThreads, nt * XC - 1);
+                const int j = f / XC, r = f - j * XC;
+                xsrc[i] = reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H + (size_t)r * 8);
+            }
             auto load_x = [&](int c) {
 #pragma unroll
-                for (int i = 0; i < XR; ++i) {
-                    // past the pass's last uint4 a lane reloads that one (never stored)
-                    const int f = min(tid + i * kThreads, nt * XC - 1);
-                    const int j = f / XC, r = f - j * XC;
-                    xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H +
-                                                                  (size_t)(c * XC + r) * 8);
-                }
+                for (int i = 0; i < XR; ++i) xr[i] = xsrc[i][c * XC];
             };
             auto store_x = [&](int c) {
                 moe::u32x4 *buf = reinterpret_cast<moe::u32x4 *>(xl) + (c & 1) * XB;
@@ -381,7 +385,9 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_e4m3_kernel(GateUpArg
             gateup_e4m3_item<CH, NCH, ST, false, XW>(a, moe::uniform(lr.e), tile, moe::uniform(lr.p0),
                                                      moe::uniform(lr.ne), tokl, xl, ush);
         if (blockIdx.x == 0) {
-            __shared__ FusedRoute R;
+            // the route in the x tile's LDS, free once the item has ended (the
+            // launch sizes it for both): no block holds static LDS for it
+            FusedRoute &R = *reinterpret_cast<FusedRoute *>(xl);
             const int id_in = (int)threadIdx.x < a.M * a.k ? a.ids[threadIdx.x] : -1;
             fused_route(a, R, id_in);
             fused_route_status(a, R);
@@ -1101,8 +1107,11 @@ namespace {
 template <int CH, int NCH, int ST, bool ROUTE>
 void gateup_launch(const GateUpArgs &a, int grid, hipStream_t st)
 {
+    // x rows of a pass (with the route built in, at least block 0's route)
+    size_t lds = (size_t)a.st * a.H * 2;
+    if (ROUTE && lds < sizeof(FusedRoute)) lds = sizeof(FusedRoute);
     hipLaunchKernelGGL((gemv_gateup_e4m3_kernel<CH, NCH, ST, ROUTE>), dim3(grid), dim3(kThreads),
-                       (size_t)a.st * a.H * 2, st, a);
+                       lds, st, a);
 }
 
 // Unrolled kernels for 8-segment chunks (hidden a multiple of 1024), for the
@@ -1129,7 +1138,8 @@ template <bool ROUTE>
 bool gateup_launch_xw(const GateUpArgs &a, int grid, hipStream_t st)
 {
     if (a.H != 7168) return false;
-    const size_t lds = 2 * (size_t)MOE_E4M3_GU_ST * 4 * 16 * sizeof(uint4);
+    size_t lds = 2 * (size_t)MOE_E4M3_GU_ST * 4 * 16 * sizeof(uint4);
+    if (ROUTE && lds < sizeof(FusedRoute)) lds = sizeof(FusedRoute);
     hipLaunchKernelGGL((gemv_gateup_e4m3_kernel<4, 14, MOE_E4M3_GU_ST, ROUTE, true>), dim3(grid),
                        dim3(kThreads), lds, st, a);
     return true;

@@ -165,7 +165,9 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     static_assert(!XW || NCH > 0, "chunked x staging is an unrolled form");
     extern __shared__ uint4 xl[];                    // [a.st][H / 8], permuted per segment
     __shared__ float ush[ST][16];
-    __shared__ typename std::conditional<ROUTE, FusedRoute, NoRoute>::type R;
+    // with the route built in, block 0's route goes to the x tile's LDS once
+    // its item has ended (the launch sizes it for both)
+    auto &R = *reinterpret_cast<typename std::conditional<ROUTE, FusedRoute, NoRoute>::type *>(xl);
     __shared__ int32_t tokl[ROUTE ? 128 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -215,6 +217,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
     const int srow = rows + 16;
     constexpr int XC = CH * 32;                      // XW: uint4 of one slot's x per chunk
     constexpr int XB = ST * XC;                      // XW: uint4 per buffer
+    const moe::u32x4 *xsrc[XW ? (XB + kThreads - 1) / kThreads : 1];   // XW: each x load's source in chunk 0
     const size_t xbytes = XW ? 2 * (size_t)XB * 16 : (size_t)a.st * H * 2;
     uint8_t *scl = reinterpret_cast<uint8_t *>(xl) + xbytes + wave * 8 * srow;
 
@@ -285,9 +288,12 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
                 moe::u32x4 xr[(XB + kThreads - 1) / kThreads];
 #pragma unroll
                 for (int i = 0; i < (XB + kThreads - 1) / kThreads; ++i) {
+                    // past the pass's last uint4 a lane reloads that one (never stored)
                     const int f = min(tid + i * kThreads, nt * XC - 1);
                     const int j = f / XC, r = x_src(f - j * XC);
-                    xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H + (size_t)r * 8);
+                    // (the chunks of a load differ by XC uint4: looked up once per pass)
+                    xsrc[i] = reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H + (size_t)r * 8);
+                    xr[i] = xsrc[i][0];
                 }
                 load_w(w[0], v[0], 0);
 #pragma unroll
@@ -342,12 +348,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_gateup_nvfp4_kernel(GateUpAr
                     // x leaves those weight loads in flight
                     if (c + 1 < NCH) {
 #pragma unroll
-                        for (int i = 0; i < XR; ++i) {
-                            const int f = min(tid + i * kThreads, nt * XC - 1);
-                            const int j = f / XC, r = x_src(f - j * XC);
-                            xr[i] = *reinterpret_cast<const moe::u32x4 *>(a.x + (size_t)tok[s0 + j] * H +
-                                                                          (size_t)((c + 1) * XC + r) * 8);
-                        }
+                        for (int i = 0; i < XR; ++i) xr[i] = xsrc[i][(c + 1) * XC];
                     }
                     if (c + 2 < NCH) load_w(w[(c + 2) % 3], v[(c + 2) % 3], c + 2);
                     __builtin_amdgcn_sched_barrier(0);
@@ -1105,7 +1106,8 @@ template <int CH, int NCH, int ST, bool ROUTE>
 void gateup_launch(const GateUpArgs &a, int grid, hipStream_t st)
 {
     // x rows of a pass, then (unrolled form) the scale rows of the 4 waves
-    const size_t lds = (size_t)a.st * a.H * 2 + (NCH > 0 ? 32 * (size_t)(a.H / 16 + 16) : 0);
+    size_t lds = (size_t)a.st * a.H * 2 + (NCH > 0 ? 32 * (size_t)(a.H / 16 + 16) : 0);
+    if (ROUTE && lds < sizeof(FusedRoute)) lds = sizeof(FusedRoute);
     hipLaunchKernelGGL((gemv_gateup_nvfp4_kernel<CH, NCH, ST, ROUTE>), dim3(grid), dim3(kThreads),
                        lds, st, a);
 }
@@ -1136,7 +1138,8 @@ template <bool ROUTE>
 bool gateup_launch_xw(const GateUpArgs &a, int grid, hipStream_t st)
 {
     if (a.H != 6144) return false;
-    const size_t lds = 2 * (size_t)kGUXW * 4 * 32 * sizeof(uint4) + 32 * (size_t)(a.H / 16 + 16);
+    size_t lds = 2 * (size_t)kGUXW * 4 * 32 * sizeof(uint4) + 32 * (size_t)(a.H / 16 + 16);
+    if (ROUTE && lds < sizeof(FusedRoute)) lds = sizeof(FusedRoute);
     hipLaunchKernelGGL((gemv_gateup_nvfp4_kernel<4, 6, kGUXW, ROUTE, true>), dim3(grid), dim3(kThreads),
                        lds, st, a);
     return true;
