@@ -1198,7 +1198,7 @@ bool down_launch_unrolled(const DownArgs &a, int nch, int grid, hipStream_t st)
 template <int NCH>
 void down_rg_launch(const DownArgs &a, int grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((gemv_down_rg_e4m3_kernel<2, NCH, 4, 2>), dim3(grid), dim3(kThreads),
+    hipLaunchKernelGGL((gemv_down_rg_e4m3_kernel<1, 2 * NCH, 4, 2>), dim3(grid), dim3(kThreads),
                        (size_t)a.st * a.I * 4, st, a);
 }
 

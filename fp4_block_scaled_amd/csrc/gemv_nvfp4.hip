@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void gemv_down_nvfp4_kernel(DownArgs a)
 // of two.  The group scales of the wave's rows go to LDS with the h rows.  The
 // products of a slot are the down item's, in the same order.
 template <int CH, int NCH, int ST, int RG>
-__global__ __launch_bounds__(kThreads, 3) void gemv_down_rg_nvfp4_kernel(DownArgs a)
+__global__ __launch_bounds__(kThreads, 4) void gemv_down_rg_nvfp4_kernel(DownArgs a)
 {
     extern __shared__ float4 hl[];                   // [a.st][I / 4] h rows, then the scale rows
     constexpr int I4 = NCH * CH * 64, I = I4 * 4;    // float4 per h row, K
@@ -1198,7 +1198,7 @@ void down_rg_launch(const DownArgs &a, int grid, hipStream_t st)
 {
     constexpr int RG = 2;
     const size_t lds = (size_t)a.st * a.I * 4 + 4 * 8 * RG * (size_t)(a.I / 16 + 16);
-    hipLaunchKernelGGL((gemv_down_rg_nvfp4_kernel<2, NCH, 4, RG>), dim3(grid), dim3(kThreads), lds,
+    hipLaunchKernelGGL((gemv_down_rg_nvfp4_kernel<1, 2 * NCH, 4, RG>), dim3(grid), dim3(kThreads), lds,
                        st, a);
 }
 
