@@ -786,7 +786,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_down_rg_nvfp4_kernel(DownArg
 // an LDS region of its own) with the down item's products in the down item's
 // order, and the block adds the slots' rows in slot order.
 template <int CH, int NCH, int RG>
-__global__ __launch_bounds__(512, 4) void gemv_down1_nvfp4_kernel(Down1Args a)
+__global__ __launch_bounds__(512, RG <= 2 ? 4 : 2) void gemv_down1_nvfp4_kernel(Down1Args a)
 {
     extern __shared__ float4 hl[];                   // per wave: h row, scale rows; row sums, slot table
     constexpr int ROWS = 8 * RG;
@@ -1211,6 +1211,13 @@ void down1_launch(const Down1Args &a, hipStream_t st)
                        a);
 }
 
+template <int NCH>
+void down1_launch_rg(const Down1Args &a, int rg, hipStream_t st)
+{
+    if (rg == 3) down1_launch<2, NCH, 3>(a, st);
+    else down1_launch<2, NCH, 2>(a, st);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_gateup_nvfp4(const GemvBankDev &gate, const GemvBankDev &up,
@@ -1291,11 +1298,25 @@ hipError_t launch_gemv_down1_nvfp4(const GemvBankDev &down, const float *h, cons
     a.codes = down.codes; a.scales = (const uint8_t *)down.scales; a.scale2 = down.scale2;
     a.h = h; a.ids = ids; a.t2p = t2p; a.w = w; a.y = y; a.out = out;
     a.H = hidden; a.k = k;
+    // A block owns 8 x RG output rows for every slot and the grid is a single
+    // round, so the busiest CU holds ceil(blocks / CUs) x RG row groups per
+    // slot.  Three row groups per wave where that is fewer than with two: at
+    // 6144 rows, 256 blocks of 24 rows (one per CU) instead of 384 blocks of
+    // 16 (two on half of the CUs, one on the rest).
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    auto busiest = [&](int rg) { return (hidden / (8 * rg) + cus - 1) / cus * rg; };
+    const int rg = hidden % 24 == 0 && busiest(3) < busiest(2) ? 3 : 2;
     switch (inter / 512) {
-    case 1: down1_launch<2, 1, 2>(a, st); break;
-    case 2: down1_launch<2, 2, 2>(a, st); break;
-    case 3: down1_launch<2, 3, 2>(a, st); break;
-    default: down1_launch<2, 4, 2>(a, st); break;
+    case 1: down1_launch_rg<1>(a, rg, st); break;
+    case 2: down1_launch_rg<2>(a, rg, st); break;
+    case 3: down1_launch_rg<3>(a, rg, st); break;
+    default: down1_launch_rg<4>(a, rg, st); break;
     }
     return hipGetLastError();
 }

@@ -227,6 +227,11 @@ REDUCED = [
     ("nvfp4_h1024_i2048", "nvfp4_m1", dict(hidden=1024, inter=2048, experts=10, top_k=8), [1]),
     # several tokens: the down GEMVs' four-slot passes over two row groups per wave
     ("nvfp4_h512_i2048", "nvfp4_m1", dict(hidden=512, inter=2048, experts=6, top_k=4), [3, 5]),
+    # one token, hidden a multiple of 24 with more 16-row blocks than the 256
+    # CUs: the combining down kernel takes 24-row blocks
+    ("nvfp4_h4608_i1536", "nvfp4_m1", dict(hidden=4608, inter=1536, experts=8, top_k=8), [1]),
+    ("nvfp4_h6144_i512", "nvfp4_m1", dict(hidden=6144, inter=512, experts=6, top_k=5), [1]),
+    ("nvfp4_h6144_i2048", "nvfp4_m1", dict(hidden=6144, inter=2048, experts=5, top_k=3), [1]),
     ("e4m3_h640_i1280", "tiny_e4m3_m1", dict(hidden=640, inter=1280, experts=5, top_k=3), [4, 6]),
 ]
 
