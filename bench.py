@@ -360,9 +360,9 @@ TRAFFIC = {
     "decode_e4m3_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
         "src": "b3c8a47ce876f043d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 173073, "write_kib": 1070},
     "nvfp4_m1": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "41fb2dfe57e2e52fd7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 41622, "write_kib": 49},
+        "src": "857c056872b489cdd7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 41626, "write_kib": 49},
     "nvfp4_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "41fb2dfe57e2e52fd7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 64867, "write_kib": 835},
+        "src": "857c056872b489cdd7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 64881, "write_kib": 835},
     "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h"],
         "src": "e7bd3c69fc01c3df46ff9d1401442f7fe0174e2455c8b818", "fetch_kib": 4022574, "write_kib": 68917},
     "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
@@ -370,7 +370,7 @@ TRAFFIC = {
     "verify_e4m3_m8": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
         "src": "b3c8a47ce876f043d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 646016, "write_kib": 514},
     "nvfp4_m16": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "41fb2dfe57e2e52fd7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 444740, "write_kib": 768},
+        "src": "857c056872b489cdd7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 444735, "write_kib": 768},
 }
 
 
