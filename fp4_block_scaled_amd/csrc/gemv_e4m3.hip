@@ -863,6 +863,141 @@ __global__ __launch_bounds__(512, RG <= 2 ? 4 : 2) void gemv_down1_e4m3_kernel(D
     }
 }
 
+// The same for hidden sizes that are multiples of 28 (7168 = 256 x 28), where
+// 16-row blocks leave the CUs unevenly loaded: at 7168 rows they make 448
+// blocks, two on most CUs and one on the rest, and a CU streams at about the
+// same rate with one block as with two, so the CUs with two set the length.
+// Here a block owns 28 output rows for every slot (one block per CU at
+// 7168) and has two waves per slot.  Rows stay in 8-row groups aligned to 8
+// with 8 lanes per row, as in the down item: the block's rows lie in the four
+// aligned groups from base8 = row0 rounded down to 8, and wave 2j + hh takes
+// groups 2hh and 2hh + 1 of slot j.  Four rows of the end group belong to the
+// neighbouring block; their lanes load the same bytes as the lanes 4 rows
+// away (no extra traffic) and store nothing.  Each wave stages slot j's h row
+// in an LDS region of its own.  Every row's products and their order are the
+// down item's (y is bit-identical), and the block adds the slots' rows in
+// slot order.
+template <int CH, int NCH>
+__global__ __launch_bounds__(1024, 4) void gemv_down1p_e4m3_kernel(Down1Args a)
+{
+    extern __shared__ float4 hl[];                   // [16][I/4] h rows, [8][28] row sums, slot table
+    constexpr int ROWS = 28;
+    constexpr int I4 = NCH * CH * 32, I = I4 * 4;    // float4 per h row, K
+    constexpr int NSEG = I / 128, HV = I4 / 64;      // 128-wide segments; h float4 per lane
+    static_assert(I4 % 64 == 0 && NSEG <= 64, "K must be a multiple of 256 up to 8192");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = moe::uniform(tid >> 6);
+    const int j = wv >> 1, hh = wv & 1;              // this wave's slot and half
+    const int grp = lane >> 3, sub = lane & 7;
+    const int H = a.H, row0 = blockIdx.x * ROWS, base8 = row0 & ~7;
+    float *sums = reinterpret_cast<float *>(hl + 16 * I4);
+    const int pc = tid < a.k ? a.t2p[tid] : -1;
+    const float wc = tid < a.k ? a.w[tid] : 0.0f;
+    const int p = j < a.k ? moe::uniform(a.t2p[j]) : -1;   // packed row; -1: no slot
+    const int e = j < a.k ? moe::uniform(a.ids[j]) : 0;     // (loaded beside p, not after it)
+    const bool live = p >= 0;
+    // the lane's row in each of its two groups; rows outside the block read
+    // the row 4 away, inside the same group
+    const int g0 = base8 + hh * 16;                  // first row of the wave's first group
+    int own[2], src[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int r = g0 + g * 8 + grp;
+        own[g] = r >= row0 && r < row0 + ROWS;
+        src[g] = own[g] ? grp : grp ^ 4;
+    }
+    moe::f32x4 *hw = reinterpret_cast<moe::f32x4 *>(hl + wv * I4);
+    const uint8_t *wb = moe::uniform_ptr(a.codes + ((size_t)e * H + g0) * I);
+    uint32_t lo0 = (uint32_t)src[0] * I + sub * 16, lo1 = (uint32_t)(8 + src[1]) * I + sub * 16;
+    asm volatile("" : "+s"(wb), "+v"(lo0), "+v"(lo1));
+    auto load_w = [&](uint4 (&wc)[2][CH], int c) {
+#pragma unroll
+        for (int sg = 0; sg < CH; ++sg) {
+            wc[0][sg] = load16(wb + (c * CH + sg) * 128 + lo0);
+            wc[1][sg] = load16(wb + (c * CH + sg) * 128 + lo1);
+        }
+    };
+    if (live) {
+        // h row loads, then the first weight chunk, then the h stores
+        uint4 w[3][2][CH];
+        moe::f32x4 hr[HV];
+#pragma unroll
+        for (int i = 0; i < HV; ++i)
+            hr[i] = *reinterpret_cast<const moe::f32x4 *>(a.h + (size_t)p * I + h_src(lane + i * 64) * 4);
+        // each aligned 8-row group lies inside one 128-row scale block
+        const float *scb = a.scales + (size_t)e * (H >> 7) * NSEG;
+        const float sc0 = lane < NSEG ? scb[(g0 >> 7) * NSEG + lane] : 0.0f;
+        const float sc1 = lane < NSEG ? scb[((g0 + 8) >> 7) * NSEG + lane] : 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(w[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < HV; ++i) hw[lane + i * 64] = hr[i];
+        __builtin_amdgcn_sched_barrier(0);
+        if (NCH > 1) load_w(w[1], 1);
+        // the h region is this wave's own: a wave-level barrier orders its
+        // LDS stores before the reads of the other lanes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (c + 2 < NCH) load_w(w[(c + 2) % 3], c + 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sg = 0; sg < CH; ++sg) {
+                const int seg = c * CH + sg;
+                const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc0), seg));
+                const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc1), seg));
+                float d[2] = {0.0f, 0.0f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const moe::f32x4 hv = hw[seg * 32 + q * 8 + sub];
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        const uint4 wq = w[c % 3][g][sg];
+                        const uint32_t dw = q == 0 ? wq.x : q == 1 ? wq.y : q == 2 ? wq.z : wq.w;
+                        const f32x2 w01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw, false);
+                        const f32x2 w23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)dw, true);
+                        d[g] = fmaf(w01.x, hv.x, d[g]);
+                        d[g] = fmaf(w01.y, hv.y, d[g]);
+                        d[g] = fmaf(w23.x, hv.z, d[g]);
+                        d[g] = fmaf(w23.y, hv.w, d[g]);
+                    }
+                }
+                acc[0] = fmaf(d[0], s0, acc[0]);
+                acc[1] = fmaf(d[1], s1, acc[1]);
+                // (pins the groups' sums here, as in the 16-row kernel)
+                asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const float v = moe::sum8_lanes(acc[g]);
+            const int r = g0 + g * 8 + grp;
+            if (sub == 0 && own[g]) {
+                a.y[(size_t)p * H + r] = v;
+                sums[j * ROWS + r - row0] = v;
+            }
+        }
+    }
+    int *cp = reinterpret_cast<int *>(sums + 8 * ROWS);
+    float *cw = reinterpret_cast<float *>(cp + 8);
+    if (tid < 8) {
+        cp[tid] = pc;
+        cw[tid] = wc;
+    }
+    moe::lds_barrier();
+    if (tid < ROWS) {
+        float o = 0.0f;
+        for (int jj = 0; jj < a.k; ++jj)
+            if (cp[jj] >= 0) o = __fadd_rn(o, __fmul_rn(cw[jj], sums[jj * ROWS + tid]));
+        a.out[row0 + tid] = o;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // fused decode layer: route pack, gate/up + SwiGLU, down and combine in one launch
 // ---------------------------------------------------------------------------
@@ -1210,6 +1345,14 @@ void down1_launch(const Down1Args &a, hipStream_t st)
                        (size_t)8 * I * 4 + 8 * 8 * RG * 4 + 64, st, a);
 }
 
+template <int CH, int NCH>
+void down1p_launch(const Down1Args &a, hipStream_t st)
+{
+    constexpr int I = NCH * CH * 128;
+    hipLaunchKernelGGL((gemv_down1p_e4m3_kernel<CH, NCH>), dim3(a.H / 28), dim3(1024),
+                       (size_t)16 * I * 4 + 8 * 28 * 4 + 64, st, a);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_gateup_e4m3(const GemvBankDev &gate, const GemvBankDev &up,
@@ -1296,6 +1439,27 @@ hipError_t launch_gemv_down1_e4m3(const GemvBankDev &down, const float *h, const
     a.codes = down.codes; a.scales = (const float *)down.scales; a.h = h;
     a.ids = ids; a.t2p = t2p; a.w = w; a.y = y; a.out = out;
     a.H = hidden; a.k = k;
+    // The grid is a single round, so the CU with the most rows sets the
+    // length: 28-row blocks (16 waves, a 4 KB h row per wave, so inter up to
+    // 2048) where hidden is a multiple of 28 and they leave the busiest CU
+    // fewer rows than 16-row blocks do.
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    auto busiest = [&](int rows) { return (hidden / rows + cus - 1) / cus * rows; };
+    if (hidden % 28 == 0 && inter <= 2048 && busiest(28) < busiest(16)) {
+        switch (inter / 512) {
+        case 1: down1p_launch<4, 1>(a, st); break;
+        case 2: down1p_launch<4, 2>(a, st); break;
+        case 3: down1p_launch<4, 3>(a, st); break;
+        default: down1p_launch<4, 4>(a, st); break;
+        }
+        return hipGetLastError();
+    }
     switch (inter / 512) {
     case 1: down1_launch<4, 1, 2>(a, st); break;
     case 2: down1_launch<4, 2, 2>(a, st); break;

@@ -233,6 +233,11 @@ REDUCED = [
     ("nvfp4_h6144_i512", "nvfp4_m1", dict(hidden=6144, inter=512, experts=6, top_k=5), [1]),
     ("nvfp4_h6144_i2048", "nvfp4_m1", dict(hidden=6144, inter=2048, experts=5, top_k=3), [1]),
     ("e4m3_h640_i1280", "tiny_e4m3_m1", dict(hidden=640, inter=1280, experts=5, top_k=3), [4, 6]),
+    # one token, hidden a multiple of 28 with more 16-row blocks than the 256
+    # CUs: the combining down kernel takes 28-row blocks, two waves per slot
+    ("e4m3_h4480_i1024", "tiny_e4m3_m1", dict(hidden=4480, inter=1024, experts=10, top_k=8), [1]),
+    ("e4m3_h7168_i512", "tiny_e4m3_m1", dict(hidden=7168, inter=512, experts=6, top_k=5), [1]),
+    ("e4m3_h4480_i1536", "tiny_e4m3_m1", dict(hidden=4480, inter=1536, experts=5, top_k=3), [1]),
 ]
 
 
