@@ -865,15 +865,16 @@ __global__ __launch_bounds__(512, RG <= 2 ? 4 : 2) void gemv_down1_e4m3_kernel(D
 
 // The same for hidden sizes that are multiples of 28 (7168 = 256 x 28), where
 // 16-row blocks leave the CUs unevenly loaded: at 7168 rows they make 448
-// blocks, two on most CUs and one on the rest, and a CU streams at about the
-// same rate with one block as with two, so the CUs with two set the length.
-// Here a block owns 28 output rows for every slot (one block per CU at
-// 7168) and has two waves per slot.  Rows stay in 8-row groups aligned to 8
-// with 8 lanes per row, as in the down item: the block's rows lie in the four
-// aligned groups from base8 = row0 rounded down to 8, and wave 2j + hh takes
-// groups 2hh and 2hh + 1 of slot j.  Four rows of the end group belong to the
-// neighbouring block; their lanes load the same bytes as the lanes 4 rows
-// away (no extra traffic) and store nothing.  Each wave stages slot j's h row
+// blocks, two on most CUs and one on the rest, and the CUs with one block
+// finish early and sit idle while those with two stream on.  Here a block
+// owns 28 output rows for every slot (one block per CU at 7168) and has two
+// waves per slot.  Rows stay in 8-row groups aligned to 8 with 8 lanes per
+// row, as in the down item: the block's rows lie in the four aligned groups
+// from base8 = row0 rounded down to 8, and wave 2j + hh takes groups 2hh and
+// 2hh + 1 of slot j.  When row0 is not a multiple of 8, the first group holds
+// 4 rows of the previous block, else the last group holds 4 rows of the next
+// one; the lanes of those rows load the same bytes as the lanes 4 rows away
+// (no extra traffic) and store nothing.  Each wave stages slot j's h row
 // in an LDS region of its own.  Every row's products and their order are the
 // down item's (y is bit-identical), and the block adds the slots' rows in
 // slot order.
