@@ -1112,6 +1112,24 @@ void gateup_launch(const GateUpArgs &a, int grid, hipStream_t st)
                        lds, st, a);
 }
 
+// Passes of one slot: unrolled kernels for 2-segment chunks (hidden a
+// multiple of 512 up to 8192).  At one token the launch is a single round of
+// blocks, and the smaller chunks start multiplying sooner: 16.8-17.0 against
+// 17.0-17.3 us with 4-segment chunks at hidden 6144.
+template <bool ROUTE, int N = 1>
+bool gateup_launch_unrolled1(const GateUpArgs &a, int nch, int grid, hipStream_t st)
+{
+    if constexpr (N > 16) {
+        return false;
+    } else {
+        if (nch == N) {
+            gateup_launch<2, N, 1, ROUTE>(a, grid, st);
+            return true;
+        }
+        return gateup_launch_unrolled1<ROUTE, N + 1>(a, nch, grid, st);
+    }
+}
+
 // Unrolled kernels for 4-segment chunks (hidden a multiple of 1024 up to
 // 8192) per pass size; every other shape runs the looped kernel.
 template <int ST, bool ROUTE>
@@ -1150,11 +1168,11 @@ void gateup_dispatch(const GateUpArgs &a, int grid, hipStream_t st)
 {
     if (a.st > gemv_gateup_pass_slots(a.st, a.H, kGUST) && a.st <= kGUXW && gateup_launch_xw<ROUTE>(a, grid, st))
         return;
+    if (a.st <= 1 && a.H % 512 == 0 && gateup_launch_unrolled1<ROUTE>(a, a.H / 512, grid, st)) return;
     const int ch = gemv_chunk_segs(kFmtNVFP4, a.H), nch = a.H / kSegK / ch;
     bool done = false;
-    if (ch == 4) {
-        if (a.st <= 1) done = gateup_launch_unrolled<1, ROUTE>(a, nch, grid, st);
-        else if (a.st <= 2) done = gateup_launch_unrolled<2, ROUTE>(a, nch, grid, st);
+    if (ch == 4 && a.st > 1) {
+        if (a.st <= 2) done = gateup_launch_unrolled<2, ROUTE>(a, nch, grid, st);
         else done = gateup_launch_unrolled<8, ROUTE>(a, nch, grid, st);
     }
     if (!done) {
@@ -1211,10 +1229,12 @@ void down1_launch(const Down1Args &a, hipStream_t st)
                        a);
 }
 
+// (the 24-row blocks stream 1-segment chunks: 10.7 against 11.2 us with 2
+// at 6144 x 1536)
 template <int NCH>
 void down1_launch_rg(const Down1Args &a, int rg, hipStream_t st)
 {
-    if (rg == 3) down1_launch<2, NCH, 3>(a, st);
+    if (rg == 3) down1_launch<1, 2 * NCH, 3>(a, st);
     else down1_launch<2, NCH, 2>(a, st);
 }
 
