@@ -356,21 +356,21 @@ def cpu_baseline(wl, banks, x, sets, budget_s, stride=1, act_fp8=False):
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC = {
     "decode_e4m3_m1": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
-        "src": "b02957c371de2375d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 115083, "write_kib": 65},
+        "src": "cde11db9bf57e724d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 115083, "write_kib": 65},
     "decode_e4m3_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
-        "src": "b02957c371de2375d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 173069, "write_kib": 1070},
+        "src": "cde11db9bf57e724d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 173074, "write_kib": 1070},
     "nvfp4_m1": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "857c056872b489cdd7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 41626, "write_kib": 49},
+        "src": "9a1dcecde0b5c179d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 41626, "write_kib": 49},
     "nvfp4_m1/fused": {"kernel": "moe_fused_decode", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "857c056872b489cdd7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 64881, "write_kib": 835},
+        "src": "9a1dcecde0b5c179d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 64883, "write_kib": 835},
     "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h"],
         "src": "e7bd3c69fc01c3df46ff9d1401442f7fe0174e2455c8b818", "fetch_kib": 4022574, "write_kib": 68917},
     "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
         "src": "90d4f2b67c21b99a46ff9d1401442f7fe0174e2455c8b818", "fetch_kib": 2060542, "write_kib": 196608},
     "verify_e4m3_m8": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
-        "src": "b02957c371de2375d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 646022, "write_kib": 514},
+        "src": "cde11db9bf57e724d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 646018, "write_kib": 514},
     "nvfp4_m16": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],
-        "src": "857c056872b489cdd7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 444735, "write_kib": 768},
+        "src": "9a1dcecde0b5c179d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 444742, "write_kib": 768},
 }
 
 
