@@ -152,6 +152,38 @@ def test_route_pack_bit_exact_small_routes(case):
     assert_pack_equal(gpu_pack(ids, E), oracle.route_pack(ids, E), ids.size)
 
 
+@pytest.mark.parametrize("case", ["s65", "s128_e160", "s200_invalid", "s256_e512", "s256_one_expert",
+                                  "s129_dups", "s96_k12"])
+def test_route_pack_bit_exact_mid_routes(case):
+    """Routes of 65 to 256 slots (the one-workgroup pack above the one-wave one)."""
+    rng = np.random.default_rng(31)
+    if case == "s65":
+        ids, E = rng.integers(0, 20, (65, 1)).astype(np.int32), 20
+    elif case == "s128_e160":
+        E = 160
+        ids = np.stack([rng.choice(E, 8, replace=False) for _ in range(16)]).astype(np.int32)
+    elif case == "s200_invalid":
+        E = 50
+        ids = rng.integers(0, E, (25, 8)).astype(np.int32)
+        flat = ids.ravel()
+        pos = rng.choice(flat.size, 30, replace=False)
+        flat[pos[:10]] = -1
+        flat[pos[10:20]] = E + rng.integers(0, 9, 10)
+        flat[pos[20:]] = -rng.integers(2, 99, 10)
+    elif case == "s256_e512":
+        E = 512
+        ids = np.stack([rng.choice(E, 8, replace=False) for _ in range(32)]).astype(np.int32)
+    elif case == "s256_one_expert":
+        ids, E = np.full((32, 8), 3, np.int32), 9
+    elif case == "s129_dups":
+        ids, E = rng.integers(0, 3, (43, 3)).astype(np.int32), 3
+    else:
+        ids, E = rng.integers(-1, 24, (8, 12)).astype(np.int32), 24
+    assert 64 < ids.size <= 256
+    print(f"route_pack mid {case} S={ids.size} E={E}", flush=True)
+    assert_pack_equal(gpu_pack(ids, E), oracle.route_pack(ids, E), ids.size)
+
+
 # --------------------------------------------------------------------------
 # layer parity
 # --------------------------------------------------------------------------
