@@ -8,8 +8,11 @@
 // list doubles as the union of the rows' experts that the multi-row GEMV
 // sweeps once per expert.
 //
-// One workgroup of 1024 threads (16 wave64s); wave w owns a contiguous run
-// of whole 64-slot groups, so ordering by (wave, group, lane) is slot order:
+// Routes of up to 64 slots and of 65 to 128 take one-wave kernels of their
+// own (below); 8192 slots and more a split pack of three launches.  The
+// general form is one workgroup of 1024 threads (16 wave64s); wave w owns a
+// contiguous run of whole 64-slot groups, so ordering by (wave, group, lane)
+// is slot order:
 //   1. Each wave counts its slots per expert.  Inside a group, lanes holding
 //      the same expert find each other by ballots over the id bits; the
 //      lowest such lane adds the group's count to the wave's LDS counter (one
@@ -367,6 +370,99 @@ __global__ __launch_bounds__(64) void route_pack_small_kernel(
     }
 }
 
+// Routes of 65 to 128 slots (verify and NVFP4 at 16 tokens): one wave, lane
+// l holding slots l and l + 64.  The key is the expert of a valid slot and E
+// for any other slot, so it sorts after every expert.  One ballot per key bit
+// and half, most significant bit first, gives for each of a lane's two keys
+// the slots of each half holding a smaller key (lt) and an equal one (eq).  A
+// valid slot's packed position is then popcount(lt) plus the equal keys in
+// earlier slots: the stable pack.  The first slot of each expert holds that
+// expert's first packed row, and expert_offsets is the suffix minimum of
+// those rows over the experts (an expert with no slot takes the next one's),
+// with the valid-slot count past the last.  Same tables, bit for bit, as the
+// general kernel.
+__global__ __launch_bounds__(64) void route_pack_pair_kernel(
+    const int32_t *__restrict__ ids, int32_t S, int32_t k, int32_t E,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
+    int32_t *__restrict__ sorted_token, int32_t *__restrict__ token_to_perm,
+    int32_t *__restrict__ active, int32_t *__restrict__ num_active,
+    int32_t *__restrict__ status)
+{
+    __shared__ int32_t fp[MOE_MAX_EXPERTS + 1];      // first packed row per expert, else nvalid
+    const int lane = threadIdx.x;
+    const int id0 = lane < S ? ids[lane] : -1;
+    const int id1 = lane + 64 < S ? ids[lane + 64] : -1;
+    const bool v0 = id0 >= 0 && id0 < E, v1 = id1 >= 0 && id1 < E;
+    const int k0 = v0 ? id0 : E, k1 = v1 ? id1 : E;
+    const int nbad = __popcll(__ballot(lane < S && !v0 && id0 != -1)) +
+                     __popcll(__ballot(lane + 64 < S && !v1 && id1 != -1));
+    const int nvalid = __popcll(__ballot(v0)) + __popcll(__ballot(v1));
+    uint64_t lt00 = 0, eq00 = ~0ull, lt01 = 0, eq01 = ~0ull;   // key k0 against halves 0, 1
+    uint64_t lt10 = 0, eq10 = ~0ull, lt11 = 0, eq11 = ~0ull;   // key k1 against halves 0, 1
+    for (int b = 9; b >= 0; --b) {                   // keys <= E <= 512
+        const uint64_t b0 = __ballot((k0 >> b) & 1), b1 = __ballot((k1 >> b) & 1);
+        if ((k0 >> b) & 1) {
+            lt00 |= eq00 & ~b0; eq00 &= b0;
+            lt01 |= eq01 & ~b1; eq01 &= b1;
+        } else {
+            eq00 &= ~b0; eq01 &= ~b1;
+        }
+        if ((k1 >> b) & 1) {
+            lt10 |= eq10 & ~b0; eq10 &= b0;
+            lt11 |= eq11 & ~b1; eq11 &= b1;
+        } else {
+            eq10 &= ~b0; eq11 &= ~b1;
+        }
+    }
+    const uint64_t below = (1ull << lane) - 1;
+    // slot l has the earlier slots of half 0 below it; slot 64 + l all of
+    // half 0 and the earlier slots of half 1
+    const int pos0 = __popcll(lt00) + __popcll(lt01) + __popcll(eq00 & below);
+    const int pos1 = __popcll(lt10) + __popcll(lt11) + __popcll(eq10) + __popcll(eq11 & below);
+    const bool first0 = v0 && (eq00 & below) == 0;
+    const bool first1 = v1 && eq10 == 0 && (eq11 & below) == 0;
+    const uint64_t fm0 = __ballot(first0), fm1 = __ballot(first1);
+    const int na = __popcll(fm0) + __popcll(fm1);
+    if (lane < S) token_to_perm[lane] = v0 ? pos0 : -1;
+    if (lane + 64 < S) token_to_perm[lane + 64] = v1 ? pos1 : -1;
+    if (v0) {
+        sorted_slot[pos0] = lane;
+        sorted_token[pos0] = lane / k;
+    }
+    if (v1) {
+        sorted_slot[pos1] = lane + 64;
+        sorted_token[pos1] = (lane + 64) / k;
+    }
+    // the ascending active list: an expert's rank is the distinct experts below it
+    if (first0) active[__popcll(lt00 & fm0) + __popcll(lt01 & fm1)] = k0;
+    if (first1) active[__popcll(lt10 & fm0) + __popcll(lt11 & fm1)] = k1;
+    const int A = S < E ? S : E;
+    for (int i = na + lane; i < A; i += 64) active[i] = -1;
+    // expert_offsets
+    for (int e = lane; e <= E; e += 64) fp[e] = nvalid;
+    moe::lds_barrier();
+    if (first0) fp[k0] = pos0;
+    if (first1) fp[k1] = pos1;
+    moe::lds_barrier();
+    int carry = nvalid;
+    for (int c0 = E & ~63; c0 >= 0; c0 -= 64) {
+        const int e = c0 + lane;
+        int v = e <= E ? fp[e] : nvalid;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_down(v, d, 64);
+            if (lane + d < 64) v = min(v, o);
+        }
+        v = min(v, carry);
+        if (e <= E) offsets[e] = v;
+        carry = __builtin_amdgcn_readfirstlane(v);
+    }
+    if (lane == 0) {
+        *num_active = na;
+        *status = nbad;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route_pack(const int32_t *ids, int32_t M, int32_t k, int32_t E,
@@ -375,6 +471,12 @@ hipError_t launch_route_pack(const int32_t *ids, int32_t M, int32_t k, int32_t E
     const int32_t S = M * k;
     if (S <= 64) {
         hipLaunchKernelGGL(route_pack_small_kernel, dim3(1), dim3(64), 0, st, ids, S, k, E, r.offsets,
+                           r.sorted_slot, r.sorted_token, r.token_to_perm, r.active, r.num_active,
+                           r.status);
+        return hipGetLastError();
+    }
+    if (S <= 128) {
+        hipLaunchKernelGGL(route_pack_pair_kernel, dim3(1), dim3(64), 0, st, ids, S, k, E, r.offsets,
                            r.sorted_slot, r.sorted_token, r.token_to_perm, r.active, r.num_active,
                            r.status);
         return hipGetLastError();

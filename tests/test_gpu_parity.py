@@ -155,7 +155,8 @@ def test_route_pack_bit_exact_small_routes(case):
 @pytest.mark.parametrize("case", ["s65", "s128_e160", "s200_invalid", "s256_e512", "s256_one_expert",
                                   "s129_dups", "s96_k12"])
 def test_route_pack_bit_exact_mid_routes(case):
-    """Routes of 65 to 256 slots (the one-workgroup pack above the one-wave one)."""
+    """Routes of 65 to 256 slots: up to 128 a one-wave kernel with two slots
+    per lane, above that the one-workgroup one."""
     rng = np.random.default_rng(31)
     if case == "s65":
         ids, E = rng.integers(0, 20, (65, 1)).astype(np.int32), 20
