@@ -185,6 +185,30 @@ def test_route_pack_bit_exact_mid_routes(case):
     assert_pack_equal(gpu_pack(ids, E), oracle.route_pack(ids, E), ids.size)
 
 
+def test_route_pack_bit_exact_random_65_to_128_slots():
+    """60 random routes of 65 to 128 slots (the two-slots-per-lane one-wave
+    kernel): random top_k dividing S, expert counts from 1 to 512, invalid
+    ids of every kind in a third of them, a handful of experts in others."""
+    rng = np.random.default_rng(37)
+    n = 0
+    while n < 60:
+        S = int(rng.integers(65, 129))
+        k = int(rng.choice([d for d in range(1, 13) if S % d == 0]))
+        E = int(rng.choice([1, 2, 3, 7, 20, 64, 100, 160, 256, 257, 511, 512]))
+        if k > E:
+            continue
+        ids = rng.integers(0, E, S).astype(np.int32)
+        if n % 3 == 0:
+            pos = rng.choice(S, int(rng.integers(1, 20)), replace=False)
+            ids[pos] = rng.choice([-1, E, E + 5, -7], pos.size)
+        if n % 7 == 0:
+            ids[:] = rng.integers(0, min(E, 3), S)
+        ids = ids.reshape(S // k, k)
+        assert_pack_equal(gpu_pack(ids, E), oracle.route_pack(ids, E), ids.size)
+        n += 1
+    print(f"route_pack random mid: {n} routes", flush=True)
+
+
 # --------------------------------------------------------------------------
 # layer parity
 # --------------------------------------------------------------------------
