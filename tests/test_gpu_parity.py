@@ -295,6 +295,9 @@ REDUCED = [
     ("e4m3_h4480_i1024", "tiny_e4m3_m1", dict(hidden=4480, inter=1024, experts=10, top_k=8), [1]),
     ("e4m3_h7168_i512", "tiny_e4m3_m1", dict(hidden=7168, inter=512, experts=6, top_k=5), [1]),
     ("e4m3_h4480_i1536", "tiny_e4m3_m1", dict(hidden=4480, inter=1536, experts=5, top_k=3), [1]),
+    # the same forms with one slot: every other wave of the block has none
+    ("e4m3_h7168_i1024_k1", "tiny_e4m3_m1", dict(hidden=7168, inter=1024, experts=3, top_k=1), [1]),
+    ("nvfp4_h6144_i1536_k1", "nvfp4_m1", dict(hidden=6144, inter=1536, experts=3, top_k=1), [1]),
 ]
 
 
