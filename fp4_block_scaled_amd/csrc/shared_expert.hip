@@ -6,13 +6,16 @@
 //
 // One expert of width W gives only W/16 blocks in the GEMV layout of the
 // routed tiers, so both projections here give a whole wave to one weight row:
-//   gate/up: a block = 2 h rows; wave w streams row 2r + (w & 1) of the gate
-//            (w < 2) or up (w >= 2) bank, lane l holding bytes 1024 j + 16 l of
-//            the row for j < H/512 in registers, then loops over the tokens,
-//            reading their x from L2, and reduces over the 64 lanes; the gate
+//   gate/up: a block = 2R h rows; wave w streams R rows of the gate (w < 2)
+//            or up (w >= 2) bank, rows 2Rb + R(w & 1) + r, lane l holding bytes
+//            1024 j + 16 l of each row for j < H/512 in registers, then loops
+//            over the tokens, reading their x from L2 once per R rows (R up to
+//            2 for H <= 7168, else 1), and reduces over the 64 lanes; the gate
 //            waves apply the clamped SwiGLU and write h (FP32).
-//   down:    a block = 4 output rows, one per wave, the same way over W with
-//            the FP32 h rows read from L2.
+//   down:    a block = 4 waves of R output rows each, the same way over W
+//            with the FP32 h rows read from L2 once per R rows (R up to 4 for
+//            W <= 2048, 2 for W <= 4096, else 1: the weights of a wave's rows
+//            stay in registers).
 // Products are bf16 x bf16 in v_dot2_f32_bf16 (gate/up) and FP32 (down), so
 // only the summation order differs from the FP64 definition.
 #include "moe_internal.h"
@@ -51,43 +54,57 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
     return gc / (1.0f + expf(-gc)) * uc;
 }
 
-// NJ = H / 512 loads of 16 bytes per lane
-template <int NJ>
+// NJ = H / 512 loads of 16 bytes per lane and row; R rows per wave
+template <int NJ, int R>
 __global__ __launch_bounds__(kThreads) void shared_gateup_kernel(const uint16_t *__restrict__ gate,
                                                                  const uint16_t *__restrict__ up,
                                                                  const uint16_t *__restrict__ x,
                                                                  int32_t M, int32_t H, int32_t W,
                                                                  float limit, float *__restrict__ h)
 {
-    __shared__ float gu[4][kMaxTok];
+    __shared__ float gu[4][R][kMaxTok];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
-    const int row = 2 * blockIdx.x + (wave & 1);
+    const int row0 = 2 * R * blockIdx.x + R * (wave & 1);
     const uint8_t *rp = reinterpret_cast<const uint8_t *>(moe::uniform_ptr(wave < 2 ? gate : up) +
-                                                          (size_t)row * H);
-    uint4 w[NJ];
+                                                          (size_t)row0 * H);
+    uint4 w[R][NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) w[j] = load16(rp + j * 1024 + lane * 16);
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) w[r][j] = load16(rp + (size_t)r * H * 2 + j * 1024 + lane * 16);
     for (int t = 0; t < M; ++t) {
         const uint8_t *xp = reinterpret_cast<const uint8_t *>(x + (size_t)t * H);
-        float acc = 0.0f;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const uint4 xv = *reinterpret_cast<const uint4 *>(xp + j * 1024 + lane * 16);
-            acc = dot2(w[j].x, xv.x, acc);
-            acc = dot2(w[j].y, xv.y, acc);
-            acc = dot2(w[j].z, xv.z, acc);
-            acc = dot2(w[j].w, xv.w, acc);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                acc[r] = dot2(w[r][j].x, xv.x, acc[r]);
+                acc[r] = dot2(w[r][j].y, xv.y, acc[r]);
+                acc[r] = dot2(w[r][j].z, xv.z, acc[r]);
+                acc[r] = dot2(w[r][j].w, xv.w, acc[r]);
+            }
         }
-        acc = wave_sum(acc);
-        if (lane == 0) gu[wave][t] = acc;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float v = wave_sum(acc[r]);
+            if (lane == 0) gu[wave][r][t] = v;
+        }
     }
     __syncthreads();
-    if (wave < 2 && lane < M) h[(size_t)lane * W + row] = swiglu_clamp(gu[wave][lane], gu[wave + 2][lane], limit);
+    if (wave < 2 && lane < M) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            h[(size_t)lane * W + row0 + r] = swiglu_clamp(gu[wave][r][lane], gu[wave + 2][r][lane], limit);
+    }
 }
 
-// NJ = W / 512 loads of 16 bytes per lane
-template <int NJ>
+// NJ = W / 512 loads of 16 bytes per lane and row; R rows per wave
+template <int NJ, int R>
 __global__ __launch_bounds__(kThreads) void shared_down_kernel(const uint16_t *__restrict__ down,
                                                                const float *__restrict__ h,
                                                                int32_t M, int32_t H, int32_t W,
@@ -95,46 +112,95 @@ __global__ __launch_bounds__(kThreads) void shared_down_kernel(const uint16_t *_
 {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
-    const int row = 4 * blockIdx.x + wave;
-    if (row >= H) return;                            // whole wave
-    const uint8_t *rp = reinterpret_cast<const uint8_t *>(moe::uniform_ptr(down) + (size_t)row * W);
-    uint4 w[NJ];
+    const int row0 = (4 * blockIdx.x + wave) * R;
+    if (row0 >= H) return;                           // whole wave (H is a multiple of 4R)
+    const uint8_t *rp = reinterpret_cast<const uint8_t *>(moe::uniform_ptr(down) + (size_t)row0 * W);
+    uint4 w[R][NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) w[j] = load16(rp + j * 1024 + lane * 16);
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) w[r][j] = load16(rp + (size_t)r * W * 2 + j * 1024 + lane * 16);
     for (int t = 0; t < M; ++t) {
         const float *hp = h + (size_t)t * W;
-        float acc = 0.0f;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const float4 a = *reinterpret_cast<const float4 *>(hp + j * 512 + lane * 8);
             const float4 b = *reinterpret_cast<const float4 *>(hp + j * 512 + lane * 8 + 4);
-            const uint32_t q[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
             const float hv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc = fmaf(__uint_as_float(q[i] << 16), hv[2 * i], acc);
-                acc = fmaf(__uint_as_float(q[i] & 0xFFFF0000u), hv[2 * i + 1], acc);
+            for (int r = 0; r < R; ++r) {
+                const uint32_t q[4] = {w[r][j].x, w[r][j].y, w[r][j].z, w[r][j].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[r] = fmaf(__uint_as_float(q[i] << 16), hv[2 * i], acc[r]);
+                    acc[r] = fmaf(__uint_as_float(q[i] & 0xFFFF0000u), hv[2 * i + 1], acc[r]);
+                }
             }
         }
-        acc = wave_sum(acc);
-        if (lane == 0) out[(size_t)t * H + row] = acc;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float v = wave_sum(acc[r]);
+            if (lane == 0) out[(size_t)t * H + row0 + r] = v;
+        }
     }
+}
+
+// Rows per wave: with several tokens the largest R the registers allow (the
+// x or h reads from L2 shrink by R); with one token the R whose grid puts the
+// fewest rows on the busiest CU, the larger R on a tie (1536 gate/up rows:
+// 3 blocks of 2 on the busiest CU with R = 1 against 2 of 4 with R = 2).
+int pick_rows(int32_t M, int rows, int rows_per_block_r1, int rmax)
+{
+    if (M > 1) return rmax;
+    static int cus = 0;
+    if (!cus && (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess || cus < 1))
+        cus = 256;
+    int best = 1, best_rows = 1 << 30;
+    for (int r = 1; r <= rmax; r *= 2) {
+        const int per = rows_per_block_r1 * r;
+        const int busiest = (rows / per + cus - 1) / cus * per;
+        if (busiest <= best_rows) best = r, best_rows = busiest;
+    }
+    return best;
+}
+
+template <int NJ, int R>
+void gateup_launch_r(const uint16_t *gate, const uint16_t *up, const uint16_t *x, int32_t M, int32_t H,
+                     int32_t W, float limit, float *h, hipStream_t st)
+{
+    hipLaunchKernelGGL((shared_gateup_kernel<NJ, R>), dim3((unsigned)(W / (2 * R))), dim3(kThreads), 0, st,
+                       gate, up, x, M, H, W, limit, h);
 }
 
 template <int NJ>
 void gateup_launch(const uint16_t *gate, const uint16_t *up, const uint16_t *x, int32_t M,
                    int32_t H, int32_t W, float limit, float *h, hipStream_t st)
 {
-    hipLaunchKernelGGL(shared_gateup_kernel<NJ>, dim3((unsigned)(W / 2)), dim3(kThreads), 0, st, gate,
-                       up, x, M, H, W, limit, h);
+    constexpr int RMAX = NJ <= 14 ? 2 : 1;
+    if (pick_rows(M, W, 2, RMAX) == 2) gateup_launch_r<NJ, RMAX>(gate, up, x, M, H, W, limit, h, st);
+    else gateup_launch_r<NJ, 1>(gate, up, x, M, H, W, limit, h, st);
+}
+
+template <int NJ, int R>
+void down_launch_r(const uint16_t *down, const float *h, int32_t M, int32_t H, int32_t W, float *out,
+                   hipStream_t st)
+{
+    hipLaunchKernelGGL((shared_down_kernel<NJ, R>), dim3((unsigned)(H / (4 * R))), dim3(kThreads), 0, st,
+                       down, h, M, H, W, out);
 }
 
 template <int NJ>
 void down_launch(const uint16_t *down, const float *h, int32_t M, int32_t H, int32_t W, float *out,
                  hipStream_t st)
 {
-    hipLaunchKernelGGL(shared_down_kernel<NJ>, dim3((unsigned)((H + 3) / 4)), dim3(kThreads), 0, st,
-                       down, h, M, H, W, out);
+    constexpr int RMAX = NJ <= 4 ? 4 : NJ <= 8 ? 2 : 1;
+    const int r = pick_rows(M, H, 4, RMAX);
+    if (r == 4) down_launch_r<NJ, RMAX>(down, h, M, H, W, out, st);
+    else if (r == 2) down_launch_r<NJ, (RMAX >= 2 ? 2 : 1)>(down, h, M, H, W, out, st);
+    else down_launch_r<NJ, 1>(down, h, M, H, W, out, st);
 }
 
 template <int... N>
