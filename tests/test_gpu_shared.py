@@ -93,6 +93,21 @@ def test_shared_expert_workspace_reuse_and_zero_token():
     check_fp(a, ref, "shared reuse")
 
 
+@pytest.mark.parametrize("H,W", [(7168, 2048), (6144, 1536), (1024, 4096)])
+def test_shared_expert_token_alone_matches_batch(H, W):
+    """A token's shared-expert row is the same bits alone (M = 1) as inside a
+    batch of 16: the rows per wave differ between the two calls (at H7168
+    W2048 the down launch holds 1 row per wave alone and 4 in the batch; at
+    H6144 W1536 gate/up 1 against 2 and down 2 against 4), while each output's
+    sum keeps its order."""
+    print(f"shared alone-vs-batch H{H} W{W}", flush=True)
+    gate, up, down, x = shared_case(16, H, W, seed=H + W + 3)
+    batch = run_shared(gate, up, down, x)
+    for t in (0, 7, 15):
+        alone = run_shared(gate, up, down, x[t:t + 1].contiguous())
+        assert np.array_equal(alone[0], batch[t]), t
+
+
 def test_shared_expert_rejects_on_device():
     gate, up, down, x = shared_case(17, 512, 512, seed=3)
     out = torch.empty((17, 512), dtype=torch.float32, device="cuda")
