@@ -15,17 +15,22 @@
 // MFMA and multiply the FP32 sums by scale_2 at the end: every product is
 // exact and only the order of the FP32 sums differs from the definition.
 //
-// h between the projections: the gate/up epilogue computes h = SwiGLU(g, u)
-// in FP32 and stores it as two bf16 arrays, hi = bf16(h) and lo = bf16(h -
-// hi), so that hi + lo carries h to about 2^-16 relative; the down GEMM runs
-// the MFMA on both (y = W hi + W lo), keeping the FP32 h of the GEMV tier.
+// h between the projections is a 16-bit activation, as in the W4A16 form,
+// held as FP16 rather than bf16: the gate/up epilogue computes h = SwiGLU(g,
+// u) in FP32 and rounds h * 2^-k to FP16 (RNE), with 2^-k chosen from the
+// clamp limit so that |h| * 2^-k stays at or below 32768 (k = 0 for any limit
+// up to 181).  FP16's 11-bit significand keeps the layer's output within about
+// 2e-4 relative L2 of the exact one, where a bf16 h would cost about 1e-3.
+// The down GEMM decodes its NVFP4 weights to FP16, exactly (a product of at
+// most 6 significant bits between 2^-10 and 2688), runs the FP16 MFMA once,
+// and multiplies the FP32 sums by scale_2 * 2^k.
 //
 // Kernels (tiles from gemm_tiles_kernel: 128 expert-sorted rows each):
 //   gemm_gateup_nvfp4_kernel  one block = 128 rows x 64 h columns: 64 gate and
-//                             64 up weight rows per K step, SwiGLU, hi/lo h.
+//                             64 up weight rows per K step, SwiGLU, FP16 h.
 //   gemm_down_nvfp4_kernel    one block = 128 rows x 128 outputs of y.
 // Block: 256 threads = 4 waves as 2 (64 rows each) x 2 (column halves).  Per
-// K step of 64: the A rows (128 bytes of bf16 each) move from global memory
+// K step of 64: the A rows (128 bytes of bf16 x or FP16 h) move from global memory
 // straight into swizzled LDS, with the B codes (32 bytes per weight row) and
 // group scales (4 bytes per row) beside them, four stages deep.  Each wave
 // decodes its own B operands from LDS: lane l of a 16x16x32 MFMA operand
@@ -33,19 +38,22 @@
 // group scale.
 #include "gemm_common.h"
 
+#include <cmath>
+
 namespace {
 
 using moe::f32x2;
 using moe::f32x4;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TM = 128;      // rows per tile
 constexpr int KS = 64;       // K per step (128 bytes of a bf16 row)
 
 struct NvGemmArgs {
-    const uint16_t *a;            // gate/up: x [M][K]; down: h hi [S][K]
-    const uint16_t *a2;           // down: h lo [S][K]
+    const uint16_t *a;            // gate/up: x bf16 [M][K]; down: h FP16 [S][K]
     const int32_t *sorted_token;  // gate/up gathers A rows through it
     const uint8_t *c0, *c1;       // gate and up codes (down: c0), [E][N][K/2]
     const uint8_t *s0, *s1;       // their group scales [E][N][K/16]
@@ -53,15 +61,21 @@ struct NvGemmArgs {
     const int32_t *offsets;
     const int4 *tiles;
     const int32_t *ntiles;
-    uint16_t *hhi, *hlo;          // gate/up output [S][N]
+    uint16_t *h;                  // gate/up output, FP16 h * hscale [S][N]
     float *y;                     // down output [S][N]
     int32_t K, N, ntn;            // ntn: column blocks
     float limit;
+    float hscale;                 // gate/up: 2^-k; down: 2^k
 };
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Eight consecutive K values of one weight row: code dword c (element 2i in
@@ -80,26 +94,40 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t c, float sc)
     return __builtin_bit_cast(bf16x8, o);
 }
 
-// 16-byte A operand of lane `lane` (K values 8(lane/16) .. +7 of K half ks)
-// for tile row `row`
-__device__ __forceinline__ bf16x8 a_op(const uint8_t *tile, int row, int ks, int lane)
+// The same eight weights as FP16: E2M1 pairs convert exactly and the E4M3
+// group scale is an FP16 value, so the packed products are exact too.
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t c, float sc)
 {
-    return *reinterpret_cast<const bf16x8 *>(tile + row * 128 + swz(row, ks * 4 + (lane >> 4)) * 16);
+    const _Float16 h = (_Float16)sc;
+    const f16x2 s2 = {h, h};
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((int)c, 1.0f, 0) * s2;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((int)c, 1.0f, 1) * s2;
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((int)c, 1.0f, 2) * s2;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((int)c, 1.0f, 3) * s2;
+    return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-// B operand of lane `lane` for B row `br` and K half ks: the code dword of
-// its 8 K values and the scale of their 16-group, from the stage's code and
+// 16-byte A operand of lane `lane` (K values 8(lane/16) .. +7 of K half ks)
+// for tile row `row`
+template <typename T>
+__device__ __forceinline__ T a_op(const uint8_t *tile, int row, int ks, int lane)
+{
+    return *reinterpret_cast<const T *>(tile + row * 128 + swz(row, ks * 4 + (lane >> 4)) * 16);
+}
+
+// FP16 B operand of lane `lane` for B row `br` and K half ks: the code dword
+// of its 8 K values and the scale of their 16-group, from the stage's code and
 // scale regions (codes row-major 32 bytes per row; scales one dword per row,
 // rows in runs of 32 per 256 bytes)
-__device__ __forceinline__ bf16x8 b_op(const uint8_t *codes, const uint8_t *scales, int br, int ks,
-                                       int lane)
+__device__ __forceinline__ f16x8 b_op16(const uint8_t *codes, const uint8_t *scales, int br, int ks,
+                                        int lane)
 {
     const uint32_t c = *reinterpret_cast<const uint32_t *>(codes + br * 32 + ks * 16 + (lane >> 4) * 4);
     const uint32_t sd = *reinterpret_cast<const uint32_t *>(scales + (br >> 5) * 256 + (br & 31) * 4);
     const uint32_t sb = sd >> ((lane >> 5) * 8);       // group 2 ks + lane/32 in byte 2 ks
     const float sc = ks == 0 ? __builtin_amdgcn_cvt_f32_fp8((int)sb, 0)
                              : __builtin_amdgcn_cvt_f32_fp8((int)sb, 2);
-    return dequant8(c, sc);
+    return dequant8_f16(c, sc);
 }
 
 __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
@@ -109,15 +137,8 @@ __device__ __forceinline__ float swiglu_clamp(float g, float u, float L)
     return gc / (1.0f + expf(-gc)) * uc;
 }
 
-// bf16 of a finite float, round to nearest even
-__device__ __forceinline__ uint32_t bf16_rne(float f)
-{
-    const uint32_t b = __float_as_uint(f);
-    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
 // ---------------------------------------------------------------------------
-// gate + up (+ SwiGLU, h as hi/lo bf16)
+// gate + up (+ SwiGLU, h as FP16)
 // ---------------------------------------------------------------------------
 // Block: W waves; wave w = all 128 rows x h columns 32w..32w+31 of both gate
 // and up, so each decoded B operand feeds 8 MFMAs (one per 16-row group).
@@ -204,7 +225,7 @@ __global__ __launch_bounds__(GuLayout<W>::threads, OCC) void gemm_gateup_nvfp4_k
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 av[8];
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) av[mt] = a_op(st + Lo::A, mt * 16 + (lane & 15), ks, lane);
+            for (int mt = 0; mt < 8; ++mt) av[mt] = a_op<bf16x8>(st + Lo::A, mt * 16 + (lane & 15), ks, lane);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const int rg = wave * 32 + nt * 16 + (lane & 15);
@@ -222,12 +243,11 @@ __global__ __launch_bounds__(GuLayout<W>::threads, OCC) void gemm_gateup_nvfp4_k
     k_loop<NST, Lo::dma>(KB, sm, Lo::STAGE, issue, compute);
     __syncthreads();
 
-    // epilogue: h = SwiGLU(sg g, su u) -> hi, lo tiles [128][128] bf16 in LDS
-    // (rows padded to 136 elements), then 16-byte stores of the valid rows
+    // epilogue: h = SwiGLU(sg g, su u) -> FP16 tile [128][128] in LDS (rows
+    // padded to 136 elements), then 16-byte stores of the valid rows
     constexpr int C = Lo::cols, CP = C + 8;
-    static_assert(2 * TM * CP * 2 <= NST * Lo::STAGE, "h tiles exceed the stages");
+    static_assert(TM * CP * 2 <= NST * Lo::STAGE, "the h tile exceeds the stages");
     uint16_t *th = reinterpret_cast<uint16_t *>(sm);
-    uint16_t *tl = th + TM * CP;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -237,9 +257,7 @@ __global__ __launch_bounds__(GuLayout<W>::threads, OCC) void gemm_gateup_nvfp4_k
                 const int r = mt * 16 + (lane >> 4) * 4 + i;
                 const int c = wave * 32 + nt * 16 + (lane & 15);
                 const float h = swiglu_clamp(accg[mt][nt][i] * sg, accu[mt][nt][i] * su, a.limit);
-                const uint32_t hi = bf16_rne(h);
-                th[r * CP + c] = (uint16_t)hi;
-                tl[r * CP + c] = (uint16_t)bf16_rne(h - __uint_as_float(hi << 16));
+                th[r * CP + c] = __builtin_bit_cast(uint16_t, (_Float16)(h * a.hscale));
             }
     __syncthreads();
     constexpr int cpr = C / 8;                        // 16-byte chunks per row
@@ -248,8 +266,7 @@ __global__ __launch_bounds__(GuLayout<W>::threads, OCC) void gemm_gateup_nvfp4_k
         const int ch = tid + Lo::threads * j, r = ch / cpr, part = ch % cpr;
         if (r < rows) {
             const size_t o = (size_t)(p0 + r) * N + n0 + part * 8;
-            *reinterpret_cast<uint4 *>(a.hhi + o) = *reinterpret_cast<const uint4 *>(th + r * CP + part * 8);
-            *reinterpret_cast<uint4 *>(a.hlo + o) = *reinterpret_cast<const uint4 *>(tl + r * CP + part * 8);
+            *reinterpret_cast<uint4 *>(a.h + o) = *reinterpret_cast<const uint4 *>(th + r * CP + part * 8);
         }
     }
 }
@@ -259,15 +276,14 @@ __global__ __launch_bounds__(GuLayout<W>::threads, OCC) void gemm_gateup_nvfp4_k
 // ---------------------------------------------------------------------------
 // Block: 2 x NW waves, wave (wm, wn) = 64 rows x 64 outputs; the tile is
 // 128 rows x 64 NW outputs.  Wave w loads B rows 32w..32w+31.
-// Stage: A hi [128][128 B] | A lo [128][128 B] | B codes [64 NW][32 B] | B scales
+// Stage: A (FP16 h) [128][128 B] | B codes [64 NW][32 B] | B scales
 template <int NW>
 struct DnLayout {
     static constexpr int threads = 128 * NW;
     static constexpr int cols = 64 * NW;
-    static constexpr int A = 0, A2 = TM * 128, C = 2 * TM * 128, S = C + 64 * NW * 32,
-                         STAGE = S + 2 * NW * 256;
-    static constexpr int arun = 8 / NW;          // runs of 8 rows per wave, for hi and for lo
-    static constexpr int dma = 2 * arun + 2;
+    static constexpr int A = 0, C = TM * 128, S = C + 64 * NW * 32, STAGE = S + 2 * NW * 256;
+    static constexpr int arun = 8 / NW;          // runs of 8 rows per wave
+    static constexpr int dma = arun + 2;
 };
 
 template <int NW, int NST, int OCC>
@@ -285,7 +301,7 @@ __global__ __launch_bounds__(DnLayout<NW>::threads, OCC) void gemm_down_nvfp4_ke
     const int rows = moe::uniform(min(TM, a.offsets[e + 1] - p0));
     const int K = a.K, N = a.N, KB = K / KS;
     const int n0 = nb * Lo::cols;
-    const float sd = a.g0[e];
+    const float sd = a.g0[e] * a.hscale;           // scale_2 x 2^k
 
     uint32_t aoff[Lo::arun];
 #pragma unroll
@@ -301,13 +317,9 @@ __global__ __launch_bounds__(DnLayout<NW>::threads, OCC) void gemm_down_nvfp4_ke
 
     auto issue = [&](int kb, uint8_t *st) {
         const uint8_t *ab = reinterpret_cast<const uint8_t *>(a.a) + (size_t)kb * 128;
-        const uint8_t *ab2 = reinterpret_cast<const uint8_t *>(a.a2) + (size_t)kb * 128;
 #pragma unroll
         for (int j = 0; j < Lo::arun; ++j)
             dma16(ab, aoff[j], lds_addr(st + Lo::A + (wave * Lo::arun + j) * 1024));
-#pragma unroll
-        for (int j = 0; j < Lo::arun; ++j)
-            dma16(ab2, aoff[j], lds_addr(st + Lo::A2 + (wave * Lo::arun + j) * 1024));
         dma16(cbase + (size_t)kb * 32, coff, lds_addr(st + Lo::C + wave * 1024));
         dma4(sbase + (size_t)kb * 4, soff, lds_addr(st + Lo::S + wave * 256));
     };
@@ -321,21 +333,14 @@ __global__ __launch_bounds__(DnLayout<NW>::threads, OCC) void gemm_down_nvfp4_ke
     auto compute = [&](const uint8_t *st, int) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 ah[4], al[4];
+            f16x8 ah[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int r = wm * 64 + mt * 16 + (lane & 15);
-                ah[mt] = a_op(st + Lo::A, r, ks, lane);
-                al[mt] = a_op(st + Lo::A2, r, ks, lane);
-            }
+            for (int mt = 0; mt < 4; ++mt) ah[mt] = a_op<f16x8>(st + Lo::A, wm * 64 + mt * 16 + (lane & 15), ks, lane);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                const bf16x8 b = b_op(st + Lo::C, st + Lo::S, wn * 64 + nt * 16 + (lane & 15), ks, lane);
+                const f16x8 b = b_op16(st + Lo::C, st + Lo::S, wn * 64 + nt * 16 + (lane & 15), ks, lane);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    acc[mt][nt] = mfma_bf16(ah[mt], b, acc[mt][nt]);
-                    acc[mt][nt] = mfma_bf16(al[mt], b, acc[mt][nt]);
-                }
+                for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_f16(ah[mt], b, acc[mt][nt]);
             }
         }
     };
@@ -363,14 +368,23 @@ constexpr int GU_W = 4, GU_NST = 3, GU_OCC = 2, DN_NW = 2, DN_NST = 2, DN_OCC = 
 static_assert(GU_OCC * GU_NST * GuLayout<GU_W>::STAGE <= 160 * 1024, "gate/up stages exceed LDS");
 static_assert(DN_OCC * DN_NST * DnLayout<DN_NW>::STAGE <= 160 * 1024, "down stages exceed LDS");
 
+// 2^-k for the FP16 h: |silu(gc)| <= max(L, 0.28) and |uc| <= L, so |h| * 2^-k
+// stays at or below 32768 (FP16's largest finite value is 65504)
+int h16_shift(float limit)
+{
+    const double bound = (limit > 0.28f ? (double)limit : 0.28) * (double)limit;
+    int k = 0;
+    while (k < 100 && bound > std::ldexp(32768.0, k)) ++k;
+    return k;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_gateup_nvfp4(const uint16_t *x, const int32_t *sorted_token,
                                     const GemvBankDev &gate, const GemvBankDev &up,
                                     const int32_t *offsets, const int4 *tiles,
                                     const int32_t *ntiles, int32_t tmax, int32_t hidden,
-                                    int32_t inter, float limit, uint16_t *hhi, uint16_t *hlo,
-                                    hipStream_t st)
+                                    int32_t inter, float limit, uint16_t *h16, hipStream_t st)
 {
     using Lo = GuLayout<GU_W>;
     if (inter % Lo::cols || hidden % KS) return hipErrorInvalidValue;
@@ -380,24 +394,26 @@ hipError_t launch_gemm_gateup_nvfp4(const uint16_t *x, const int32_t *sorted_tok
     a.s0 = (const uint8_t *)gate.scales; a.s1 = (const uint8_t *)up.scales;
     a.g0 = gate.scale2; a.g1 = up.scale2;
     a.offsets = offsets; a.tiles = tiles; a.ntiles = ntiles;
-    a.hhi = hhi; a.hlo = hlo; a.K = hidden; a.N = inter; a.ntn = inter / Lo::cols; a.limit = limit;
+    a.h = h16; a.K = hidden; a.N = inter; a.ntn = inter / Lo::cols; a.limit = limit;
+    a.hscale = std::ldexp(1.0f, -h16_shift(limit));
     hipLaunchKernelGGL((gemm_gateup_nvfp4_kernel<GU_W, GU_NST, GU_OCC>), dim3((unsigned)(tmax * a.ntn)),
                        dim3(Lo::threads), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_down_nvfp4(const uint16_t *hhi, const uint16_t *hlo, const GemvBankDev &down,
+hipError_t launch_gemm_down_nvfp4(const uint16_t *h16, const GemvBankDev &down,
                                   const int32_t *offsets, const int4 *tiles, const int32_t *ntiles,
-                                  int32_t tmax, int32_t hidden, int32_t inter, float *y,
+                                  int32_t tmax, int32_t hidden, int32_t inter, float limit, float *y,
                                   hipStream_t st)
 {
     using Lo = DnLayout<DN_NW>;
     if (hidden % Lo::cols || inter % KS) return hipErrorInvalidValue;
     NvGemmArgs a{};
-    a.a = hhi; a.a2 = hlo;
+    a.a = h16;
     a.c0 = down.codes; a.s0 = (const uint8_t *)down.scales; a.g0 = down.scale2;
     a.offsets = offsets; a.tiles = tiles; a.ntiles = ntiles;
     a.y = y; a.K = inter; a.N = hidden; a.ntn = hidden / Lo::cols;
+    a.hscale = std::ldexp(1.0f, h16_shift(limit));
     hipLaunchKernelGGL((gemm_down_nvfp4_kernel<DN_NW, DN_NST, DN_OCC>), dim3((unsigned)(tmax * a.ntn)),
                        dim3(Lo::threads), 0, st, a);
     return hipGetLastError();

@@ -163,9 +163,9 @@ bool gemm_dims_ok(int64_t M, int64_t S, int32_t hidden, int32_t inter, int32_t e
            S * inter * elem_bytes < (int64_t(1) << 31);
 }
 
-// Scratch of the bf16 GEMM tier: h hi and h lo bf16 [S][inter], the tiles.
+// Scratch of the 16-bit GEMM tier: h FP16 [S][inter], the tiles.
 struct GemmA16Scratch {
-    uint16_t *hhi, *hlo;
+    uint16_t *h16;
     int4 *tiles;
     int32_t *ntiles;
 };
@@ -173,16 +173,14 @@ struct GemmA16Scratch {
 size_t gemm_a16_scratch_bytes(int64_t S, int32_t E, int32_t inter)
 {
     const int64_t tmax = gemm_max_tiles((int32_t)S, E);
-    return 2 * moe::align256(2 * (size_t)(S * inter)) +
-           moe::align256(sizeof(int4) * (size_t)tmax) + 256;
+    return moe::align256(2 * (size_t)(S * inter)) + moe::align256(sizeof(int4) * (size_t)tmax) + 256;
 }
 
 GemmA16Scratch carve_gemm_a16(char *p, int64_t S, int32_t E, int32_t inter)
 {
     GemmA16Scratch g;
     const int64_t tmax = gemm_max_tiles((int32_t)S, E);
-    g.hhi = (uint16_t *)p;  p += moe::align256(2 * (size_t)(S * inter));
-    g.hlo = (uint16_t *)p;  p += moe::align256(2 * (size_t)(S * inter));
+    g.h16 = (uint16_t *)p;  p += moe::align256(2 * (size_t)(S * inter));
     g.tiles = (int4 *)p;    p += moe::align256(sizeof(int4) * (size_t)tmax);
     g.ntiles = (int32_t *)p;
     return g;
@@ -397,11 +395,11 @@ static moe_status_t expert_ffn(const moe_bank_t *gate, const moe_bank_t *up, con
         if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: tile schedule launch");
         stage_mark(1, s);
         e = launch_gemm_gateup_nvfp4(x_bf16, r.sorted_token, bg, bu, r.offsets, gs.tiles, gs.ntiles,
-                                     tmax, hidden, inter, limit, gs.hhi, gs.hlo, s);
+                                     tmax, hidden, inter, limit, gs.h16, s);
         if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: gate/up GEMM launch");
         stage_mark(2, s);
-        e = launch_gemm_down_nvfp4(gs.hhi, gs.hlo, bd, r.offsets, gs.tiles, gs.ntiles, tmax, hidden,
-                                   inter, y_packed, s);
+        e = launch_gemm_down_nvfp4(gs.h16, bd, r.offsets, gs.tiles, gs.ntiles, tmax, hidden, inter,
+                                   limit, y_packed, s);
         if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: down GEMM launch");
         stage_mark(3, s);
         return MOE_OK;

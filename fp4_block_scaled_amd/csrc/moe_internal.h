@@ -116,17 +116,17 @@ hipError_t launch_gemm_down(const uint8_t *hq, const float *hs, const uint8_t *d
                             const int32_t *ntiles, int32_t tmax, int32_t hidden, int32_t inter,
                             float *y, hipStream_t st);
 
-// bf16 MFMA GEMM tier (NVFP4 banks, wide M): gate/up with SwiGLU writes h as
-// a pair of bf16 arrays (hi, lo) [S][inter]; down reads both.
+// 16-bit MFMA GEMM tier (NVFP4 banks, wide M): gate/up (bf16 x) with SwiGLU
+// writes h as FP16 [S][inter], scaled by a power of two picked from the clamp
+// limit; down (FP16 MFMA) reads it and takes the same limit to undo the scale.
 hipError_t launch_gemm_gateup_nvfp4(const uint16_t *x, const int32_t *sorted_token,
                                     const GemvBankDev &gate, const GemvBankDev &up,
                                     const int32_t *offsets, const int4 *tiles,
                                     const int32_t *ntiles, int32_t tmax, int32_t hidden,
-                                    int32_t inter, float limit, uint16_t *hhi, uint16_t *hlo,
-                                    hipStream_t st);
-hipError_t launch_gemm_down_nvfp4(const uint16_t *hhi, const uint16_t *hlo, const GemvBankDev &down,
+                                    int32_t inter, float limit, uint16_t *h16, hipStream_t st);
+hipError_t launch_gemm_down_nvfp4(const uint16_t *h16, const GemvBankDev &down,
                                   const int32_t *offsets, const int4 *tiles, const int32_t *ntiles,
-                                  int32_t tmax, int32_t hidden, int32_t inter, float *y,
+                                  int32_t tmax, int32_t hidden, int32_t inter, float limit, float *y,
                                   hipStream_t st);
 
 // shared and residual ([M][hidden] FP32) may be null; each is added after

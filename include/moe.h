@@ -80,13 +80,15 @@ enum {
     /* Not a tier of moe_expert_ffn: the workspace mode of moe_layer_fused
      * (route pack, gate/up, SwiGLU, down and combine in one launch). */
     MOE_MODE_FUSED = 3,
-    /* Grouped bf16 MFMA GEMM over expert-sorted rows for NVFP4 banks: the
-     * pages' W4A16 form (bf16 activations as given; "spark_model
+    /* Grouped 16-bit MFMA GEMM over expert-sorted rows for NVFP4 banks: the
+     * pages' W4A16 form (16-bit activations; "spark_model
      * glm5next_mlp/forward.rs", fn w4a16_gemv and its batched variant) at
-     * prefill widths.  Each E2M1 code times its E4M3 group scale is exact in
-     * bf16; scale_2 multiplies the FP32 sums.  h is kept as a bf16 pair
-     * (hi, lo) whose sum is the FP32 h to about 2^-16.  NVFP4 banks only;
-     * scales must be 4-byte aligned. */
+     * prefill widths.  gate/up takes x as the bf16 it is; h passes between
+     * the projections as FP16 (rounded once from the FP32 SwiGLU, times a
+     * power of two picked from the clamp limit so it cannot overflow).  Each
+     * E2M1 code times its E4M3 group scale is exact in bf16 and in FP16;
+     * scale_2 multiplies the FP32 sums.  NVFP4 banks only; scales must be
+     * 4-byte aligned. */
     MOE_MODE_GEMM_A16 = 4
 };
 

@@ -86,12 +86,12 @@ def test_auto_workspace_sizes_the_tier_each_format_runs():
     from fp4_block_scaled_amd import binding as B
     L = B.lib
     # NVFP4 above MOE_GEMV_MAX_M tokens runs the bf16 GEMM tier: route region
-    # + max(GEMV scratch for 16 tokens, h hi + h lo bf16 [S][I] + tiles + count)
+    # + max(GEMV scratch for 16 tokens, h FP16 [S][I] + tiles + count)
     M, k, E, H, I = 20, 8, 20, 1024, 512
     S = M * k
     tmax = min(S, E) + (S + 127) // 128
     route = a256(4 * (E + 1)) + 3 * a256(4 * S) + a256(4 * min(S, E)) + a256(8)
-    a16 = 2 * a256(2 * S * I) + a256(16 * tmax) + 256
+    a16 = a256(2 * S * I) + a256(16 * tmax) + 256
     assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_GEMM_A16) == route + a16
     gemv16 = a256(4 * 16 * k * I)
     assert L.moe_workspace_bytes(M, k, E, H, I, B.MOE_W_NVFP4_B16, B.MOE_MODE_AUTO) == \
