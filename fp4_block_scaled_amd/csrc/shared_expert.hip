@@ -156,8 +156,12 @@ int pick_rows(int32_t M, int rows, int rows_per_block_r1, int rmax)
 {
     if (M > 1) return rmax;
     static int cus = 0;
-    if (!cus && (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess || cus < 1))
-        cus = 256;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+    }
     int best = 1, best_rows = 1 << 30;
     for (int r = 1; r <= rmax; r *= 2) {
         const int per = rows_per_block_r1 * r;
