@@ -366,7 +366,7 @@ TRAFFIC = {
     "prefill_e4m3_m4096": {"kernel": "gemm_gateup", "files": ["gemm_fp8.hip", "gemm_common.h", "moe_device.h"],
         "src": "e7bd3c69fc01c3df46ff9d1401442f7fe0174e2455c8b818", "fetch_kib": 4022574, "write_kib": 68917},
     "nvfp4_m4096": {"kernel": "gemm_gateup_nvfp4", "files": ["gemm_nvfp4.hip", "gemm_common.h", "moe_device.h"],
-        "src": "bf39c323f43a847146ff9d1401442f7fe0174e2455c8b818", "fetch_kib": 2153835, "write_kib": 98304},
+        "src": "268b195ef0d0f1e646ff9d1401442f7fe0174e2455c8b818", "fetch_kib": 2153835, "write_kib": 98304},
     "verify_e4m3_m8": {"kernel": "gemv_gateup", "files": ["gemv_e4m3.hip", "fused_common.h", "moe_device.h"],
         "src": "cde11db9bf57e724d7277bb1a4b625a5e0174e2455c8b818", "fetch_kib": 646018, "write_kib": 514},
     "nvfp4_m16": {"kernel": "gemv_gateup", "files": ["gemv_nvfp4.hip", "fused_common.h", "moe_device.h"],

@@ -17,13 +17,15 @@
 //
 // h between the projections is a 16-bit activation, as in the W4A16 form,
 // held as FP16 rather than bf16: the gate/up epilogue computes h = SwiGLU(g,
-// u) in FP32 and rounds h * 2^-k to FP16 (RNE), with 2^-k chosen from the
-// clamp limit so that |h| * 2^-k stays at or below 32768 (k = 0 for any limit
-// up to 181).  FP16's 11-bit significand keeps the layer's output within about
-// 2e-4 relative L2 of the exact one, where a bf16 h would cost about 1e-3.
-// The down GEMM decodes its NVFP4 weights to FP16, exactly (a product of at
-// most 6 significant bits between 2^-10 and 2688), runs the FP16 MFMA once,
-// and multiplies the FP32 sums by scale_2 * 2^k.
+// u) in FP32 and rounds h * 2^-k to FP16 (RNE), with the power of two chosen
+// from the clamp limit so that the bound on |h| lands in (16384, 32768]: no
+// overflow, and h keeps FP16's full 11-bit significand down to 2^-15 of its
+// bound instead of falling into FP16's subnormals under a small limit (k = -9
+// for the limit 7).  FP16 then keeps the layer's output within about 2e-4
+// relative L2 of the exact one, where a bf16 h would cost about 1e-3.  The
+// down GEMM decodes its NVFP4 weights to FP16, exactly (a product of at most
+// 6 significant bits between 2^-10 and 2688), runs the FP16 MFMA once, and
+// multiplies the FP32 sums by 2^k (exact), then by scale_2.
 //
 // Kernels (tiles from gemm_tiles_kernel: 128 expert-sorted rows each):
 //   gemm_gateup_nvfp4_kernel  one block = 128 rows x 64 h columns: 64 gate and
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(DnLayout<NW>::threads, OCC) void gemm_down_nvfp4_ke
     const int rows = moe::uniform(min(TM, a.offsets[e + 1] - p0));
     const int K = a.K, N = a.N, KB = K / KS;
     const int n0 = nb * Lo::cols;
-    const float sd = a.g0[e] * a.hscale;           // scale_2 x 2^k
+    const float sd = a.g0[e], hk = a.hscale;       // scale_2, 2^k
 
     uint32_t aoff[Lo::arun];
 #pragma unroll
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(DnLayout<NW>::threads, OCC) void gemm_down_nvfp4_ke
             if (r < rows) {
                 float *yr = a.y + (size_t)(p0 + r) * N + n0 + wn * 64 + (lane & 15);
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) yr[nt * 16] = acc[mt][nt][i] * sd;
+                for (int nt = 0; nt < 4; ++nt) yr[nt * 16] = acc[mt][nt][i] * hk * sd;
             }
         }
 }
@@ -368,13 +370,15 @@ constexpr int GU_W = 4, GU_NST = 3, GU_OCC = 2, DN_NW = 2, DN_NST = 2, DN_OCC = 
 static_assert(GU_OCC * GU_NST * GuLayout<GU_W>::STAGE <= 160 * 1024, "gate/up stages exceed LDS");
 static_assert(DN_OCC * DN_NST * DnLayout<DN_NW>::STAGE <= 160 * 1024, "down stages exceed LDS");
 
-// 2^-k for the FP16 h: |silu(gc)| <= max(L, 0.28) and |uc| <= L, so |h| * 2^-k
-// stays at or below 32768 (FP16's largest finite value is 65504)
+// k for the FP16 h: |silu(gc)| <= max(L, 0.28) and |uc| <= L, so with the
+// bound in (16384, 32768] after the factor 2^-k, |h| * 2^-k stays below FP16's
+// largest finite value (65504) with room for the rounding of the FP32 SwiGLU
 int h16_shift(float limit)
 {
     const double bound = (limit > 0.28f ? (double)limit : 0.28) * (double)limit;
     int k = 0;
     while (k < 100 && bound > std::ldexp(32768.0, k)) ++k;
+    while (k > -100 && bound <= std::ldexp(16384.0, k)) --k;
     return k;
 }
 

@@ -85,7 +85,8 @@ enum {
      * glm5next_mlp/forward.rs", fn w4a16_gemv and its batched variant) at
      * prefill widths.  gate/up takes x as the bf16 it is; h passes between
      * the projections as FP16 (rounded once from the FP32 SwiGLU, times a
-     * power of two picked from the clamp limit so it cannot overflow).  Each
+     * power of two picked from the clamp limit so that it neither overflows
+     * nor falls into FP16's subnormals).  Each
      * E2M1 code times its E4M3 group scale is exact in bf16 and in FP16;
      * scale_2 multiplies the FP32 sums.  NVFP4 banks only; scales must be
      * 4-byte aligned. */

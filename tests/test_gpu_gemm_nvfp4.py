@@ -9,7 +9,7 @@ a power-of-two factor picked from the clamp limit.  The layer's tolerance
 oracle's plain FP64 layer, on the whole output and on every packed y row:
 reduced shapes with several full and partial 128-row tiles per expert and K
 loops of 4 to 20 steps, one expert taking every token, invalid ids, h past
-FP16's range under a large limit, the tier forced at a handful of tokens
+FP16's largest value and below its smallest normal one, the tier forced at a handful of tokens
 (against the GEMV tier too), and the prefill size M=4096 on sampled
 tokens."""
 import gc
@@ -89,24 +89,29 @@ def test_a16_tier_skewed_and_invalid_ids():
     run_a16(case, ids, w, label="skewed")
 
 
-def test_a16_tier_large_limit_keeps_h_in_fp16_range():
-    """Clamp limit 3000 and x times 1024 (exact in bf16): about 2.6 % of h
-    lies past FP16's largest finite value 65504 (max |h| about 2.5e5).  The
-    tier scales h by 2^-9 before the FP16 rounding and the down GEMM undoes
-    it, so the layer still meets the tolerance."""
+@pytest.mark.parametrize("limit,xmul", [(3000.0, 1024), (1e-5, 1)], ids=["past_fp16_max", "below_fp16_normal"])
+def test_a16_tier_h_range_factor(limit, xmul):
+    """h far outside FP16's normal range.  Clamp limit 3000 with x times 1024
+    (exact in bf16): about 2.6 % of h lies past FP16's largest finite value
+    65504 (max |h| about 3e5).  Clamp limit 1e-5: every |h| lies below FP16's
+    smallest normal value 2^-14 (max |h| about 2.4e-6), where FP16 holds only a
+    few significant bits.  The tier scales h by a power of two before the FP16
+    rounding (2^-9 and 2^33 here) and the down GEMM undoes it, so the layer
+    meets the tolerance either way."""
     base = workloads.WORKLOADS["nvfp4_m4096"]
-    wl = workloads.with_shape(base, name="nv_big_h", hidden=512, inter=256, experts=6, top_k=2,
-                              M=64, limit=3000.0)
+    wl = workloads.with_shape(base, name=f"nv_h_range_{limit}", hidden=512, inter=256, experts=6,
+                              top_k=2, M=64, limit=limit)
     case = get_case(wl)
-    case.x.mul_(1024)
+    case.x.mul_(xmul)
     ids, w, _ = workloads.make_routes(wl, 0)
     used = np.unique(ids[ids >= 0])
     hb = [host_bank(b, used) for b in case.banks]
     h = oracle.expert_slots(hb[0], hb[1], hb[2], x_bits(case.x), np.searchsorted(used, ids).astype(np.int32),
                             wl.limit, False, want=("h",))["h"]
-    print(f"A16 tier large h: max |h| {np.abs(h).max():.3e}", flush=True)
-    assert np.abs(h).max() > 65504.0
-    run_a16(case, ids, w, label="large h")
+    hmax = float(np.abs(h).max())
+    print(f"A16 tier h range, limit {limit}: max |h| {hmax:.3e}", flush=True)
+    assert hmax > 65504.0 if limit > 1 else 0.0 < hmax < 2.0 ** -14
+    run_a16(case, ids, w, label=f"h range {limit}")
 
 
 @pytest.mark.parametrize("M", [1, 5, 16])
