@@ -10,8 +10,9 @@ oracle's plain FP64 layer, on the whole output and on every packed y row:
 reduced shapes with several full and partial 128-row tiles per expert and K
 loops of 4 to 20 steps, one expert taking every token, invalid ids, h past
 FP16's largest value and below its smallest normal one, the tier forced at a handful of tokens
-(against the GEMV tier too), and the prefill size M=4096 on sampled
-tokens."""
+(against the GEMV tier too), and the prefill size M=4096 on at least 128
+tokens (the first and last rows of every tile of the heaviest experts, ragged
+last tiles of lighter ones, random tokens)."""
 import gc
 
 import numpy as np
@@ -130,19 +131,40 @@ def test_a16_tier_forced_at_few_tokens_matches_gemv(M):
     check_fp(out[:M], gemv[:M], f"A16 vs GEMV M{M}", max_frac=1e-3, rel_l2=5e-4)
 
 
+def a16_prefill_tokens(ids, tabs, E, rng):
+    """Tokens whose rows are the first and last rows of every 128-row tile of
+    the five heaviest experts, the last rows of the ragged last tile of five
+    lighter ones (at most 24 each), the first and last token, and random
+    tokens, at least 128 in all."""
+    off = tabs["expert_offsets"]
+    st = tabs["sorted_token"]
+    counts = np.diff(off[:E + 1])
+    order = np.argsort(-counts, kind="stable")
+    toks = {0, ids.shape[0] - 1}
+    for e in order[:5]:
+        n = int(counts[e])
+        for a in range(0, n, 128):
+            toks.add(int(st[off[e] + a]))
+            toks.add(int(st[off[e] + min(a + 127, n - 1)]))
+    lighter = [e for e in order[5:] if counts[e] % 128]
+    for e in rng.choice(lighter, 5, replace=False):
+        n = int(counts[e])
+        for r in range(n - n % 128, n)[-24:]:
+            toks.add(int(st[off[e] + r]))
+    while len(toks) < 128:
+        toks.add(int(rng.integers(0, ids.shape[0])))
+    return np.array(sorted(toks))
+
+
 def test_a16_tier_prefill_full_size_sampled_tokens():
     wl = workloads.WORKLOADS["nvfp4_m4096"]
     case = get_case(wl)
     ids, w, info = workloads.make_routes(wl, 0)
-    counts = np.bincount(ids.ravel(), minlength=wl.experts)
-    heavy = int(np.argmax(counts))
-    rng = np.random.default_rng(11)
-    toks = set(rng.choice(wl.M, 5, replace=False).tolist())
-    toks |= {0, wl.M - 1}
-    toks.add(int(np.nonzero((ids == heavy).any(axis=1))[0][-1]))
-    tokens = np.array(sorted(toks))
-    print(f"NVFP4 prefill M=4096: max load {info['max_load']} (expert {heavy}), mean "
-          f"{info['mean_load']:.1f}, checking tokens {tokens.tolist()}", flush=True)
+    # the route tables decide which tokens sit at tile borders
+    _, _, tabs, _ = case.run(ids, w, B.MOE_MODE_AUTO)
+    tokens = a16_prefill_tokens(ids, tabs, wl.experts, np.random.default_rng(11))
+    print(f"NVFP4 prefill M=4096: max load {info['max_load']}, mean {info['mean_load']:.1f}; "
+          f"checking {len(tokens)} tokens end to end", flush=True)
     out = run_a16(case, ids, w, tokens=tokens, label="nvfp4 prefill", mode=B.MOE_MODE_AUTO)
     # run to run bit identity
     out2, _, _, _ = case.run(ids, w, B.MOE_MODE_AUTO)
