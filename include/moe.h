@@ -46,7 +46,7 @@ enum {
     MOE_ERR_FORMAT = 3,      /* weight formats disagree / scale2 misuse      */
     MOE_ERR_WORKSPACE = 4,   /* ws_bytes below moe_workspace_bytes()         */
     MOE_ERR_HIP = 5,         /* a HIP launch failed                          */
-    MOE_ERR_UNSUPPORTED = 6  /* valid request this build does not serve      */
+    MOE_ERR_UNSUPPORTED = 6  /* valid request the library does not serve    */
 };
 
 /* Weight formats. */
