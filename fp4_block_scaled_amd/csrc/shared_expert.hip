@@ -103,25 +103,34 @@ __global__ __launch_bounds__(kThreads) void shared_gateup_kernel(const uint16_t 
     }
 }
 
-// NJ = W / 512 loads of 16 bytes per lane and row; R rows per wave
-template <int NJ, int R>
+// NJ = W / 512 loads of 16 bytes per lane and row; R rows per wave.  LH
+// (one token, one row per wave, where each wave's h reads from L2 are twice
+// its weight bytes): the block's 4 waves share the h row through LDS (W
+// floats of dynamic LDS): 16.6 against 17.1 us for the whole shared expert at
+// H7168 W2048.  With two rows per wave (H6144 W1536) it ran 0.25 us slower.
+template <int NJ, int R, bool LH>
 __global__ __launch_bounds__(kThreads) void shared_down_kernel(const uint16_t *__restrict__ down,
                                                                const float *__restrict__ h,
                                                                int32_t M, int32_t H, int32_t W,
                                                                float *__restrict__ out)
 {
+    extern __shared__ float hsm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = moe::uniform(tid >> 6);
-    const int row0 = (4 * blockIdx.x + wave) * R;
-    if (row0 >= H) return;                           // whole wave (H is a multiple of 4R)
+    const int row0 = (4 * blockIdx.x + wave) * R;    // < H: the grid is H / (4R) blocks
     const uint8_t *rp = reinterpret_cast<const uint8_t *>(moe::uniform_ptr(down) + (size_t)row0 * W);
     uint4 w[R][NJ];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) w[r][j] = load16(rp + (size_t)r * W * 2 + j * 1024 + lane * 16);
+    if constexpr (LH) {
+        for (int i = tid * 4; i < W; i += kThreads * 4)
+            *reinterpret_cast<float4 *>(hsm + i) = *reinterpret_cast<const float4 *>(h + i);
+        __syncthreads();
+    }
     for (int t = 0; t < M; ++t) {
-        const float *hp = h + (size_t)t * W;
+        const float *hp = LH ? hsm : h + (size_t)t * W;
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.0f;
@@ -192,8 +201,12 @@ template <int NJ, int R>
 void down_launch_r(const uint16_t *down, const float *h, int32_t M, int32_t H, int32_t W, float *out,
                    hipStream_t st)
 {
-    hipLaunchKernelGGL((shared_down_kernel<NJ, R>), dim3((unsigned)(H / (4 * R))), dim3(kThreads), 0, st,
-                       down, h, M, H, W, out);
+    if (M == 1 && R == 1)
+        hipLaunchKernelGGL((shared_down_kernel<NJ, R, true>), dim3((unsigned)(H / (4 * R))), dim3(kThreads),
+                           (size_t)W * 4, st, down, h, M, H, W, out);
+    else
+        hipLaunchKernelGGL((shared_down_kernel<NJ, R, false>), dim3((unsigned)(H / (4 * R))), dim3(kThreads),
+                           0, st, down, h, M, H, W, out);
 }
 
 template <int NJ>
